@@ -1,0 +1,168 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ *               (libssmscan.so).
+ *
+ * Sources (web pages; cited by title and section/equation):
+ *   [SPEC]      "ТЕХНИЧЕСКОЕ ЗАДАНИЕ: Реализовать selective scan (Mamba)"
+ *               (aivaro.ru practice task 53)
+ *   [EXPLAINED] "Mamba CUDA 实现解析" (mamba-code-explained README)
+ *   [BLELLOCH]  "从顺序到并行用PyTorch实现Blelloch算法加速Mamba状态空间模型"
+ *               (lpnh.cn news 821471)
+ *   [CUTILE]    "Прорыв в оптимизации SSM-моделей" (aikraft.ru digest of the
+ *               cuTile Mamba-2 forward kernels)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to dense, contiguous,
+ *     row-major memory owned by the caller.  The library never frees them
+ *     and keeps no reference after the enqueued work completes.
+ *   - Calls only enqueue work on `stream` and return; they never
+ *     synchronise the host.  Results are ready when the stream reaches them.
+ *   - Outputs must not alias inputs.
+ *   - Errors are reported by status code only; nothing is thrown across the
+ *     ABI.  All argument checks run before any HIP call, so a rejected call
+ *     has no side effect.  ssm_last_error_message() describes the most
+ *     recent failure on the calling thread.
+ *   - Every tensor base pointer must be 16-byte aligned (any allocation
+ *     from hipMalloc or PyTorch is).
+ *   - Floating-point inputs are either all float32 or all bfloat16
+ *     (`in_dtype`), except the parameters documented as float32.
+ *     Arithmetic is float32 throughout (bf16 inputs are widened exactly).
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle type (identical to the typedef in the HIP headers). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = 1, /* bad pointer, size, alignment or enum value */
+  SSM_ERR_UNSUPPORTED = 2, /* valid request outside the documented limits,
+                              or a device that is not gfx950 */
+  SSM_ERR_HIP = 3          /* a HIP runtime call failed */
+} ssm_status;
+
+typedef enum ssm_dtype {
+  SSM_F32 = 0,  /* IEEE float32 */
+  SSM_BF16 = 1  /* bfloat16 (upper half of a float32) */
+} ssm_dtype;
+
+typedef struct ssm_scan_context *ssm_handle;
+
+/* Static text for a status code (never NULL). */
+const char *ssm_status_string(ssm_status status);
+
+/* Human-readable reason for the most recent non-OK status returned on the
+ * calling thread ("" if none).  Valid until the next call on this thread. */
+const char *ssm_last_error_message(void);
+
+/* Create a handle bound to HIP device `hip_device`.  Reads the device
+ * properties once, rejects non-gfx950 devices with SSM_ERR_UNSUPPORTED and
+ * fixes the per-shape launch table.  Allocates no per-call memory.  The
+ * handle is immutable afterwards and may be used from several threads and
+ * streams at once.  *out is set to NULL on failure. */
+ssm_status ssm_scan_create(ssm_handle *out, int hip_device);
+
+/* Destroy a handle (NULL is accepted).  The handle owns no device memory,
+ * so destroying it while work enqueued with it is still in flight is safe. */
+ssm_status ssm_scan_destroy(ssm_handle handle);
+
+/*
+ * Mamba-1 selective scan, forward ([SPEC] Stage 1 items 3-4; [EXPLAINED]
+ * eqs. (4)-(12); [BLELLOCH] section 4.1).  For every row (b, d) and time t,
+ * with the state h[b,d,:] starting at zero:
+ *
+ *   delta_t = delta[b,d,t] + delta_bias[d]       (bias optional)
+ *   delta_t = softplus(delta_t)                   if delta_softplus != 0
+ *   h[n]    = exp(delta_t * A[d,n]) * h[n] + delta_t * B[b,n,t] * u[b,d,t]
+ *   y[b,d,t] = sum_n C[b,n,t] * h[n]  +  D[d] * u[b,d,t]   (D optional)
+ *   y[b,d,t] *= silu(z[b,d,t])                    (z optional)
+ *   last_state[b,d,n] = h[n] after t = seqlen-1   (optional output)
+ *
+ * The recurrence is evaluated as an associative scan over (a, v) pairs with
+ * the combine operator of [EXPLAINED] eq. (10); the result equals the plain
+ * sequential loop up to float32 rounding.
+ *
+ * Layouts (row-major):
+ *   u, delta, z, y : [batch, dim, seqlen]      element type in_dtype
+ *   B, C           : [batch, dstate, seqlen]   element type in_dtype
+ *   A              : [dim, dstate]             float32
+ *   D, delta_bias  : [dim]                     float32
+ *   last_state     : [batch, dim, dstate]      float32
+ * Nullable: D, z, delta_bias, last_state.  y has the input element type.
+ *
+ * Limits: batch, dim, seqlen >= 1; 1 <= dstate <= 64 ([SPEC] Definition of
+ * Done asks for documented limits; there is no seqlen limit).  batch*dim
+ * and seqlen must each fit in 2^31-1.  Sizes <= 0 return
+ * SSM_ERR_INVALID_ARG without touching the device ([SPEC] Definition of
+ * Done: batch=0 must not crash).  The initial state is zero.
+ */
+ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void *u,
+                                  const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D,
+                                  const void *z, const float *delta_bias,
+                                  int delta_softplus, void *y,
+                                  float *last_state, int64_t batch,
+                                  int64_t dim, int64_t dstate, int64_t seqlen,
+                                  ssm_dtype in_dtype, hipStream_t stream);
+
+/*
+ * Workspace size in bytes needed by ssd_chunk_scan_fwd for these sizes
+ * (the caller allocates it, so the library never allocates device memory).
+ * Returns SSM_ERR_INVALID_ARG / SSM_ERR_UNSUPPORTED for sizes that
+ * ssd_chunk_scan_fwd would reject.
+ */
+ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch,
+                                         int64_t seqlen, int64_t nheads,
+                                         int64_t headdim, int64_t dstate,
+                                         int64_t ngroups, int64_t chunk_size,
+                                         size_t *bytes);
+
+/*
+ * Mamba-2 (SSD) chunked scan, forward ([CUTILE]: chunk cumulative sums of
+ * the log-decay, chunk states advanced with the jump formula, fused output
+ * with causal mask and skip connection).  For every (b, head h) with group
+ * g = h / (nheads/ngroups) and state S[b,h,:,:] starting at zero:
+ *
+ *   dt_t  = dt[b,t,h] + dt_bias[h];  softplus if dt_softplus != 0
+ *   S[p,n] = exp(dt_t * A[h]) * S[p,n] + dt_t * x[b,t,h,p] * B[b,t,g,n]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] * S[p,n] + D[h] * x[b,t,h,p]
+ *   final_state[b,h,p,n] = S[p,n] after t = seqlen-1
+ *
+ * computed chunk by chunk (chunk_size tokens) with matrix products.
+ *
+ * Layouts (row-major):
+ *   x, y        : [batch, seqlen, nheads, headdim]   in_dtype
+ *   dt          : [batch, seqlen, nheads]            in_dtype
+ *   B, C        : [batch, seqlen, ngroups, dstate]   in_dtype
+ *   A, D, dt_bias : [nheads]                         float32
+ *   final_state : [batch, nheads, headdim, dstate]   float32
+ * Nullable: D, dt_bias, final_state.  `workspace` must hold at least
+ * ssd_chunk_scan_workspace_size() bytes (16-byte aligned device memory,
+ * caller-owned, contents need not be initialised; it is overwritten).
+ *
+ * Limits: nheads % ngroups == 0; chunk_size in {64, 128, 256};
+ * headdim in {32, 64, 128}; dstate in {16, 32, 64, 128, 256}.
+ */
+ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C,
+                              const float *D, const float *dt_bias,
+                              int dt_softplus, void *y, float *final_state,
+                              void *workspace, size_t workspace_bytes,
+                              int64_t batch, int64_t seqlen, int64_t nheads,
+                              int64_t headdim, int64_t dstate, int64_t ngroups,
+                              int64_t chunk_size, ssm_dtype in_dtype,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

@@ -1,0 +1,155 @@
+"""fp64 CPU oracle for the Mamba selective scan (Mamba-1) and its SSD form (Mamba-2).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only users.  The product path (the HIP library and
+its Python binding) never imports this package, and this package imports
+nothing from the product path.
+
+The arithmetic lives in ``ssm_oracle.c`` (plain C, double precision, one
+sequential time loop per independent row).  This module only builds/loads it
+and marshals numpy arrays.  Sources are cited in that file's header.
+
+Build: ``python -m oracle.build`` or ``oracle.build_library()`` (gcc, -O2, no
+fast-math, so every operation is IEEE double).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "libssm_oracle.so")
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build_library() -> str:
+    """Compile ssm_oracle.c into libssm_oracle.so next to it (always rebuilds)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build_library()
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_selective_scan_f64.restype = ctypes.c_int
+    lib.oracle_selective_scan_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_ssd_f64.restype = ctypes.c_int
+    lib.oracle_ssd_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _f32(a, shape=None):
+    """Contiguous float32 view (values must already be exactly float32)."""
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(a, dtype=np.float32)
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {arr.shape}")
+    return arr
+
+
+def _p32(a):
+    return None if a is None else a.ctypes.data_as(_f32p)
+
+
+def default_threads() -> int:
+    return max(1, min(len(os.sched_getaffinity(0)), 64))
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   delta_softplus=True, rows=None, want_y=True,
+                   want_state=True, nthreads=None):
+    """Mamba-1 selective scan in fp64.
+
+    u, delta, z: [batch, dim, seqlen]; A: [dim, dstate]; B, C: [batch, dstate,
+    seqlen]; D, delta_bias: [dim].  ``rows`` optionally restricts the work to
+    flat row indices b*dim+d (outputs then follow that order).
+    Returns (y [nrows, seqlen] or None, last_state [nrows, dstate] or None),
+    both float64; with rows=None, nrows = batch*dim in (b, d) order.
+    """
+    lib = _load()
+    u = _f32(u)
+    batch, dim, seqlen = u.shape
+    dstate = np.asarray(A).shape[1]
+    delta = _f32(delta, (batch, dim, seqlen))
+    A = _f32(A, (dim, dstate))
+    B = _f32(B, (batch, dstate, seqlen))
+    C = _f32(C, (batch, dstate, seqlen))
+    D = _f32(D, (dim,))
+    z = _f32(z, (batch, dim, seqlen))
+    delta_bias = _f32(delta_bias, (dim,))
+    if rows is None:
+        nrows = batch * dim
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.shape[0]
+    y = np.empty((nrows, seqlen), np.float64) if want_y else None
+    st = np.empty((nrows, dstate), np.float64) if want_state else None
+    rc = lib.oracle_selective_scan_f64(
+        _p32(u), _p32(delta), _p32(A), _p32(B), _p32(C), _p32(D), _p32(z),
+        _p32(delta_bias), int(bool(delta_softplus)), batch, dim, dstate, seqlen,
+        None if rows_arr is None else rows_arr.ctypes.data_as(_i64p), nrows,
+        None if y is None else y.ctypes.data_as(_f64p),
+        None if st is None else st.ctypes.data_as(_f64p),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_selective_scan_f64 failed with code {rc}")
+    return y, st
+
+
+def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,
+             want_y=True, want_state=True, nthreads=None):
+    """Mamba-2 (scalar A per head) recurrence in fp64.
+
+    x: [batch, seqlen, nheads, headdim]; dt: [batch, seqlen, nheads];
+    A, D, dt_bias: [nheads]; B, C: [batch, seqlen, ngroups, dstate].
+    Returns (y [batch, seqlen, nheads, headdim], final_state [batch, nheads,
+    headdim, dstate]) as float64 (either may be None).
+    """
+    lib = _load()
+    x = _f32(x)
+    batch, seqlen, nheads, headdim = x.shape
+    B = _f32(B)
+    ngroups, dstate = B.shape[2], B.shape[3]
+    if B.shape[:2] != (batch, seqlen):
+        raise ValueError("B shape mismatch")
+    dt = _f32(dt, (batch, seqlen, nheads))
+    A = _f32(A, (nheads,))
+    C = _f32(C, (batch, seqlen, ngroups, dstate))
+    D = _f32(D, (nheads,))
+    dt_bias = _f32(dt_bias, (nheads,))
+    y = np.empty((batch, seqlen, nheads, headdim), np.float64) if want_y else None
+    st = np.empty((batch, nheads, headdim, dstate), np.float64) if want_state else None
+    rc = lib.oracle_ssd_f64(
+        _p32(x), _p32(dt), _p32(A), _p32(B), _p32(C), _p32(D), _p32(dt_bias),
+        int(bool(dt_softplus)), batch, seqlen, nheads, headdim, dstate, ngroups,
+        None if y is None else y.ctypes.data_as(_f64p),
+        None if st is None else st.ctypes.data_as(_f64p),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_ssd_f64 failed with code {rc}")
+    return y, st
