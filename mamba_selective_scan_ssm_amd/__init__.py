@@ -1,0 +1,230 @@
+"""Python binding of libssmscan.so (the MI355X selective-scan library).
+
+The functions named like the C ABI (``ssm_scan_create``,
+``ssm_selective_scan_fwd``, ``ssd_chunk_scan_workspace_size``,
+``ssd_chunk_scan_fwd``, ...) only marshal arguments: tensors become device
+pointers, sizes come from tensor shapes, and the stream is PyTorch's current
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind.  If the library has not been built, every
+call raises.
+
+``selective_scan_fwd`` and ``ssd_chunk_scan`` are conveniences that also
+allocate the outputs (and the SSD workspace) with PyTorch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssmscan.so")
+
+SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP = 0, 1, 2, 3
+SSM_F32, SSM_BF16 = 0, 1
+
+# Every symbol declared in include/ssm_scan.h.
+EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
+           "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssd_chunk_scan_workspace_size",
+           "ssd_chunk_scan_fwd")
+
+_lib = None
+_lib_lock = threading.Lock()
+_handles: Dict[int, ctypes.c_void_p] = {}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class SsmScanError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} -- {message}")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libssmscan.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mamba_selective_scan_ssm_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.ssm_status_string.restype = ctypes.c_char_p
+        lib.ssm_status_string.argtypes = [ctypes.c_int]
+        lib.ssm_last_error_message.restype = ctypes.c_char_p
+        lib.ssm_last_error_message.argtypes = []
+        lib.ssm_scan_create.restype = ctypes.c_int
+        lib.ssm_scan_create.argtypes = [ctypes.POINTER(_vp), ctypes.c_int]
+        lib.ssm_scan_destroy.restype = ctypes.c_int
+        lib.ssm_scan_destroy.argtypes = [_vp]
+        lib.ssm_selective_scan_fwd.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+            _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_int
+        lib.ssd_chunk_scan_workspace_size.argtypes = [
+            _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssm_status_string(int(status)).decode()
+
+
+ssm_status_string = status_string
+
+
+def ssm_last_error_message() -> str:
+    return load_library().ssm_last_error_message().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SSM_OK:
+        raise SsmScanError(fn, status, ssm_last_error_message())
+
+
+# ---------------------------------------------------------------------------
+# Raw C-ABI mirrors (pointers and sizes)
+# ---------------------------------------------------------------------------
+
+def ssm_scan_create(device: int) -> ctypes.c_void_p:
+    h = _vp()
+    _check("ssm_scan_create", load_library().ssm_scan_create(ctypes.byref(h), int(device)))
+    return h
+
+
+def ssm_scan_destroy(handle) -> None:
+    _check("ssm_scan_destroy", load_library().ssm_scan_destroy(handle))
+
+
+def get_handle(device: int) -> ctypes.c_void_p:
+    """Process-wide handle for a device (created on first use)."""
+    with _lib_lock:
+        h = _handles.get(device)
+    if h is None:
+        h = ssm_scan_create(device)
+        with _lib_lock:
+            _handles.setdefault(device, h)
+            h = _handles[device]
+    return h
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need_cuda_contig(name, t, allow_none=False):
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device) -> int:
+    import torch
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
+                           last_state, handle=None) -> None:
+    """Enqueue the Mamba-1 scan on the current stream (tensor form of the C
+    entry point of the same name; y and last_state are caller-allocated)."""
+    for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
+                         ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
+                         ("delta_bias", delta_bias, True), ("y", y, False),
+                         ("last_state", last_state, True)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssm_selective_scan_fwd(
+        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
+        batch, dim, dstate, seqlen, _dtype_code(u), _stream_ptr(u.device))
+    _check("ssm_selective_scan_fwd", st)
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, return_last_state=True):
+    """Allocating form: returns (y, last_state or None)."""
+    import torch
+    y = torch.empty_like(u)
+    ls = (torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
+                      device=u.device) if return_last_state else None)
+    ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, ls)
+    return y, ls
+
+
+def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                  chunk_size, handle=None, device: int = 0) -> int:
+    if handle is None:
+        handle = get_handle(device)
+    n = ctypes.c_size_t()
+    st = load_library().ssd_chunk_scan_workspace_size(
+        handle, batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, ctypes.byref(n))
+    _check("ssd_chunk_scan_workspace_size", st)
+    return int(n.value)
+
+
+def ssd_chunk_scan_fwd(x, dt, A, B, C, D, dt_bias, dt_softplus, y, final_state, workspace,
+                       chunk_size, handle=None) -> None:
+    """Enqueue the Mamba-2 chunked scan on the current stream (tensor form of
+    the C entry point; y, final_state and workspace are caller-allocated)."""
+    for name, t, opt in (("x", x, False), ("dt", dt, False), ("A", A, False), ("B", B, False),
+                         ("C", C, False), ("D", D, True), ("dt_bias", dt_bias, True),
+                         ("y", y, False), ("final_state", final_state, True),
+                         ("workspace", workspace, False)):
+        _need_cuda_contig(name, t, opt)
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    dev = x.device.index if x.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssd_chunk_scan_fwd(
+        handle, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+        int(bool(dt_softplus)), _ptr(y), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), batch, seqlen, nheads, headdim, dstate,
+        ngroups, chunk_size, _dtype_code(x), _stream_ptr(x.device))
+    _check("ssd_chunk_scan_fwd", st)
+
+
+def ssd_chunk_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, chunk_size=256,
+                   return_final_state=True) -> Tuple:
+    """Allocating form: returns (y, final_state or None)."""
+    import torch
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    dev = x.device.index if x.device.index is not None else 0
+    nbytes = ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                           chunk_size, device=dev)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x)
+    fs = (torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
+          if return_final_state else None)
+    ssd_chunk_scan_fwd(x, dt, A, B, C, D, dt_bias, dt_softplus, y, fs, ws, chunk_size)
+    return y, fs

@@ -1,0 +1,273 @@
+// api.cpp -- the C ABI of libssmscan.so: handles, argument validation,
+// launch-shape selection and kernel launches.  See include/ssm_scan.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "selective_scan_launch.h"
+#include "ssd_launch.h"
+#include "ssm_scan.h"
+
+struct ssm_scan_context {
+  int device;
+  int num_cus;
+  char arch[64];
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssm_status fail(ssm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ssm_status ok() {
+  g_last_error.clear();
+  return SSM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const char* name;
+  const void* p;
+  uint64_t bytes;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Checks that every non-null span is 16-byte aligned and that no output
+// overlaps any other span.
+ssm_status check_spans(const Span* in, int nin, const Span* out, int nout) {
+  for (int i = 0; i < nin; ++i)
+    if (in[i].p && !aligned16(in[i].p))
+      return fail(SSM_ERR_INVALID_ARG, "%s is not 16-byte aligned", in[i].name);
+  for (int i = 0; i < nout; ++i)
+    if (out[i].p && !aligned16(out[i].p))
+      return fail(SSM_ERR_INVALID_ARG, "%s is not 16-byte aligned", out[i].name);
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(out[i], in[j]))
+        return fail(SSM_ERR_INVALID_ARG, "output %s overlaps input %s", out[i].name, in[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(out[i], out[j]))
+        return fail(SSM_ERR_INVALID_ARG, "outputs %s and %s overlap", out[i].name, out[j].name);
+  }
+  return SSM_OK;
+}
+
+// Makes the handle's device current for the duration of a call.
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int device) : want_(device) {
+    if (hipGetDevice(&prev_) != hipSuccess) { err_ = true; return; }
+    if (prev_ != want_ && hipSetDevice(want_) != hipSuccess) err_ = true;
+  }
+  ~DeviceGuard() {
+    if (!err_ && prev_ != want_) (void)hipSetDevice(prev_);
+  }
+  bool failed() const { return err_; }
+
+ private:
+  int want_;
+  int prev_ = -1;
+  bool err_ = false;
+};
+
+ssm::ScanTile pick_scan_tile(const ssm_scan_context* h, int64_t batch, int64_t dim,
+                             int64_t dstate) {
+  // Row-parallel shapes give one wave per SIMD or more on their own; below
+  // that, each time chunk is also split over several waves.
+  const int64_t row_tiles = batch * ((dim + 63) / 64);
+  const int64_t simds = 4 * (int64_t)(h->num_cus > 0 ? h->num_cus : 256);
+  using ssm::ScanTileId;
+  if (dstate <= 4) {
+    return {row_tiles >= simds ? ScanTileId::kN4_Seq : ScanTileId::kN4_Split};
+  } else if (dstate <= 8) {
+    return {row_tiles * 2 >= simds ? ScanTileId::kN8_Seq : ScanTileId::kN8_Split};
+  } else if (dstate <= 16) {
+    return {row_tiles * 4 >= simds ? ScanTileId::kN16_Seq : ScanTileId::kN16_Split};
+  }
+  return {row_tiles * 4 >= simds ? ScanTileId::kN64_Seq : ScanTileId::kN64_Split};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssm_status_string(ssm_status status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG: invalid argument";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: outside the supported limits";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: HIP runtime error";
+  }
+  return "unknown ssm_status";
+}
+
+const char* ssm_last_error_message(void) { return g_last_error.c_str(); }
+
+ssm_status ssm_scan_create(ssm_handle* out, int hip_device) {
+  if (!out) return fail(SSM_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipGetDeviceCount: %s", hipGetErrorString(e));
+  if (hip_device < 0 || hip_device >= count)
+    return fail(SSM_ERR_INVALID_ARG, "device %d out of range (%d devices)", hip_device, count);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, hip_device);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(SSM_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                hip_device, prop.gcnArchName);
+  ssm_scan_context* h = new (std::nothrow) ssm_scan_context;
+  if (!h) return fail(SSM_ERR_HIP, "out of host memory");
+  h->device = hip_device;
+  h->num_cus = prop.multiProcessorCount;
+  std::snprintf(h->arch, sizeof(h->arch), "%s", prop.gcnArchName);
+  *out = h;
+  return ok();
+}
+
+ssm_status ssm_scan_destroy(ssm_handle handle) {
+  delete handle;
+  return ok();
+}
+
+ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* delta,
+                                  const float* A, const void* B, const void* C, const float* D,
+                                  const void* z, const float* delta_bias, int delta_softplus,
+                                  void* y, float* last_state, int64_t batch, int64_t dim,
+                                  int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
+                                  hipStream_t stream) {
+  // ---- sizes -------------------------------------------------------------
+  if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
+  if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
+  if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
+  if (seqlen <= 0) return fail(SSM_ERR_INVALID_ARG, "seqlen must be >= 1 (got %lld)", (long long)seqlen);
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
+  if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
+  if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
+    return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
+  if (batch * dim > (int64_t(1) << 62) / seqlen)
+    return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
+  // ---- pointers ----------------------------------------------------------
+  if (!u) return fail(SSM_ERR_INVALID_ARG, "u is NULL");
+  if (!delta) return fail(SSM_ERR_INVALID_ARG, "delta is NULL");
+  if (!A) return fail(SSM_ERR_INVALID_ARG, "A is NULL");
+  if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
+  if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
+  if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nrow = (uint64_t)batch * dim * seqlen;
+  const uint64_t nbc = (uint64_t)batch * dstate * seqlen;
+  const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
+                     {"A", A, (uint64_t)dim * dstate * 4}, {"B", B, nbc * es},
+                     {"C", C, nbc * es},           {"D", D, (uint64_t)dim * 4},
+                     {"z", z, nrow * es},          {"delta_bias", delta_bias, (uint64_t)dim * 4}};
+  const Span out[] = {{"y", y, nrow * es},
+                      {"last_state", last_state, (uint64_t)batch * dim * dstate * 4}};
+  ssm_status st = check_spans(in, 8, out, 2);
+  if (st != SSM_OK) return st;
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+
+  // ---- launch ------------------------------------------------------------
+  ssm::ScanParams p;
+  p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+  p.delta_bias = delta_bias; p.y = y; p.last_state = last_state;
+  p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate; p.seqlen = (int)seqlen;
+  p.delta_softplus = delta_softplus ? 1 : 0;
+  DeviceGuard guard(handle->device);
+  if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
+  const ssm::ScanTile tile = pick_scan_tile(handle, batch, dim, dstate);
+  hipError_t e = ssm::launch_selective_scan(p, tile, in_dtype == SSM_BF16, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch, int64_t seqlen,
+                                         int64_t nheads, int64_t headdim, int64_t dstate,
+                                         int64_t ngroups, int64_t chunk_size, size_t* bytes) {
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  ssm::SsdShape s;
+  ssm_status st = ssm::ssd_validate_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                          chunk_size, &s, &g_last_error);
+  if (st != SSM_OK) return st;
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  *bytes = ssm::ssd_workspace_bytes(s);
+  return ok();
+}
+
+ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void* x, const void* dt, const float* A,
+                              const void* B, const void* C, const float* D, const float* dt_bias,
+                              int dt_softplus, void* y, float* final_state, void* workspace,
+                              size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                              int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                              int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream) {
+  ssm::SsdShape s;
+  ssm_status st = ssm::ssd_validate_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                          chunk_size, &s, &g_last_error);
+  if (st != SSM_OK) return st;
+  if (in_dtype != SSM_BF16 && in_dtype != SSM_F32)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (in_dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "ssd_chunk_scan_fwd supports bf16 inputs only");
+  if (!x) return fail(SSM_ERR_INVALID_ARG, "x is NULL");
+  if (!dt) return fail(SSM_ERR_INVALID_ARG, "dt is NULL");
+  if (!A) return fail(SSM_ERR_INVALID_ARG, "A is NULL");
+  if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
+  if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
+  if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
+  if (!workspace) return fail(SSM_ERR_INVALID_ARG, "workspace is NULL");
+  const size_t need = ssm::ssd_workspace_bytes(s);
+  if (workspace_bytes < need)
+    return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  const uint64_t es = 2;
+  const uint64_t nx = (uint64_t)batch * seqlen * nheads * headdim;
+  const uint64_t nbc = (uint64_t)batch * seqlen * ngroups * dstate;
+  const Span in[] = {{"x", x, nx * es},
+                     {"dt", dt, (uint64_t)batch * seqlen * nheads * es},
+                     {"A", A, (uint64_t)nheads * 4},
+                     {"B", B, nbc * es},
+                     {"C", C, nbc * es},
+                     {"D", D, (uint64_t)nheads * 4},
+                     {"dt_bias", dt_bias, (uint64_t)nheads * 4}};
+  const Span out[] = {{"y", y, nx * es},
+                      {"final_state", final_state, (uint64_t)batch * nheads * headdim * dstate * 4},
+                      {"workspace", workspace, need}};
+  st = check_spans(in, 7, out, 3);
+  if (st != SSM_OK) return st;
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+
+  ssm::SsdParams p;
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
+  p.dt_softplus = dt_softplus ? 1 : 0; p.y = y; p.final_state = final_state;
+  p.workspace = workspace; p.shape = s;
+  DeviceGuard guard(handle->device);
+  if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
+  hipError_t e = ssm::launch_ssd(p, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

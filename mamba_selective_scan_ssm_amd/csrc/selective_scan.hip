@@ -1,0 +1,390 @@
+// selective_scan.hip -- Mamba-1 selective-scan forward kernel for gfx950.
+//
+// Sources (web pages; cited by title and section/equation):
+//   [SPEC]      "ТЕХНИЧЕСКОЕ ЗАДАНИЕ: Реализовать selective scan (Mamba)",
+//               Stage 1 items 3-4 (recurrence, softplus, D skip, silu gate).
+//   [EXPLAINED] "Mamba CUDA 实现解析", eqs. (4)-(7) (diagonal per-channel
+//               recurrence), eqs. (8)-(12) (the associative combine operator
+//               and the prefix-scan form), prefix-sum figure.
+//   [BLELLOCH]  "从顺序到并行用PyTorch实现Blelloch算法加速Mamba状态空间模型",
+//               section 3.2 (chunk long sequences instead of materialising
+//               [B, L, ED, N] tensors).
+//
+// Work decomposition (one workgroup = 64 consecutive channels d of one batch
+// entry b, over the whole sequence):
+//   * lane  = channel d (64 rows per wave), so every lane of a wave reads the
+//     same B[b,:,t] and C[b,:,t]: they are staged once per time chunk in LDS
+//     as float32 and read back as wave-wide broadcasts;
+//   * G waves split the dstate axis (NG states each) and share the per-step
+//     work (loads, softplus, gate) through LDS; their partial readouts
+//     sum_n C h are added in LDS;
+//   * W waves split each time chunk into W slots of T steps.  Slots run the
+//     lane-local recurrence from the identity, publish (prod a, v) pairs,
+//     and a serial pass over the W slots applies the combine operator of
+//     [EXPLAINED] eq. (10) with the running carry to produce every slot's
+//     carry-in; the slots then rescan with their carry-in.  With W = 1 a
+//     wave runs the plain recurrence and no scan is needed.
+//   * exp(delta*A) is computed as exp2(delta*A2) with A2 = A*log2(e)
+//     pre-scaled once per row; the product of a slot's decays is
+//     exp2(A2 * sum(delta)), one exp per state per slot.
+// Nothing of size [b, d, L, N] is ever written to memory.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "selective_scan_launch.h"
+
+namespace ssm {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
+// log1p(w) for w in (0, 1] is ln(s) + (w - (s - 1)) / s with s = fl(1 + w);
+// the correction term is below 2^-24 and is used without the division by s
+// (relative error < 2^-24 / ln 2), which keeps small w accurate.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float w = fast_exp2(-fabsf(x) * kLog2e);
+  const float s = 1.0f + w;
+  const float corr = w - (s - 1.0f);
+  return fmaxf(x, 0.0f) + __builtin_fmaf(fast_log2(s), kLn2, corr);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z})   ([SPEC] Stage 1 reference)
+__device__ __forceinline__ float silu_f(float z) {
+  return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// ---- element access ------------------------------------------------------
+
+template <typename In> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPer16B = 4;
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static void unpack(const uint4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
+  __device__ static void store(float* p, int64_t i, float x) { p[i] = x; }
+  __device__ static uint4 pack(const float* x) {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                      __float_as_uint(x[2]), __float_as_uint(x[3]));
+  }
+};
+template <> struct Elem<uint16_t> {  // bfloat16 bit pattern
+  static constexpr int kPer16B = 8;
+  __device__ static float widen(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+  __device__ static float load(const uint16_t* p, int64_t i) { return widen(p[i]); }
+  __device__ static void unpack(const uint4& v, float* o) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = __uint_as_float(w[k] << 16);
+      o[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+  // float -> bf16, round to nearest even (inputs are finite here).
+  __device__ static uint16_t narrow(float x) {
+    const __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static void store(uint16_t* p, int64_t i, float x) { p[i] = narrow(x); }
+  __device__ static uint4 pack(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)narrow(x[2 * k]) | ((uint32_t)narrow(x[2 * k + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// Load K consecutive elements p[base + t0 .. base + t0 + K) as float, with
+// zeros past `limit`.  Uses 16-byte loads when the segment is aligned and
+// complete.
+template <typename In, int K>
+__device__ __forceinline__ void load_seg(const In* __restrict__ p, int64_t base, int t0,
+                                         int limit, float (&out)[K]) {
+  constexpr int V = Elem<In>::kPer16B;
+  if constexpr (K % V == 0) {
+    if (((base + t0) % V) == 0 && t0 + K <= limit) {
+      const uint4* q = reinterpret_cast<const uint4*>(p + base + t0);
+#pragma unroll
+      for (int k = 0; k < K / V; ++k) {
+        const uint4 v = q[k];
+        Elem<In>::unpack(v, out + k * V);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    out[k] = (t0 + k < limit) ? Elem<In>::load(p, base + t0 + k) : 0.0f;
+}
+
+template <typename In, int K>
+__device__ __forceinline__ void store_seg(In* __restrict__ p, int64_t base, int t0, int limit,
+                                          const float (&v)[K]) {
+  constexpr int V = Elem<In>::kPer16B;
+  if constexpr (K % V == 0) {
+    if (((base + t0) % V) == 0 && t0 + K <= limit) {
+      uint4* q = reinterpret_cast<uint4*>(p + base + t0);
+#pragma unroll
+      for (int k = 0; k < K / V; ++k) q[k] = Elem<In>::pack(v + k * V);
+      return;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if (t0 + k < limit) Elem<In>::store(p, base + t0 + k, v[k]);
+}
+
+// ---- the kernel ------------------------------------------------------------
+
+// NG: states per wave; G: waves splitting the states; W: time slots per
+// chunk; T: steps per slot.  Block = 64 * G * W threads.
+template <typename In, int NG, int G, int W, int T>
+__global__ void __launch_bounds__(64 * G * W)
+selective_scan_fwd_kernel(ScanParams prm) {
+  constexpr int NT = NG * G;       // states covered by one workgroup (>= dstate)
+  constexpr int TC = W * T;        // steps per chunk
+  constexpr int TG = T / G;        // steps of a slot whose per-step work one wave owns
+  constexpr int NTHR = 64 * G * W;
+  static_assert(T % G == 0, "T must be a multiple of G");
+  constexpr int PAIRS = (NT + G * W - 1) / (G * W);  // scan pairs per thread (W > 1)
+
+  __shared__ float sB[TC][NT];
+  __shared__ float sC[TC][NT];
+  __shared__ float2 sDD[W][T][64];                  // (delta, delta*u) per step and row
+  __shared__ float sP[W > 1 ? W : 1][W > 1 ? NT : 1][64];   // slot decay products
+  __shared__ float sV[W > 1 ? W : 1][W > 1 ? NT : 1][64];   // slot values / carry-ins
+  __shared__ float sY[G > 1 ? G : 1][G > 1 ? W : 1][G > 1 ? T : 1][64];  // partial readouts
+
+  const In* __restrict__ u = static_cast<const In*>(prm.u);
+  const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(prm.B);
+  const In* __restrict__ Cm = static_cast<const In*>(prm.C);
+  const In* __restrict__ z = static_cast<const In*>(prm.z);
+  In* __restrict__ y = static_cast<In*>(prm.y);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wv % G;
+  const int w = wv / G;
+  const int b = blockIdx.y;
+  const int d = blockIdx.x * 64 + lane;
+  const bool row_ok = d < prm.dim;
+  const int L = prm.seqlen;
+  const int N = prm.dstate;
+  const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
+  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+
+  // Per-row constants for this wave's states.
+  float A2[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = g * NG + k;
+    A2[k] = (row_ok && n < N) ? prm.A[(int64_t)d * N + n] * kLog2e : 0.0f;
+  }
+  const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
+  const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
+
+  float h[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) h[k] = 0.0f;
+  float carry[PAIRS];
+#pragma unroll
+  for (int k = 0; k < PAIRS; ++k) carry[k] = 0.0f;
+
+  const int nchunks = (L + TC - 1) / TC;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * TC;
+    if (G == 1 || ch == 0) __syncthreads();  // previous chunk's LDS readers are done
+
+    // -- stage B and C for the chunk (float32, [t][n], zero-padded) ---------
+    for (int e = tid; e < NT * TC; e += NTHR) {
+      const int n = e / TC, tt = e % TC;
+      const int t = c0 + tt;
+      const bool ok = n < N && t < L;
+      sB[tt][n] = ok ? Elem<In>::load(Bm, bc_base + (int64_t)n * L + t) : 0.0f;
+      sC[tt][n] = ok ? Elem<In>::load(Cm, bc_base + (int64_t)n * L + t) : 0.0f;
+    }
+
+    // -- per-step work for this wave's share of its slot --------------------
+    const int ts = c0 + w * T + g * TG;  // first step owned by this wave
+    float uk[TG], gk[TG];
+    {
+      float dr[TG];
+      if (row_ok) {
+        load_seg<In, TG>(u, row_base, ts, L, uk);
+        load_seg<In, TG>(dlt, row_base, ts, L, dr);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TG; ++j) uk[j] = dr[j] = 0.0f;
+      }
+      if (z && row_ok) {
+        float zk[TG];
+        load_seg<In, TG>(z, row_base, ts, L, zk);
+#pragma unroll
+        for (int j = 0; j < TG; ++j) gk[j] = silu_f(zk[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TG; ++j) gk[j] = 1.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < TG; ++j) {
+        float dl = dr[j] + bias;
+        if (prm.delta_softplus) dl = softplus_f(dl);
+        if (ts + j >= L || !row_ok) dl = 0.0f;  // padding steps are the identity
+        sDD[w][g * TG + j][lane] = make_float2(dl, dl * uk[j]);
+      }
+    }
+    __syncthreads();
+
+    // -- recurrence over this wave's slot and states --------------------------
+    float yp[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) yp[j] = 0.0f;
+
+    if constexpr (W == 1) {
+      // Plain recurrence ([EXPLAINED] eq. (7)) with the state kept in registers.
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const float2 dd = sDD[0][j][lane];
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+          const float a = fast_exp2(dd.x * A2[k]);
+          h[k] = __builtin_fmaf(a, h[k], dd.y * sB[j][g * NG + k]);
+          yp[j] = __builtin_fmaf(sC[j][g * NG + k], h[k], yp[j]);
+        }
+      }
+    } else {
+      // Pass 1: slot aggregate from the identity (1, 0).
+      float acache[T][NG];
+      float v[NG];
+#pragma unroll
+      for (int k = 0; k < NG; ++k) v[k] = 0.0f;
+      float dsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const float2 dd = sDD[w][j][lane];
+        dsum += dd.x;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+          const float a = fast_exp2(dd.x * A2[k]);
+          acache[j][k] = a;
+          v[k] = __builtin_fmaf(a, v[k], dd.y * sB[w * T + j][g * NG + k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        sP[w][g * NG + k][lane] = fast_exp2(A2[k] * dsum);
+        sV[w][g * NG + k][lane] = v[k];
+      }
+      __syncthreads();
+      // Serial combine over the W slots for the (state, row) pairs this
+      // thread owns: carry-in of slot s = carry (+) slot_0 (+) ... (+) slot_{s-1}.
+#pragma unroll
+      for (int q = 0; q < PAIRS; ++q) {
+        const int n = wv + q * (G * W);
+        if (n < NT) {
+          float c = carry[q];
+#pragma unroll
+          for (int s = 0; s < W; ++s) {
+            const float p = sP[s][n][lane];
+            const float vv = sV[s][n][lane];
+            sV[s][n][lane] = c;
+            c = __builtin_fmaf(p, c, vv);
+          }
+          carry[q] = c;
+        }
+      }
+      __syncthreads();
+      // Pass 2: rescan the slot from its carry-in and read out y.
+#pragma unroll
+      for (int k = 0; k < NG; ++k) h[k] = sV[w][g * NG + k][lane];
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const float2 dd = sDD[w][j][lane];
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+          h[k] = __builtin_fmaf(acache[j][k], h[k], dd.y * sB[w * T + j][g * NG + k]);
+          yp[j] = __builtin_fmaf(sC[w * T + j][g * NG + k], h[k], yp[j]);
+        }
+      }
+    }
+
+    // -- combine the state groups' readouts, skip term, gate, store ----------
+    float yo[TG];
+    if constexpr (G > 1) {
+#pragma unroll
+      for (int j = 0; j < T; ++j) sY[g][w][j][lane] = yp[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < TG; ++j) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) acc += sY[gg][w][g * TG + j][lane];
+        yo[j] = acc;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TG; ++j) yo[j] = yp[j];
+    }
+#pragma unroll
+    for (int j = 0; j < TG; ++j) yo[j] = __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j];
+    if (row_ok) store_seg<In, TG>(y, row_base, ts, L, yo);
+  }
+
+  // -- final state -----------------------------------------------------------
+  if (prm.last_state && row_ok) {
+    float* ls = prm.last_state + ((int64_t)b * prm.dim + d) * N;
+    if constexpr (W == 1) {
+#pragma unroll
+      for (int k = 0; k < NG; ++k)
+        if (g * NG + k < N) ls[g * NG + k] = h[k];
+    } else {
+#pragma unroll
+      for (int q = 0; q < PAIRS; ++q) {
+        const int n = wv + q * (G * W);
+        if (n < N) ls[n] = carry[q];
+      }
+    }
+  }
+}
+
+template <typename In, int NG, int G, int W, int T>
+hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)((p.dim + 63) / 64), (unsigned)p.batch);
+  dim3 block(64 * G * W);
+  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, G, W, T>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename In>
+hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
+  switch (t.id) {
+    case ScanTileId::kN4_Seq: return launch_cfg<In, 4, 1, 1, 32>(p, s);
+    case ScanTileId::kN8_Seq: return launch_cfg<In, 4, 2, 1, 32>(p, s);
+    case ScanTileId::kN16_Seq: return launch_cfg<In, 4, 4, 1, 32>(p, s);
+    case ScanTileId::kN64_Seq: return launch_cfg<In, 16, 4, 1, 16>(p, s);
+    case ScanTileId::kN4_Split: return launch_cfg<In, 4, 1, 8, 8>(p, s);
+    case ScanTileId::kN8_Split: return launch_cfg<In, 4, 2, 4, 16>(p, s);
+    case ScanTileId::kN16_Split: return launch_cfg<In, 4, 4, 4, 16>(p, s);
+    case ScanTileId::kN64_Split: return launch_cfg<In, 16, 4, 2, 4>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
+                                 hipStream_t stream) {
+  return bf16 ? launch_typed<uint16_t>(p, tile, stream) : launch_typed<float>(p, tile, stream);
+}
+
+}  // namespace ssm

@@ -1,0 +1,44 @@
+// selective_scan_launch.h -- internal interface between the C-ABI layer and
+// the Mamba-1 scan kernels (not installed, not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Device pointers and sizes of one ssm_selective_scan_fwd call (already
+// validated by the C-ABI layer).
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;           // nullable
+  const void* z;            // nullable
+  const float* delta_bias;  // nullable
+  void* y;
+  float* last_state;        // nullable
+  int batch;
+  int dim;
+  int dstate;
+  int seqlen;
+  int delta_softplus;
+};
+
+// Compiled kernel shapes.  "Seq": each wave runs the whole sequence for its
+// rows (no time split).  "Split": each time chunk is split over several
+// waves whose carries are combined with the associative operator.
+enum class ScanTileId : int {
+  kN4_Seq, kN8_Seq, kN16_Seq, kN64_Seq,
+  kN4_Split, kN8_Split, kN16_Split, kN64_Split,
+};
+
+struct ScanTile {
+  ScanTileId id;
+};
+
+hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
+                                 hipStream_t stream);
+
+}  // namespace ssm

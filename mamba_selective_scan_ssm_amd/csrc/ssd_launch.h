@@ -1,0 +1,65 @@
+// ssd_launch.h -- internal interface between the C-ABI layer and the Mamba-2
+// (SSD) chunked-scan kernels (not installed, not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "ssm_scan.h"
+
+namespace ssm {
+
+struct SsdShape {
+  int batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+  int nchunks;  // ceil(seqlen / chunk)
+};
+
+struct SsdParams {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const float* dt_bias;  // nullable
+  int dt_softplus;
+  void* y;
+  float* final_state;    // nullable
+  void* workspace;
+  SsdShape shape;
+};
+
+// Workspace layout (all float32, 256-byte aligned sections):
+//   dtv    [batch, nheads, nchunks*chunk]   step sizes after bias/softplus
+//   cs     [batch, nheads, nchunks*chunk]   within-chunk inclusive cumsum of A*dt
+//   states [batch, nchunks, nheads, headdim, dstate]
+//          chunk-local states, then (in place) the state entering each chunk
+struct SsdLayout {
+  size_t dtv_off, cs_off, states_off, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline SsdLayout ssd_layout(const SsdShape& s) {
+  SsdLayout l;
+  const size_t per_bh = (size_t)s.nchunks * s.chunk * sizeof(float);
+  l.dtv_off = 0;
+  l.cs_off = align256(l.dtv_off + (size_t)s.batch * s.nheads * per_bh);
+  l.states_off = align256(l.cs_off + (size_t)s.batch * s.nheads * per_bh);
+  l.total = align256(l.states_off + (size_t)s.batch * s.nchunks * s.nheads * s.headdim *
+                                        s.dstate * sizeof(float));
+  return l;
+}
+
+inline size_t ssd_workspace_bytes(const SsdShape& s) { return ssd_layout(s).total; }
+
+// Validates sizes against the documented limits; fills *out on success and
+// writes a reason into *msg on failure.
+ssm_status ssd_validate_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t dstate, int64_t ngroups, int64_t chunk, SsdShape* out,
+                              std::string* msg);
+
+hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
+
+}  // namespace ssm

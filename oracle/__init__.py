@@ -76,7 +76,7 @@ def _p32(a):
 
 
 def default_threads() -> int:
-    return max(1, min(len(os.sched_getaffinity(0)), 64))
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -189,3 +189,25 @@ def ssd_inputs(cfg: SSDConfig, seed: int = 0, batch=None, seqlen=None,
         "D": normal(seed, "D", (h,)),
         "dt_bias": inverse_softplus_dt_bias(seed, "dt0", h),
     }
+
+
+# ---------------------------------------------------------------------------
+# Upload helpers (plumbing: numpy -> torch device tensors)
+# ---------------------------------------------------------------------------
+
+def to_device(arr: Optional[np.ndarray], dtype: str, device="cuda"):
+    """float32 numpy array -> torch tensor on `device` in "f32" or "bf16"
+    (bf16 arrays must already be bf16-exact; the bits are copied as-is)."""
+    if arr is None:
+        return None
+    import torch
+    if dtype == "bf16":
+        bits = bf16_bits(arr).view(np.int16)
+        return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def to_host_f64(t) -> np.ndarray:
+    """torch tensor (f32 or bf16, any device) -> float64 numpy array."""
+    import torch
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)

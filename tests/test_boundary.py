@@ -1,0 +1,106 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+symbol the header declares, and rejects invalid arguments before any HIP call
+(the exercise spec's Definition of Done: batch=0 is invalid but must not
+crash)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_selective_scan_ssm_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_scan.h")
+
+# Fake, 16-byte aligned, never dereferenced device addresses.
+P = [0x10000000 * (i + 1) for i in range(16)]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+|ssd_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssm.load_library()
+    declared = header_functions()
+    assert set(declared) == set(ssm.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, 1, 2, 3):
+        assert ssm.status_string(code)
+    assert "unknown" in ssm.status_string(99)
+
+
+def scan(handle=None, u=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], D=None, z=None, bias=None,
+         y=P[5], ls=None, batch=2, dim=4, dstate=4, seqlen=8, dtype=ssm.SSM_F32):
+    lib = ssm.load_library()
+    st = lib.ssm_selective_scan_fwd(handle, u, delta, A, B, C, D, z, bias, 1, y, ls,
+                                    batch, dim, dstate, seqlen, dtype, None)
+    return st, ssm.ssm_last_error_message()
+
+
+@pytest.mark.parametrize("field,value,word", [
+    ("batch", 0, "batch"), ("batch", -3, "batch"), ("dim", 0, "dim"),
+    ("seqlen", 0, "seqlen"), ("dstate", 0, "dstate")])
+def test_nonpositive_sizes_rejected(field, value, word):
+    st, msg = scan(**{field: value})
+    assert st == ssm.SSM_ERR_INVALID_ARG
+    assert word in msg
+
+
+def test_limits_and_enums():
+    st, msg = scan(dstate=65)
+    assert st == ssm.SSM_ERR_UNSUPPORTED and "dstate" in msg
+    st, msg = scan(dtype=7)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "dtype" in msg
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "y"])
+def test_required_pointers(name):
+    st, msg = scan(**{name: None})
+    assert st == ssm.SSM_ERR_INVALID_ARG and f"{name} is NULL" in msg
+
+
+def test_misaligned_and_overlapping_pointers():
+    st, msg = scan(u=P[0] + 4)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg
+    st, msg = scan(y=P[0])          # y aliases u
+    assert st == ssm.SSM_ERR_INVALID_ARG and "overlaps" in msg
+    st, msg = scan(ls=P[5] + 16)    # last_state inside y
+    assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg
+
+
+def test_null_handle_is_last_check():
+    st, msg = scan(D=P[6], z=P[7], bias=P[8], ls=P[9])
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg
+
+
+def ssd_ws(batch=2, seqlen=64, nheads=4, headdim=64, dstate=16, ngroups=1, chunk=64):
+    lib = ssm.load_library()
+    n = ctypes.c_size_t(123)
+    st = lib.ssd_chunk_scan_workspace_size(None, batch, seqlen, nheads, headdim, dstate,
+                                           ngroups, chunk, ctypes.byref(n))
+    return st, ssm.ssm_last_error_message(), n.value
+
+
+def test_ssd_shape_checks():
+    assert ssd_ws()[0] == ssm.SSM_ERR_INVALID_ARG            # valid shape, NULL handle
+    assert "handle" in ssd_ws()[1]
+    assert ssd_ws(nheads=6, ngroups=4)[0] == ssm.SSM_ERR_INVALID_ARG
+    assert ssd_ws(chunk=100)[0] == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd_ws(headdim=48)[0] == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd_ws(dstate=100)[0] == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd_ws(batch=0)[0] == ssm.SSM_ERR_INVALID_ARG
+    assert ssd_ws(batch=0)[2] == 0
+
+
+def test_create_rejects_bad_arguments():
+    lib = ssm.load_library()
+    assert lib.ssm_scan_create(None, 0) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_scan_destroy(None) == ssm.SSM_OK
