@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the Mamba-1 selective-scan forward pass on one
+MI355X, on the Mamba-1.4B-shaped workload (batch 8, dim 4096, dstate 16,
+seqlen 2048; bf16 u/delta/B/C/z, fp32 A/D/delta_bias/state; softplus with
+bias, D skip, silu(z) gate, last_state output).
+
+One step = one ssm_selective_scan_fwd call over the whole batch (inputs
+resident in HBM).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+                    [--no-cpu-baseline] [--calib-copy] [--ssd]
+
+Algorithmic HBM bytes per call (inputs read once, outputs written once):
+    u, delta, z: 3*b*d*L*es   y: b*d*L*es   B, C: 2*b*N*L*es
+    A: 4*d*N   D, delta_bias: 2*4*d   last_state: 4*b*d*N
+Algorithmic FLOPs per call: per state update (b,d,t,n) 7 (delta*A, exp,
+delta*u*B, state FMA = 2, readout FMA = 2); per (b,d,t) 12 (bias add, softplus
+exp+log+add, delta*u, D skip FMA = 2, gate exp+add+rcp+mul, gate product).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan fwd HBM GB/s and % of peak, Mamba-1.4B shape, 1×MI355X"
+HBM_PEAK_GBS = 8000.0
+# fp32 vector peak without packed-FP32 instructions (the build disables
+# them): 256 CUs x 64 lanes x 2 FLOP (FMA) x 2.4 GHz.
+VALU_PEAK_TFLOPS = 78.6
+FLOP_PER_UPDATE = 7
+FLOP_PER_STEP = 12
+
+
+def mamba1_bytes(b, d, n, L, es):
+    return (4 * b * d * L * es + 2 * b * n * L * es + 4 * d * n + 8 * d + 4 * b * d * n)
+
+
+def mamba1_flops(b, d, n, L):
+    return b * d * L * (FLOP_PER_UPDATE * n + FLOP_PER_STEP)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="m1p4b", choices=["m1p4b", "m130m", "long", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ssd", action="store_true", help="also time the Mamba-2 chunked scan")
+    return ap.parse_args()
+
+
+def calib_copy(torch):
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}))
+
+
+KERNEL_SRC = os.path.join(ROOT, "mamba_selective_scan_ssm_amd", "csrc", "selective_scan.hip")
+
+
+def measured_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", " ", "|")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(x, cfg, oracle, min_seconds=1.0):
+    """Time the oracle (as it stands) on the whole workload on the host,
+    repeating it until at least `min_seconds` of wall time (about 16 s of CPU
+    work on 16 threads)."""
+    threads = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.selective_scan(**x, delta_softplus=cfg.softplus, want_y=True, want_state=True,
+                              nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    b, d, L = x["u"].shape
+    n = x["A"].shape[1]
+    es = 2 if cfg.dtype == "bf16" else 4
+    return {"value": reps * mamba1_bytes(b, d, n, L, es) / dt / 1e9, "unit": "GB/s",
+            "cores": threads, "kind": "oracle", "seconds": round(dt, 3), "repetitions": reps,
+            "sample": f"the whole {cfg.name} workload ({b * d} rows x {L} steps x {n} states, "
+                      f"fp64 sequential loop per row, rows over {threads} threads), run {reps}x"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the scan shards over "
+              "(batch, channel) rows with no communication, so N GPUs run N independent "
+              "copies of this workload.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        calib_copy(torch)
+        return
+
+    import mamba_selective_scan_ssm_amd as ssm
+    import synth
+
+    ssm.load_library()
+    cfg = synth.MAMBA1_CONFIGS[args.workload]
+    x = synth.mamba1_inputs(cfg, seed=2)
+    b, d, L = x["u"].shape
+    n = x["A"].shape[1]
+    es = 2 if cfg.dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    io = {k: synth.to_device(v, cfg.dtype if k in ("u", "delta", "z", "B", "C") else "f32", dev)
+          for k, v in x.items()}
+    y = torch.empty_like(io["u"])
+    ls = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    handle = ssm.get_handle(0)
+
+    def step():
+        ssm.ssm_selective_scan_fwd(io["u"], io["delta"], io["A"], io["B"], io["C"], io["D"],
+                                   io["z"], io["delta_bias"], cfg.softplus, y, ls, handle=handle)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    nbytes = mamba1_bytes(b, d, n, L, es)
+    flops = mamba1_flops(b, d, n, L)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    kern_s = ev_ms * 1e-3
+    hbm_gbs = nbytes / kern_s / 1e9
+    achieved_tf = flops / kern_s / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Mamba-1 selective scan fwd, batch {b}, dim {d}, "
+                               f"dstate {n}, seqlen {L}, {cfg.dtype} u/delta/B/C/z, fp32 "
+                               "A/D/delta_bias/last_state, softplus(delta+bias), D skip, "
+                               "silu(z) gate",
+                   "batch": b, "dim": d, "dstate": n, "seqlen": L, "parallelism": "none"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(b * d * L / (ms_per_step * 1e-3), 1),
+        "state_updates_per_s": round(b * d * L * n / (ms_per_step * 1e-3), 1),
+        "kernel_avg_us_hip_events": round(ev_ms * 1e3, 3),
+        "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes},
+        "roofline": {"bound": "alu", "achieved": round(achieved_tf, 3),
+                     "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_tf / VALU_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("selective_scan_fwd_kernel", cfg.name, KERNEL_SRC),
+                     "kernel": "selective_scan_fwd_kernel", "flops_per_launch": flops},
+    }
+    if args.ssd:
+        out["ssd"] = bench_ssd(args, torch, ssm, synth)
+    if not args.no_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cpu_baseline(x, cfg, oracle)
+    print(json.dumps(out), flush=True)
+
+
+def bench_ssd(args, torch, ssm, synth):
+    cfg = synth.SSD_CONFIGS["ssd"]
+    s = synth.ssd_inputs(cfg, seed=4)
+    dev = torch.device("cuda:0")
+    t = {k: synth.to_device(v, "bf16" if k in ("x", "dt", "B", "C") else "f32", dev)
+         for k, v in s.items()}
+    b, L, h, p = s["x"].shape
+    n = s["B"].shape[3]
+    ws = torch.empty(ssm.ssd_chunk_scan_workspace_size(b, L, h, p, n, cfg.ngroups, cfg.chunk),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty_like(t["x"])
+    fs = torch.empty((b, h, p, n), dtype=torch.float32, device=dev)
+
+    def step():
+        ssm.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"],
+                               True, y, fs, ws, cfg.chunk)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    Q, g = cfg.chunk, cfg.ngroups
+    nc = math.ceil(L / Q)
+    flops = 2 * b * nc * (g * Q * Q * n + h * Q * Q * p + 2 * h * Q * n * p)
+    nbytes = 2 * (2 * b * L * h * p + b * L * h + 2 * b * L * g * n) + 3 * 4 * h + 4 * b * h * p * n
+    return {"workload": f"SSD chunked scan: batch {b}, seqlen {L}, heads {h}, headdim {p}, "
+                        f"dstate {n}, groups {g}, chunk {Q}, bf16",
+            "ms_per_call": round(ms, 5), "tokens_per_s": round(b * L / (ms * 1e-3), 1),
+            "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac_bf16_2500": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4),
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "flops": flops, "bytes": nbytes}
+
+
+if __name__ == "__main__":
+    main()

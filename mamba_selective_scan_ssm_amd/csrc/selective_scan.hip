@@ -102,12 +102,19 @@ template <> struct Elem<uint16_t> {  // bfloat16 bit pattern
   }
 };
 
-// Load K consecutive elements p[base + t0 .. base + t0 + K) as float, with
-// zeros past `limit`.  Uses 16-byte loads when the segment is aligned and
-// complete.
+// Raw (undecoded) input words for K consecutive elements of one row, held in
+// registers between the load of a time chunk and its use one chunk later.
 template <typename In, int K>
-__device__ __forceinline__ void load_seg(const In* __restrict__ p, int64_t base, int t0,
-                                         int limit, float (&out)[K]) {
+struct RawSeg {
+  static constexpr int kWords = (K * (int)sizeof(In) + 3) / 4;
+  uint32_t w[kWords];
+};
+
+// Load p[base + t0 .. base + t0 + K) into raw words, zero past `limit`.
+// 16-byte loads when the segment is 16-byte aligned and complete.
+template <typename In, int K>
+__device__ __forceinline__ void load_raw(const In* __restrict__ p, int64_t base, int t0,
+                                         int limit, RawSeg<In, K>& r) {
   constexpr int V = Elem<In>::kPer16B;
   if constexpr (K % V == 0) {
     if (((base + t0) % V) == 0 && t0 + K <= limit) {
@@ -115,14 +122,41 @@ __device__ __forceinline__ void load_seg(const In* __restrict__ p, int64_t base,
 #pragma unroll
       for (int k = 0; k < K / V; ++k) {
         const uint4 v = q[k];
-        Elem<In>::unpack(v, out + k * V);
+        r.w[4 * k] = v.x; r.w[4 * k + 1] = v.y; r.w[4 * k + 2] = v.z; r.w[4 * k + 3] = v.w;
       }
       return;
     }
   }
+  if constexpr (K * sizeof(In) == 8) {  // one 8-byte load
+    if (((base + t0) % (8 / sizeof(In))) == 0 && t0 + K <= limit) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p + base + t0);
+      r.w[0] = v.x; r.w[1] = v.y;
+      return;
+    }
+  }
+  if constexpr (sizeof(In) == 4) {
 #pragma unroll
-  for (int k = 0; k < K; ++k)
-    out[k] = (t0 + k < limit) ? Elem<In>::load(p, base + t0 + k) : 0.0f;
+    for (int k = 0; k < K; ++k)
+      r.w[k] = (t0 + k < limit) ? reinterpret_cast<const uint32_t*>(p)[base + t0 + k] : 0u;
+  } else {
+#pragma unroll
+    for (int k = 0; k < r.kWords; ++k) r.w[k] = 0u;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (t0 + k < limit) r.w[k / 2] |= (uint32_t)p[base + t0 + k] << (16 * (k & 1));
+  }
+}
+
+template <typename In, int K>
+__device__ __forceinline__ void decode_raw(const RawSeg<In, K>& r, float (&out)[K]) {
+  if constexpr (sizeof(In) == 4) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) out[k] = __uint_as_float(r.w[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      out[k] = __uint_as_float((k & 1) ? (r.w[k / 2] & 0xffff0000u) : (r.w[k / 2] << 16));
+  }
 }
 
 template <typename In, int K>
@@ -155,6 +189,12 @@ selective_scan_fwd_kernel(ScanParams prm) {
   constexpr int NTHR = 64 * G * W;
   static_assert(T % G == 0, "T must be a multiple of G");
   constexpr int PAIRS = (NT + G * W - 1) / (G * W);  // scan pairs per thread (W > 1)
+  // B/C staging: 16-byte units, NT rows x UPR units per tensor and chunk.
+  constexpr int EPU = Elem<In>::kPer16B;             // elements per unit
+  static_assert(TC % EPU == 0, "chunk must hold whole 16-byte units");
+  constexpr int UPR = TC / EPU;
+  constexpr int UNITS = 2 * NT * UPR;
+  constexpr int RB = (UNITS + NTHR - 1) / NTHR;      // units per thread
 
   __shared__ float sB[TC][NT];
   __shared__ float sC[TC][NT];
@@ -178,6 +218,7 @@ selective_scan_fwd_kernel(ScanParams prm) {
   const int b = blockIdx.y;
   const int d = blockIdx.x * 64 + lane;
   const bool row_ok = d < prm.dim;
+  const bool has_z = z != nullptr;
   const int L = prm.seqlen;
   const int N = prm.dstate;
   const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
@@ -200,35 +241,63 @@ selective_scan_fwd_kernel(ScanParams prm) {
 #pragma unroll
   for (int k = 0; k < PAIRS; ++k) carry[k] = 0.0f;
 
+  // Raw chunk data, loaded one chunk ahead of its use.
+  RawSeg<In, TG> ru, rd, rz;
+  RawSeg<In, EPU> rbc[RB];
+  auto load_chunk = [&](int c0) {
+    const int ts = c0 + w * T + g * TG;
+    if (row_ok) {
+      load_raw<In, TG>(u, row_base, ts, L, ru);
+      load_raw<In, TG>(dlt, row_base, ts, L, rd);
+      if (has_z) load_raw<In, TG>(z, row_base, ts, L, rz);
+    }
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * NTHR;
+      const int n = e % NT, rest = e / NT;
+      const int seg = rest % UPR, x = rest / UPR;
+      if (e < UNITS && n < N) {
+        const In* src = x ? Cm : Bm;
+        load_raw<In, EPU>(src, bc_base + (int64_t)n * L, c0 + seg * EPU, L, rbc[q]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
+      }
+    }
+  };
+
   const int nchunks = (L + TC - 1) / TC;
+  load_chunk(0);
   for (int ch = 0; ch < nchunks; ++ch) {
     const int c0 = ch * TC;
-    if (G == 1 || ch == 0) __syncthreads();  // previous chunk's LDS readers are done
+    if (G == 1) __syncthreads();  // previous chunk's LDS readers are done
 
-    // -- stage B and C for the chunk (float32, [t][n], zero-padded) ---------
-    for (int e = tid; e < NT * TC; e += NTHR) {
-      const int n = e / TC, tt = e % TC;
-      const int t = c0 + tt;
-      const bool ok = n < N && t < L;
-      sB[tt][n] = ok ? Elem<In>::load(Bm, bc_base + (int64_t)n * L + t) : 0.0f;
-      sC[tt][n] = ok ? Elem<In>::load(Cm, bc_base + (int64_t)n * L + t) : 0.0f;
+    // -- decode: B and C into LDS as float32 [t][n] --------------------------
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * NTHR;
+      if (e < UNITS) {
+        const int n = e % NT, rest = e / NT;
+        const int seg = rest % UPR, x = rest / UPR;
+        float v[EPU];
+        decode_raw<In, EPU>(rbc[q], v);
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) {
+          if (x) sC[seg * EPU + i][n] = v[i];
+          else sB[seg * EPU + i][n] = v[i];
+        }
+      }
     }
-
-    // -- per-step work for this wave's share of its slot --------------------
+    // -- decode: per-step work for this wave's share of its slot ------------
     const int ts = c0 + w * T + g * TG;  // first step owned by this wave
     float uk[TG], gk[TG];
     {
       float dr[TG];
-      if (row_ok) {
-        load_seg<In, TG>(u, row_base, ts, L, uk);
-        load_seg<In, TG>(dlt, row_base, ts, L, dr);
-      } else {
-#pragma unroll
-        for (int j = 0; j < TG; ++j) uk[j] = dr[j] = 0.0f;
-      }
-      if (z && row_ok) {
+      decode_raw<In, TG>(ru, uk);
+      decode_raw<In, TG>(rd, dr);
+      if (has_z) {
         float zk[TG];
-        load_seg<In, TG>(z, row_base, ts, L, zk);
+        decode_raw<In, TG>(rz, zk);
 #pragma unroll
         for (int j = 0; j < TG; ++j) gk[j] = silu_f(zk[j]);
       } else {
@@ -243,6 +312,7 @@ selective_scan_fwd_kernel(ScanParams prm) {
         sDD[w][g * TG + j][lane] = make_float2(dl, dl * uk[j]);
       }
     }
+    if (ch + 1 < nchunks) load_chunk(c0 + TC);
     __syncthreads();
 
     // -- recurrence over this wave's slot and states --------------------------
@@ -251,15 +321,40 @@ selective_scan_fwd_kernel(ScanParams prm) {
     for (int j = 0; j < T; ++j) yp[j] = 0.0f;
 
     if constexpr (W == 1) {
-      // Plain recurrence ([EXPLAINED] eq. (7)) with the state kept in registers.
+      // Plain recurrence ([EXPLAINED] eq. (7)) with the state kept in
+      // registers.  LDS operands are fetched one block of JB steps ahead of
+      // their use so that their latency overlaps the previous block's math.
+      constexpr int JB = T >= 8 ? 8 : T;
+      static_assert(T % JB == 0, "T must be a multiple of the block");
+      float2 ddq[2][JB];
+      float bq[2][JB][NG], cq[2][JB][NG];
+      auto fetch = [&](int buf, int j0) {
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const float2 dd = sDD[0][j][lane];
+        for (int jj = 0; jj < JB; ++jj) {
+          ddq[buf][jj] = sDD[0][j0 + jj][lane];
 #pragma unroll
-        for (int k = 0; k < NG; ++k) {
-          const float a = fast_exp2(dd.x * A2[k]);
-          h[k] = __builtin_fmaf(a, h[k], dd.y * sB[j][g * NG + k]);
-          yp[j] = __builtin_fmaf(sC[j][g * NG + k], h[k], yp[j]);
+          for (int k = 0; k < NG; ++k) {
+            bq[buf][jj][k] = sB[j0 + jj][g * NG + k];
+            cq[buf][jj][k] = sC[j0 + jj][g * NG + k];
+          }
+        }
+      };
+      fetch(0, 0);
+#pragma unroll
+      for (int jb = 0; jb < T / JB; ++jb) {
+        const int cur = jb & 1;
+        if (jb + 1 < T / JB) fetch(cur ^ 1, (jb + 1) * JB);
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj) {
+          const float2 dd = ddq[cur][jj];
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NG; ++k) {
+            const float a = fast_exp2(dd.x * A2[k]);
+            h[k] = __builtin_fmaf(a, h[k], dd.y * bq[cur][jj][k]);
+            acc = __builtin_fmaf(cq[cur][jj][k], h[k], acc);
+          }
+          yp[jb * JB + jj] = acc;
         }
       }
     } else {
