@@ -1,0 +1,40 @@
+// device_math.h -- small float32 device helpers shared by the scan kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
+// log1p(w) for w in (0, 1] is ln(s) + (w - (s - 1)) / s with s = fl(1 + w);
+// the correction term is below 2^-24 and is used without the division by s
+// (relative error < 2^-24 / ln 2), which keeps small w accurate.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float w = fast_exp2(-fabsf(x) * kLog2e);
+  const float s = 1.0f + w;
+  const float corr = w - (s - 1.0f);
+  return fmaxf(x, 0.0f) + __builtin_fmaf(fast_log2(s), kLn2, corr);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z})
+__device__ __forceinline__ float silu_f(float z) {
+  return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+}  // namespace ssm

@@ -31,33 +31,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_math.h"
 #include "selective_scan_launch.h"
 
 namespace ssm {
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
-// log1p(w) for w in (0, 1] is ln(s) + (w - (s - 1)) / s with s = fl(1 + w);
-// the correction term is below 2^-24 and is used without the division by s
-// (relative error < 2^-24 / ln 2), which keeps small w accurate.
-__device__ __forceinline__ float softplus_f(float x) {
-  const float w = fast_exp2(-fabsf(x) * kLog2e);
-  const float s = 1.0f + w;
-  const float corr = w - (s - 1.0f);
-  return fmaxf(x, 0.0f) + __builtin_fmaf(fast_log2(s), kLn2, corr);
-}
-
-// silu(z) = z * sigmoid(z) = z / (1 + e^{-z})   ([SPEC] Stage 1 reference)
-__device__ __forceinline__ float silu_f(float z) {
-  return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
-}
 
 // ---- element access ------------------------------------------------------
 
@@ -196,8 +174,8 @@ selective_scan_fwd_kernel(ScanParams prm) {
   constexpr int UNITS = 2 * NT * UPR;
   constexpr int RB = (UNITS + NTHR - 1) / NTHR;      // units per thread
 
-  __shared__ float sB[TC][NT];
-  __shared__ float sC[TC][NT];
+  __shared__ alignas(16) float sB[TC][NT];
+  __shared__ alignas(16) float sC[TC][NT];
   __shared__ float2 sDD[W][T][64];                  // (delta, delta*u) per step and row
   __shared__ float sP[W > 1 ? W : 1][W > 1 ? NT : 1][64];   // slot decay products
   __shared__ float sV[W > 1 ? W : 1][W > 1 ? NT : 1][64];   // slot values / carry-ins

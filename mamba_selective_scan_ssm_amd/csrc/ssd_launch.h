@@ -30,25 +30,22 @@ struct SsdParams {
   SsdShape shape;
 };
 
-// Workspace layout (all float32, 256-byte aligned sections):
-//   dtv    [batch, nheads, nchunks*chunk]   step sizes after bias/softplus
-//   cs     [batch, nheads, nchunks*chunk]   within-chunk inclusive cumsum of A*dt
-//   states [batch, nchunks, nheads, headdim, dstate]
-//          chunk-local states, then (in place) the state entering each chunk
+// Workspace layout (256-byte aligned sections):
+//   states [batch, nchunks, nheads, headdim, dstate] bf16: each chunk's
+//          local state (chunk-state kernel), then, in place, the state
+//          entering that chunk (state-pass kernel)
+//   decay  [batch, nheads, nchunks] float32: exp(sum of A*dt over the chunk)
 struct SsdLayout {
-  size_t dtv_off, cs_off, states_off, total;
+  size_t states_off, decay_off, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline SsdLayout ssd_layout(const SsdShape& s) {
   SsdLayout l;
-  const size_t per_bh = (size_t)s.nchunks * s.chunk * sizeof(float);
-  l.dtv_off = 0;
-  l.cs_off = align256(l.dtv_off + (size_t)s.batch * s.nheads * per_bh);
-  l.states_off = align256(l.cs_off + (size_t)s.batch * s.nheads * per_bh);
-  l.total = align256(l.states_off + (size_t)s.batch * s.nchunks * s.nheads * s.headdim *
-                                        s.dstate * sizeof(float));
+  l.states_off = 0;
+  l.decay_off = align256((size_t)s.batch * s.nchunks * s.nheads * s.headdim * s.dstate * 2);
+  l.total = align256(l.decay_off + (size_t)s.batch * s.nheads * s.nchunks * sizeof(float));
   return l;
 }
 
