@@ -149,7 +149,7 @@ ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch,
  * caller-owned, contents need not be initialised; it is overwritten).
  *
  * Limits: nheads % ngroups == 0; chunk_size in {64, 128, 256};
- * headdim in {32, 64, 128}; dstate in {16, 32, 64, 128, 256}.
+ * headdim in {32, 64, 128}; dstate in {32, 64, 128, 256}; bf16 inputs only.
  */
 ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void *x, const void *dt,
                               const float *A, const void *B, const void *C,

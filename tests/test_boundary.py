@@ -81,7 +81,7 @@ def test_null_handle_is_last_check():
     assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg
 
 
-def ssd_ws(batch=2, seqlen=64, nheads=4, headdim=64, dstate=16, ngroups=1, chunk=64):
+def ssd_ws(batch=2, seqlen=64, nheads=4, headdim=64, dstate=32, ngroups=1, chunk=64):
     lib = ssm.load_library()
     n = ctypes.c_size_t(123)
     st = lib.ssd_chunk_scan_workspace_size(None, batch, seqlen, nheads, headdim, dstate,
@@ -96,6 +96,7 @@ def test_ssd_shape_checks():
     assert ssd_ws(chunk=100)[0] == ssm.SSM_ERR_UNSUPPORTED
     assert ssd_ws(headdim=48)[0] == ssm.SSM_ERR_UNSUPPORTED
     assert ssd_ws(dstate=100)[0] == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd_ws(dstate=16)[0] == ssm.SSM_ERR_UNSUPPORTED
     assert ssd_ws(batch=0)[0] == ssm.SSM_ERR_INVALID_ARG
     assert ssd_ws(batch=0)[2] == 0
 
