@@ -124,17 +124,28 @@ __device__ __forceinline__ void interleave_pairs(const uint4& r0, const uint4& r
   }
 }
 
+// Raw dt of this thread's position (thread t <-> position t of the chunk),
+// zero past the chunk or the sequence; loaded one head ahead of its use.
+__device__ __forceinline__ uint32_t load_dt_bits(const SsdArgs& a, int b, int c, int h) {
+  const int t = threadIdx.x;
+  const int64_t pos = (int64_t)c * a.chunk + t;
+  if (t < a.chunk && pos < a.seqlen) return a.dt[((int64_t)b * a.seqlen + pos) * a.nheads + h];
+  return 0u;
+}
+
 // For one (batch, chunk, head): sDt[s] = dt_s after bias and softplus and
 // sCs2[s] = log2(e) * sum_{m <= s} A_h dt_m (inclusive, within the chunk), for
-// s < chunk; positions past the sequence end have dt = 0.  256 threads.
-__device__ void chunk_log_decay(const SsdArgs& a, int b, int c, int h, float* sCs2, float* sDt,
-                                float* sTmp) {
+// s < chunk; positions past the sequence end have dt = 0.  `dt_bits` is this
+// thread's raw dt (from load_dt_bits).  Every thread of the block calls it;
+// threads at or past the chunk length contribute nothing.
+__device__ void chunk_log_decay(const SsdArgs& a, int c, int h, uint32_t dt_bits, float* sCs2,
+                                float* sDt, float* sTmp) {
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
   const int64_t pos = (int64_t)c * a.chunk + t;
   float dtv = 0.0f;
   if (t < a.chunk && pos < a.seqlen) {
-    float v = bf16_bits_to_f32(a.dt[((int64_t)b * a.seqlen + pos) * a.nheads + h]);
+    float v = bf16_bits_to_f32(dt_bits);
     if (a.dt_bias) v += a.dt_bias[h];
     dtv = a.dt_softplus ? softplus_f(v) : v;
   }
@@ -144,37 +155,67 @@ __device__ void chunk_log_decay(const SsdArgs& a, int b, int c, int h, float* sC
     const float o = __shfl_up(v, off, 64);
     if (lane >= off) v += o;
   }
-  if (lane == 63) sTmp[wv] = v;
+  if (lane == 63 && wv < kQMax / 64) sTmp[wv] = v;
   __syncthreads();
-  float add = 0.0f;
-  for (int w = 0; w < wv; ++w) add += sTmp[w];
-  sCs2[t] = v + add;
-  sDt[t] = dtv;
+  if (t < a.chunk) {
+    float add = 0.0f;
+    for (int w = 0; w < wv; ++w) add += sTmp[w];
+    sCs2[t] = v + add;
+    sDt[t] = dtv;
+  }
   __syncthreads();
 }
 
 // ---- 1. chunk states ---------------------------------------------------------
 
-template <int P, int NB>
-__global__ void __launch_bounds__(256) ssd_chunk_state_kernel(SsdArgs a) {
+// One workgroup (NW waves) per (chunk, batch, head group).  B^T of the chunk is
+// staged once; each head's (w x)^T is staged from registers loaded while the
+// previous head was computing.
+template <int P, int NB, int NW>
+__global__ void __launch_bounds__(64 * NW) ssd_chunk_state_kernel(SsdArgs a) {
   __shared__ alignas(16) uint16_t sBt[NB][kRowQ];  // B^T of one state block: [n][s]
   __shared__ alignas(16) uint16_t sXt[P][kRowQ];   // (w x)^T of one head: [p][s]
   __shared__ float sCs2[kQMax], sDt[kQMax], sW[kQMax], sTmp[4];
-  constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + 3) / 4;
+  constexpr int NTHR = 64 * NW;
+  constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
+  constexpr int XTASKS = (P / 8) * (kQMax / 2);
+  constexpr int XPT = (XTASKS + NTHR - 1) / NTHR;  // x staging tasks per thread (at Q = 256)
 
   const int c = blockIdx.x, b = blockIdx.y;
   const int hpg = a.nheads / a.ngroups;
   const int h0 = blockIdx.z * a.heads_per_wg_state;
+  const int nh = min(a.heads_per_wg_state, a.nheads - h0);
   const int g = h0 / hpg;
   const int Q = a.chunk, N = a.dstate, L = a.seqlen;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int64_t pos0 = (int64_t)c * Q;
+  const int xtasks = (P / 8) * (Q / 2);
+
+  // Per-head inputs held in registers one head ahead.
+  uint4 xr0[XPT], xr1[XPT];
+  uint32_t dtb = 0;
+  auto prefetch = [&](int h) {
+    dtb = load_dt_bits(a, b, c, h);
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) {
+      const int task = tid + k * NTHR;
+      xr0[k] = xr1[k] = make_uint4(0, 0, 0, 0);
+      if (task < xtasks) {
+        const int sp = task % (Q / 2), po = task / (Q / 2);
+        const int s = 2 * sp;
+        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h;
+        if (pos0 + s < L) xr0[k] = load16(a.x + row * P + 8 * po);
+        if (pos0 + s + 1 < L) xr1[k] = load16(a.x + (row + a.nheads) * P + 8 * po);
+      }
+    }
+  };
 
   for (int nb0 = 0; nb0 < N; nb0 += NB) {
+    prefetch(h0);
     __syncthreads();  // earlier readers of sBt are done
     // B^T[n][s] for this state block, two positions per 32-bit LDS word.
-    for (int task = tid; task < (NB / 8) * (Q / 2); task += 256) {
+    for (int task = tid; task < (NB / 8) * (Q / 2); task += NTHR) {
       const int sp = task % (Q / 2), no = task / (Q / 2);
       const int s = 2 * sp;
       const int64_t row = ((int64_t)b * L + pos0 + s) * a.ngroups + g;
@@ -186,35 +227,36 @@ __global__ void __launch_bounds__(256) ssd_chunk_state_kernel(SsdArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sBt[8 * no + i][s]) = w[i];
     }
-    for (int hh = 0; hh < a.heads_per_wg_state; ++hh) {
+    for (int hh = 0; hh < nh; ++hh) {
       const int h = h0 + hh;
-      if (h >= a.nheads) break;
-      chunk_log_decay(a, b, c, h, sCs2, sDt, sTmp);
+      chunk_log_decay(a, c, h, dtb, sCs2, sDt, sTmp);
       const float cs_last = sCs2[Q - 1];
       if (tid < Q) sW[tid] = fast_exp2(cs_last - sCs2[tid]) * sDt[tid];
       if (nb0 == 0 && tid == 0)
         a.decay[((int64_t)b * a.nheads + h) * a.nchunks + c] = fast_exp2(cs_last);
       __syncthreads();
-      // (w x)^T[p][s], rounded to bf16.
-      for (int task = tid; task < (P / 8) * (Q / 2); task += 256) {
-        const int sp = task % (Q / 2), po = task / (Q / 2);
-        const int s = 2 * sp;
-        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h;
-        uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
-        if (pos0 + s < L) r0 = load16(a.x + row * P + 8 * po);
-        if (pos0 + s + 1 < L) r1 = load16(a.x + (row + a.nheads) * P + 8 * po);
-        const float w0 = sW[s], w1 = sW[s + 1];
-        const uint32_t e0[4] = {r0.x, r0.y, r0.z, r0.w}, e1[4] = {r1.x, r1.y, r1.z, r1.w};
+      // (w x)^T[p][s], rounded to bf16, from the prefetched rows.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t b0 = (i & 1) ? (e0[i / 2] >> 16) : (e0[i / 2] & 0xffffu);
-          const uint32_t b1 = (i & 1) ? (e1[i / 2] >> 16) : (e1[i / 2] & 0xffffu);
-          const uint32_t v0 = f32_to_bf16_bits(bf16_bits_to_f32(b0) * w0);
-          const uint32_t v1 = f32_to_bf16_bits(bf16_bits_to_f32(b1) * w1);
-          *reinterpret_cast<uint32_t*>(&sXt[8 * po + i][s]) = v0 | (v1 << 16);
+      for (int k = 0; k < XPT; ++k) {
+        const int task = tid + k * NTHR;
+        if (task < xtasks) {
+          const int sp = task % (Q / 2), po = task / (Q / 2);
+          const int s = 2 * sp;
+          const float w0 = sW[s], w1 = sW[s + 1];
+          const uint32_t e0[4] = {xr0[k].x, xr0[k].y, xr0[k].z, xr0[k].w};
+          const uint32_t e1[4] = {xr1[k].x, xr1[k].y, xr1[k].z, xr1[k].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t b0 = (i & 1) ? (e0[i / 2] >> 16) : (e0[i / 2] & 0xffffu);
+            const uint32_t b1 = (i & 1) ? (e1[i / 2] >> 16) : (e1[i / 2] & 0xffffu);
+            const uint32_t v0 = f32_to_bf16_bits(bf16_bits_to_f32(b0) * w0);
+            const uint32_t v1 = f32_to_bf16_bits(bf16_bits_to_f32(b1) * w1);
+            *reinterpret_cast<uint32_t*>(&sXt[8 * po + i][s]) = v0 | (v1 << 16);
+          }
         }
       }
       __syncthreads();
+      if (hh + 1 < nh) prefetch(h + 1);
       // S_c^T[n][p] = sum_s B^T[n][s] (w x)^T[p][s]
       f32x4 acc[TPW];
 #pragma unroll
@@ -223,7 +265,7 @@ __global__ void __launch_bounds__(256) ssd_chunk_state_kernel(SsdArgs a) {
         const int s = ks * 32 + 8 * q4;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-          const int tile = wv + 4 * t;
+          const int tile = wv + NW * t;
           if (tile < TILES) {
             const int nt = tile / PT, pt = tile % PT;
             const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&sBt[nt * 16 + r16][s]));
@@ -236,7 +278,7 @@ __global__ void __launch_bounds__(256) ssd_chunk_state_kernel(SsdArgs a) {
       uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const int tile = wv + 4 * t;
+        const int tile = wv + NW * t;
         if (tile < TILES) {
           const int nt = tile / PT, pt = tile % PT;
           const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
@@ -286,115 +328,143 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
 
 // ---- 3. chunk output ---------------------------------------------------------
 
+// One workgroup of 16 waves per (chunk, batch, head group); wave w owns the
+// 16 output positions l = 16w .. 16w+15 of the chunk (waves past the chunk
+// length only help staging) and needs the s-tiles 0..w (causality).  G^T = B C^T is built once per workgroup from B staged
+// 32 states at a time and kept (bf16) in registers for all heads of the
+// group; each head's x^T and carried state are staged in LDS from registers
+// loaded while the previous head was computing.
 template <int P, int N>
-__global__ void __launch_bounds__(256) ssd_chunk_out_kernel(SsdArgs a) {
-  __shared__ alignas(16) uint16_t sXt[P][kRowQ];  // x^T of one head: [p][s]
-  __shared__ float sCs2[kQMax], sDt[kQMax], sTmp[4];
-  constexpr int KN = N / 32;       // contraction steps over the state axis
-  constexpr int ST = kQMax / 16;   // most s-tiles a wave can need
+__global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
+  constexpr int KN = N / 32;         // contraction steps over the state axis
+  constexpr int ST = kQMax / 16;     // most s-tiles a wave can need
   constexpr int PT = P / 16;
+  constexpr int kRowN = N + 8;       // LDS row stride (bf16) of [p][n]
+  constexpr int NTHR = 1024;
+  constexpr int XPT = ((P / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
+  constexpr int SPT = (P * N / 8 + NTHR - 1) / NTHR;
+  __shared__ alignas(16) uint16_t sXt[P][kRowQ];   // x^T of one head: [p][s]
+  __shared__ alignas(16) uint16_t sS[P][kRowN];    // S_in of one head: [p][n]
+  __shared__ alignas(16) uint16_t sBk[kQMax][40];  // 32 states of B: [s][n] (+pad)
+  __shared__ float sCs2[kQMax], sDt[kQMax], sTmp[4];
 
   const int Q = a.chunk, L = a.seqlen;
-  const int nlb = Q / 64;
-  const int c = blockIdx.x / nlb, lb = blockIdx.x % nlb;
-  const int b = blockIdx.y;
+  const int c = blockIdx.x, b = blockIdx.y;
   const int hpg = a.nheads / a.ngroups;
   const int h0 = blockIdx.z * a.heads_per_wg_out;
+  const int nh = min(a.heads_per_wg_out, a.nheads - h0);
   const int g = h0 / hpg;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int l0 = lb * 64;
-  const int lt = l0 + 16 * wv;      // first position of this wave's 16 output columns
-  const int l = lt + r16;           // this lane's output position within the chunk
-  const int ns = lt / 16 + 1;       // s-tiles 0..ns-1 cover every s <= lt + 15
-  const int send = l0 + 64;         // staged positions [0, send)
+  const int l = 16 * wv + r16;       // this lane's output position within the chunk
+  const bool active = 16 * wv < Q;   // wave owns positions inside the chunk
+  const int ns = active ? wv + 1 : 0;  // s-tiles 0..wv cover every s <= l
   const int64_t pos0 = (int64_t)c * Q;
-  const bool l_ok = pos0 + l < L;
+  const bool l_ok = active && pos0 + l < L;
+  const int xtasks = (P / 8) * (Q / 2);
 
-  // C row of this lane's position, 8 states per contraction step.
-  uint4 cr[KN];
-  {
-    const uint16_t* crow = a.C + (((int64_t)b * L + pos0 + l) * a.ngroups + g) * N;
+  const uint16_t* crow = a.C + (((int64_t)b * L + pos0 + (l_ok ? l : 0)) * a.ngroups + g) * N;
+
+  // Per-head inputs held in registers one head ahead.
+  uint4 xr0[XPT], xr1[XPT], sr[SPT];
+  uint32_t dtb = 0;
+  auto prefetch = [&](int h) {
+    dtb = load_dt_bits(a, b, c, h);
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk)
-      cr[kk] = l_ok ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0);
-  }
-  // G^T[s][l] = sum_n B[s][n] C[l][n] for the s-tiles this wave needs.
+    for (int k = 0; k < XPT; ++k) {
+      const int task = tid + k * NTHR;
+      xr0[k] = xr1[k] = make_uint4(0, 0, 0, 0);
+      if (task < xtasks) {
+        const int sp = task % (Q / 2), po = task / (Q / 2);
+        const int s = 2 * sp;
+        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h;
+        if (pos0 + s < L) xr0[k] = load16(a.x + row * P + 8 * po);
+        if (pos0 + s + 1 < L) xr1[k] = load16(a.x + (row + a.nheads) * P + 8 * po);
+      }
+    }
+    const uint16_t* sin = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int task = tid + k * NTHR;
+      sr[k] = (c > 0 && task < P * N / 8) ? load16(sin + 8 * task) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  prefetch(h0);
+
+  // G^T[s][l] = sum_n B[s][n] C[l][n] for s-tiles 0..ns-1, B staged 32
+  // states at a time.
   f32x4 gacc[ST];
 #pragma unroll
   for (int st = 0; st < ST; ++st) gacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
   for (int kk = 0; kk < KN; ++kk) {
-    const bf16x8 bop = as_bf16x8(cr[kk]);
+    __syncthreads();  // earlier readers of sBk are done
+    for (int task = tid; task < Q * 4; task += NTHR) {
+      const int s = task >> 2, part = task & 3;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (pos0 + s < L)
+        v = load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + kk * 32 + 8 * part);
+      *reinterpret_cast<uint4*>(&sBk[s][8 * part]) = v;
+    }
+    const bf16x8 bop =
+        as_bf16x8(l_ok ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0));
+    __syncthreads();
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       if (st < ns) {
-        const int s = st * 16 + r16;
-        uint4 ar = make_uint4(0, 0, 0, 0);
-        if (pos0 + s < L)
-          ar = load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + kk * 32 + 8 * q4);
-        gacc[st] = mfma_bf16(as_bf16x8(ar), bop, gacc[st]);
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&sBk[st * 16 + r16][8 * q4]));
+        gacc[st] = mfma_bf16(av, bop, gacc[st]);
       }
     }
   }
-
-  for (int hh = 0; hh < a.heads_per_wg_out; ++hh) {
-    const int h = h0 + hh;
-    if (h >= a.nheads) break;
-    chunk_log_decay(a, b, c, h, sCs2, sDt, sTmp);
-    // x^T[p][s] for s in [0, send), exact bf16.
-    for (int task = tid; task < (P / 8) * (send / 2); task += 256) {
-      const int sp = task % (send / 2), po = task / (send / 2);
-      const int s = 2 * sp;
-      const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h;
-      uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
-      if (pos0 + s < L) r0 = load16(a.x + row * P + 8 * po);
-      if (pos0 + s + 1 < L) r1 = load16(a.x + (row + a.nheads) * P + 8 * po);
-      uint32_t w[8];
-      interleave_pairs(r0, r1, w);
+  // Keep G^T as bf16: pair j holds tiles 2j (slots 0-3) and 2j+1 (slots 4-7).
+  bf16x8 gpk[ST / 2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sXt[8 * po + i][s]) = w[i];
+  for (int j = 0; j < ST / 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gpk[j][i] = static_cast<__bf16>(gacc[2 * j][i]);
+      gpk[j][4 + i] = static_cast<__bf16>(gacc[2 * j + 1][i]);
     }
-    __syncthreads();
 
-    // M^T operands: slot (q4, half*4 + i) of pair j holds s = 32j + 16*half + 4*q4 + i.
-    const float cs_l = sCs2[l];
-    bf16x8 mop[ST / 2];
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    // C row of this lane's position for the carried-state product (loaded
+    // early; its latency overlaps the scan and the staging).
+    uint4 cr[KN];
 #pragma unroll
-    for (int j = 0; j < ST / 2; ++j) {
+    for (int kk = 0; kk < KN; ++kk)
+      cr[kk] = (l_ok && c > 0) ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0);
+    chunk_log_decay(a, c, h, dtb, sCs2, sDt, sTmp);
+    // stage x^T[p][s] (exact bf16) and S_in[p][n] from the prefetched registers
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int st = 2 * j + half;
+    for (int k = 0; k < XPT; ++k) {
+      const int task = tid + k * NTHR;
+      if (task < xtasks) {
+        const int sp = task % (Q / 2), po = task / (Q / 2);
+        uint32_t w[8];
+        interleave_pairs(xr0[k], xr1[k], w);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = st * 16 + 4 * q4 + i;
-          float v = 0.0f;
-          if (st < ns && s <= l) v = gacc[st][i] * fast_exp2(cs_l - sCs2[s]) * sDt[s];
-          mop[j][half * 4 + i] = static_cast<__bf16>(v);
-        }
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sXt[8 * po + i][2 * sp]) = w[i];
       }
     }
-    // Y^T[p][l] = sum_s x^T[p][s] M^T[s][l]
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int task = tid + k * NTHR;
+      if (task < P * N / 8) {
+        const int p = task / (N / 8), n8 = task % (N / 8);
+        *reinterpret_cast<uint4*>(&sS[p][8 * n8]) = sr[k];
+      }
+    }
+    __syncthreads();
+    if (hh + 1 < nh) prefetch(h + 1);
+
+    const float cs_l = active ? sCs2[l] : 0.0f;
     f32x4 yacc[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < ST / 2; ++j) {
-      if (2 * j < ns) {
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const uint16_t* row = &sXt[pt * 16 + r16][0];
-          const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * j + 4 * q4);
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * j + 16 + 4 * q4);
-          const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          yacc[pt] = mfma_bf16(av, mop[j], yacc[pt]);
-        }
-      }
-    }
-    // Y^T[p][l] += sum_n S_in[p][n] exp(cs_l) C[l][n]   (S_in = 0 for chunk 0)
-    if (c > 0) {
+    // Y^T[p][l] = sum_n S_in[p][n] exp(cs_l) C[l][n]   (S_in = 0 for chunk 0)
+    if (c > 0 && active) {
       const float el = fast_exp2(cs_l);
-      const uint16_t* sin = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
         const bf16x8 craw = as_bf16x8(cr[kk]);
@@ -403,8 +473,37 @@ __global__ void __launch_bounds__(256) ssd_chunk_out_kernel(SsdArgs a) {
         for (int i = 0; i < 8; ++i) cop[i] = static_cast<__bf16>(static_cast<float>(craw[i]) * el);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
-          const bf16x8 av = as_bf16x8(load16(sin + (int64_t)(pt * 16 + r16) * N + kk * 32 + 8 * q4));
+          const bf16x8 av =
+              as_bf16x8(*reinterpret_cast<const uint4*>(&sS[pt * 16 + r16][kk * 32 + 8 * q4]));
           yacc[pt] = mfma_bf16(av, cop, yacc[pt]);
+        }
+      }
+    }
+    // Y^T[p][l] += sum_s x^T[p][s] M^T[s][l], M^T built pair by pair:
+    // slot (q4, half*4 + i) of pair j holds s = 32j + 16*half + 4*q4 + i.
+#pragma unroll
+    for (int j = 0; j < ST / 2; ++j) {
+      if (2 * j < ns) {
+        bf16x8 mop;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int st = 2 * j + half;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = st * 16 + 4 * q4 + i;
+            float v = 0.0f;
+            if (st < ns && s <= l)
+              v = static_cast<float>(gpk[j][half * 4 + i]) * fast_exp2(cs_l - sCs2[s]) * sDt[s];
+            mop[half * 4 + i] = static_cast<__bf16>(v);
+          }
+        }
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const uint16_t* row = &sXt[pt * 16 + r16][0];
+          const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * j + 4 * q4);
+          const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * j + 16 + 4 * q4);
+          const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          yacc[pt] = mfma_bf16(av, mop, yacc[pt]);
         }
       }
     }
@@ -458,13 +557,11 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.dstate = s.dstate; a.ngroups = s.ngroups; a.chunk = s.chunk; a.nchunks = s.nchunks;
   const int hpg = s.nheads / s.ngroups;
   a.heads_per_wg_state = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256);
-  const int nlb = s.chunk / 64;
-  a.heads_per_wg_out =
-      heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * nlb * s.batch, 1024);
+  a.heads_per_wg_out = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256);
 
   constexpr int NB = N > 128 ? 128 : N;
   dim3 g1(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_state - 1) / a.heads_per_wg_state);
-  hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB>), g1, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB, 16>), g1, dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t PN = (int64_t)P * N;
@@ -472,8 +569,8 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(ssd_state_pass_kernel, g2, dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g3(s.nchunks * nlb, s.batch, (s.nheads + a.heads_per_wg_out - 1) / a.heads_per_wg_out);
-  hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N>), g3, dim3(256), 0, stream, a);
+  dim3 g3(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_out - 1) / a.heads_per_wg_out);
+  hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N>), g3, dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
