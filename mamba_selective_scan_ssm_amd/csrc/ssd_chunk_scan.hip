@@ -124,62 +124,90 @@ __device__ __forceinline__ void interleave_pairs(const uint4& r0, const uint4& r
   }
 }
 
-// Raw dt of this thread's position (thread t <-> position t of the chunk),
-// zero past the chunk or the sequence; loaded one head ahead of its use.
-__device__ __forceinline__ uint32_t load_dt_bits(const SsdArgs& a, int b, int c, int h) {
-  const int t = threadIdx.x;
+constexpr int kHGMax = 8;           // most heads one workgroup handles
+
+// Raw dt for the log-decay of every head of a workgroup's group: NTHR
+// threads form NTHR/256 groups of 256; round r covers heads
+// r*(NTHR/256) .. and thread t of a group owns chunk position t.  Loaded
+// early so that the latency overlaps other work.
+template <int NTHR>
+__device__ __forceinline__ void load_group_dt(const SsdArgs& a, int b, int c, int h0, int nh,
+                                              uint32_t (&dtb)[kHGMax / (NTHR / 256)]) {
+  constexpr int NGRP = NTHR / 256, ROUNDS = kHGMax / NGRP;
+  const int tid = threadIdx.x, grp = tid >> 8, t = tid & 255;
   const int64_t pos = (int64_t)c * a.chunk + t;
-  if (t < a.chunk && pos < a.seqlen) return a.dt[((int64_t)b * a.seqlen + pos) * a.nheads + h];
-  return 0u;
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int hh = NGRP * r + grp;
+    dtb[r] = (hh < nh && t < a.chunk && pos < a.seqlen)
+                 ? a.dt[((int64_t)b * a.seqlen + pos) * a.nheads + h0 + hh]
+                 : 0u;
+  }
 }
 
-// For one (batch, chunk, head): sDt[s] = dt_s after bias and softplus and
-// sCs2[s] = log2(e) * sum_{m <= s} A_h dt_m (inclusive, within the chunk), for
-// s < chunk; positions past the sequence end have dt = 0.  `dt_bits` is this
-// thread's raw dt (from load_dt_bits).  Every thread of the block calls it;
-// threads at or past the chunk length contribute nothing.
-__device__ void chunk_log_decay(const SsdArgs& a, int c, int h, uint32_t dt_bits, float* sCs2,
-                                float* sDt, float* sTmp) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, wv = t >> 6;
+// Log-decay of every head of the group for one (batch, chunk):
+// sDt[hh][s] = dt after bias and softplus, sCs2[hh][s] = log2(e) * inclusive
+// within-chunk cumsum of A_h dt (positions past the sequence end have
+// dt = 0).
+template <int NTHR>
+__device__ void group_log_decay(const SsdArgs& a, int c, int h0, int nh,
+                                const uint32_t (&dtb)[kHGMax / (NTHR / 256)],
+                                float (*sCs2)[kQMax], float (*sDt)[kQMax], float* sTmp) {
+  constexpr int NGRP = NTHR / 256, ROUNDS = kHGMax / NGRP;
+  const int tid = threadIdx.x;
+  const int grp = tid >> 8, t = tid & 255, lane = tid & 63, w4 = (tid >> 6) & 3;
   const int64_t pos = (int64_t)c * a.chunk + t;
-  float dtv = 0.0f;
-  if (t < a.chunk && pos < a.seqlen) {
-    float v = bf16_bits_to_f32(dt_bits);
-    if (a.dt_bias) v += a.dt_bias[h];
-    dtv = a.dt_softplus ? softplus_f(v) : v;
-  }
-  float v = a.A[h] * kLog2e * dtv;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63 && wv < kQMax / 64) sTmp[wv] = v;
-  __syncthreads();
-  if (t < a.chunk) {
+  for (int r = 0; r < ROUNDS; ++r) {
+    if (NGRP * r >= nh) break;
+    const int hh = NGRP * r + grp;
+    float dtv = 0.0f, ah = 0.0f;
+    if (hh < nh) {
+      ah = a.A[h0 + hh] * kLog2e;
+      if (t < a.chunk && pos < a.seqlen) {
+        float v = bf16_bits_to_f32(dtb[r]);
+        if (a.dt_bias) v += a.dt_bias[h0 + hh];
+        dtv = a.dt_softplus ? softplus_f(v) : v;
+      }
+    }
+    float v = ah * dtv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(v, off, 64);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) sTmp[grp * 4 + w4] = v;
+    __syncthreads();
     float add = 0.0f;
-    for (int w = 0; w < wv; ++w) add += sTmp[w];
-    sCs2[t] = v + add;
-    sDt[t] = dtv;
+    for (int w = 0; w < w4; ++w) add += sTmp[grp * 4 + w];
+    if (hh < nh) {
+      sCs2[hh][t] = v + add;
+      sDt[hh][t] = dtv;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 // ---- 1. chunk states ---------------------------------------------------------
 
-// One workgroup (NW waves) per (chunk, batch, head group).  B^T of the chunk is
-// staged once; each head's (w x)^T is staged from registers loaded while the
-// previous head was computing.
-template <int P, int NB, int NW>
-__global__ void __launch_bounds__(64 * NW) ssd_chunk_state_kernel(SsdArgs a) {
-  __shared__ alignas(16) uint16_t sBt[NB][kRowQ];  // B^T of one state block: [n][s]
-  __shared__ alignas(16) uint16_t sXt[P][kRowQ];   // (w x)^T of one head: [p][s]
-  __shared__ float sCs2[kQMax], sDt[kQMax], sW[kQMax], sTmp[4];
-  constexpr int NTHR = 64 * NW;
+// One 1024-thread workgroup per (chunk, batch, head group).  Every global
+// load that does not depend on earlier results is issued at the start.  B^T
+// of the chunk is staged once per state block; each head's (w x)^T is staged
+// from registers loaded while the previous head computed, into one of two
+// LDS buffers when both fit.
+template <int P, int NB>
+__global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
+  constexpr int NTHR = 1024, NW = 16;
+  constexpr bool DB = (size_t)(NB + 2 * P) * kRowQ * 2 + 2 * kHGMax * kQMax * 4 <= 156 * 1024;
+  constexpr int NBUF = DB ? 2 : 1;
+  __shared__ alignas(16) uint16_t sBt[NB][kRowQ];        // B^T of one state block: [n][s]
+  __shared__ alignas(16) uint16_t sXt[NBUF][P][kRowQ];   // (w x)^T of one head: [p][s]
+  __shared__ alignas(16) float sCs2[kHGMax][kQMax];
+  __shared__ alignas(16) float sDt[kHGMax][kQMax];
+  __shared__ float sTmp[16];
   constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
-  constexpr int XTASKS = (P / 8) * (kQMax / 2);
-  constexpr int XPT = (XTASKS + NTHR - 1) / NTHR;  // x staging tasks per thread (at Q = 256)
+  constexpr int XPT = ((P / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
+  constexpr int BPT = ((NB / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
 
   const int c = blockIdx.x, b = blockIdx.y;
   const int hpg = a.nheads / a.ngroups;
@@ -187,16 +215,15 @@ __global__ void __launch_bounds__(64 * NW) ssd_chunk_state_kernel(SsdArgs a) {
   const int nh = min(a.heads_per_wg_state, a.nheads - h0);
   const int g = h0 / hpg;
   const int Q = a.chunk, N = a.dstate, L = a.seqlen;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int r16 = lane & 15, q4 = lane >> 4;
   const int64_t pos0 = (int64_t)c * Q;
   const int xtasks = (P / 8) * (Q / 2);
+  const int btasks = (NB / 8) * (Q / 2);
 
-  // Per-head inputs held in registers one head ahead.
-  uint4 xr0[XPT], xr1[XPT];
-  uint32_t dtb = 0;
-  auto prefetch = [&](int h) {
-    dtb = load_dt_bits(a, b, c, h);
+  uint4 xr0[XPT], xr1[XPT], br0[BPT], br1[BPT];
+  auto prefetch = [&](int hh) {
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
@@ -204,59 +231,83 @@ __global__ void __launch_bounds__(64 * NW) ssd_chunk_state_kernel(SsdArgs a) {
       if (task < xtasks) {
         const int sp = task % (Q / 2), po = task / (Q / 2);
         const int s = 2 * sp;
-        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h;
+        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h0 + hh;
         if (pos0 + s < L) xr0[k] = load16(a.x + row * P + 8 * po);
         if (pos0 + s + 1 < L) xr1[k] = load16(a.x + (row + a.nheads) * P + 8 * po);
       }
     }
   };
-
-  for (int nb0 = 0; nb0 < N; nb0 += NB) {
-    prefetch(h0);
-    __syncthreads();  // earlier readers of sBt are done
-    // B^T[n][s] for this state block, two positions per 32-bit LDS word.
-    for (int task = tid; task < (NB / 8) * (Q / 2); task += NTHR) {
-      const int sp = task % (Q / 2), no = task / (Q / 2);
-      const int s = 2 * sp;
-      const int64_t row = ((int64_t)b * L + pos0 + s) * a.ngroups + g;
-      uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
-      if (pos0 + s < L) r0 = load16(a.B + row * N + nb0 + 8 * no);
-      if (pos0 + s + 1 < L) r1 = load16(a.B + (row + a.ngroups) * N + nb0 + 8 * no);
-      uint32_t w[8];
-      interleave_pairs(r0, r1, w);
+  auto load_b = [&](int nb0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sBt[8 * no + i][s]) = w[i];
+    for (int k = 0; k < BPT; ++k) {
+      const int task = tid + k * NTHR;
+      br0[k] = br1[k] = make_uint4(0, 0, 0, 0);
+      if (task < btasks) {
+        const int sp = task % (Q / 2), no = task / (Q / 2);
+        const int s = 2 * sp;
+        const int64_t row = ((int64_t)b * L + pos0 + s) * a.ngroups + g;
+        if (pos0 + s < L) br0[k] = load16(a.B + row * N + nb0 + 8 * no);
+        if (pos0 + s + 1 < L) br1[k] = load16(a.B + (row + a.ngroups) * N + nb0 + 8 * no);
+      }
     }
-    for (int hh = 0; hh < nh; ++hh) {
-      const int h = h0 + hh;
-      chunk_log_decay(a, c, h, dtb, sCs2, sDt, sTmp);
-      const float cs_last = sCs2[Q - 1];
-      if (tid < Q) sW[tid] = fast_exp2(cs_last - sCs2[tid]) * sDt[tid];
-      if (nb0 == 0 && tid == 0)
-        a.decay[((int64_t)b * a.nheads + h) * a.nchunks + c] = fast_exp2(cs_last);
-      __syncthreads();
-      // (w x)^T[p][s], rounded to bf16, from the prefetched rows.
+  };
+  // (w x)^T[p][s] = x[s][p] exp2(cs_last - cs_s) dt_s, rounded to bf16.
+  auto stage = [&](int hh, int buf) {
+    const float cs_last = sCs2[hh][Q - 1];
 #pragma unroll
-      for (int k = 0; k < XPT; ++k) {
-        const int task = tid + k * NTHR;
-        if (task < xtasks) {
-          const int sp = task % (Q / 2), po = task / (Q / 2);
-          const int s = 2 * sp;
-          const float w0 = sW[s], w1 = sW[s + 1];
-          const uint32_t e0[4] = {xr0[k].x, xr0[k].y, xr0[k].z, xr0[k].w};
-          const uint32_t e1[4] = {xr1[k].x, xr1[k].y, xr1[k].z, xr1[k].w};
+    for (int k = 0; k < XPT; ++k) {
+      const int task = tid + k * NTHR;
+      if (task < xtasks) {
+        const int sp = task % (Q / 2), po = task / (Q / 2);
+        const int s = 2 * sp;
+        const float w0 = fast_exp2(cs_last - sCs2[hh][s]) * sDt[hh][s];
+        const float w1 = fast_exp2(cs_last - sCs2[hh][s + 1]) * sDt[hh][s + 1];
+        const uint32_t e0[4] = {xr0[k].x, xr0[k].y, xr0[k].z, xr0[k].w};
+        const uint32_t e1[4] = {xr1[k].x, xr1[k].y, xr1[k].z, xr1[k].w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t b0 = (i & 1) ? (e0[i / 2] >> 16) : (e0[i / 2] & 0xffffu);
-            const uint32_t b1 = (i & 1) ? (e1[i / 2] >> 16) : (e1[i / 2] & 0xffffu);
-            const uint32_t v0 = f32_to_bf16_bits(bf16_bits_to_f32(b0) * w0);
-            const uint32_t v1 = f32_to_bf16_bits(bf16_bits_to_f32(b1) * w1);
-            *reinterpret_cast<uint32_t*>(&sXt[8 * po + i][s]) = v0 | (v1 << 16);
-          }
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b0 = (i & 1) ? (e0[i / 2] >> 16) : (e0[i / 2] & 0xffffu);
+          const uint32_t b1 = (i & 1) ? (e1[i / 2] >> 16) : (e1[i / 2] & 0xffffu);
+          const uint32_t v0 = f32_to_bf16_bits(bf16_bits_to_f32(b0) * w0);
+          const uint32_t v1 = f32_to_bf16_bits(bf16_bits_to_f32(b1) * w1);
+          *reinterpret_cast<uint32_t*>(&sXt[buf][8 * po + i][s]) = v0 | (v1 << 16);
         }
       }
-      __syncthreads();
-      if (hh + 1 < nh) prefetch(h + 1);
+    }
+  };
+
+  uint32_t dtb[kHGMax / (NTHR / 256)];
+  load_group_dt<NTHR>(a, b, c, h0, nh, dtb);
+  load_b(0);
+  prefetch(0);
+  group_log_decay<NTHR>(a, c, h0, nh, dtb, sCs2, sDt, sTmp);
+  if (tid < nh)
+    a.decay[((int64_t)b * a.nheads + h0 + tid) * a.nchunks + c] = fast_exp2(sCs2[tid][Q - 1]);
+
+  for (int nb0 = 0; nb0 < N; nb0 += NB) {
+    if (nb0 > 0) {
+      load_b(nb0);
+      prefetch(0);
+      __syncthreads();  // earlier readers of sBt and sXt are done
+    }
+    // B^T[n][s] for this state block, two positions per 32-bit LDS word.
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int task = tid + k * NTHR;
+      if (task < btasks) {
+        const int sp = task % (Q / 2), no = task / (Q / 2);
+        uint32_t w[8];
+        interleave_pairs(br0[k], br1[k], w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sBt[8 * no + i][2 * sp]) = w[i];
+      }
+    }
+    stage(0, 0);
+    if (nh > 1) prefetch(1);
+    __syncthreads();
+    for (int hh = 0; hh < nh; ++hh) {
+      const int h = h0 + hh;
+      const int buf = DB ? (hh & 1) : 0;
       // S_c^T[n][p] = sum_s B^T[n][s] (w x)^T[p][s]
       f32x4 acc[TPW];
 #pragma unroll
@@ -269,7 +320,8 @@ __global__ void __launch_bounds__(64 * NW) ssd_chunk_state_kernel(SsdArgs a) {
           if (tile < TILES) {
             const int nt = tile / PT, pt = tile % PT;
             const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&sBt[nt * 16 + r16][s]));
-            const bf16x8 bv = as_bf16x8(*reinterpret_cast<const uint4*>(&sXt[pt * 16 + r16][s]));
+            const bf16x8 bv =
+                as_bf16x8(*reinterpret_cast<const uint4*>(&sXt[buf][pt * 16 + r16][s]));
             acc[t] = mfma_bf16(av, bv, acc[t]);
           }
         }
@@ -287,6 +339,12 @@ __global__ void __launch_bounds__(64 * NW) ssd_chunk_state_kernel(SsdArgs a) {
           o.y = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
           *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
         }
+      }
+      if (hh + 1 < nh) {
+        if (!DB) __syncthreads();  // readers of the single buffer are done
+        stage(hh + 1, DB ? ((hh + 1) & 1) : 0);
+        if (hh + 2 < nh) prefetch(hh + 2);
+        __syncthreads();
       }
     }
   }
@@ -328,25 +386,47 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
 
 // ---- 3. chunk output ---------------------------------------------------------
 
-// One workgroup of 16 waves per (chunk, batch, head group); wave w owns the
-// 16 output positions l = 16w .. 16w+15 of the chunk (waves past the chunk
-// length only help staging) and needs the s-tiles 0..w (causality).  G^T = B C^T is built once per workgroup from B staged
-// 32 states at a time and kept (bf16) in registers for all heads of the
-// group; each head's x^T and carried state are staged in LDS from registers
-// loaded while the previous head was computing.
+// One 512-thread workgroup (8 waves) per (chunk, batch, head group).  The
+// chunk's 16-position output tiles are paired so every wave does the same
+// causal work: wave w owns tiles A = w and B = Q/16-1-w and needs s-tiles
+// 0..A for A and 0..B for B, which pack into exactly Q/32 + 1 pairs of
+// s-tiles (9 for Q = 256).  G^T = B C^T for those pairs is built once per
+// workgroup (B staged up to 128 states at a time) and kept as bf16 in
+// registers for every head of the group.  The log-decays of all heads are
+// computed up front; each head's x^T and carried state are staged from
+// registers loaded while the previous head computed, into one of two LDS
+// buffers when both fit, so a head costs one barrier.  The carried-state
+// product uses C as loaded and is scaled by exp(cs_l) once per column.
 template <int P, int N>
-__global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
+__global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr int KN = N / 32;         // contraction steps over the state axis
-  constexpr int ST = kQMax / 16;     // most s-tiles a wave can need
+  constexpr int NP = kQMax / 32 + 1; // s-tile pairs per wave (at Q = 256)
   constexpr int PT = P / 16;
+  constexpr int KB = N < 128 ? N : 128;  // states of B per staging round
+  constexpr int kRowB = KB + 8;
   constexpr int kRowN = N + 8;       // LDS row stride (bf16) of [p][n]
-  constexpr int NTHR = 1024;
+  constexpr int NTHR = 512;
   constexpr int XPT = ((P / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
   constexpr int SPT = (P * N / 8 + NTHR - 1) / NTHR;
-  __shared__ alignas(16) uint16_t sXt[P][kRowQ];   // x^T of one head: [p][s]
-  __shared__ alignas(16) uint16_t sS[P][kRowN];    // S_in of one head: [p][n]
-  __shared__ alignas(16) uint16_t sBk[kQMax][40];  // 32 states of B: [s][n] (+pad)
-  __shared__ float sCs2[kQMax], sDt[kQMax], sTmp[4];
+  constexpr int BPT = (kQMax * KB / 8 + NTHR - 1) / NTHR;
+  // LDS: x^T [p][s] and S_in [p][n] of one head (two buffers when they
+  // fit); B [s][n] for the G^T phase shares the same bytes (it is only used
+  // before the first head is staged).
+  constexpr size_t kXtBytes = (size_t)P * kRowQ * 2;
+  constexpr size_t kSBytes = (size_t)P * kRowN * 2;
+  constexpr size_t kBBytes = (size_t)kQMax * kRowB * 2;
+  constexpr size_t kFixed = 2 * kHGMax * kQMax * 4 + 64;
+  constexpr bool DB = 2 * (kXtBytes + kSBytes) + kFixed <= 156 * 1024;
+  constexpr int NBUF = DB ? 2 : 1;
+  constexpr size_t kBufBytes = NBUF * (kXtBytes + kSBytes);
+  constexpr size_t kRawBytes = kBufBytes > kBBytes ? kBufBytes : kBBytes;
+  __shared__ alignas(16) uint8_t sRaw[kRawBytes];
+  __shared__ alignas(16) float sCs2[kHGMax][kQMax];
+  __shared__ alignas(16) float sDt[kHGMax][kQMax];
+  __shared__ float sTmp[16];
+  auto sXt = reinterpret_cast<uint16_t (*)[P][kRowQ]>(sRaw);
+  auto sS = reinterpret_cast<uint16_t (*)[P][kRowN]>(sRaw + NBUF * kXtBytes);
+  auto sBs = reinterpret_cast<uint16_t (*)[kRowB]>(sRaw);
 
   const int Q = a.chunk, L = a.seqlen;
   const int c = blockIdx.x, b = blockIdx.y;
@@ -354,22 +434,23 @@ __global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
   const int h0 = blockIdx.z * a.heads_per_wg_out;
   const int nh = min(a.heads_per_wg_out, a.nheads - h0);
   const int g = h0 / hpg;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int l = 16 * wv + r16;       // this lane's output position within the chunk
-  const bool active = 16 * wv < Q;   // wave owns positions inside the chunk
-  const int ns = active ? wv + 1 : 0;  // s-tiles 0..wv cover every s <= l
+  const int nlt = Q / 16;                    // output tiles in the chunk
+  const bool active = wv < nlt / 2;
+  const int ltile[2] = {wv, nlt - 1 - wv};   // this wave's two output tiles
+  const int npA = (wv + 2) / 2;              // s-tile pairs of tile A (ceil((A+1)/2))
+  const int npB = (nlt - wv + 1) / 2;        // s-tile pairs of tile B
   const int64_t pos0 = (int64_t)c * Q;
-  const bool l_ok = active && pos0 + l < L;
+  const int lcol[2] = {16 * ltile[0] + r16, 16 * ltile[1] + r16};  // this lane's positions
+  const bool lok[2] = {active && pos0 + lcol[0] < L, active && pos0 + lcol[1] < L};
   const int xtasks = (P / 8) * (Q / 2);
+  const int btasks = Q * KB / 8;
 
-  const uint16_t* crow = a.C + (((int64_t)b * L + pos0 + (l_ok ? l : 0)) * a.ngroups + g) * N;
-
-  // Per-head inputs held in registers one head ahead.
-  uint4 xr0[XPT], xr1[XPT], sr[SPT];
-  uint32_t dtb = 0;
-  auto prefetch = [&](int h) {
-    dtb = load_dt_bits(a, b, c, h);
+  uint4 xr0[XPT], xr1[XPT], sr[SPT], br[BPT], cr[2][KN];
+  auto prefetch = [&](int hh) {
+    const int h = h0 + hh;
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
@@ -389,53 +470,19 @@ __global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
       sr[k] = (c > 0 && task < P * N / 8) ? load16(sin + 8 * task) : make_uint4(0, 0, 0, 0);
     }
   };
-  prefetch(h0);
-
-  // G^T[s][l] = sum_n B[s][n] C[l][n] for s-tiles 0..ns-1, B staged 32
-  // states at a time.
-  f32x4 gacc[ST];
+  // B[s][kb0 .. kb0+KB) rows, 16 bytes per task.
+  auto load_b = [&](int kb0) {
 #pragma unroll
-  for (int st = 0; st < ST; ++st) gacc[st] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int kk = 0; kk < KN; ++kk) {
-    __syncthreads();  // earlier readers of sBk are done
-    for (int task = tid; task < Q * 4; task += NTHR) {
-      const int s = task >> 2, part = task & 3;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (pos0 + s < L)
-        v = load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + kk * 32 + 8 * part);
-      *reinterpret_cast<uint4*>(&sBk[s][8 * part]) = v;
+    for (int k = 0; k < BPT; ++k) {
+      const int task = tid + k * NTHR;
+      const int s = task / (KB / 8), part = task % (KB / 8);
+      br[k] = (task < btasks && pos0 + s < L)
+                  ? load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + kb0 + 8 * part)
+                  : make_uint4(0, 0, 0, 0);
     }
-    const bf16x8 bop =
-        as_bf16x8(l_ok ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0));
-    __syncthreads();
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-      if (st < ns) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&sBk[st * 16 + r16][8 * q4]));
-        gacc[st] = mfma_bf16(av, bop, gacc[st]);
-      }
-    }
-  }
-  // Keep G^T as bf16: pair j holds tiles 2j (slots 0-3) and 2j+1 (slots 4-7).
-  bf16x8 gpk[ST / 2];
-#pragma unroll
-  for (int j = 0; j < ST / 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gpk[j][i] = static_cast<__bf16>(gacc[2 * j][i]);
-      gpk[j][4 + i] = static_cast<__bf16>(gacc[2 * j + 1][i]);
-    }
-
-  for (int hh = 0; hh < nh; ++hh) {
-    const int h = h0 + hh;
-    // C row of this lane's position for the carried-state product (loaded
-    // early; its latency overlaps the scan and the staging).
-    uint4 cr[KN];
-#pragma unroll
-    for (int kk = 0; kk < KN; ++kk)
-      cr[kk] = (l_ok && c > 0) ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0);
-    chunk_log_decay(a, c, h, dtb, sCs2, sDt, sTmp);
-    // stage x^T[p][s] (exact bf16) and S_in[p][n] from the prefetched registers
+  };
+  // x^T[p][s] (exact bf16) and S_in[p][n] from the prefetched registers.
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
@@ -444,7 +491,8 @@ __global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
         uint32_t w[8];
         interleave_pairs(xr0[k], xr1[k], w);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sXt[8 * po + i][2 * sp]) = w[i];
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<uint32_t*>(&sXt[buf][8 * po + i][2 * sp]) = w[i];
       }
     }
 #pragma unroll
@@ -452,64 +500,151 @@ __global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
       const int task = tid + k * NTHR;
       if (task < P * N / 8) {
         const int p = task / (N / 8), n8 = task % (N / 8);
-        *reinterpret_cast<uint4*>(&sS[p][8 * n8]) = sr[k];
+        *reinterpret_cast<uint4*>(&sS[buf][p][8 * n8]) = sr[k];
+      }
+    }
+  };
+
+  // Issue the independent loads: C rows of this lane's two positions, B, dt.
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* crow =
+        a.C + (((int64_t)b * L + pos0 + (lok[t] ? lcol[t] : 0)) * a.ngroups + g) * N;
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk)
+      cr[t][kk] = lok[t] ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t dtb[kHGMax / (NTHR / 256)];
+  load_b(0);
+  load_group_dt<NTHR>(a, b, c, h0, nh, dtb);
+
+  // Pair p of this wave: output tile t = (p < npA ? A : B), s-tiles
+  // st0 = 2*(p - first pair of t) and st0 + 1; tiles past the output tile's
+  // diagonal are zero.
+  auto pair_tile = [&](int p) { return p < npA ? 0 : 1; };
+  auto pair_st0 = [&](int p) { return p < npA ? 2 * p : 2 * (p - npA); };
+  auto pair_on = [&](int p) { return active && p < npA + npB; };
+
+  // G^T[s][l] = sum_n B[s][n] C[l][n] for this wave's pairs.
+  f32x4 gacc[2 * NP];
+#pragma unroll
+  for (int k = 0; k < 2 * NP; ++k) gacc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int kb0 = 0; kb0 < N; kb0 += KB) {
+    if (kb0 > 0) __syncthreads();  // earlier readers of sBs are done
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int task = tid + k * NTHR;
+      if (task < btasks) {
+        const int s = task / (KB / 8), part = task % (KB / 8);
+        *reinterpret_cast<uint4*>(&sBs[s][8 * part]) = br[k];
       }
     }
     __syncthreads();
-    if (hh + 1 < nh) prefetch(h + 1);
-
-    const float cs_l = active ? sCs2[l] : 0.0f;
-    f32x4 yacc[PT];
+    if (kb0 + KB < N) load_b(kb0 + KB);
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) yacc[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // Y^T[p][l] = sum_n S_in[p][n] exp(cs_l) C[l][n]   (S_in = 0 for chunk 0)
+    for (int p = 0; p < NP; ++p) {
+      if (!pair_on(p)) continue;
+      const int t = pair_tile(p), st0 = pair_st0(p);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int st = st0 + half;
+        if (st > ltile[t]) continue;
+#pragma unroll
+        for (int kq = 0; kq < KB / 32; ++kq) {
+          const bf16x8 av =
+              as_bf16x8(*reinterpret_cast<const uint4*>(&sBs[st * 16 + r16][kq * 32 + 8 * q4]));
+          const bf16x8 bop = as_bf16x8(t ? cr[1][kb0 / 32 + kq] : cr[0][kb0 / 32 + kq]);
+          gacc[2 * p + half] = mfma_bf16(av, bop, gacc[2 * p + half]);
+        }
+      }
+    }
+  }
+  // Keep G^T as bf16: pair p holds s-tiles st0 (slots 0-3) and st0+1 (slots 4-7).
+  bf16x8 gpk[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gpk[p][i] = static_cast<__bf16>(gacc[2 * p][i]);
+      gpk[p][4 + i] = static_cast<__bf16>(gacc[2 * p + 1][i]);
+    }
+
+  prefetch(0);
+  group_log_decay<NTHR>(a, c, h0, nh, dtb, sCs2, sDt, sTmp);  // its barriers also retire sBs
+  stage(0);
+  if (nh > 1) prefetch(1);
+  __syncthreads();
+
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    const int buf = DB ? (hh & 1) : 0;
+    const float csl[2] = {active ? sCs2[hh][lcol[0]] : 0.0f, active ? sCs2[hh][lcol[1]] : 0.0f};
+    f32x4 yacc[2][PT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) yacc[t][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Y^T[p][l] = exp(cs_l) sum_n S_in[p][n] C[l][n]   (S_in = 0 for chunk 0)
     if (c > 0 && active) {
-      const float el = fast_exp2(cs_l);
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
-        const bf16x8 craw = as_bf16x8(cr[kk]);
-        bf16x8 cop;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cop[i] = static_cast<__bf16>(static_cast<float>(craw[i]) * el);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
           const bf16x8 av =
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sS[pt * 16 + r16][kk * 32 + 8 * q4]));
-          yacc[pt] = mfma_bf16(av, cop, yacc[pt]);
+              as_bf16x8(*reinterpret_cast<const uint4*>(&sS[buf][pt * 16 + r16][kk * 32 + 8 * q4]));
+          yacc[0][pt] = mfma_bf16(av, as_bf16x8(cr[0][kk]), yacc[0][pt]);
+          yacc[1][pt] = mfma_bf16(av, as_bf16x8(cr[1][kk]), yacc[1][pt]);
         }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float el = fast_exp2(csl[t]);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) yacc[t][pt] *= el;
       }
     }
     // Y^T[p][l] += sum_s x^T[p][s] M^T[s][l], M^T built pair by pair:
-    // slot (q4, half*4 + i) of pair j holds s = 32j + 16*half + 4*q4 + i.
+    // slot (q4, half*4 + i) of pair p holds s = 16*(st0 + half) + 4*q4 + i.
 #pragma unroll
-    for (int j = 0; j < ST / 2; ++j) {
-      if (2 * j < ns) {
-        bf16x8 mop;
+    for (int p = 0; p < NP; ++p) {
+      if (!pair_on(p)) continue;
+      const int t = pair_tile(p), st0 = pair_st0(p);
+      const int lt = ltile[t];
+      const float cs_l = t ? csl[1] : csl[0];
+      const int l = t ? lcol[1] : lcol[0];
+      const bool diag = st0 + 1 >= lt;  // pair reaches the output tile's diagonal
+      bf16x8 mop;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int st = 2 * j + half;
+      for (int half = 0; half < 2; ++half) {
+        const int st = st0 + half;
+        const int s0 = st * 16 + 4 * q4;
+        const float4 cs4 = *reinterpret_cast<const float4*>(&sCs2[hh][s0 & (kQMax - 1)]);
+        const float4 dt4 = *reinterpret_cast<const float4*>(&sDt[hh][s0 & (kQMax - 1)]);
+        const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
+        const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int s = st * 16 + 4 * q4 + i;
-            float v = 0.0f;
-            if (st < ns && s <= l)
-              v = static_cast<float>(gpk[j][half * 4 + i]) * fast_exp2(cs_l - sCs2[s]) * sDt[s];
-            mop[half * 4 + i] = static_cast<__bf16>(v);
-          }
+        for (int i = 0; i < 4; ++i) {
+          float v = static_cast<float>(gpk[p][half * 4 + i]) * fast_exp2(cs_l - csv[i]) * dtv[i];
+          if (diag && !(st <= lt && s0 + i <= l)) v = 0.0f;
+          mop[half * 4 + i] = static_cast<__bf16>(v);
         }
+      }
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-          const uint16_t* row = &sXt[pt * 16 + r16][0];
-          const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * j + 4 * q4);
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * j + 16 + 4 * q4);
-          const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          yacc[pt] = mfma_bf16(av, mop, yacc[pt]);
-        }
+      for (int pt = 0; pt < PT; ++pt) {
+        const uint16_t* row = &sXt[buf][pt * 16 + r16][0];
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * st0 + 4 * q4);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * st0 + 16 + 4 * q4);
+        const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        if (t) yacc[1][pt] = mfma_bf16(av, mop, yacc[1][pt]);
+        else yacc[0][pt] = mfma_bf16(av, mop, yacc[0][pt]);
       }
     }
     // y[l][p .. p+3] = Y^T[p .. p+3][l] + D_h x[l][p .. p+3]
-    if (l_ok) {
-      const float Dh = a.D ? a.D[h] : 0.0f;
+    const float Dh = a.D ? a.D[h] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (!lok[t]) continue;
+      const int l = lcol[t];
       uint16_t* yrow = a.y + (((int64_t)b * L + pos0 + l) * a.nheads + h) * P;
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
@@ -517,12 +652,18 @@ __global__ void __launch_bounds__(1024) ssd_chunk_out_kernel(SsdArgs a) {
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          v[i] = __builtin_fmaf(Dh, bf16_bits_to_f32(sXt[p + i][l]), yacc[pt][i]);
+          v[i] = __builtin_fmaf(Dh, bf16_bits_to_f32(sXt[buf][p + i][l]), yacc[t][pt][i]);
         uint2 o;
         o.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
         o.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
         *reinterpret_cast<uint2*>(yrow + p) = o;
       }
+    }
+    if (hh + 1 < nh) {
+      if (!DB) __syncthreads();  // readers of the single buffer are done
+      stage(DB ? ((hh + 1) & 1) : 0);
+      if (hh + 2 < nh) prefetch(hh + 2);
+      __syncthreads();
     }
   }
 }
@@ -561,7 +702,7 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
 
   constexpr int NB = N > 128 ? 128 : N;
   dim3 g1(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_state - 1) / a.heads_per_wg_state);
-  hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB, 16>), g1, dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB>), g1, dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t PN = (int64_t)P * N;
@@ -570,7 +711,7 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g3(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_out - 1) / a.heads_per_wg_out);
-  hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N>), g3, dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N>), g3, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ CASES = [  # (batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
     (2, 1000, 2, 64, 256, 1, 64),
     (1, 777, 6, 64, 128, 3, 256),
     (3, 129, 2, 32, 128, 2, 64),
+    (2, 4096, 32, 32, 64, 1, 256),   # several heads per workgroup
+    (1, 2048, 16, 64, 128, 2, 128),
 ]
 
 
