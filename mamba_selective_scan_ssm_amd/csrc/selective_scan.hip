@@ -282,11 +282,14 @@ selective_scan_fwd_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < TG; ++j) gk[j] = 1.0f;
       }
+      // Steps past the end are the identity (delta = 0).  Rows past `dim`
+      // compute on zeros and are never stored, so they need no mask.
+      const bool tail = ts + TG > L;
 #pragma unroll
       for (int j = 0; j < TG; ++j) {
         float dl = dr[j] + bias;
         if (prm.delta_softplus) dl = softplus_f(dl);
-        if (ts + j >= L || !row_ok) dl = 0.0f;  // padding steps are the identity
+        if (tail && ts + j >= L) dl = 0.0f;
         sDD[w][g * TG + j][lane] = make_float2(dl, dl * uk[j]);
       }
     }

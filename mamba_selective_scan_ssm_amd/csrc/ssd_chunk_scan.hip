@@ -81,7 +81,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQMax = 256;          // largest chunk
-constexpr int kRowQ = kQMax + 8;    // LDS row stride (bf16) of [row][position] tiles
 
 struct SsdArgs {
   const uint16_t* x;
@@ -112,16 +111,28 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Interleave rows r0 (position s) and r1 (position s+1), 8 bf16 each, into
-// eight 32-bit words: word i = (r0[i], r1[i]).
-__device__ __forceinline__ void interleave_pairs(const uint4& r0, const uint4& r1, uint32_t (&w)[8]) {
-  const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
-  const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w[2 * i] = (a[i] & 0xffffu) | (b[i] << 16);
-    w[2 * i + 1] = (a[i] >> 16) | (b[i] & 0xffff0000u);
-  }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposed read of a row-major 16-bit LDS tile T[k][m] (ds_read_b64_tr_b16).
+// Within each 16-lane group, lane L addresses row k0 + L/4, columns
+// m0 + 4*(L%4) .. +3; lane j of the group then receives T[k0 .. k0+3][m0 + j]
+// (checked on the device).  k0 may differ between lane groups.
+__device__ __forceinline__ uint2 lds_col4(const uint16_t* tile, int stride, int k0, int m0) {
+  const int L = threadIdx.x & 15;
+  const uint16_t* p = tile + (k0 + (L >> 2)) * stride + m0 + 4 * (L & 3);
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) uint16_t*)p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// MFMA operand with contraction index k over rows of a row-major LDS tile:
+// lane group q gets T[kb + 8q .. kb + 8q + 7][m0 + lane%16].
+__device__ __forceinline__ bf16x8 lds_kop(const uint16_t* tile, int stride, int kb, int m0) {
+  const int q = (threadIdx.x & 63) >> 4;
+  const uint2 lo = lds_col4(tile, stride, kb + 8 * q, m0);
+  const uint2 hi = lds_col4(tile, stride, kb + 8 * q + 4, m0);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 constexpr int kHGMax = 8;           // most heads one workgroup handles
@@ -190,24 +201,29 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int h0, int nh,
 
 // ---- 1. chunk states ---------------------------------------------------------
 
-// One 1024-thread workgroup per (chunk, batch, head group).  Every global
-// load that does not depend on earlier results is issued at the start.  B^T
-// of the chunk is staged once per state block; each head's (w x)^T is staged
-// from registers loaded while the previous head computed, into one of two
-// LDS buffers when both fit.
+// One 1024-thread workgroup per (chunk, batch, head group).  B of the chunk
+// (one state block at a time) and each head's w*x are kept in LDS in their
+// natural row-major layouts, written with coalesced 16-byte loads; the MFMA
+// operands, whose contraction index runs over rows, are read back with the
+// transposing LDS read.  Every global load that does not depend on earlier
+// results is issued at the start; each head's x comes from registers loaded
+// while the previous head computed, into one of two LDS buffers when both
+// fit.
 template <int P, int NB>
 __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   constexpr int NTHR = 1024, NW = 16;
-  constexpr bool DB = (size_t)(NB + 2 * P) * kRowQ * 2 + 2 * kHGMax * kQMax * 4 <= 156 * 1024;
+  constexpr int kRowB = NB + 16;   // LDS row strides (bf16); words = 8 (mod 32) spreads banks
+  constexpr int kRowX = P + 16;
+  constexpr bool DB = (size_t)kQMax * (kRowB + 2 * kRowX) * 2 + 2 * kHGMax * kQMax * 4 <= 156 * 1024;
   constexpr int NBUF = DB ? 2 : 1;
-  __shared__ alignas(16) uint16_t sBt[NB][kRowQ];        // B^T of one state block: [n][s]
-  __shared__ alignas(16) uint16_t sXt[NBUF][P][kRowQ];   // (w x)^T of one head: [p][s]
+  __shared__ alignas(16) uint16_t sB[kQMax][kRowB];         // B[s][n] of one state block
+  __shared__ alignas(16) uint16_t sX[NBUF][kQMax][kRowX];   // (w x)[s][p] of one head
   __shared__ alignas(16) float sCs2[kHGMax][kQMax];
   __shared__ alignas(16) float sDt[kHGMax][kQMax];
   __shared__ float sTmp[16];
   constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
-  constexpr int XPT = ((P / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
-  constexpr int BPT = ((NB / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
+  constexpr int XPT = (kQMax * P / 8 + NTHR - 1) / NTHR;
+  constexpr int BPT = (kQMax * NB / 8 + NTHR - 1) / NTHR;
 
   const int c = blockIdx.x, b = blockIdx.y;
   const int hpg = a.nheads / a.ngroups;
@@ -219,59 +235,48 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int r16 = lane & 15, q4 = lane >> 4;
   const int64_t pos0 = (int64_t)c * Q;
-  const int xtasks = (P / 8) * (Q / 2);
-  const int btasks = (NB / 8) * (Q / 2);
+  const int xtasks = Q * P / 8;
+  const int btasks = Q * NB / 8;
 
-  uint4 xr0[XPT], xr1[XPT], br0[BPT], br1[BPT];
+  uint4 xr[XPT], br[BPT];
   auto prefetch = [&](int hh) {
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
-      xr0[k] = xr1[k] = make_uint4(0, 0, 0, 0);
-      if (task < xtasks) {
-        const int sp = task % (Q / 2), po = task / (Q / 2);
-        const int s = 2 * sp;
-        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h0 + hh;
-        if (pos0 + s < L) xr0[k] = load16(a.x + row * P + 8 * po);
-        if (pos0 + s + 1 < L) xr1[k] = load16(a.x + (row + a.nheads) * P + 8 * po);
-      }
+      const int s = task / (P / 8), po = task % (P / 8);
+      xr[k] = (task < xtasks && pos0 + s < L)
+                  ? load16(a.x + (((int64_t)b * L + pos0 + s) * a.nheads + h0 + hh) * P + 8 * po)
+                  : make_uint4(0, 0, 0, 0);
     }
   };
   auto load_b = [&](int nb0) {
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
-      br0[k] = br1[k] = make_uint4(0, 0, 0, 0);
-      if (task < btasks) {
-        const int sp = task % (Q / 2), no = task / (Q / 2);
-        const int s = 2 * sp;
-        const int64_t row = ((int64_t)b * L + pos0 + s) * a.ngroups + g;
-        if (pos0 + s < L) br0[k] = load16(a.B + row * N + nb0 + 8 * no);
-        if (pos0 + s + 1 < L) br1[k] = load16(a.B + (row + a.ngroups) * N + nb0 + 8 * no);
-      }
+      const int s = task / (NB / 8), part = task % (NB / 8);
+      br[k] = (task < btasks && pos0 + s < L)
+                  ? load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + nb0 + 8 * part)
+                  : make_uint4(0, 0, 0, 0);
     }
   };
-  // (w x)^T[p][s] = x[s][p] exp2(cs_last - cs_s) dt_s, rounded to bf16.
+  // (w x)[s][p] = x[s][p] exp2(cs_last - cs_s) dt_s, rounded to bf16.
   auto stage = [&](int hh, int buf) {
     const float cs_last = sCs2[hh][Q - 1];
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
       if (task < xtasks) {
-        const int sp = task % (Q / 2), po = task / (Q / 2);
-        const int s = 2 * sp;
-        const float w0 = fast_exp2(cs_last - sCs2[hh][s]) * sDt[hh][s];
-        const float w1 = fast_exp2(cs_last - sCs2[hh][s + 1]) * sDt[hh][s + 1];
-        const uint32_t e0[4] = {xr0[k].x, xr0[k].y, xr0[k].z, xr0[k].w};
-        const uint32_t e1[4] = {xr1[k].x, xr1[k].y, xr1[k].z, xr1[k].w};
+        const int s = task / (P / 8), po = task % (P / 8);
+        const float w = fast_exp2(cs_last - sCs2[hh][s]) * sDt[hh][s];
+        const uint32_t e[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+        uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t b0 = (i & 1) ? (e0[i / 2] >> 16) : (e0[i / 2] & 0xffffu);
-          const uint32_t b1 = (i & 1) ? (e1[i / 2] >> 16) : (e1[i / 2] & 0xffffu);
-          const uint32_t v0 = f32_to_bf16_bits(bf16_bits_to_f32(b0) * w0);
-          const uint32_t v1 = f32_to_bf16_bits(bf16_bits_to_f32(b1) * w1);
-          *reinterpret_cast<uint32_t*>(&sXt[buf][8 * po + i][s]) = v0 | (v1 << 16);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = f32_to_bf16_bits(bf16_bits_to_f32(e[i] & 0xffffu) * w);
+          const uint32_t hi = f32_to_bf16_bits(__uint_as_float(e[i] & 0xffff0000u) * w);
+          o[i] = lo | (hi << 16);
         }
+        *reinterpret_cast<uint4*>(&sX[buf][s][8 * po]) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
   };
@@ -288,18 +293,14 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
     if (nb0 > 0) {
       load_b(nb0);
       prefetch(0);
-      __syncthreads();  // earlier readers of sBt and sXt are done
+      __syncthreads();  // earlier readers of sB and sX are done
     }
-    // B^T[n][s] for this state block, two positions per 32-bit LDS word.
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
       if (task < btasks) {
-        const int sp = task % (Q / 2), no = task / (Q / 2);
-        uint32_t w[8];
-        interleave_pairs(br0[k], br1[k], w);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&sBt[8 * no + i][2 * sp]) = w[i];
+        const int s = task / (NB / 8), part = task % (NB / 8);
+        *reinterpret_cast<uint4*>(&sB[s][8 * part]) = br[k];
       }
     }
     stage(0, 0);
@@ -308,20 +309,18 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
     for (int hh = 0; hh < nh; ++hh) {
       const int h = h0 + hh;
       const int buf = DB ? (hh & 1) : 0;
-      // S_c^T[n][p] = sum_s B^T[n][s] (w x)^T[p][s]
+      // S_c^T[n][p] = sum_s B[s][n] (w x)[s][p]
       f32x4 acc[TPW];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       for (int ks = 0; ks < Q / 32; ++ks) {
-        const int s = ks * 32 + 8 * q4;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           const int tile = wv + NW * t;
           if (tile < TILES) {
             const int nt = tile / PT, pt = tile % PT;
-            const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&sBt[nt * 16 + r16][s]));
-            const bf16x8 bv =
-                as_bf16x8(*reinterpret_cast<const uint4*>(&sXt[buf][pt * 16 + r16][s]));
+            const bf16x8 av = lds_kop(&sB[0][0], kRowB, ks * 32, nt * 16);
+            const bf16x8 bv = lds_kop(&sX[buf][0][0], kRowX, ks * 32, pt * 16);
             acc[t] = mfma_bf16(av, bv, acc[t]);
           }
         }
@@ -406,13 +405,14 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr int kRowB = KB + 8;
   constexpr int kRowN = N + 8;       // LDS row stride (bf16) of [p][n]
   constexpr int NTHR = 512;
-  constexpr int XPT = ((P / 8) * (kQMax / 2) + NTHR - 1) / NTHR;
+  constexpr int kRowX = P + 16;      // LDS row stride (bf16) of x [s][p]
+  constexpr int XPT = (kQMax * P / 8 + NTHR - 1) / NTHR;
   constexpr int SPT = (P * N / 8 + NTHR - 1) / NTHR;
   constexpr int BPT = (kQMax * KB / 8 + NTHR - 1) / NTHR;
-  // LDS: x^T [p][s] and S_in [p][n] of one head (two buffers when they
-  // fit); B [s][n] for the G^T phase shares the same bytes (it is only used
-  // before the first head is staged).
-  constexpr size_t kXtBytes = (size_t)P * kRowQ * 2;
+  // LDS: x [s][p] and S_in [p][n] of one head (two buffers when they fit);
+  // B [s][n] for the G^T phase shares the same bytes (it is only used before
+  // the first head is staged).
+  constexpr size_t kXtBytes = (size_t)kQMax * kRowX * 2;
   constexpr size_t kSBytes = (size_t)P * kRowN * 2;
   constexpr size_t kBBytes = (size_t)kQMax * kRowB * 2;
   constexpr size_t kFixed = 2 * kHGMax * kQMax * 4 + 64;
@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   __shared__ alignas(16) float sCs2[kHGMax][kQMax];
   __shared__ alignas(16) float sDt[kHGMax][kQMax];
   __shared__ float sTmp[16];
-  auto sXt = reinterpret_cast<uint16_t (*)[P][kRowQ]>(sRaw);
+  auto sX = reinterpret_cast<uint16_t (*)[kQMax][kRowX]>(sRaw);
   auto sS = reinterpret_cast<uint16_t (*)[P][kRowN]>(sRaw + NBUF * kXtBytes);
   auto sBs = reinterpret_cast<uint16_t (*)[kRowB]>(sRaw);
 
@@ -445,23 +445,19 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   const int64_t pos0 = (int64_t)c * Q;
   const int lcol[2] = {16 * ltile[0] + r16, 16 * ltile[1] + r16};  // this lane's positions
   const bool lok[2] = {active && pos0 + lcol[0] < L, active && pos0 + lcol[1] < L};
-  const int xtasks = (P / 8) * (Q / 2);
+  const int xtasks = Q * P / 8;
   const int btasks = Q * KB / 8;
 
-  uint4 xr0[XPT], xr1[XPT], sr[SPT], br[BPT], cr[2][KN];
+  uint4 xr[XPT], sr[SPT], br[BPT], cr[2][KN];
   auto prefetch = [&](int hh) {
     const int h = h0 + hh;
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
-      xr0[k] = xr1[k] = make_uint4(0, 0, 0, 0);
-      if (task < xtasks) {
-        const int sp = task % (Q / 2), po = task / (Q / 2);
-        const int s = 2 * sp;
-        const int64_t row = ((int64_t)b * L + pos0 + s) * a.nheads + h;
-        if (pos0 + s < L) xr0[k] = load16(a.x + row * P + 8 * po);
-        if (pos0 + s + 1 < L) xr1[k] = load16(a.x + (row + a.nheads) * P + 8 * po);
-      }
+      const int s = task / (P / 8), po = task % (P / 8);
+      xr[k] = (task < xtasks && pos0 + s < L)
+                  ? load16(a.x + (((int64_t)b * L + pos0 + s) * a.nheads + h) * P + 8 * po)
+                  : make_uint4(0, 0, 0, 0);
     }
     const uint16_t* sin = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
 #pragma unroll
@@ -481,18 +477,14 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
                   : make_uint4(0, 0, 0, 0);
     }
   };
-  // x^T[p][s] (exact bf16) and S_in[p][n] from the prefetched registers.
+  // x[s][p] and S_in[p][n] from the prefetched registers.
   auto stage = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
       if (task < xtasks) {
-        const int sp = task % (Q / 2), po = task / (Q / 2);
-        uint32_t w[8];
-        interleave_pairs(xr0[k], xr1[k], w);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint32_t*>(&sXt[buf][8 * po + i][2 * sp]) = w[i];
+        const int s = task / (P / 8), po = task % (P / 8);
+        *reinterpret_cast<uint4*>(&sX[buf][s][8 * po]) = xr[k];
       }
     }
 #pragma unroll
@@ -603,7 +595,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
         for (int pt = 0; pt < PT; ++pt) yacc[t][pt] *= el;
       }
     }
-    // Y^T[p][l] += sum_s x^T[p][s] M^T[s][l], M^T built pair by pair:
+    // Y^T[p][l] += sum_s x[s][p] M^T[s][l], M^T built pair by pair:
     // slot (q4, half*4 + i) of pair p holds s = 16*(st0 + half) + 4*q4 + i.
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -631,9 +623,9 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
       }
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
-        const uint16_t* row = &sXt[buf][pt * 16 + r16][0];
-        const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * st0 + 4 * q4);
-        const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 * st0 + 16 + 4 * q4);
+        // x[16 st0 + 4 q4 + i][16 pt + r16] and x[16 st0 + 16 + 4 q4 + i][...]
+        const uint2 lo = lds_col4(&sX[buf][0][0], kRowX, 16 * st0 + 4 * q4, pt * 16);
+        const uint2 hi = lds_col4(&sX[buf][0][0], kRowX, 16 * st0 + 16 + 4 * q4, pt * 16);
         const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         if (t) yacc[1][pt] = mfma_bf16(av, mop, yacc[1][pt]);
         else yacc[0][pt] = mfma_bf16(av, mop, yacc[0][pt]);
@@ -649,10 +641,12 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         const int p = pt * 16 + 4 * q4;
+        const uint2 xv = *reinterpret_cast<const uint2*>(&sX[buf][l][p]);
+        const float xs[4] = {bf16_bits_to_f32(xv.x & 0xffffu), __uint_as_float(xv.x & 0xffff0000u),
+                             bf16_bits_to_f32(xv.y & 0xffffu), __uint_as_float(xv.y & 0xffff0000u)};
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[i] = __builtin_fmaf(Dh, bf16_bits_to_f32(sXt[buf][p + i][l]), yacc[t][pt][i]);
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(Dh, xs[i], yacc[t][pt][i]);
         uint2 o;
         o.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
         o.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
@@ -700,7 +694,8 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.heads_per_wg_state = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256);
   a.heads_per_wg_out = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256);
 
-  constexpr int NB = N > 128 ? 128 : N;
+  // state block: B[chunk][NB] and one head's x[chunk][P] share the LDS
+  constexpr int NB = (P == 128 && N >= 128) ? 64 : (N > 128 ? 128 : N);
   dim3 g1(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_state - 1) / a.heads_per_wg_state);
   hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB>), g1, dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
