@@ -137,6 +137,10 @@ __device__ __forceinline__ bf16x8 lds_kop(const uint16_t* tile, int stride, int 
 
 constexpr int kHGMax = 8;           // most heads one workgroup handles
 
+// Most heads per output-kernel workgroup: the largest shape keeps fewer so
+// that its per-head decay tables fit in LDS beside the x and state tiles.
+constexpr int out_heads_max(int P, int N) { return P * N >= 128 * 256 ? 4 : kHGMax; }
+
 // Raw dt for the log-decay of every head of a workgroup's group: NTHR
 // threads form NTHR/256 groups of 256; round r covers heads
 // r*(NTHR/256) .. and thread t of a group owns chunk position t.  Loaded
@@ -160,10 +164,14 @@ __device__ __forceinline__ void load_group_dt(const SsdArgs& a, int b, int c, in
 // sDt[hh][s] = dt after bias and softplus, sCs2[hh][s] = log2(e) * inclusive
 // within-chunk cumsum of A_h dt (positions past the sequence end have
 // dt = 0).
+//
+// With sW given, also sW[hh][t] = dt_t exp2(cs[t | 31] - cs[t]): dt times the
+// decay from position t to the end of its 32-position group.
 template <int NTHR>
 __device__ void group_log_decay(const SsdArgs& a, int c, int h0, int nh,
                                 const uint32_t (&dtb)[kHGMax / (NTHR / 256)],
-                                float (*sCs2)[kQMax], float (*sDt)[kQMax], float* sTmp) {
+                                float (*sCs2)[kQMax], float (*sDt)[kQMax], float* sTmp,
+                                float (*sW)[kQMax] = nullptr) {
   constexpr int NGRP = NTHR / 256, ROUNDS = kHGMax / NGRP;
   const int tid = threadIdx.x;
   const int grp = tid >> 8, t = tid & 255, lane = tid & 63, w4 = (tid >> 6) & 3;
@@ -191,9 +199,12 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int h0, int nh,
     __syncthreads();
     float add = 0.0f;
     for (int w = 0; w < w4; ++w) add += sTmp[grp * 4 + w];
+    const float cs = v + add;
+    const float cs_end = __shfl(cs, lane | 31, 64);
     if (hh < nh) {
-      sCs2[hh][t] = v + add;
+      sCs2[hh][t] = cs;
       sDt[hh][t] = dtv;
+      if (sW) sW[hh][t] = dtv * fast_exp2(cs_end - cs);
     }
     __syncthreads();
   }
@@ -399,7 +410,7 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
 template <int P, int N>
 __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr int KN = N / 32;         // contraction steps over the state axis
-  constexpr int NP = kQMax / 32 + 1; // s-tile pairs per wave (at Q = 256)
+  constexpr int NPN = kQMax / 32 - 1; // off-diagonal s-tile pairs per wave (at Q = 256)
   constexpr int PT = P / 16;
   constexpr int KB = N < 128 ? N : 128;  // states of B per staging round
   constexpr int kRowB = KB + 8;
@@ -415,14 +426,16 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr size_t kXtBytes = (size_t)kQMax * kRowX * 2;
   constexpr size_t kSBytes = (size_t)P * kRowN * 2;
   constexpr size_t kBBytes = (size_t)kQMax * kRowB * 2;
-  constexpr size_t kFixed = 2 * kHGMax * kQMax * 4 + 64;
+  constexpr int HG = out_heads_max(P, N);  // most heads per workgroup
+  constexpr size_t kFixed = 3 * HG * kQMax * 4 + 64;
   constexpr bool DB = 2 * (kXtBytes + kSBytes) + kFixed <= 156 * 1024;
   constexpr int NBUF = DB ? 2 : 1;
   constexpr size_t kBufBytes = NBUF * (kXtBytes + kSBytes);
   constexpr size_t kRawBytes = kBufBytes > kBBytes ? kBufBytes : kBBytes;
   __shared__ alignas(16) uint8_t sRaw[kRawBytes];
-  __shared__ alignas(16) float sCs2[kHGMax][kQMax];
-  __shared__ alignas(16) float sDt[kHGMax][kQMax];
+  __shared__ alignas(16) float sCs2[HG][kQMax];
+  __shared__ alignas(16) float sDt[HG][kQMax];
+  __shared__ alignas(16) float sW[HG][kQMax];
   __shared__ float sTmp[16];
   auto sX = reinterpret_cast<uint16_t (*)[kQMax][kRowX]>(sRaw);
   auto sS = reinterpret_cast<uint16_t (*)[P][kRowN]>(sRaw + NBUF * kXtBytes);
@@ -510,17 +523,33 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   load_b(0);
   load_group_dt<NTHR>(a, b, c, h0, nh, dtb);
 
-  // Pair p of this wave: output tile t = (p < npA ? A : B), s-tiles
-  // st0 = 2*(p - first pair of t) and st0 + 1; tiles past the output tile's
-  // diagonal are zero.
-  auto pair_tile = [&](int p) { return p < npA ? 0 : 1; };
-  auto pair_st0 = [&](int p) { return p < npA ? 2 * p : 2 * (p - npA); };
-  auto pair_on = [&](int p) { return active && p < npA + npB; };
+  // Pairs of s-tiles: the last pair of each output tile touches its diagonal
+  // and has its own registers; of the others, tile A takes slots 0 .. npA-2
+  // (s-tiles 2p, 2p+1) and tile B slots NPN-1-j for j < npB-1 (s-tiles 2j,
+  // 2j+1).  npA + npB <= NPN + 2 keeps the two ranges apart, so every
+  // register index below is static.  s-tiles past the diagonal are zero.
+  const int ltA = ltile[0], ltB = ltile[1];
 
   // G^T[s][l] = sum_n B[s][n] C[l][n] for this wave's pairs.
-  f32x4 gacc[2 * NP];
+  f32x4 gacc[2 * NPN], gdacc[4];
 #pragma unroll
-  for (int k = 0; k < 2 * NP; ++k) gacc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < 2 * NPN; ++k) gacc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) gdacc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto gt_pair = [&](f32x4& g0, f32x4& g1, int st0, int lt, const uint4 (&cv)[KN], int kb0) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int st = st0 + half;
+      if (st > lt) continue;
+      f32x4& acc = half ? g1 : g0;
+#pragma unroll
+      for (int kq = 0; kq < KB / 32; ++kq) {
+        const bf16x8 av =
+            as_bf16x8(*reinterpret_cast<const uint4*>(&sBs[st * 16 + r16][kq * 32 + 8 * q4]));
+        acc = mfma_bf16(av, as_bf16x8(cv[kb0 / 32 + kq]), acc);
+      }
+    }
+  };
   for (int kb0 = 0; kb0 < N; kb0 += KB) {
     if (kb0 > 0) __syncthreads();  // earlier readers of sBs are done
 #pragma unroll
@@ -533,36 +562,37 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     }
     __syncthreads();
     if (kb0 + KB < N) load_b(kb0 + KB);
+    if (active) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      if (!pair_on(p)) continue;
-      const int t = pair_tile(p), st0 = pair_st0(p);
+      for (int p = 0; p < NPN; ++p)
+        if (p < npA - 1) gt_pair(gacc[2 * p], gacc[2 * p + 1], 2 * p, ltA, cr[0], kb0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int st = st0 + half;
-        if (st > ltile[t]) continue;
-#pragma unroll
-        for (int kq = 0; kq < KB / 32; ++kq) {
-          const bf16x8 av =
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sBs[st * 16 + r16][kq * 32 + 8 * q4]));
-          const bf16x8 bop = as_bf16x8(t ? cr[1][kb0 / 32 + kq] : cr[0][kb0 / 32 + kq]);
-          gacc[2 * p + half] = mfma_bf16(av, bop, gacc[2 * p + half]);
-        }
-      }
+      for (int j = 0; j < NPN; ++j)
+        if (j < npB - 1)
+          gt_pair(gacc[2 * (NPN - 1 - j)], gacc[2 * (NPN - 1 - j) + 1], 2 * j, ltB, cr[1], kb0);
+      gt_pair(gdacc[0], gdacc[1], 2 * (npA - 1), ltA, cr[0], kb0);
+      gt_pair(gdacc[2], gdacc[3], 2 * (npB - 1), ltB, cr[1], kb0);
     }
   }
-  // Keep G^T as bf16: pair p holds s-tiles st0 (slots 0-3) and st0+1 (slots 4-7).
-  bf16x8 gpk[NP];
+  // Keep G^T as bf16: a pair holds s-tiles st0 (slots 0-3) and st0+1 (slots 4-7).
+  bf16x8 gpk[NPN], gdk[2];
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
+  for (int p = 0; p < NPN; ++p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gpk[p][i] = static_cast<__bf16>(gacc[2 * p][i]);
       gpk[p][4 + i] = static_cast<__bf16>(gacc[2 * p + 1][i]);
     }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gdk[t][i] = static_cast<__bf16>(gdacc[2 * t][i]);
+      gdk[t][4 + i] = static_cast<__bf16>(gdacc[2 * t + 1][i]);
+    }
 
   prefetch(0);
-  group_log_decay<NTHR>(a, c, h0, nh, dtb, sCs2, sDt, sTmp);  // its barriers also retire sBs
+  group_log_decay<NTHR>(a, c, h0, nh, dtb, sCs2, sDt, sTmp, sW);  // its barriers also retire sBs
   stage(0);
   if (nh > 1) prefetch(1);
   __syncthreads();
@@ -571,6 +601,8 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     const int h = h0 + hh;
     const int buf = DB ? (hh & 1) : 0;
     const float csl[2] = {active ? sCs2[hh][lcol[0]] : 0.0f, active ? sCs2[hh][lcol[1]] : 0.0f};
+    // the decay never grows within the chunk: dt >= 0 (softplus) and A_h <= 0
+    const bool fact = a.dt_softplus && a.A[h] <= 0.0f;
     f32x4 yacc[2][PT];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -595,41 +627,75 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
         for (int pt = 0; pt < PT; ++pt) yacc[t][pt] *= el;
       }
     }
-    // Y^T[p][l] += sum_s x[s][p] M^T[s][l], M^T built pair by pair:
-    // slot (q4, half*4 + i) of pair p holds s = 16*(st0 + half) + 4*q4 + i.
+    // Y^T[p][l] += sum_s x[s][p] M^T[s][l], M^T[s][l] = G^T[s][l] dt_s
+    // exp2(cs_l - cs_s) built pair by pair: slot (q4, half*4 + i) of a pair
+    // holds s = 16*(st0 + half) + 4*q4 + i.
+    auto pair_mma = [&](const bf16x8& mop, int st0, f32x4 (&acc)[PT]) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      if (!pair_on(p)) continue;
-      const int t = pair_tile(p), st0 = pair_st0(p);
-      const int lt = ltile[t];
-      const float cs_l = t ? csl[1] : csl[0];
-      const int l = t ? lcol[1] : lcol[0];
-      const bool diag = st0 + 1 >= lt;  // pair reaches the output tile's diagonal
+      for (int pt = 0; pt < PT; ++pt) {
+        // x[16 st0 + 4 q4 + i][16 pt + r16] and x[16 st0 + 16 + 4 q4 + i][...]
+        const uint2 lo = lds_col4(&sX[buf][0][0], kRowX, 16 * st0 + 4 * q4, pt * 16);
+        const uint2 hi = lds_col4(&sX[buf][0][0], kRowX, 16 * st0 + 16 + 4 * q4, pt * 16);
+        acc[pt] = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), mop, acc[pt]);
+      }
+    };
+    // Direct form, with the causal mask s <= l when the pair reaches the
+    // diagonal.
+    auto pair_direct = [&](const bf16x8& g, int st0, int l, float cs_l, bool mask,
+                           f32x4 (&acc)[PT]) {
       bf16x8 mop;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int st = st0 + half;
-        const int s0 = st * 16 + 4 * q4;
+        const int s0 = (st0 + half) * 16 + 4 * q4;
         const float4 cs4 = *reinterpret_cast<const float4*>(&sCs2[hh][s0 & (kQMax - 1)]);
         const float4 dt4 = *reinterpret_cast<const float4*>(&sDt[hh][s0 & (kQMax - 1)]);
         const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
         const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = static_cast<float>(gpk[p][half * 4 + i]) * fast_exp2(cs_l - csv[i]) * dtv[i];
-          if (diag && !(st <= lt && s0 + i <= l)) v = 0.0f;
+          float v = static_cast<float>(g[half * 4 + i]) * fast_exp2(cs_l - csv[i]) * dtv[i];
+          if (mask && s0 + i > l) v = 0.0f;
           mop[half * 4 + i] = static_cast<__bf16>(v);
         }
       }
+      pair_mma(mop, st0, acc);
+    };
+    // Factored form for a pair wholly before the output tile when the decay
+    // never grows (cs non-increasing): exp2(cs_l - cs_s) = exp2(cs_l - R)
+    // exp2(R - cs_s) with R = cs at the pair's last position, both factors
+    // in [0, 1]; dt_s exp2(R - cs_s) is sW.
+    auto pair_fact = [&](const bf16x8& g, int st0, float cs_l, f32x4 (&acc)[PT]) {
+      const float f = fast_exp2(cs_l - sCs2[hh][(16 * st0 + 31) & (kQMax - 1)]);
+      bf16x8 mop;
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        // x[16 st0 + 4 q4 + i][16 pt + r16] and x[16 st0 + 16 + 4 q4 + i][...]
-        const uint2 lo = lds_col4(&sX[buf][0][0], kRowX, 16 * st0 + 4 * q4, pt * 16);
-        const uint2 hi = lds_col4(&sX[buf][0][0], kRowX, 16 * st0 + 16 + 4 * q4, pt * 16);
-        const bf16x8 av = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-        if (t) yacc[1][pt] = mfma_bf16(av, mop, yacc[1][pt]);
-        else yacc[0][pt] = mfma_bf16(av, mop, yacc[0][pt]);
+      for (int half = 0; half < 2; ++half) {
+        const int s0 = (st0 + half) * 16 + 4 * q4;
+        const float4 w4 = *reinterpret_cast<const float4*>(&sW[hh][s0 & (kQMax - 1)]);
+        const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          mop[half * 4 + i] = static_cast<__bf16>(static_cast<float>(g[half * 4 + i]) * (wv4[i] * f));
       }
+      pair_mma(mop, st0, acc);
+    };
+    if (active) {
+      if (fact) {
+#pragma unroll
+        for (int p = 0; p < NPN; ++p)
+          if (p < npA - 1) pair_fact(gpk[p], 2 * p, csl[0], yacc[0]);
+#pragma unroll
+        for (int j = 0; j < NPN; ++j)
+          if (j < npB - 1) pair_fact(gpk[NPN - 1 - j], 2 * j, csl[1], yacc[1]);
+      } else {
+#pragma unroll
+        for (int p = 0; p < NPN; ++p)
+          if (p < npA - 1) pair_direct(gpk[p], 2 * p, lcol[0], csl[0], false, yacc[0]);
+#pragma unroll
+        for (int j = 0; j < NPN; ++j)
+          if (j < npB - 1) pair_direct(gpk[NPN - 1 - j], 2 * j, lcol[1], csl[1], false, yacc[1]);
+      }
+      pair_direct(gdk[0], 2 * (npA - 1), lcol[0], csl[0], true, yacc[0]);
+      pair_direct(gdk[1], 2 * (npB - 1), lcol[1], csl[1], true, yacc[1]);
     }
     // y[l][p .. p+3] = Y^T[p .. p+3][l] + D_h x[l][p .. p+3]
     const float Dh = a.D ? a.D[h] : 0.0f;
@@ -664,9 +730,9 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
 
 // Largest divisor of `hpg` (heads per group) that still leaves at least
 // `target` workgroups, so that a workgroup's heads share one group.
-int heads_per_workgroup(int hpg, int nheads, int64_t base_wgs, int64_t target) {
+int heads_per_workgroup(int hpg, int nheads, int64_t base_wgs, int64_t target, int dmax) {
   int best = 1;
-  for (int d = 1; d <= hpg && d <= 8; ++d)
+  for (int d = 1; d <= hpg && d <= dmax; ++d)
     if (hpg % d == 0 && base_wgs * (nheads / d) >= target) best = d;
   return best;
 }
@@ -691,8 +757,10 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.batch = s.batch; a.seqlen = s.seqlen; a.nheads = s.nheads; a.headdim = s.headdim;
   a.dstate = s.dstate; a.ngroups = s.ngroups; a.chunk = s.chunk; a.nchunks = s.nchunks;
   const int hpg = s.nheads / s.ngroups;
-  a.heads_per_wg_state = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256);
-  a.heads_per_wg_out = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256);
+  a.heads_per_wg_state =
+      heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256, kHGMax);
+  a.heads_per_wg_out =
+      heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256, out_heads_max(P, N));
 
   // state block: B[chunk][NB] and one head's x[chunk][P] share the LDS
   constexpr int NB = (P == 128 && N >= 128) ? 64 : (N > 128 ? 128 : N);
