@@ -107,6 +107,13 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Sequence position for a load: positions past the end read the last row
+// instead.  Those rows only ever meet a weight of zero (dt = 0 past the end)
+// or feed outputs that are not stored, so every load can be issued
+// unconditionally; a load under a condition makes the compiler wait for it
+// (and for every load issued before it) right away.
+__device__ __forceinline__ int64_t load_pos(int64_t pos, int L) { return pos < L ? pos : L - 1; }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -146,17 +153,26 @@ constexpr int out_heads_max(int P, int N) { return P * N >= 128 * 256 ? 4 : kHGM
 // r*(NTHR/256) .. and thread t of a group owns chunk position t.  Loaded
 // early so that the latency overlaps other work.
 template <int NTHR>
+struct GroupRaw {
+  static constexpr int ROUNDS = kHGMax / (NTHR / 256);
+  uint32_t dt[ROUNDS];             // raw dt (bf16 bits) of this thread's position
+  float A[ROUNDS], bias[ROUNDS], D[ROUNDS];  // per-head scalars (uniform per wave)
+};
+
+template <int NTHR>
 __device__ __forceinline__ void load_group_dt(const SsdArgs& a, int b, int c, int h0, int nh,
-                                              uint32_t (&dtb)[kHGMax / (NTHR / 256)]) {
-  constexpr int NGRP = NTHR / 256, ROUNDS = kHGMax / NGRP;
-  const int tid = threadIdx.x, grp = tid >> 8, t = tid & 255;
+                                              GroupRaw<NTHR>& g) {
+  constexpr int NGRP = NTHR / 256, ROUNDS = GroupRaw<NTHR>::ROUNDS;
+  const int tid = threadIdx.x, t = tid & 255;
+  const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int64_t pos = (int64_t)c * a.chunk + t;
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    const int hh = NGRP * r + grp;
-    dtb[r] = (hh < nh && t < a.chunk && pos < a.seqlen)
-                 ? a.dt[((int64_t)b * a.seqlen + pos) * a.nheads + h0 + hh]
-                 : 0u;
+    const int hh = min(NGRP * r + grp, nh - 1);  // the consumer skips hh >= nh
+    g.dt[r] = a.dt[((int64_t)b * a.seqlen + load_pos(pos, a.seqlen)) * a.nheads + h0 + hh];
+    g.A[r] = a.A[h0 + hh];
+    g.bias[r] = a.dt_bias ? a.dt_bias[h0 + hh] : 0.0f;
+    g.D[r] = a.D ? a.D[h0 + hh] : 0.0f;
   }
 }
 
@@ -166,13 +182,13 @@ __device__ __forceinline__ void load_group_dt(const SsdArgs& a, int b, int c, in
 // dt = 0).
 //
 // With sW given, also sW[hh][t] = dt_t exp2(cs[t | 31] - cs[t]): dt times the
-// decay from position t to the end of its 32-position group.
+// decay from position t to the end of its 32-position group.  With sHead
+// given, sHead[hh] = (A_h, D_h).
 template <int NTHR>
-__device__ void group_log_decay(const SsdArgs& a, int c, int h0, int nh,
-                                const uint32_t (&dtb)[kHGMax / (NTHR / 256)],
+__device__ void group_log_decay(const SsdArgs& a, int c, int nh, const GroupRaw<NTHR>& g,
                                 float (*sCs2)[kQMax], float (*sDt)[kQMax], float* sTmp,
-                                float (*sW)[kQMax] = nullptr) {
-  constexpr int NGRP = NTHR / 256, ROUNDS = kHGMax / NGRP;
+                                float (*sW)[kQMax] = nullptr, float2* sHead = nullptr) {
+  constexpr int NGRP = NTHR / 256, ROUNDS = GroupRaw<NTHR>::ROUNDS;
   const int tid = threadIdx.x;
   const int grp = tid >> 8, t = tid & 255, lane = tid & 63, w4 = (tid >> 6) & 3;
   const int64_t pos = (int64_t)c * a.chunk + t;
@@ -182,12 +198,12 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int h0, int nh,
     const int hh = NGRP * r + grp;
     float dtv = 0.0f, ah = 0.0f;
     if (hh < nh) {
-      ah = a.A[h0 + hh] * kLog2e;
+      ah = g.A[r] * kLog2e;
       if (t < a.chunk && pos < a.seqlen) {
-        float v = bf16_bits_to_f32(dtb[r]);
-        if (a.dt_bias) v += a.dt_bias[h0 + hh];
+        const float v = bf16_bits_to_f32(g.dt[r]) + g.bias[r];
         dtv = a.dt_softplus ? softplus_f(v) : v;
       }
+      if (sHead && t == 0) sHead[hh] = make_float2(g.A[r], g.D[r]);
     }
     float v = ah * dtv;
 #pragma unroll
@@ -255,9 +271,8 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
       const int s = task / (P / 8), po = task % (P / 8);
-      xr[k] = (task < xtasks && pos0 + s < L)
-                  ? load16(a.x + (((int64_t)b * L + pos0 + s) * a.nheads + h0 + hh) * P + 8 * po)
-                  : make_uint4(0, 0, 0, 0);
+      xr[k] = load16(a.x + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.nheads + h0 + hh) * P +
+                     8 * po);
     }
   };
   auto load_b = [&](int nb0) {
@@ -265,9 +280,8 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
       const int s = task / (NB / 8), part = task % (NB / 8);
-      br[k] = (task < btasks && pos0 + s < L)
-                  ? load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + nb0 + 8 * part)
-                  : make_uint4(0, 0, 0, 0);
+      br[k] = load16(a.B + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.ngroups + g) * N + nb0 +
+                     8 * part);
     }
   };
   // (w x)[s][p] = x[s][p] exp2(cs_last - cs_s) dt_s, rounded to bf16.
@@ -292,11 +306,11 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
     }
   };
 
-  uint32_t dtb[kHGMax / (NTHR / 256)];
-  load_group_dt<NTHR>(a, b, c, h0, nh, dtb);
+  GroupRaw<NTHR> graw;
+  load_group_dt<NTHR>(a, b, c, h0, nh, graw);
   load_b(0);
   prefetch(0);
-  group_log_decay<NTHR>(a, c, h0, nh, dtb, sCs2, sDt, sTmp);
+  group_log_decay<NTHR>(a, c, nh, graw, sCs2, sDt, sTmp);
   if (tid < nh)
     a.decay[((int64_t)b * a.nheads + h0 + tid) * a.nchunks + c] = fast_exp2(sCs2[tid][Q - 1]);
 
@@ -337,24 +351,35 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
         }
       }
       // lane holds S_c[p][n .. n+3] with p = pt*16 + r16, n = nt*16 + 4*q4
-      uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
+      uint2 so[TPW];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const int tile = wv + NW * t;
-        if (tile < TILES) {
-          const int nt = tile / PT, pt = tile % PT;
-          const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
-          uint2 o;
-          o.x = (uint32_t)f32_to_bf16_bits(acc[t][0]) | ((uint32_t)f32_to_bf16_bits(acc[t][1]) << 16);
-          o.y = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
-          *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
-        }
+        so[t].x = (uint32_t)f32_to_bf16_bits(acc[t][0]) | ((uint32_t)f32_to_bf16_bits(acc[t][1]) << 16);
+        so[t].y = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
       }
+      auto store_s = [&]() {
+        uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const int tile = wv + NW * t;
+          if (tile < TILES) {
+            const int nt = tile / PT, pt = tile % PT;
+            const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
+            *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = so[t];
+          }
+        }
+      };
+      // Stage the next head before storing this one, and keep stage, stores
+      // and the next prefetch on one path, so that waiting for the staged
+      // loads never waits for these stores.
       if (hh + 1 < nh) {
         if (!DB) __syncthreads();  // readers of the single buffer are done
         stage(hh + 1, DB ? ((hh + 1) & 1) : 0);
+        store_s();
         if (hh + 2 < nh) prefetch(hh + 2);
         __syncthreads();
+      } else {
+        store_s();
       }
     }
   }
@@ -436,6 +461,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   __shared__ alignas(16) float sCs2[HG][kQMax];
   __shared__ alignas(16) float sDt[HG][kQMax];
   __shared__ alignas(16) float sW[HG][kQMax];
+  __shared__ float2 sHead[HG];
   __shared__ float sTmp[16];
   auto sX = reinterpret_cast<uint16_t (*)[kQMax][kRowX]>(sRaw);
   auto sS = reinterpret_cast<uint16_t (*)[P][kRowN]>(sRaw + NBUF * kXtBytes);
@@ -468,15 +494,13 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
       const int s = task / (P / 8), po = task % (P / 8);
-      xr[k] = (task < xtasks && pos0 + s < L)
-                  ? load16(a.x + (((int64_t)b * L + pos0 + s) * a.nheads + h) * P + 8 * po)
-                  : make_uint4(0, 0, 0, 0);
+      xr[k] = load16(a.x + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.nheads + h) * P + 8 * po);
     }
     const uint16_t* sin = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
       const int task = tid + k * NTHR;
-      sr[k] = (c > 0 && task < P * N / 8) ? load16(sin + 8 * task) : make_uint4(0, 0, 0, 0);
+      sr[k] = load16(sin + 8 * min(task, P * N / 8 - 1));  // unused for chunk 0
     }
   };
   // B[s][kb0 .. kb0+KB) rows, 16 bytes per task.
@@ -485,9 +509,8 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
       const int s = task / (KB / 8), part = task % (KB / 8);
-      br[k] = (task < btasks && pos0 + s < L)
-                  ? load16(a.B + (((int64_t)b * L + pos0 + s) * a.ngroups + g) * N + kb0 + 8 * part)
-                  : make_uint4(0, 0, 0, 0);
+      br[k] = load16(a.B + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.ngroups + g) * N + kb0 +
+                     8 * part);
     }
   };
   // x[s][p] and S_in[p][n] from the prefetched registers.
@@ -510,18 +533,22 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     }
   };
 
-  // Issue the independent loads: C rows of this lane's two positions, B, dt.
+  // Issue the independent loads: dt and the head scalars first (their wait
+  // covers nothing else), then C rows of this lane's two positions, B, and
+  // the first head's x and carried state.
+  GroupRaw<NTHR> graw;
+  load_group_dt<NTHR>(a, b, c, h0, nh, graw);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const uint16_t* crow =
         a.C + (((int64_t)b * L + pos0 + (lok[t] ? lcol[t] : 0)) * a.ngroups + g) * N;
 #pragma unroll
     for (int kk = 0; kk < KN; ++kk)
-      cr[t][kk] = lok[t] ? load16(crow + kk * 32 + 8 * q4) : make_uint4(0, 0, 0, 0);
+      cr[t][kk] = load16(crow + kk * 32 + 8 * q4);  // rows past the end feed unstored columns
   }
-  uint32_t dtb[kHGMax / (NTHR / 256)];
   load_b(0);
-  load_group_dt<NTHR>(a, b, c, h0, nh, dtb);
+  prefetch(0);
+  group_log_decay<NTHR>(a, c, nh, graw, sCs2, sDt, sTmp, sW, sHead);
 
   // Pairs of s-tiles: the last pair of each output tile touches its diagonal
   // and has its own registers; of the others, tile A takes slots 0 .. npA-2
@@ -591,8 +618,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
       gdk[t][4 + i] = static_cast<__bf16>(gdacc[2 * t + 1][i]);
     }
 
-  prefetch(0);
-  group_log_decay<NTHR>(a, c, h0, nh, dtb, sCs2, sDt, sTmp, sW);  // its barriers also retire sBs
+  __syncthreads();  // readers of sBs are done before the head buffers reuse its bytes
   stage(0);
   if (nh > 1) prefetch(1);
   __syncthreads();
@@ -602,7 +628,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     const int buf = DB ? (hh & 1) : 0;
     const float csl[2] = {active ? sCs2[hh][lcol[0]] : 0.0f, active ? sCs2[hh][lcol[1]] : 0.0f};
     // the decay never grows within the chunk: dt >= 0 (softplus) and A_h <= 0
-    const bool fact = a.dt_softplus && a.A[h] <= 0.0f;
+    const bool fact = a.dt_softplus && sHead[hh].x <= 0.0f;
     f32x4 yacc[2][PT];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -698,12 +724,11 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
       pair_direct(gdk[1], 2 * (npB - 1), lcol[1], csl[1], true, yacc[1]);
     }
     // y[l][p .. p+3] = Y^T[p .. p+3][l] + D_h x[l][p .. p+3]
-    const float Dh = a.D ? a.D[h] : 0.0f;
+    const float Dh = sHead[hh].y;
+    uint2 yo[2][PT];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if (!lok[t]) continue;
-      const int l = lcol[t];
-      uint16_t* yrow = a.y + (((int64_t)b * L + pos0 + l) * a.nheads + h) * P;
+      const int l = lcol[t] & (kQMax - 1);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         const int p = pt * 16 + 4 * q4;
@@ -713,17 +738,31 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(Dh, xs[i], yacc[t][pt][i]);
-        uint2 o;
-        o.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-        o.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(yrow + p) = o;
+        yo[t][pt].x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        yo[t][pt].y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
       }
     }
+    auto store_y = [&]() {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (!lok[t]) continue;
+        uint16_t* yrow = a.y + (((int64_t)b * L + pos0 + lcol[t]) * a.nheads + h) * P;
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+          *reinterpret_cast<uint2*>(yrow + pt * 16 + 4 * q4) = yo[t][pt];
+      }
+    };
+    // Stage the next head before storing this one, and keep stage, stores
+    // and the next prefetch on one path: waiting for the staged loads then
+    // never waits for these stores.
     if (hh + 1 < nh) {
       if (!DB) __syncthreads();  // readers of the single buffer are done
       stage(DB ? ((hh + 1) & 1) : 0);
+      store_y();
       if (hh + 2 < nh) prefetch(hh + 2);
       __syncthreads();
+    } else {
+      store_y();
     }
   }
 }
