@@ -70,14 +70,17 @@ def calib_copy(torch):
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}))
 
 
-KERNEL_SRC = os.path.join(ROOT, "mamba_selective_scan_ssm_amd", "csrc", "selective_scan.hip")
+CSRC = os.path.join(ROOT, "mamba_selective_scan_ssm_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "selective_scan.hip")
+SSD_SRC = os.path.join(CSRC, "ssd_chunk_scan.hip")
 
 
-def measured_traffic(kernel: str, workload: str, src: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the kernel source as it is now (else None)."""
+def measured_traffic(name: str, src: str, per: str = "launch"):
+    """HBM bytes per launch (or per call) from the committed rocprofv3 counter
+    summary profiles/<name>_hbm_traffic.md, if it was taken on the kernel
+    source as it is now (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -86,9 +89,10 @@ def measured_traffic(kernel: str, workload: str, src: str):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    key = f"traffic_bytes_per_{per}"
+    if fields.get("kernel_source_sha256") != sha or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return int(fields[key])
 
 
 def cpu_baseline(x, cfg, oracle, min_seconds=1.0):
@@ -188,7 +192,7 @@ def main():
         "roofline": {"bound": "alu", "achieved": round(achieved_tf, 3),
                      "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tf / VALU_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("selective_scan_fwd_kernel", cfg.name, KERNEL_SRC),
+                     "traffic": measured_traffic(f"selective_scan_fwd_kernel_{cfg.name}", KERNEL_SRC),
                      "kernel": "selective_scan_fwd_kernel", "flops_per_launch": flops},
     }
     if args.ssd:
@@ -236,7 +240,8 @@ def bench_ssd(args, torch, ssm, synth):
             "ms_per_call": round(ms, 5), "tokens_per_s": round(b * L / (ms * 1e-3), 1),
             "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "mfma_frac_bf16_2500": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4),
-            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "flops": flops, "bytes": nbytes}
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "flops": flops, "bytes": nbytes,
+            "traffic": measured_traffic("ssd_chunk_scan_ssd", SSD_SRC, per="call")}
 
 
 if __name__ == "__main__":
