@@ -10,26 +10,42 @@
 //               section 3.2 (chunk long sequences instead of materialising
 //               [B, L, ED, N] tensors).
 //
-// Work decomposition (one workgroup = 64 consecutive channels d of one batch
-// entry b, over the whole sequence):
-//   * lane  = channel d (64 rows per wave), so every lane of a wave reads the
-//     same B[b,:,t] and C[b,:,t]: they are staged once per time chunk in LDS
-//     as float32 and read back as wave-wide broadcasts;
-//   * G waves split the dstate axis (NG states each) and share the per-step
-//     work (loads, softplus, gate) through LDS; their partial readouts
-//     sum_n C h are added in LDS;
+// Two kernels:
+//
+// selective_scan_fwd_kernel (whenever there are rows enough to fill the chip):
+//   * a channel d of one batch entry b is a row; its dstate axis is split
+//     over LPC consecutive lanes (a lane group), NG states per lane, so a
+//     wave holds 64/LPC rows and every lane runs the plain recurrence
+//     ([EXPLAINED] eq. (7)) for its states over the whole sequence;
+//   * B[b,:,t] and C[b,:,t] are the same for every row: each time chunk of
+//     them is staged once per workgroup in LDS as float32 (double-buffered,
+//     one barrier per chunk);
+//   * the per-step work of a row (16-byte loads of u, delta, z; bias,
+//     softplus, delta*u, silu(z); skip term, gate and 16-byte stores) is
+//     split over the lanes of its group, a contiguous slice of the chunk
+//     each; delta and delta*u reach the other lanes of the group by DPP
+//     broadcasts folded into the multiplies that consume them, and the
+//     group's partial readouts sum_n C h are reduce-scattered back to the
+//     owners of the steps with DPP adds.  No per-step value goes through LDS.
+//
+// selective_scan_split_kernel (too few rows to give every SIMD a wave):
+//   * lane = row (64 rows per wave); G waves split the dstate axis (NG
+//     states each) and share the per-step work through LDS; their partial
+//     readouts are added in LDS;
 //   * W waves split each time chunk into W slots of T steps.  Slots run the
 //     lane-local recurrence from the identity, publish (prod a, v) pairs,
 //     and a serial pass over the W slots applies the combine operator of
 //     [EXPLAINED] eq. (10) with the running carry to produce every slot's
-//     carry-in; the slots then rescan with their carry-in.  With W = 1 a
-//     wave runs the plain recurrence and no scan is needed.
-//   * exp(delta*A) is computed as exp2(delta*A2) with A2 = A*log2(e)
-//     pre-scaled once per row; the product of a slot's decays is
-//     exp2(A2 * sum(delta)), one exp per state per slot.
-// Nothing of size [b, d, L, N] is ever written to memory.
+//     carry-in; the slots then rescan with their carry-in.
+//
+// Both compute exp(delta*A) as exp2(delta*A2) with A2 = A*log2(e) pre-scaled
+// once per row; the product of a slot's decays is exp2(A2 * sum(delta)), one
+// exp per state per slot.  Nothing of size [b, d, L, N] is ever written to
+// memory.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_math.h"
 #include "selective_scan_launch.h"
@@ -154,13 +170,250 @@ __device__ __forceinline__ void store_seg(In* __restrict__ p, int64_t base, int 
     if (t0 + k < limit) Elem<In>::store(p, base + t0 + k, v[k]);
 }
 
-// ---- the kernel ------------------------------------------------------------
+// ---- lane-group exchange (DPP) ---------------------------------------------
 
-// NG: states per wave; G: waves splitting the states; W: time slots per
-// chunk; T: steps per slot.  Block = 64 * G * W threads.
+constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int kSwapPairs = quad_perm(1, 0, 3, 2);   // lane ^ 1
+constexpr int kSwapHalves = quad_perm(2, 3, 0, 1);  // lane ^ 2
+
+// Every lane of a group of LPC (1, 2 or 4) consecutive lanes reads slot s of
+// its group.
+template <int LPC>
+constexpr int group_bcast(int s) {
+  return LPC == 4 ? quad_perm(s, s, s, s) : LPC == 2 ? quad_perm(s, s, 2 + s, 2 + s)
+                                                     : quad_perm(0, 1, 2, 3);
+}
+
+// A DPP quad permute of v.  Written with bound_ctrl and a zero "old" value so
+// that the compiler can fold it into the VALU instruction that consumes it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
+// ---- row-parallel kernel -----------------------------------------------------
+
+// NG: states per lane; LPC: lanes per row (NG*LPC >= dstate); T: steps per
+// time chunk.  Block = 256 threads = 4 waves of 64/LPC rows each.
+template <typename In, int NG, int LPC, int T>
+__global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm) {
+  constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
+  constexpr int RPW = 64 / LPC;      // rows per wave
+  constexpr int RPB = 4 * RPW;       // rows per workgroup
+  constexpr int TS = T / LPC;        // steps whose per-step work one lane owns
+  constexpr int EPU = Elem<In>::kPer16B;
+  static_assert(NG % 4 == 0 && T % EPU == 0 && T % LPC == 0, "tile shape");
+  constexpr int UPR = T / EPU;       // 16-byte units per state row of a chunk
+  constexpr int UNITS = 2 * NS * UPR;
+  constexpr int RB = (UNITS + 255) / 256;
+
+  __shared__ alignas(16) float sB[2][T][NS];
+  __shared__ alignas(16) float sC[2][T][NS];
+
+  const In* __restrict__ u = static_cast<const In*>(prm.u);
+  const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(prm.B);
+  const In* __restrict__ Cm = static_cast<const In*>(prm.C);
+  const In* __restrict__ z = static_cast<const In*>(prm.z);
+  In* __restrict__ y = static_cast<In*>(prm.y);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = lane % LPC;       // position in the row's lane group
+  const int b = blockIdx.y;
+  const int d = blockIdx.x * RPB + wv * RPW + lane / LPC;
+  const bool row_ok = d < prm.dim;
+  const bool has_z = z != nullptr;
+  const int L = prm.seqlen;
+  const int N = prm.dstate;
+  const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
+  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+
+  // Per-row constants for this lane's states n = slot*NG + k.
+  float A2[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    A2[k] = (row_ok && n < N) ? prm.A[(int64_t)d * N + n] * kLog2e : 0.0f;
+  }
+  const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
+  const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
+
+  float h[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) h[k] = 0.0f;
+
+  // Raw chunk data, loaded one chunk ahead of its use.
+  RawSeg<In, TS> ru, rd, rz;
+  RawSeg<In, EPU> rbc[RB];
+  auto load_chunk = [&](int c0) {
+    const int ts = c0 + slot * TS;
+    if (row_ok) {
+      load_raw<In, TS>(u, row_base, ts, L, ru);
+      load_raw<In, TS>(dlt, row_base, ts, L, rd);
+      if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
+    }
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * 256;
+      const int n = e % NS, rest = e / NS;
+      const int seg = rest % UPR, x = rest / UPR;
+      if (e < UNITS && n < N) {
+        load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, rbc[q]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
+      }
+    }
+  };
+
+  const int nchunks = (L + T - 1) / T;
+  load_chunk(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * T;
+    const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
+
+    // -- B and C of this chunk into LDS as float32 [t][n] --------------------
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * 256;
+      if (e < UNITS) {
+        const int n = e % NS, rest = e / NS;
+        const int seg = rest % UPR, x = rest / UPR;
+        float v[EPU];
+        decode_raw<In, EPU>(rbc[q], v);
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) {
+          if (x) sC[buf][seg * EPU + i][n] = v[i];
+          else sB[buf][seg * EPU + i][n] = v[i];
+        }
+      }
+    }
+    // -- per-step work for this lane's slice of the chunk ---------------------
+    const int ts = c0 + slot * TS;
+    float uk[TS], gk[TS], dl[TS], du[TS];
+    {
+      float dr[TS];
+      decode_raw<In, TS>(ru, uk);
+      decode_raw<In, TS>(rd, dr);
+      if (has_z) {
+        float zk[TS];
+        decode_raw<In, TS>(rz, zk);
+#pragma unroll
+        for (int j = 0; j < TS; ++j) gk[j] = silu_f(zk[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) gk[j] = 1.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float v = dr[j] + bias;
+        dl[j] = prm.delta_softplus ? softplus_f(v) : v;
+      }
+      // Steps past the end are the identity (delta = 0).  Rows past `dim`
+      // compute on zeros and are never stored.
+      if (ts + TS > L) {
+#pragma unroll
+        for (int j = 0; j < TS; ++j)
+          if (ts + j >= L) dl[j] = 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < TS; ++j) du[j] = dl[j] * uk[j];
+    }
+    if (ch + 1 < nchunks) load_chunk(c0 + T);
+    __syncthreads();
+
+    // -- recurrence over the chunk ([EXPLAINED] eq. (7)) -----------------------
+    float yp[T];
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      float dt, dut;  // delta and delta*u of step t, from the lane that owns it
+      if constexpr (LPC > 1) {
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+      } else {
+        dt = dl[t];
+        dut = du[t];
+      }
+      float acc = 0.0f;
+#pragma unroll
+      for (int k4 = 0; k4 < NG; k4 += 4) {
+        const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG + k4]);
+        const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
+        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+        const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = fast_exp2(dt * A2[k4 + i]);
+          h[k4 + i] = __builtin_fmaf(a, h[k4 + i], dut * bv[i]);
+          acc = __builtin_fmaf(cv[i], h[k4 + i], acc);
+        }
+      }
+      yp[t] = acc;
+    });
+
+    // -- sum the group's partial readouts onto the owners of the steps ---------
+    float yo[TS];
+    if constexpr (LPC == 4) {
+      float s1[T / 2];
+      const bool lo = slot < 2;  // lanes 0, 1 keep the first half of the chunk
+#pragma unroll
+      for (int j = 0; j < T / 2; ++j) {
+        const float keep = lo ? yp[j] : yp[T / 2 + j];
+        const float send = lo ? yp[T / 2 + j] : yp[j];
+        s1[j] = keep + dpp_f<kSwapHalves>(send);
+      }
+      const bool ev = (slot & 1) == 0;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float keep = ev ? s1[j] : s1[TS + j];
+        const float send = ev ? s1[TS + j] : s1[j];
+        yo[j] = keep + dpp_f<kSwapPairs>(send);
+      }
+    } else if constexpr (LPC == 2) {
+      const bool ev = slot == 0;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float keep = ev ? yp[j] : yp[TS + j];
+        const float send = ev ? yp[TS + j] : yp[j];
+        yo[j] = keep + dpp_f<kSwapPairs>(send);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TS; ++j) yo[j] = yp[j];
+    }
+    // -- skip term, gate, store -------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < TS; ++j) yo[j] = __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j];
+    if (row_ok) store_seg<In, TS>(y, row_base, ts, L, yo);
+  }
+
+  // -- final state -------------------------------------------------------------
+  if (prm.last_state && row_ok) {
+    float* ls = prm.last_state + ((int64_t)b * prm.dim + d) * N;
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      if (slot * NG + k < N) ls[slot * NG + k] = h[k];
+  }
+}
+
+// ---- time-split kernel -------------------------------------------------------
+
+// NG: states per wave; G: waves splitting the states; W (> 1): time slots
+// per chunk; T: steps per slot.  Block = 64 * G * W threads.
 template <typename In, int NG, int G, int W, int T>
 __global__ void __launch_bounds__(64 * G * W)
-selective_scan_fwd_kernel(ScanParams prm) {
+selective_scan_split_kernel(ScanParams prm) {
+  static_assert(W > 1, "the row-parallel kernel covers W = 1");
   constexpr int NT = NG * G;       // states covered by one workgroup (>= dstate)
   constexpr int TC = W * T;        // steps per chunk
   constexpr int TG = T / G;        // steps of a slot whose per-step work one wave owns
@@ -301,44 +554,7 @@ selective_scan_fwd_kernel(ScanParams prm) {
 #pragma unroll
     for (int j = 0; j < T; ++j) yp[j] = 0.0f;
 
-    if constexpr (W == 1) {
-      // Plain recurrence ([EXPLAINED] eq. (7)) with the state kept in
-      // registers.  LDS operands are fetched one block of JB steps ahead of
-      // their use so that their latency overlaps the previous block's math.
-      constexpr int JB = T >= 8 ? 8 : T;
-      static_assert(T % JB == 0, "T must be a multiple of the block");
-      float2 ddq[2][JB];
-      float bq[2][JB][NG], cq[2][JB][NG];
-      auto fetch = [&](int buf, int j0) {
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-          ddq[buf][jj] = sDD[0][j0 + jj][lane];
-#pragma unroll
-          for (int k = 0; k < NG; ++k) {
-            bq[buf][jj][k] = sB[j0 + jj][g * NG + k];
-            cq[buf][jj][k] = sC[j0 + jj][g * NG + k];
-          }
-        }
-      };
-      fetch(0, 0);
-#pragma unroll
-      for (int jb = 0; jb < T / JB; ++jb) {
-        const int cur = jb & 1;
-        if (jb + 1 < T / JB) fetch(cur ^ 1, (jb + 1) * JB);
-#pragma unroll
-        for (int jj = 0; jj < JB; ++jj) {
-          const float2 dd = ddq[cur][jj];
-          float acc = 0.0f;
-#pragma unroll
-          for (int k = 0; k < NG; ++k) {
-            const float a = fast_exp2(dd.x * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], dd.y * bq[cur][jj][k]);
-            acc = __builtin_fmaf(cq[cur][jj][k], h[k], acc);
-          }
-          yp[jb * JB + jj] = acc;
-        }
-      }
-    } else {
+    {
       // Pass 1: slot aggregate from the identity (1, 0).
       float acache[T][NG];
       float v[NG];
@@ -419,35 +635,37 @@ selective_scan_fwd_kernel(ScanParams prm) {
   // -- final state -----------------------------------------------------------
   if (prm.last_state && row_ok) {
     float* ls = prm.last_state + ((int64_t)b * prm.dim + d) * N;
-    if constexpr (W == 1) {
 #pragma unroll
-      for (int k = 0; k < NG; ++k)
-        if (g * NG + k < N) ls[g * NG + k] = h[k];
-    } else {
-#pragma unroll
-      for (int q = 0; q < PAIRS; ++q) {
-        const int n = wv + q * (G * W);
-        if (n < N) ls[n] = carry[q];
-      }
+    for (int q = 0; q < PAIRS; ++q) {
+      const int n = wv + q * (G * W);
+      if (n < N) ls[n] = carry[q];
     }
   }
+}
+
+template <typename In, int NG, int LPC, int T>
+hipError_t launch_rows(const ScanParams& p, hipStream_t stream) {
+  constexpr int RPB = 4 * (64 / LPC);
+  dim3 grid((unsigned)((p.dim + RPB - 1) / RPB), (unsigned)p.batch);
+  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <typename In, int NG, int G, int W, int T>
 hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   dim3 grid((unsigned)((p.dim + 63) / 64), (unsigned)p.batch);
   dim3 block(64 * G * W);
-  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, G, W, T>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((selective_scan_split_kernel<In, NG, G, W, T>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename In>
 hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
   switch (t.id) {
-    case ScanTileId::kN4_Seq: return launch_cfg<In, 4, 1, 1, 32>(p, s);
-    case ScanTileId::kN8_Seq: return launch_cfg<In, 4, 2, 1, 32>(p, s);
-    case ScanTileId::kN16_Seq: return launch_cfg<In, 4, 4, 1, 32>(p, s);
-    case ScanTileId::kN64_Seq: return launch_cfg<In, 16, 4, 1, 16>(p, s);
+    case ScanTileId::kN4_Seq: return launch_rows<In, 4, 1, 16>(p, s);
+    case ScanTileId::kN8_Seq: return launch_rows<In, 4, 2, 32>(p, s);
+    case ScanTileId::kN16_Seq: return launch_rows<In, 4, 4, 32>(p, s);
+    case ScanTileId::kN64_Seq: return launch_rows<In, 16, 4, 32>(p, s);
     case ScanTileId::kN4_Split: return launch_cfg<In, 4, 1, 8, 8>(p, s);
     case ScanTileId::kN8_Split: return launch_cfg<In, 4, 2, 4, 16>(p, s);
     case ScanTileId::kN16_Split: return launch_cfg<In, 4, 4, 4, 16>(p, s);
