@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <cstdio>
+#include <type_traits>
 
 #include "device_math.h"
 #include "ssd_launch.h"
@@ -144,6 +145,14 @@ __device__ __forceinline__ bf16x8 lds_kop(const uint16_t* tile, int stride, int 
 
 constexpr int kHGMax = 8;           // most heads one workgroup handles
 
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
 // Most heads per output-kernel workgroup: the largest shape keeps fewer so
 // that its per-head decay tables fit in LDS beside the x and state tiles.
 constexpr int out_heads_max(int P, int N) { return P * N >= 128 * 256 ? 4 : kHGMax; }
@@ -233,9 +242,10 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int nh, const GroupRaw<
 // natural row-major layouts, written with coalesced 16-byte loads; the MFMA
 // operands, whose contraction index runs over rows, are read back with the
 // transposing LDS read.  Every global load that does not depend on earlier
-// results is issued at the start; each head's x comes from registers loaded
-// while the previous head computed, into one of two LDS buffers when both
-// fit.
+// results is issued at the start, and each head's x is loaded into
+// registers PD heads ahead of its use (a ring of PD + 1 register sets,
+// indexed statically by unrolling the head loop by the ring size), so that
+// several heads' loads are in flight while the small per-head product runs.
 template <int P, int NB>
 __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   constexpr int NTHR = 1024, NW = 16;
@@ -251,6 +261,14 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
   constexpr int XPT = (kQMax * P / 8 + NTHR - 1) / NTHR;
   constexpr int BPT = (kQMax * NB / 8 + NTHR - 1) / NTHR;
+  constexpr int PD = 6 / XPT < 1 ? 1 : (6 / XPT > 4 ? 4 : 6 / XPT);  // heads of x in flight
+  // When the staging tasks cover the kQMax-row tiles exactly, every task
+  // writes a row that exists (rows past the chunk are never read), so the
+  // staging needs no per-thread condition; a condition there would make the
+  // compiler wait for every outstanding load before the next prefetch.
+  constexpr bool kXExact = kQMax * P / 8 == XPT * NTHR;
+  constexpr bool kBExact = kQMax * NB / 8 == BPT * NTHR;
+  constexpr int RING = PD + 1;
 
   const int c = blockIdx.x, b = blockIdx.y;
   const int hpg = a.nheads / a.ngroups;
@@ -265,15 +283,24 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   const int xtasks = Q * P / 8;
   const int btasks = Q * NB / 8;
 
-  uint4 xr[XPT], br[BPT];
-  auto prefetch = [&](int hh) {
+  uint4 xr[RING][XPT], br[BPT];
+  const uint16_t* xsrc[XPT];  // this thread's x pieces of the group's first head
 #pragma unroll
-    for (int k = 0; k < XPT; ++k) {
-      const int task = tid + k * NTHR;
-      const int s = task / (P / 8), po = task % (P / 8);
-      xr[k] = load16(a.x + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.nheads + h0 + hh) * P +
-                     8 * po);
-    }
+  for (int k = 0; k < XPT; ++k) {
+    const int task = tid + k * NTHR;
+    const int s = task / (P / 8), po = task % (P / 8);
+    xsrc[k] = a.x + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.nheads + h0) * P + 8 * po;
+  }
+  // x of head hh into ring slot SLOT
+  auto prefetch = [&](auto slot, int hh) {
+    constexpr int SLOT = decltype(slot)::value;
+#pragma unroll
+    for (int k = 0; k < XPT; ++k) xr[SLOT][k] = load16(xsrc[k] + (int64_t)hh * P);
+  };
+  auto prefetch_first = [&]() {
+    static_for<0, PD>([&](auto jc) {
+      if (decltype(jc)::value < nh) prefetch(jc, decltype(jc)::value);
+    });
   };
   auto load_b = [&](int nb0) {
 #pragma unroll
@@ -285,15 +312,16 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
     }
   };
   // (w x)[s][p] = x[s][p] exp2(cs_last - cs_s) dt_s, rounded to bf16.
-  auto stage = [&](int hh, int buf) {
+  auto stage = [&](auto slot, int hh, int buf) {
+    constexpr int SLOT = decltype(slot)::value;
     const float cs_last = sCs2[hh][Q - 1];
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
-      if (task < xtasks) {
+      if (kXExact || task < xtasks) {
         const int s = task / (P / 8), po = task % (P / 8);
         const float w = fast_exp2(cs_last - sCs2[hh][s]) * sDt[hh][s];
-        const uint32_t e[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+        const uint32_t e[4] = {xr[SLOT][k].x, xr[SLOT][k].y, xr[SLOT][k].z, xr[SLOT][k].w};
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -309,7 +337,7 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   GroupRaw<NTHR> graw;
   load_group_dt<NTHR>(a, b, c, h0, nh, graw);
   load_b(0);
-  prefetch(0);
+  prefetch_first();
   group_log_decay<NTHR>(a, c, nh, graw, sCs2, sDt, sTmp);
   if (tid < nh)
     a.decay[((int64_t)b * a.nheads + h0 + tid) * a.nchunks + c] = fast_exp2(sCs2[tid][Q - 1]);
@@ -317,23 +345,28 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   for (int nb0 = 0; nb0 < N; nb0 += NB) {
     if (nb0 > 0) {
       load_b(nb0);
-      prefetch(0);
+      prefetch_first();
       __syncthreads();  // earlier readers of sB and sX are done
     }
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
-      if (task < btasks) {
+      if (kBExact || task < btasks) {
         const int s = task / (NB / 8), part = task % (NB / 8);
         *reinterpret_cast<uint4*>(&sB[s][8 * part]) = br[k];
       }
     }
-    stage(0, 0);
-    if (nh > 1) prefetch(1);
-    __syncthreads();
-    for (int hh = 0; hh < nh; ++hh) {
+    for (int hb = 0; hb < nh; hb += RING) static_for<0, RING>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int hh = hb + J;
+      if (hh >= nh) return;
       const int h = h0 + hh;
       const int buf = DB ? (hh & 1) : 0;
+      // a single buffer's previous readers are done (the barrier after the
+      // last head's product); two buffers alternate
+      stage(jc, hh, buf);
+      if (hh + PD < nh) prefetch(std::integral_constant<int, (J + PD) % RING>{}, hh + PD);
+      __syncthreads();
       // S_c^T[n][p] = sum_s B[s][n] (w x)[s][p]
       f32x4 acc[TPW];
 #pragma unroll
@@ -350,38 +383,22 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
           }
         }
       }
+      if (!DB || hh + 1 == nh) __syncthreads();  // readers of sX (and sB) are done
       // lane holds S_c[p][n .. n+3] with p = pt*16 + r16, n = nt*16 + 4*q4
-      uint2 so[TPW];
+      uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        so[t].x = (uint32_t)f32_to_bf16_bits(acc[t][0]) | ((uint32_t)f32_to_bf16_bits(acc[t][1]) << 16);
-        so[t].y = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
-      }
-      auto store_s = [&]() {
-        uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          const int tile = wv + NW * t;
-          if (tile < TILES) {
-            const int nt = tile / PT, pt = tile % PT;
-            const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
-            *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = so[t];
-          }
+        const int tile = wv + NW * t;
+        if (tile < TILES) {
+          const int nt = tile / PT, pt = tile % PT;
+          const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
+          uint2 o;
+          o.x = (uint32_t)f32_to_bf16_bits(acc[t][0]) | ((uint32_t)f32_to_bf16_bits(acc[t][1]) << 16);
+          o.y = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
+          *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
         }
-      };
-      // Stage the next head before storing this one, and keep stage, stores
-      // and the next prefetch on one path, so that waiting for the staged
-      // loads never waits for these stores.
-      if (hh + 1 < nh) {
-        if (!DB) __syncthreads();  // readers of the single buffer are done
-        stage(hh + 1, DB ? ((hh + 1) & 1) : 0);
-        store_s();
-        if (hh + 2 < nh) prefetch(hh + 2);
-        __syncthreads();
-      } else {
-        store_s();
       }
-    }
+    });
   }
 }
 
@@ -445,6 +462,11 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr int XPT = (kQMax * P / 8 + NTHR - 1) / NTHR;
   constexpr int SPT = (P * N / 8 + NTHR - 1) / NTHR;
   constexpr int BPT = (kQMax * KB / 8 + NTHR - 1) / NTHR;
+  // Staging tasks that cover their tile exactly need no per-thread condition
+  // (rows past the chunk are written but never read).
+  constexpr bool kXExact = kQMax * P / 8 == XPT * NTHR;
+  constexpr bool kSExact = P * N / 8 == SPT * NTHR;
+  constexpr bool kBExact = kQMax * KB / 8 == BPT * NTHR;
   // LDS: x [s][p] and S_in [p][n] of one head (two buffers when they fit);
   // B [s][n] for the G^T phase shares the same bytes (it is only used before
   // the first head is staged).
@@ -518,7 +540,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
-      if (task < xtasks) {
+      if (kXExact || task < xtasks) {
         const int s = task / (P / 8), po = task % (P / 8);
         *reinterpret_cast<uint4*>(&sX[buf][s][8 * po]) = xr[k];
       }
@@ -526,7 +548,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
       const int task = tid + k * NTHR;
-      if (task < P * N / 8) {
+      if (kSExact || task < P * N / 8) {
         const int p = task / (N / 8), n8 = task % (N / 8);
         *reinterpret_cast<uint4*>(&sS[buf][p][8 * n8]) = sr[k];
       }
@@ -582,7 +604,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
-      if (task < btasks) {
+      if (kBExact || task < btasks) {
         const int s = task / (KB / 8), part = task % (KB / 8);
         *reinterpret_cast<uint4*>(&sBs[s][8 * part]) = br[k];
       }
