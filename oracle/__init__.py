@@ -52,6 +52,16 @@ def _load():
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_selective_scan_h0_f64.restype = ctypes.c_int
+    lib.oracle_selective_scan_h0_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_ssd_h0_f64.restype = ctypes.c_int
+    lib.oracle_ssd_h0_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
     lib.oracle_ssd_f64.restype = ctypes.c_int
     lib.oracle_ssd_f64.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
@@ -79,14 +89,24 @@ def default_threads() -> int:
     return max(1, min(len(os.sched_getaffinity(0)), 16))
 
 
+def _f64(a, shape):
+    if a is None:
+        return None
+    arr = np.ascontiguousarray(a, dtype=np.float64)
+    if arr.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {arr.shape}")
+    return arr
+
+
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                    delta_softplus=True, rows=None, want_y=True,
-                   want_state=True, nthreads=None):
+                   want_state=True, nthreads=None, h0=None):
     """Mamba-1 selective scan in fp64.
 
     u, delta, z: [batch, dim, seqlen]; A: [dim, dstate]; B, C: [batch, dstate,
-    seqlen]; D, delta_bias: [dim].  ``rows`` optionally restricts the work to
-    flat row indices b*dim+d (outputs then follow that order).
+    seqlen]; D, delta_bias: [dim]; h0: optional initial state [batch, dim,
+    dstate] (float64; zero when None).  ``rows`` optionally restricts the
+    work to flat row indices b*dim+d (outputs then follow that order).
     Returns (y [nrows, seqlen] or None, last_state [nrows, dstate] or None),
     both float64; with rows=None, nrows = batch*dim in (b, d) order.
     """
@@ -109,9 +129,11 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         nrows = rows_arr.shape[0]
     y = np.empty((nrows, seqlen), np.float64) if want_y else None
     st = np.empty((nrows, dstate), np.float64) if want_state else None
-    rc = lib.oracle_selective_scan_f64(
+    h0 = _f64(h0, (batch, dim, dstate))
+    rc = lib.oracle_selective_scan_h0_f64(
         _p32(u), _p32(delta), _p32(A), _p32(B), _p32(C), _p32(D), _p32(z),
-        _p32(delta_bias), int(bool(delta_softplus)), batch, dim, dstate, seqlen,
+        _p32(delta_bias), int(bool(delta_softplus)),
+        None if h0 is None else h0.ctypes.data_as(_f64p), batch, dim, dstate, seqlen,
         None if rows_arr is None else rows_arr.ctypes.data_as(_i64p), nrows,
         None if y is None else y.ctypes.data_as(_f64p),
         None if st is None else st.ctypes.data_as(_f64p),
@@ -122,11 +144,13 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 
 
 def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,
-             want_y=True, want_state=True, nthreads=None):
+             want_y=True, want_state=True, nthreads=None, initial_state=None):
     """Mamba-2 (scalar A per head) recurrence in fp64.
 
     x: [batch, seqlen, nheads, headdim]; dt: [batch, seqlen, nheads];
-    A, D, dt_bias: [nheads]; B, C: [batch, seqlen, ngroups, dstate].
+    A, D, dt_bias: [nheads]; B, C: [batch, seqlen, ngroups, dstate];
+    initial_state: optional [batch, nheads, headdim, dstate] (float64; zero
+    when None).
     Returns (y [batch, seqlen, nheads, headdim], final_state [batch, nheads,
     headdim, dstate]) as float64 (either may be None).
     """
@@ -144,9 +168,11 @@ def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,
     dt_bias = _f32(dt_bias, (nheads,))
     y = np.empty((batch, seqlen, nheads, headdim), np.float64) if want_y else None
     st = np.empty((batch, nheads, headdim, dstate), np.float64) if want_state else None
-    rc = lib.oracle_ssd_f64(
+    init = _f64(initial_state, (batch, nheads, headdim, dstate))
+    rc = lib.oracle_ssd_h0_f64(
         _p32(x), _p32(dt), _p32(A), _p32(B), _p32(C), _p32(D), _p32(dt_bias),
-        int(bool(dt_softplus)), batch, seqlen, nheads, headdim, dstate, ngroups,
+        int(bool(dt_softplus)), None if init is None else init.ctypes.data_as(_f64p),
+        batch, seqlen, nheads, headdim, dstate, ngroups,
         None if y is None else y.ctypes.data_as(_f64p),
         None if st is None else st.ctypes.data_as(_f64p),
         int(nthreads or default_threads()))

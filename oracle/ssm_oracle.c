@@ -30,7 +30,10 @@
  *     [SPEC] Stage 1, [BLELLOCH] 4.1), with the undefined factor mu = 1.
  *   - delta_bias is added before softplus.
  *   - output order: y = (C.h + D*u) * silu(z)  ([SPEC] Stage 1 reference).
- *   - the state starts at zero.
+ *   - the state starts at zero unless an initial state v_0 is given: the
+ *     closed form of [EXPLAINED] eqs. (8)-(9) carries a v_0 term, and with it
+ *     a sequence can be scanned in pieces, each piece starting from the
+ *     state the previous one ended with.
  *   - Mamba-2 output: y = C.h + D*x (skip connection by analogy with
  *     [EXPLAINED] eq. (2)); its recurrence is the one [CUTILE] states.
  */
@@ -55,6 +58,7 @@ static double silu_d(double z) { return z / (1.0 + exp(-z)); }
 
 typedef struct {
   const float *u, *delta, *A, *B, *C, *D, *z, *delta_bias;
+  const double *h0; /* initial state [batch, dim, dstate] or NULL (zero) */
   int delta_softplus;
   int64_t batch, dim, dstate, seqlen;
   const int64_t *rows;
@@ -76,7 +80,8 @@ static void mamba1_one_row(const mamba1_job *j, int64_t out_index, int64_t row,
   const double Dd = j->D ? (double)j->D[d] : 0.0;
   const double bias = j->delta_bias ? (double)j->delta_bias[d] : 0.0;
 
-  for (int64_t n = 0; n < N; ++n) h[n] = 0.0; /* zero initial state */
+  /* initial state v_0 ([EXPLAINED] eqs. (8)-(9)); zero when not given */
+  for (int64_t n = 0; n < N; ++n) h[n] = j->h0 ? j->h0[row * N + n] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
     /* step size: delta_t = softplus(Delta_t + bias) */
     double dt = (double)dl[t] + bias;
@@ -114,15 +119,16 @@ static void *mamba1_worker(void *arg) {
 
 /* Returns 0 on success, -1 on invalid arguments, -2 on thread/alloc failure.
  * rows: optional list of flat row indices b*dim+d (NULL = all rows in order);
+ * h0: initial state [batch, dim, dstate] (nullable = zero);
  * y: [nrows, seqlen] (nullable); last_state: [nrows, dstate] (nullable). */
-int oracle_selective_scan_f64(const float *u, const float *delta,
-                              const float *A, const float *B, const float *C,
-                              const float *D, const float *z,
-                              const float *delta_bias, int delta_softplus,
-                              int64_t batch, int64_t dim, int64_t dstate,
-                              int64_t seqlen, const int64_t *rows,
-                              int64_t nrows, double *y, double *last_state,
-                              int nthreads) {
+int oracle_selective_scan_h0_f64(const float *u, const float *delta,
+                                 const float *A, const float *B, const float *C,
+                                 const float *D, const float *z,
+                                 const float *delta_bias, int delta_softplus,
+                                 const double *h0, int64_t batch, int64_t dim,
+                                 int64_t dstate, int64_t seqlen,
+                                 const int64_t *rows, int64_t nrows, double *y,
+                                 double *last_state, int nthreads) {
   if (!u || !delta || !A || !B || !C) return -1;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return -1;
   if (!rows) nrows = batch * dim;
@@ -142,6 +148,7 @@ int oracle_selective_scan_f64(const float *u, const float *delta,
     mamba1_job *j = &jobs[w];
     j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D;
     j->z = z; j->delta_bias = delta_bias; j->delta_softplus = delta_softplus;
+    j->h0 = h0;
     j->batch = batch; j->dim = dim; j->dstate = dstate; j->seqlen = seqlen;
     j->rows = rows; j->nrows = nrows; j->y = y; j->last_state = last_state;
     j->row_begin = nrows * w / nthreads;
@@ -162,6 +169,21 @@ int oracle_selective_scan_f64(const float *u, const float *delta,
   return rc;
 }
 
+/* Zero initial state. */
+int oracle_selective_scan_f64(const float *u, const float *delta,
+                              const float *A, const float *B, const float *C,
+                              const float *D, const float *z,
+                              const float *delta_bias, int delta_softplus,
+                              int64_t batch, int64_t dim, int64_t dstate,
+                              int64_t seqlen, const int64_t *rows,
+                              int64_t nrows, double *y, double *last_state,
+                              int nthreads) {
+  return oracle_selective_scan_h0_f64(u, delta, A, B, C, D, z, delta_bias,
+                                      delta_softplus, NULL, batch, dim, dstate,
+                                      seqlen, rows, nrows, y, last_state,
+                                      nthreads);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Mamba-2 (SSD): scalar A per head, B and C per group, state [P, N].       */
 /* h_t = exp(A_h dt_t) h_{t-1} + dt_t B_t x_t^T   ([CUTILE], recurrence)     */
@@ -170,6 +192,7 @@ int oracle_selective_scan_f64(const float *u, const float *delta,
 
 typedef struct {
   const float *x, *dt, *A, *B, *C, *D, *dt_bias;
+  const double *init; /* initial state [b, h, P, N] or NULL (zero) */
   int dt_softplus;
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups;
   double *y, *final_state;
@@ -188,7 +211,10 @@ static void *ssd_worker(void *arg) {
     const double Ah = (double)j->A[h];
     const double Dh = j->D ? (double)j->D[h] : 0.0;
     const double bias = j->dt_bias ? (double)j->dt_bias[h] : 0.0;
-    memset(S, 0, sizeof(double) * (size_t)(P * N));
+    if (j->init) /* the state entering the sequence (zero when not given) */
+      memcpy(S, j->init + (b * H + h) * P * N, sizeof(double) * (size_t)(P * N));
+    else
+      memset(S, 0, sizeof(double) * (size_t)(P * N));
     for (int64_t t = 0; t < L; ++t) {
       double dt = (double)j->dt[(b * L + t) * H + h] + bias; /* dt: [b, L, h] */
       if (j->dt_softplus) dt = softplus_d(dt);
@@ -215,12 +241,14 @@ static void *ssd_worker(void *arg) {
   return NULL;
 }
 
-int oracle_ssd_f64(const float *x, const float *dt, const float *A,
-                   const float *B, const float *C, const float *D,
-                   const float *dt_bias, int dt_softplus, int64_t batch,
-                   int64_t seqlen, int64_t nheads, int64_t headdim,
-                   int64_t dstate, int64_t ngroups, double *y,
-                   double *final_state, int nthreads) {
+/* init: initial state [b, h, P, N] (nullable = zero). */
+int oracle_ssd_h0_f64(const float *x, const float *dt, const float *A,
+                      const float *B, const float *C, const float *D,
+                      const float *dt_bias, int dt_softplus,
+                      const double *init, int64_t batch, int64_t seqlen,
+                      int64_t nheads, int64_t headdim, int64_t dstate,
+                      int64_t ngroups, double *y, double *final_state,
+                      int nthreads) {
   if (!x || !dt || !A || !B || !C) return -1;
   if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 ||
       dstate <= 0 || ngroups <= 0 || nheads % ngroups != 0)
@@ -237,7 +265,7 @@ int oracle_ssd_f64(const float *x, const float *dt, const float *A,
   for (int w = 0; w < nthreads; ++w) {
     ssd_job *j = &jobs[w];
     j->x = x; j->dt = dt; j->A = A; j->B = B; j->C = C; j->D = D;
-    j->dt_bias = dt_bias; j->dt_softplus = dt_softplus;
+    j->dt_bias = dt_bias; j->dt_softplus = dt_softplus; j->init = init;
     j->batch = batch; j->seqlen = seqlen; j->nheads = nheads;
     j->headdim = headdim; j->dstate = dstate; j->ngroups = ngroups;
     j->y = y; j->final_state = final_state;
@@ -257,4 +285,16 @@ int oracle_ssd_f64(const float *x, const float *dt, const float *A,
     if (ret != NULL) rc = -2;
   }
   return rc;
+}
+
+/* Zero initial state. */
+int oracle_ssd_f64(const float *x, const float *dt, const float *A,
+                   const float *B, const float *C, const float *D,
+                   const float *dt_bias, int dt_softplus, int64_t batch,
+                   int64_t seqlen, int64_t nheads, int64_t headdim,
+                   int64_t dstate, int64_t ngroups, double *y,
+                   double *final_state, int nthreads) {
+  return oracle_ssd_h0_f64(x, dt, A, B, C, D, dt_bias, dt_softplus, NULL, batch,
+                           seqlen, nheads, headdim, dstate, ngroups, y,
+                           final_state, nthreads);
 }

@@ -374,6 +374,91 @@ def test_ssd_equals_mamba1_after_relayout():
         np.testing.assert_allclose(st2[:, h], st1.reshape(batch, P, N), rtol=1e-13, atol=1e-13)
 
 
+# ---------------------------------------------------------------------------
+# Initial state v_0 ([EXPLAINED] eqs. (8)-(9) carry a v_0 term)
+# ---------------------------------------------------------------------------
+
+def _cut_time(x, k0, k1, time_axis):
+    out = {}
+    for key, v in x.items():
+        if v is None or key not in time_axis:
+            out[key] = v
+        else:
+            sl = [slice(None)] * v.ndim
+            sl[time_axis[key]] = slice(k0, k1)
+            out[key] = np.ascontiguousarray(v[tuple(sl)])
+    return out
+
+
+M1_TIME = {"u": 2, "delta": 2, "z": 2, "B": 2, "C": 2}
+SSD_TIME = {"x": 1, "dt": 1, "B": 1, "C": 1}
+
+
+@pytest.mark.parametrize("k", [1, 17, 39])
+def test_scan_in_pieces_equals_one_scan(k):
+    """Scanning [0, L) at once equals scanning [0, k) and then [k, L) from the
+    state the first piece ended with: the same operations in the same order,
+    so the outputs are bitwise equal."""
+    x = small_inputs(20, batch=2, dim=3, dstate=4, seqlen=40, gate=True, bias=True)
+    y, st = oracle.selective_scan(**x)
+    _, st1 = oracle.selective_scan(**_cut_time(x, 0, k, M1_TIME), want_y=False)
+    y2, st2 = oracle.selective_scan(**_cut_time(x, k, 40, M1_TIME), h0=st1.reshape(2, 3, 4))
+    assert np.array_equal(y.reshape(2, 3, 40)[:, :, k:], y2.reshape(2, 3, 40 - k))
+    assert np.array_equal(st, st2)
+
+
+def test_initial_state_decays_in_closed_form():
+    """With u = 0 the input term vanishes and only v_0 remains:
+    h_t[n] = exp(A[n] * sum_{s<=t} delta_s) h0[n] ([EXPLAINED] eq. (8),
+    products of exponentials as the exponential of a sum), so
+    y_t = sum_n C_t[n] h_t[n] (times the gate)."""
+    x = small_inputs(21, batch=2, dim=3, dstate=5, seqlen=30, gate=True, bias=False)
+    x["u"] = np.zeros_like(x["u"])
+    rng = np.random.default_rng(3)
+    h0 = rng.standard_normal((2, 3, 5))
+    y, st = oracle.selective_scan(**x, delta_softplus=False, h0=h0)
+    dl = x["delta"].astype(np.float64)
+    A = x["A"].astype(np.float64)
+    z = x["z"].astype(np.float64)
+    y = y.reshape(2, 3, 30)
+    for b in range(2):
+        for d in range(3):
+            cs = np.cumsum(dl[b, d])
+            h = np.exp(A[d][:, None] * cs[None, :]) * h0[b, d][:, None]      # [N, L]
+            want = (x["C"][b].astype(np.float64) * h).sum(0) * (z[b, d] / (1 + np.exp(-z[b, d])))
+            np.testing.assert_allclose(y[b, d], want, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(st.reshape(2, 3, 5)[b, d], h[:, -1], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("k", [1, 13, 39])
+def test_ssd_scan_in_pieces_equals_one_scan(k):
+    """The Mamba-2 recurrence ([CUTILE]) scanned in two pieces, the second
+    starting from the first piece's final state, equals one scan (bitwise)."""
+    s = ssd_small(22, batch=2, L=40, H=4, P=3, N=5, G=2)
+    y, st = oracle.ssd_scan(**s)
+    _, st1 = oracle.ssd_scan(**_cut_time(s, 0, k, SSD_TIME), want_y=False)
+    y2, st2 = oracle.ssd_scan(**_cut_time(s, k, 40, SSD_TIME), initial_state=st1)
+    assert np.array_equal(y[:, k:], y2)
+    assert np.array_equal(st, st2)
+
+
+def test_ssd_initial_state_decays_in_closed_form():
+    """x = 0: S_t = exp(A_h * sum_{s<=t} dt_s) S_0 and y_t[p] = C_t . S_t[p]."""
+    s = ssd_small(23, batch=1, L=20, H=2, P=3, N=4, G=1)
+    s["x"] = np.zeros_like(s["x"])
+    rng = np.random.default_rng(4)
+    init = rng.standard_normal((1, 2, 3, 4))
+    y, st = oracle.ssd_scan(**s, initial_state=init)
+    dtv = np.logaddexp(0.0, s["dt"].astype(np.float64) + s["dt_bias"].astype(np.float64)[None, None, :])
+    for h in range(2):
+        cs = np.cumsum(s["A"][h] * dtv[0, :, h])
+        for t in range(20):
+            S = np.exp(cs[t]) * init[0, h]
+            np.testing.assert_allclose(y[0, t, h], S @ s["C"][0, t, 0].astype(np.float64),
+                                       rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(st[0, h], np.exp(cs[-1]) * init[0, h], rtol=1e-12, atol=1e-13)
+
+
 def ssd_chunked_reference(x, dt, A, B, C, D, dt_bias, Q):
     """Chunked form of the SSD recurrence in fp64 numpy ([CUTILE]: chunk
     cumulative sums of A*dt in log space; per-chunk states; the jump formula
