@@ -102,7 +102,8 @@ ssm_status ssm_scan_destroy(ssm_handle handle);
  * Done asks for documented limits; there is no seqlen limit).  batch*dim
  * and seqlen must each fit in 2^31-1.  Sizes <= 0 return
  * SSM_ERR_INVALID_ARG without touching the device ([SPEC] Definition of
- * Done: batch=0 must not crash).  The initial state is zero.
+ * Done: batch=0 must not crash).  The initial state is zero (see
+ * ssm_selective_scan_fwd_with_state for a given one).
  */
 ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void *u,
                                   const void *delta, const float *A,
@@ -112,6 +113,29 @@ ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void *u,
                                   float *last_state, int64_t batch,
                                   int64_t dim, int64_t dstate, int64_t seqlen,
                                   ssm_dtype in_dtype, hipStream_t stream);
+
+/*
+ * ssm_selective_scan_fwd with an initial state: h[b,d,:] starts at
+ * initial_state[b,d,:] instead of zero (the v_0 term of the closed form in
+ * [EXPLAINED] eqs. (8)-(9)).  A sequence split into pieces and scanned piece
+ * by piece, each call given the last_state of the previous one, gives the
+ * same y and last_state as one call over the whole sequence (up to float32
+ * rounding).
+ *
+ *   initial_state : [batch, dim, dstate] float32, nullable (NULL = zero,
+ *                   which is ssm_selective_scan_fwd).  16-byte aligned.
+ *                   It may be the same pointer as last_state (the state is
+ *                   then updated in place); any other overlap with an
+ *                   output returns SSM_ERR_INVALID_ARG.
+ * Every other argument, layout, limit and error is as for
+ * ssm_selective_scan_fwd.
+ */
+ssm_status ssm_selective_scan_fwd_with_state(
+    ssm_handle handle, const void *u, const void *delta, const float *A,
+    const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, const float *initial_state,
+    void *y, float *last_state, int64_t batch, int64_t dim, int64_t dstate,
+    int64_t seqlen, ssm_dtype in_dtype, hipStream_t stream);
 
 /*
  * Workspace size in bytes needed by ssd_chunk_scan_fwd for these sizes
@@ -160,6 +184,30 @@ ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void *x, const void *dt,
                               int64_t headdim, int64_t dstate, int64_t ngroups,
                               int64_t chunk_size, ssm_dtype in_dtype,
                               hipStream_t stream);
+
+/*
+ * ssd_chunk_scan_fwd with an initial state: S[b,h,:,:] starts at
+ * initial_state[b,h,:,:] instead of zero (the v_0 term of the closed form in
+ * [EXPLAINED] eqs. (8)-(9), carried across chunks by the same jump formula
+ * as every chunk state).  Scanning a sequence in pieces, each call given the
+ * final_state of the previous one, gives the same y and final_state as one
+ * call (up to rounding; the carried state passes through bf16 between
+ * chunks as in ssd_chunk_scan_fwd).
+ *
+ *   initial_state : [batch, nheads, headdim, dstate] float32, nullable
+ *                   (NULL = zero, which is ssd_chunk_scan_fwd).  16-byte
+ *                   aligned.  It may be the same pointer as final_state (an
+ *                   in-place update); any other overlap with an output
+ *                   returns SSM_ERR_INVALID_ARG.
+ * Every other argument, layout, limit and error is as for ssd_chunk_scan_fwd.
+ */
+ssm_status ssd_chunk_scan_fwd_with_state(
+    ssm_handle handle, const void *x, const void *dt, const float *A,
+    const void *B, const void *C, const float *D, const float *dt_bias,
+    int dt_softplus, const float *initial_state, void *y, float *final_state,
+    void *workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
+    int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+    int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -26,8 +26,9 @@ SSM_F32, SSM_BF16 = 0, 1
 
 # Every symbol declared in include/ssm_scan.h.
 EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
-           "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssd_chunk_scan_workspace_size",
-           "ssd_chunk_scan_fwd")
+           "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
+           "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
+           "ssd_chunk_scan_fwd_with_state")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -66,12 +67,20 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_scan_fwd.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
             _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_scan_fwd_with_state.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_with_state.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_int
         lib.ssd_chunk_scan_workspace_size.argtypes = [
             _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
         lib.ssd_chunk_scan_fwd.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssd_chunk_scan_fwd_with_state.restype = ctypes.c_int
+        lib.ssd_chunk_scan_fwd_with_state.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
             ctypes.c_size_t, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         _lib = lib
         return lib
@@ -169,14 +178,39 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, 
     _check("ssm_selective_scan_fwd", st)
 
 
+def ssm_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                      initial_state, y, last_state, handle=None) -> None:
+    """ssm_selective_scan_fwd with an initial state [batch, dim, dstate]
+    float32 (None = zero; may be last_state itself for an in-place update)."""
+    for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
+                         ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
+                         ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
+                         ("y", y, False), ("last_state", last_state, True)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssm_selective_scan_fwd_with_state(
+        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(y),
+        _ptr(last_state), batch, dim, dstate, seqlen, _dtype_code(u), _stream_ptr(u.device))
+    _check("ssm_selective_scan_fwd_with_state", st)
+
+
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                       delta_softplus=True, return_last_state=True):
+                       delta_softplus=True, return_last_state=True, initial_state=None):
     """Allocating form: returns (y, last_state or None)."""
     import torch
     y = torch.empty_like(u)
     ls = (torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
                       device=u.device) if return_last_state else None)
-    ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, ls)
+    if initial_state is None:
+        ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, ls)
+    else:
+        ssm_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                          initial_state, y, ls)
     return y, ls
 
 
@@ -213,8 +247,30 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D, dt_bias, dt_softplus, y, final_state, 
     _check("ssd_chunk_scan_fwd", st)
 
 
+def ssd_chunk_scan_fwd_with_state(x, dt, A, B, C, D, dt_bias, dt_softplus, initial_state, y,
+                                  final_state, workspace, chunk_size, handle=None) -> None:
+    """ssd_chunk_scan_fwd with an initial state [batch, nheads, headdim,
+    dstate] float32 (None = zero; may be final_state itself)."""
+    for name, t, opt in (("x", x, False), ("dt", dt, False), ("A", A, False), ("B", B, False),
+                         ("C", C, False), ("D", D, True), ("dt_bias", dt_bias, True),
+                         ("initial_state", initial_state, True), ("y", y, False),
+                         ("final_state", final_state, True), ("workspace", workspace, False)):
+        _need_cuda_contig(name, t, opt)
+    batch, seqlen, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[2], B.shape[3]
+    dev = x.device.index if x.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssd_chunk_scan_fwd_with_state(
+        handle, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+        int(bool(dt_softplus)), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), batch, seqlen, nheads, headdim, dstate,
+        ngroups, chunk_size, _dtype_code(x), _stream_ptr(x.device))
+    _check("ssd_chunk_scan_fwd_with_state", st)
+
+
 def ssd_chunk_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, chunk_size=256,
-                   return_final_state=True) -> Tuple:
+                   return_final_state=True, initial_state=None) -> Tuple:
     """Allocating form: returns (y, final_state or None)."""
     import torch
     batch, seqlen, nheads, headdim = x.shape
@@ -226,5 +282,9 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, chunk
     y = torch.empty_like(x)
     fs = (torch.empty((batch, nheads, headdim, dstate), dtype=torch.float32, device=x.device)
           if return_final_state else None)
-    ssd_chunk_scan_fwd(x, dt, A, B, C, D, dt_bias, dt_softplus, y, fs, ws, chunk_size)
+    if initial_state is None:
+        ssd_chunk_scan_fwd(x, dt, A, B, C, D, dt_bias, dt_softplus, y, fs, ws, chunk_size)
+    else:
+        ssd_chunk_scan_fwd_with_state(x, dt, A, B, C, D, dt_bias, dt_softplus, initial_state, y,
+                                      fs, ws, chunk_size)
     return y, fs

@@ -151,12 +151,16 @@ ssm_status ssm_scan_destroy(ssm_handle handle) {
   return ok();
 }
 
-ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* delta,
-                                  const float* A, const void* B, const void* C, const float* D,
-                                  const void* z, const float* delta_bias, int delta_softplus,
-                                  void* y, float* last_state, int64_t batch, int64_t dim,
-                                  int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
-                                  hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* delta,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const void* z, const float* delta_bias, int delta_softplus,
+                               const float* initial_state, void* y, float* last_state,
+                               int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                               ssm_dtype in_dtype, hipStream_t stream) {
   // ---- sizes -------------------------------------------------------------
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
@@ -180,20 +184,25 @@ ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* 
   const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
   const uint64_t nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t state_bytes = (uint64_t)batch * dim * dstate * 4;
+  // initial_state may be last_state itself (each entry is read once, before
+  // the thread that reads it writes it); any other overlap with an output is
+  // rejected like for the other inputs.
+  const bool in_place = initial_state != nullptr && (const void*)initial_state == last_state;
   const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
                      {"A", A, (uint64_t)dim * dstate * 4}, {"B", B, nbc * es},
                      {"C", C, nbc * es},           {"D", D, (uint64_t)dim * 4},
-                     {"z", z, nrow * es},          {"delta_bias", delta_bias, (uint64_t)dim * 4}};
-  const Span out[] = {{"y", y, nrow * es},
-                      {"last_state", last_state, (uint64_t)batch * dim * dstate * 4}};
-  ssm_status st = check_spans(in, 8, out, 2);
+                     {"z", z, nrow * es},          {"delta_bias", delta_bias, (uint64_t)dim * 4},
+                     {"initial_state", in_place ? nullptr : initial_state, state_bytes}};
+  const Span out[] = {{"y", y, nrow * es}, {"last_state", last_state, state_bytes}};
+  ssm_status st = check_spans(in, 9, out, 2);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
 
   // ---- launch ------------------------------------------------------------
   ssm::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
-  p.delta_bias = delta_bias; p.y = y; p.last_state = last_state;
+  p.delta_bias = delta_bias; p.y = y; p.last_state = last_state; p.h0 = initial_state;
   p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate; p.seqlen = (int)seqlen;
   p.delta_softplus = delta_softplus ? 1 : 0;
   DeviceGuard guard(handle->device);
@@ -202,6 +211,34 @@ ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* 
   hipError_t e = ssm::launch_selective_scan(p, tile, in_dtype == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* delta,
+                                  const float* A, const void* B, const void* C, const float* D,
+                                  const void* z, const float* delta_bias, int delta_softplus,
+                                  void* y, float* last_state, int64_t batch, int64_t dim,
+                                  int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
+                                  hipStream_t stream) {
+  return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                             nullptr, y, last_state, batch, dim, dstate, seqlen, in_dtype,
+                             stream);
+}
+
+ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
+                                             const void* delta, const float* A, const void* B,
+                                             const void* C, const float* D, const void* z,
+                                             const float* delta_bias, int delta_softplus,
+                                             const float* initial_state, void* y,
+                                             float* last_state, int64_t batch, int64_t dim,
+                                             int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
+                                             hipStream_t stream) {
+  return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                             initial_state, y, last_state, batch, dim, dstate, seqlen, in_dtype,
+                             stream);
 }
 
 ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch, int64_t seqlen,
@@ -218,12 +255,16 @@ ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch, int64
   return ok();
 }
 
-ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void* x, const void* dt, const float* A,
-                              const void* B, const void* C, const float* D, const float* dt_bias,
-                              int dt_softplus, void* y, float* final_state, void* workspace,
-                              size_t workspace_bytes, int64_t batch, int64_t seqlen,
-                              int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                              int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ssm_status ssd_impl(ssm_handle handle, const void* x, const void* dt, const float* A,
+                    const void* B, const void* C, const float* D, const float* dt_bias,
+                    int dt_softplus, const float* initial_state, void* y, float* final_state,
+                    void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                    int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                    int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream) {
   ssm::SsdShape s;
   ssm_status st = ssm::ssd_validate_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                           chunk_size, &s, &g_last_error);
@@ -245,29 +286,62 @@ ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void* x, const void* dt, 
   const uint64_t es = 2;
   const uint64_t nx = (uint64_t)batch * seqlen * nheads * headdim;
   const uint64_t nbc = (uint64_t)batch * seqlen * ngroups * dstate;
+  const uint64_t state_bytes = (uint64_t)batch * nheads * headdim * dstate * 4;
+  // initial_state may be final_state itself (each entry is read once, by the
+  // thread that later writes it); any other overlap with an output is an error.
+  const bool in_place = initial_state != nullptr && (const void*)initial_state == final_state;
   const Span in[] = {{"x", x, nx * es},
                      {"dt", dt, (uint64_t)batch * seqlen * nheads * es},
                      {"A", A, (uint64_t)nheads * 4},
                      {"B", B, nbc * es},
                      {"C", C, nbc * es},
                      {"D", D, (uint64_t)nheads * 4},
-                     {"dt_bias", dt_bias, (uint64_t)nheads * 4}};
+                     {"dt_bias", dt_bias, (uint64_t)nheads * 4},
+                     {"initial_state", in_place ? nullptr : initial_state, state_bytes}};
   const Span out[] = {{"y", y, nx * es},
-                      {"final_state", final_state, (uint64_t)batch * nheads * headdim * dstate * 4},
+                      {"final_state", final_state, state_bytes},
                       {"workspace", workspace, need}};
-  st = check_spans(in, 7, out, 3);
+  st = check_spans(in, 8, out, 3);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
 
   ssm::SsdParams p;
   p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
   p.dt_softplus = dt_softplus ? 1 : 0; p.y = y; p.final_state = final_state;
-  p.workspace = workspace; p.shape = s;
+  p.initial_state = initial_state; p.workspace = workspace; p.shape = s;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
   hipError_t e = ssm::launch_ssd(p, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void* x, const void* dt, const float* A,
+                              const void* B, const void* C, const float* D, const float* dt_bias,
+                              int dt_softplus, void* y, float* final_state, void* workspace,
+                              size_t workspace_bytes, int64_t batch, int64_t seqlen,
+                              int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                              int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream) {
+  return ssd_impl(handle, x, dt, A, B, C, D, dt_bias, dt_softplus, nullptr, y, final_state,
+                  workspace, workspace_bytes, batch, seqlen, nheads, headdim, dstate, ngroups,
+                  chunk_size, in_dtype, stream);
+}
+
+ssm_status ssd_chunk_scan_fwd_with_state(ssm_handle handle, const void* x, const void* dt,
+                                         const float* A, const void* B, const void* C,
+                                         const float* D, const float* dt_bias, int dt_softplus,
+                                         const float* initial_state, void* y, float* final_state,
+                                         void* workspace, size_t workspace_bytes, int64_t batch,
+                                         int64_t seqlen, int64_t nheads, int64_t headdim,
+                                         int64_t dstate, int64_t ngroups, int64_t chunk_size,
+                                         ssm_dtype in_dtype, hipStream_t stream) {
+  return ssd_impl(handle, x, dt, A, B, C, D, dt_bias, dt_softplus, initial_state, y,
+                  final_state, workspace, workspace_bytes, batch, seqlen, nheads, headdim, dstate,
+                  ngroups, chunk_size, in_dtype, stream);
 }
 
 }  // extern "C"

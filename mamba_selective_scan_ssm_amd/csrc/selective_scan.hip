@@ -248,9 +248,13 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
   const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
 
+  // State: the initial state v_0 of [EXPLAINED] eqs. (8)-(9) when given.
   float h[NG];
 #pragma unroll
-  for (int k = 0; k < NG; ++k) h[k] = 0.0f;
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    h[k] = (prm.h0 && row_ok && n < N) ? prm.h0[((int64_t)b * prm.dim + d) * N + n] : 0.0f;
+  }
 
   // Raw chunk data, loaded one chunk ahead of its use.
   RawSeg<In, TS> ru, rd, rz;
@@ -468,9 +472,14 @@ selective_scan_split_kernel(ScanParams prm) {
   float h[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) h[k] = 0.0f;
+  // Running carry per (state, row) pair this thread folds: starts at the
+  // initial state v_0 of [EXPLAINED] eqs. (8)-(9) when given.
   float carry[PAIRS];
 #pragma unroll
-  for (int k = 0; k < PAIRS; ++k) carry[k] = 0.0f;
+  for (int q = 0; q < PAIRS; ++q) {
+    const int n = wv + q * (G * W);
+    carry[q] = (prm.h0 && row_ok && n < N) ? prm.h0[((int64_t)b * prm.dim + d) * N + n] : 0.0f;
+  }
 
   // Raw chunk data, loaded one chunk ahead of its use.
   RawSeg<In, TG> ru, rd, rz;

@@ -19,6 +19,7 @@ struct ScanParams {
   const float* delta_bias;  // nullable
   void* y;
   float* last_state;        // nullable
+  const float* h0;          // initial state [batch, dim, dstate], nullable (zero)
   int batch;
   int dim;
   int dstate;

@@ -93,6 +93,7 @@ struct SsdArgs {
   const float* dt_bias;
   uint16_t* y;
   float* final_state;
+  const float* init;  // initial state [b, h, P, N] or null (zero)
   uint16_t* states;
   float* decay;
   int dt_softplus;
@@ -410,9 +411,17 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
   const int64_t PN = (int64_t)a.headdim * a.dstate;
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (e0 >= PN) return;
+  // the state entering the sequence: the given initial state, else zero
   float S[8];
+  if (a.init) {
+    const float4* s0 = reinterpret_cast<const float4*>(a.init + (int64_t)bh * PN + e0);
+    const float4 lo = s0[0], hi = s0[1];
+    S[0] = lo.x; S[1] = lo.y; S[2] = lo.z; S[3] = lo.w;
+    S[4] = hi.x; S[5] = hi.y; S[6] = hi.z; S[7] = hi.w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) S[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) S[i] = 0.0f;
+  }
   for (int c = 0; c < a.nchunks; ++c) {
     uint16_t* ptr = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * PN + e0;
     const uint4 raw = *reinterpret_cast<const uint4*>(ptr);
@@ -522,7 +531,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
       const int task = tid + k * NTHR;
-      sr[k] = load16(sin + 8 * min(task, P * N / 8 - 1));  // unused for chunk 0
+      sr[k] = load16(sin + 8 * min(task, P * N / 8 - 1));  // unused for chunk 0 from zero
     }
   };
   // B[s][kb0 .. kb0+KB) rows, 16 bytes per task.
@@ -656,8 +665,8 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) yacc[t][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // Y^T[p][l] = exp(cs_l) sum_n S_in[p][n] C[l][n]   (S_in = 0 for chunk 0)
-    if (c > 0 && active) {
+    // Y^T[p][l] = exp(cs_l) sum_n S_in[p][n] C[l][n]   (chunk 0: the initial state, or 0)
+    if ((c > 0 || a.init) && active) {
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
 #pragma unroll
@@ -812,6 +821,7 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.dt_bias = p.dt_bias;
   a.y = static_cast<uint16_t*>(p.y);
   a.final_state = p.final_state;
+  a.init = p.initial_state;
   a.states = reinterpret_cast<uint16_t*>(static_cast<char*>(p.workspace) + lay.states_off);
   a.decay = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.decay_off);
   a.dt_softplus = p.dt_softplus;

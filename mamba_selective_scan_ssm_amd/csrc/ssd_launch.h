@@ -26,6 +26,7 @@ struct SsdParams {
   int dt_softplus;
   void* y;
   float* final_state;    // nullable
+  const float* initial_state;  // [b, h, P, N], nullable (zero)
   void* workspace;
   SsdShape shape;
 };

@@ -105,3 +105,41 @@ def test_create_rejects_bad_arguments():
     lib = ssm.load_library()
     assert lib.ssm_scan_create(None, 0) == ssm.SSM_ERR_INVALID_ARG
     assert lib.ssm_scan_destroy(None) == ssm.SSM_OK
+
+
+def scan_h0(h0, ls, y=P[5], handle=None):
+    lib = ssm.load_library()
+    st = lib.ssm_selective_scan_fwd_with_state(handle, P[0], P[1], P[2], P[3], P[4], None, None,
+                                               None, 1, h0, y, ls, 2, 4, 4, 8, ssm.SSM_F32, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_initial_state_rules():
+    # in place (initial_state == last_state) passes every check up to the handle
+    st, msg = scan_h0(P[9], P[9])
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg
+    st, msg = scan_h0(P[9], P[10])
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg
+    st, msg = scan_h0(P[9] + 4, P[10])       # misaligned
+    assert st == ssm.SSM_ERR_INVALID_ARG and "initial_state" in msg and "aligned" in msg
+    st, msg = scan_h0(P[9] + 16, P[9])       # partial overlap with last_state
+    assert st == ssm.SSM_ERR_INVALID_ARG and "initial_state" in msg
+    st, msg = scan_h0(P[5], P[10])           # overlaps y
+    assert st == ssm.SSM_ERR_INVALID_ARG and "initial_state" in msg
+
+
+def ssd_h0(init, fs):
+    lib = ssm.load_library()
+    st = lib.ssd_chunk_scan_fwd_with_state(None, P[0], P[1], P[2], P[3], P[4], None, None, 1,
+                                           init, P[5], fs, P[6], 1 << 30, 2, 64, 4, 64, 32, 1, 64,
+                                           ssm.SSM_BF16, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_ssd_initial_state_rules():
+    st, msg = ssd_h0(P[9], P[9])             # in place
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg
+    st, msg = ssd_h0(P[9] + 32, P[9])        # partial overlap with final_state
+    assert st == ssm.SSM_ERR_INVALID_ARG and "initial_state" in msg
+    st, msg = ssd_h0(P[9] + 8, P[10])        # misaligned
+    assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg

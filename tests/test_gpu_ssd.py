@@ -100,3 +100,56 @@ def test_ssd_repeatable(lib):
     y1, f1 = run(lib, s, 256)
     y2, f2 = run(lib, s, 256)
     assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
+
+
+@pytest.mark.parametrize("case", [(2, 300, 4, 64, 64, 2, 128), (1, 512, 6, 64, 128, 1, 256),
+                                  (2, 200, 2, 32, 32, 1, 64)])
+def test_ssd_initial_state(lib, case):
+    """S starts at a given state; every y and final_state entry."""
+    b, L, h, p, n, g, q = case
+    print(f"case ssd initial state {case}", flush=True)
+    s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=80 + L, batch=b, seqlen=L, nheads=h,
+                         headdim=p, dstate=n, ngroups=g)
+    init = np.random.default_rng(L).standard_normal((b, h, p, n)).astype(np.float32)
+    dev = "cuda"
+    t = {k: (None if v is None else
+             synth.to_device(v, "bf16" if k in ("x", "dt", "B", "C") else "f32", dev))
+         for k, v in s.items()}
+    y, fs = lib.ssd_chunk_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"],
+                               dt_bias=t["dt_bias"], chunk_size=q,
+                               initial_state=torch.from_numpy(init).to(dev))
+    torch.cuda.synchronize()
+    ry, rf = oracle.ssd_scan(**s, initial_state=init.astype(np.float64))
+    check("y", synth.to_host_f64(y), ry)
+    check("final_state", synth.to_host_f64(fs), rf)
+
+
+@pytest.mark.parametrize("k", [256, 300])
+def test_ssd_scan_in_pieces(lib, k):
+    """Two calls, the second from the first's final_state (updated in place),
+    match the oracle's single scan; cut at a chunk boundary and inside a chunk."""
+    b, L, h, p, n, g, q = 1, 600, 4, 64, 128, 1, 256
+    print(f"case ssd pieces k={k}", flush=True)
+    s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=90, batch=b, seqlen=L, nheads=h,
+                         headdim=p, dstate=n, ngroups=g)
+    dev = "cuda"
+    t = {kk: (None if v is None else
+              synth.to_device(v, "bf16" if kk in ("x", "dt", "B", "C") else "f32", dev))
+         for kk, v in s.items()}
+    state = torch.empty((b, h, p, n), dtype=torch.float32, device=dev)
+    ys = []
+    for i, (t0, t1) in enumerate(((0, k), (k, L))):
+        part = {kk: (v[:, t0:t1].contiguous() if kk in ("x", "dt", "B", "C") else v)
+                for kk, v in t.items()}
+        yp = torch.empty_like(part["x"])
+        nb = lib.ssd_chunk_scan_workspace_size(b, t1 - t0, h, p, n, g, q)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        lib.ssd_chunk_scan_fwd_with_state(part["x"], part["dt"], part["A"], part["B"], part["C"],
+                                          part["D"], part["dt_bias"], True,
+                                          state if i else None, yp, state, ws, q)
+        ys.append(yp)
+    torch.cuda.synchronize()
+    y = torch.cat(ys, dim=1)
+    ry, rf = oracle.ssd_scan(**s)
+    check("y", synth.to_host_f64(y), ry)
+    check("final_state", synth.to_host_f64(state), rf)
