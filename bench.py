@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--ssd", action="store_true", help="also time the Mamba-2 chunked scan")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time one decode step (state update) at the same batch/dim/dstate")
     return ap.parse_args()
 
 
@@ -197,10 +199,57 @@ def main():
     }
     if args.ssd:
         out["ssd"] = bench_ssd(args, torch, ssm, synth)
+    if args.decode:
+        out["decode"] = bench_decode(args, torch, ssm, synth, cfg)
     if not args.no_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline(x, cfg, oracle)
     print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, torch, ssm, synth, cfg):
+    """One ssm_selective_state_update per step over batch x dim rows (state
+    read and written in place)."""
+    x = synth.mamba1_inputs(cfg, seed=7, seqlen=1)
+    b, d, _ = x["u"].shape
+    n = x["A"].shape[1]
+    dev = torch.device("cuda:0")
+    t = {k: synth.to_device(v, cfg.dtype if k in ("u", "delta", "z", "B", "C") else "f32", dev)
+         for k, v in x.items()}
+    sq = {k: (t[k].reshape(b, -1) if k in ("u", "delta", "z", "B", "C") else t[k]) for k in t}
+    state = torch.zeros((b, d, n), dtype=torch.float32, device=dev)
+    y = torch.empty_like(sq["u"])
+    handle = ssm.get_handle(0)
+
+    def step():
+        ssm.ssm_selective_state_update(state, sq["u"], sq["delta"], sq["A"], sq["B"], sq["C"],
+                                       sq["D"], sq["z"], sq["delta_bias"], True, y, handle=handle)
+
+    # A step is a few microseconds of GPU work, less than a Python call costs,
+    # so the steps are captured once in a HIP graph and replayed.
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    es = 2 if cfg.dtype == "bf16" else 4
+    nbytes = 8 * b * d * n + 4 * b * d * es + 2 * b * n * es + 4 * d * n + 8 * d
+    return {"workload": f"decode step: batch {b}, dim {d}, dstate {n}, {cfg.dtype}, fp32 state "
+                        "updated in place", "timing": f"{args.steps} steps in one HIP graph",
+            "us_per_step": round(us, 3),
+            "tokens_per_s": round(b / (us * 1e-6), 1),
+            "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
 
 
 def bench_ssd(args, torch, ssm, synth):

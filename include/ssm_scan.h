@@ -138,6 +138,37 @@ ssm_status ssm_selective_scan_fwd_with_state(
     int64_t seqlen, ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * One decode step of the Mamba-1 recurrence ([SPEC] Stage 1 items 3-4;
+ * [EXPLAINED] eqs. (5)-(7); [BLELLOCH] section 1: the sequential form for
+ * online inference).  For every row (b, d), with the state updated in place:
+ *
+ *   delta   = delta[b,d] + delta_bias[d];  softplus if delta_softplus != 0
+ *   state[b,d,n] = exp(delta * A[d,n]) * state[b,d,n] + delta * B[b,n] * u[b,d]
+ *   y[b,d]  = (sum_n C[b,n] * state[b,d,n] + D[d] * u[b,d]) * silu(z[b,d])
+ *
+ * This is ssm_selective_scan_fwd_with_state for seqlen = 1 with the state
+ * updated in place (same result), with a kernel sized for one step.
+ *
+ * Layouts (row-major):
+ *   u, delta, z, y : [batch, dim]       element type in_dtype
+ *   B, C           : [batch, dstate]    element type in_dtype
+ *   A              : [dim, dstate]      float32
+ *   D, delta_bias  : [dim]              float32
+ *   state          : [batch, dim, dstate] float32, read and written
+ * Nullable: D, z, delta_bias.  Pointers 16-byte aligned; state and y must
+ * not overlap each other or any input (SSM_ERR_INVALID_ARG).
+ * Limits: batch, dim >= 1; 1 <= dstate <= 64; batch*dim <= 2^40.
+ */
+ssm_status ssm_selective_state_update(ssm_handle handle, float *state,
+                                      const void *u, const void *delta,
+                                      const float *A, const void *B,
+                                      const void *C, const float *D,
+                                      const void *z, const float *delta_bias,
+                                      int delta_softplus, void *y, int64_t batch,
+                                      int64_t dim, int64_t dstate,
+                                      ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * Workspace size in bytes needed by ssd_chunk_scan_fwd for these sizes
  * (the caller allocates it, so the library never allocates device memory).
  * Returns SSM_ERR_INVALID_ARG / SSM_ERR_UNSUPPORTED for sizes that

@@ -27,6 +27,7 @@ SSM_F32, SSM_BF16 = 0, 1
 # Every symbol declared in include/ssm_scan.h.
 EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
+           "ssm_selective_state_update",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
            "ssd_chunk_scan_fwd_with_state")
 
@@ -71,6 +72,10 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_scan_fwd_with_state.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
             _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_state_update.restype = ctypes.c_int
+        lib.ssm_selective_state_update.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+            _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_int
         lib.ssd_chunk_scan_workspace_size.argtypes = [
             _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -212,6 +217,26 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         ssm_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                                           initial_state, y, ls)
     return y, ls
+
+
+def ssm_selective_state_update(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
+                               handle=None) -> None:
+    """One decode step, state [batch, dim, dstate] float32 updated in place;
+    u, delta, z, y: [batch, dim]; B, C: [batch, dstate]."""
+    for name, t, opt in (("state", state, False), ("u", u, False), ("delta", delta, False),
+                         ("A", A, False), ("B", B, False), ("C", C, False), ("D", D, True),
+                         ("z", z, True), ("delta_bias", delta_bias, True), ("y", y, False)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim = u.shape
+    dstate = A.shape[1]
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssm_selective_state_update(
+        handle, _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), batch, dim, dstate,
+        _dtype_code(u), _stream_ptr(u.device))
+    _check("ssm_selective_state_update", st)
 
 
 def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,

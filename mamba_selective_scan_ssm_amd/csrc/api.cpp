@@ -241,6 +241,51 @@ ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
                              stream);
 }
 
+ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const void* u,
+                                      const void* delta, const float* A, const void* B,
+                                      const void* C, const float* D, const void* z,
+                                      const float* delta_bias, int delta_softplus, void* y,
+                                      int64_t batch, int64_t dim, int64_t dstate,
+                                      ssm_dtype in_dtype, hipStream_t stream) {
+  if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
+  if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
+  if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
+  if (dim > INT32_MAX || batch > INT32_MAX || batch * dim > (int64_t(1) << 40))
+    return fail(SSM_ERR_UNSUPPORTED, "batch*dim too large");
+  if (!state) return fail(SSM_ERR_INVALID_ARG, "state is NULL");
+  if (!u) return fail(SSM_ERR_INVALID_ARG, "u is NULL");
+  if (!delta) return fail(SSM_ERR_INVALID_ARG, "delta is NULL");
+  if (!A) return fail(SSM_ERR_INVALID_ARG, "A is NULL");
+  if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
+  if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
+  if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nrow = (uint64_t)batch * dim;
+  const uint64_t nbc = (uint64_t)batch * dstate;
+  const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
+                     {"A", A, (uint64_t)dim * dstate * 4}, {"B", B, nbc * es},
+                     {"C", C, nbc * es},           {"D", D, (uint64_t)dim * 4},
+                     {"z", z, nrow * es},          {"delta_bias", delta_bias, (uint64_t)dim * 4}};
+  const Span out[] = {{"y", y, nrow * es}, {"state", state, nrow * dstate * 4}};
+  ssm_status st = check_spans(in, 8, out, 2);
+  if (st != SSM_OK) return st;
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+
+  ssm::StepParams p;
+  p.state = state; p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
+  p.delta_bias = delta_bias; p.y = y;
+  p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate;
+  p.delta_softplus = delta_softplus ? 1 : 0;
+  DeviceGuard guard(handle->device);
+  if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
+  hipError_t e = ssm::launch_state_update(p, in_dtype == SSM_BF16, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch, int64_t seqlen,
                                          int64_t nheads, int64_t headdim, int64_t dstate,
                                          int64_t ngroups, int64_t chunk_size, size_t* bytes) {

@@ -42,4 +42,24 @@ struct ScanTile {
 hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
                                  hipStream_t stream);
 
+// One decode step (state_update.hip).
+struct StepParams {
+  float* state;             // [batch, dim, dstate], read and written
+  const void* u;            // [batch, dim]
+  const void* delta;        // [batch, dim]
+  const float* A;           // [dim, dstate]
+  const void* B;            // [batch, dstate]
+  const void* C;            // [batch, dstate]
+  const float* D;           // nullable
+  const void* z;            // nullable
+  const float* delta_bias;  // nullable
+  void* y;                  // [batch, dim]
+  int batch;
+  int dim;
+  int dstate;
+  int delta_softplus;
+};
+
+hipError_t launch_state_update(const StepParams& p, bool bf16, hipStream_t stream);
+
 }  // namespace ssm

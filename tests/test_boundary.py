@@ -143,3 +143,24 @@ def test_ssd_initial_state_rules():
     assert st == ssm.SSM_ERR_INVALID_ARG and "initial_state" in msg
     st, msg = ssd_h0(P[9] + 8, P[10])        # misaligned
     assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg
+
+
+def step(state=P[9], u=P[0], delta=P[1], A=P[2], B=P[3], C=P[4], y=P[5], batch=2, dim=4,
+         dstate=16, dtype=ssm.SSM_F32):
+    lib = ssm.load_library()
+    st = lib.ssm_selective_state_update(None, state, u, delta, A, B, C, None, None, None, 1, y,
+                                        batch, dim, dstate, dtype, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_state_update_checks():
+    st, msg = step()
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg
+    assert step(batch=0)[0] == ssm.SSM_ERR_INVALID_ARG
+    assert step(dstate=65)[0] == ssm.SSM_ERR_UNSUPPORTED
+    st, msg = step(state=None)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "state is NULL" in msg
+    st, msg = step(state=P[5])               # state aliases y
+    assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg
+    st, msg = step(state=P[9] + 4)           # misaligned
+    assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg

@@ -241,3 +241,51 @@ def test_scan_in_pieces(lib, k):
     ry, rs = oracle.selective_scan(**x)
     check("y", synth.to_host_f64(y).reshape(b * d, L), ry, "bf16")
     check("last_state", synth.to_host_f64(state).reshape(b * d, -1), rs, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# Decode step (ssm_selective_state_update) = one step of the scan from a state
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,dtype", [((8, 4096, 16), "bf16"), ((3, 100, 5), "f32"),
+                                         ((2, 33, 64), "f32"), ((4, 7, 1), "bf16"),
+                                         ((2, 50, 8), "f32")])
+def test_state_update_matches_one_step_scan(lib, shape, dtype):
+    b, d, n = shape
+    print(f"case decode step {shape} {dtype}", flush=True)
+    x = make_inputs(110 + n, b, d, n, 1, dtype)
+    h0 = np.random.default_rng(n + 1).standard_normal((b, d, n)).astype(np.float32)
+    dev = "cuda"
+    t = {k: (None if v is None else synth.to_device(v, dtype if k in ("u", "delta", "z", "B", "C")
+                                                     else "f32", dev))
+         for k, v in x.items()}
+    sq = {k: (t[k].reshape(t[k].shape[0], t[k].shape[1]) if k in ("u", "delta", "z", "B", "C")
+              else t[k]) for k in t}
+    state = torch.from_numpy(h0).to(dev)
+    y = torch.empty_like(sq["u"])
+    lib.ssm_selective_state_update(state, sq["u"], sq["delta"], sq["A"], sq["B"], sq["C"], sq["D"],
+                                   sq["z"], sq["delta_bias"], True, y)
+    torch.cuda.synchronize()
+    ry, rs = oracle.selective_scan(**x, h0=h0.astype(np.float64))
+    check("y", synth.to_host_f64(y).reshape(b * d, 1), ry, dtype, f32_rel=True)
+    check("state", synth.to_host_f64(state).reshape(b * d, n), rs, dtype, f32_rel=True)
+
+
+def test_decode_loop_matches_scan(lib):
+    """Twenty decode steps from a zero state give the scan's y and state."""
+    b, d, n, L = 2, 256, 16, 20
+    x = make_inputs(120, b, d, n, L, "f32")
+    dev = "cuda"
+    t = {k: (None if v is None else synth.to_device(v, "f32", dev)) for k, v in x.items()}
+    state = torch.zeros((b, d, n), dtype=torch.float32, device=dev)
+    ys = []
+    for s in range(L):
+        col = {k: t[k][:, :, s].contiguous() for k in ("u", "delta", "z", "B", "C")}
+        y = torch.empty_like(col["u"])
+        lib.ssm_selective_state_update(state, col["u"], col["delta"], t["A"], col["B"], col["C"],
+                                       t["D"], col["z"], t["delta_bias"], True, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    ry, rs = oracle.selective_scan(**x)
+    check("y", synth.to_host_f64(torch.stack(ys, dim=2)).reshape(b * d, L), ry, "f32", f32_rel=True)
+    check("state", synth.to_host_f64(state).reshape(b * d, n), rs, "f32", f32_rel=True)
