@@ -57,6 +57,11 @@ def _load():
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
+    lib.oracle_selective_scan_bwd_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
+        _f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
     lib.oracle_ssd_h0_f64.restype = ctypes.c_int
     lib.oracle_ssd_h0_f64.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
@@ -141,6 +146,47 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise RuntimeError(f"oracle_selective_scan_f64 failed with code {rc}")
     return y, st
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, dlast=None, nthreads=None):
+    """Gradients of selective_scan (y, last_state) in fp64 by reverse-mode
+    differentiation of the sequential loop, for upstream gradients dy
+    [batch, dim, seqlen] and dlast [batch, dim, dstate] (None = zero).
+
+    Returns a dict: du, ddelta, dz (None without z) [batch, dim, seqlen];
+    dA [dim, dstate]; dB, dC [batch, dstate, seqlen]; dD, ddelta_bias [dim];
+    dh0 [batch, dim, dstate].
+    """
+    lib = _load()
+    u = _f32(u)
+    batch, dim, seqlen = u.shape
+    dstate = np.asarray(A).shape[1]
+    delta = _f32(delta, (batch, dim, seqlen))
+    A = _f32(A, (dim, dstate))
+    B = _f32(B, (batch, dstate, seqlen))
+    C = _f32(C, (batch, dstate, seqlen))
+    D = _f32(D, (dim,))
+    z = _f32(z, (batch, dim, seqlen))
+    delta_bias = _f32(delta_bias, (dim,))
+    h0 = _f64(h0, (batch, dim, dstate))
+    dy = _f64(dy, (batch, dim, seqlen))
+    dlast = _f64(dlast, (batch, dim, dstate))
+    out = {k: np.empty(shape, np.float64) for k, shape in (
+        ("du", (batch, dim, seqlen)), ("ddelta", (batch, dim, seqlen)),
+        ("dA", (dim, dstate)), ("dB", (batch, dstate, seqlen)), ("dC", (batch, dstate, seqlen)),
+        ("dD", (dim,)), ("ddelta_bias", (dim,)), ("dh0", (batch, dim, dstate)))}
+    out["dz"] = np.empty((batch, dim, seqlen), np.float64) if z is not None else None
+    p64 = lambda a: None if a is None else a.ctypes.data_as(_f64p)
+    rc = lib.oracle_selective_scan_bwd_f64(
+        _p32(u), _p32(delta), _p32(A), _p32(B), _p32(C), _p32(D), _p32(z), _p32(delta_bias),
+        int(bool(delta_softplus)), p64(h0), p64(dy), p64(dlast), batch, dim, dstate, seqlen,
+        p64(out["du"]), p64(out["ddelta"]), p64(out["dA"]), p64(out["dB"]), p64(out["dC"]),
+        p64(out["dD"]), p64(out["dz"]), p64(out["ddelta_bias"]), p64(out["dh0"]),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_selective_scan_bwd_f64 failed with code {rc}")
+    return out
 
 
 def ssd_scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,

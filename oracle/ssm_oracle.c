@@ -185,6 +185,189 @@ int oracle_selective_scan_f64(const float *u, const float *delta,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Mamba-1 backward: gradients of the forward above with respect to every    */
+/* input, by reverse-mode differentiation of the sequential loop.            */
+/*                                                                          */
+/* Forward (per row, 0-based t), as above:                                  */
+/*   s_t = delta[t] + bias;  dt_t = softplus(s_t) or s_t                     */
+/*   a_t[n] = exp(dt_t A[n]);  h_t[n] = a_t[n] h_{t-1}[n] + dt_t B_t[n] u_t  */
+/*   yh_t = sum_n C_t[n] h_t[n] + D u_t;  y_t = yh_t silu(z_t) or yh_t       */
+/* Backward, with g_t = dy_t and lam[n] = dL/dh_t[n] carried backwards:      */
+/*   dyh_t = g_t silu(z_t);  dz_t = g_t yh_t silu'(z_t)                      */
+/*   lam[n] = C_t[n] dyh_t + a_{t+1}[n] lam[n]     (lam = dlast at t = L)    */
+/*   dC_t[n] += dyh_t h_t[n];  dD += dyh_t u_t;  du_t = dyh_t D + ...        */
+/*   from h_t = a h_{t-1} + dt B u:                                          */
+/*     ddt_t += sum_n lam[n] (a_t[n] A[n] h_{t-1}[n] + B_t[n] u_t)           */
+/*     dA[n] += lam[n] a_t[n] dt_t h_{t-1}[n]                                 */
+/*     dB_t[n] += lam[n] dt_t u_t;  du_t += sum_n lam[n] dt_t B_t[n]         */
+/*   ds_t = ddt_t sigmoid(s_t) (softplus) or ddt_t;  ddelta_t = ds_t;        */
+/*   dbias += ds_t;  dh0[n] = a_0[n] lam[n] after t = 0.                      */
+/* silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).                           */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const float *u, *delta, *A, *B, *C, *D, *z, *delta_bias;
+  const double *h0, *dy, *dlast;
+  int delta_softplus;
+  int64_t batch, dim, dstate, seqlen;
+  /* per-row outputs (disjoint between workers) */
+  double *du, *ddelta, *dz, *dh0;
+  /* this worker's private accumulators for the shared-parameter gradients */
+  double *dA, *dB, *dC, *dD, *dbias;
+  int64_t row_begin, row_end;
+} mamba1_bwd_job;
+
+static double sigmoid_d(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void *mamba1_bwd_worker(void *arg) {
+  const mamba1_bwd_job *j = (const mamba1_bwd_job *)arg;
+  const int64_t N = j->dstate, L = j->seqlen;
+  double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N)); /* h_{-1..L-1} */
+  double *dts = (double *)malloc(sizeof(double) * (size_t)L);
+  double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !dts || !lam) {
+    free(hs); free(dts); free(lam);
+    return (void *)1;
+  }
+  for (int64_t row = j->row_begin; row < j->row_end; ++row) {
+    const int64_t b = row / j->dim, d = row % j->dim;
+    const float *u = j->u + row * L, *dl = j->delta + row * L;
+    const float *z = j->z ? j->z + row * L : NULL;
+    const float *A = j->A + d * N;
+    const float *B = j->B + b * N * L, *C = j->C + b * N * L;
+    const double Dd = j->D ? (double)j->D[d] : 0.0;
+    const double bias = j->delta_bias ? (double)j->delta_bias[d] : 0.0;
+    const double *dy = j->dy + row * L;
+    /* forward, keeping every state: hs[(t+1)*N + n] = h_t[n], hs[n] = h_{-1} */
+    for (int64_t n = 0; n < N; ++n) hs[n] = j->h0 ? j->h0[row * N + n] : 0.0;
+    for (int64_t t = 0; t < L; ++t) {
+      double dt = (double)dl[t] + bias;
+      if (j->delta_softplus) dt = softplus_d(dt);
+      dts[t] = dt;
+      for (int64_t n = 0; n < N; ++n) {
+        const double a = exp(dt * (double)A[n]);
+        hs[(t + 1) * N + n] = a * hs[t * N + n] + dt * (double)B[n * L + t] * (double)u[t];
+      }
+    }
+    /* backward */
+    for (int64_t n = 0; n < N; ++n) lam[n] = j->dlast ? j->dlast[row * N + n] : 0.0;
+    for (int64_t t = L - 1; t >= 0; --t) {
+      const double dt = dts[t], ut = (double)u[t];
+      const double *h = hs + (t + 1) * N, *hp = hs + t * N;
+      double yh = Dd * ut;
+      for (int64_t n = 0; n < N; ++n) yh += (double)C[n * L + t] * h[n];
+      double dyh = dy[t];
+      if (z) {
+        const double zt = (double)z[t], sg = sigmoid_d(zt);
+        dyh = dy[t] * zt * sg;
+        j->dz[row * L + t] = dy[t] * yh * sg * (1.0 + zt * (1.0 - sg));
+      }
+      j->dD[d] += dyh * ut;
+      double du = dyh * Dd, ddt = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        /* lam currently holds a_{t+1} lam_{t+1} (or dlast); add the readout */
+        lam[n] += (double)C[n * L + t] * dyh;
+        j->dC[(b * N + n) * L + t] += dyh * h[n];
+        const double a = exp(dt * (double)A[n]);
+        const double bt = (double)B[n * L + t];
+        ddt += lam[n] * (a * (double)A[n] * hp[n] + bt * ut);
+        j->dA[d * N + n] += lam[n] * a * dt * hp[n];
+        j->dB[(b * N + n) * L + t] += lam[n] * dt * ut;
+        du += lam[n] * dt * bt;
+        lam[n] *= a; /* now dL/dh_{t-1} */
+      }
+      double ds = ddt;
+      if (j->delta_softplus) ds *= sigmoid_d((double)dl[t] + bias);
+      j->ddelta[row * L + t] = ds;
+      j->dbias[d] += ds;
+      j->du[row * L + t] = du;
+    }
+    if (j->dh0)
+      for (int64_t n = 0; n < N; ++n) j->dh0[row * N + n] = lam[n];
+  }
+  free(hs); free(dts); free(lam);
+  return NULL;
+}
+
+/* Gradients of oracle_selective_scan_h0_f64's outputs (y, last_state) with
+ * upstream gradients dy [batch, dim, seqlen] and dlast [batch, dim, dstate]
+ * (nullable = zero).  Outputs (all written, float64): du, ddelta, dz (dz only
+ * when z is given, else may be NULL) [batch, dim, seqlen]; dA [dim, dstate];
+ * dB, dC [batch, dstate, seqlen]; dD, ddelta_bias [dim]; dh0 [batch, dim,
+ * dstate] (nullable).  Shared-parameter gradients are summed per worker and
+ * then over workers in a fixed order.  Returns 0, -1 (arguments) or -2. */
+int oracle_selective_scan_bwd_f64(const float *u, const float *delta,
+                                  const float *A, const float *B, const float *C,
+                                  const float *D, const float *z,
+                                  const float *delta_bias, int delta_softplus,
+                                  const double *h0, const double *dy,
+                                  const double *dlast, int64_t batch,
+                                  int64_t dim, int64_t dstate, int64_t seqlen,
+                                  double *du, double *ddelta, double *dA,
+                                  double *dB, double *dC, double *dD,
+                                  double *dz, double *ddelta_bias, double *dh0,
+                                  int nthreads) {
+  if (!u || !delta || !A || !B || !C || !dy) return -1;
+  if (!du || !ddelta || !dA || !dB || !dC || !dD || !ddelta_bias) return -1;
+  if (z && !dz) return -1;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return -1;
+  const int64_t rows = batch * dim, N = dstate, L = seqlen;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 64) nthreads = 64;
+  if ((int64_t)nthreads > rows) nthreads = (int)rows;
+  const size_t nA = (size_t)(dim * N), nBC = (size_t)(batch * N * L), nd = (size_t)dim;
+  const size_t per = nA + 2 * nBC + 2 * nd;
+  double *acc = (double *)calloc((size_t)nthreads * per, sizeof(double));
+  if (!acc) return -2;
+  mamba1_bwd_job jobs[64];
+  pthread_t tids[64];
+  int started[64];
+  int rc = 0;
+  for (int w = 0; w < nthreads; ++w) {
+    mamba1_bwd_job *j = &jobs[w];
+    double *base = acc + (size_t)w * per;
+    j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D; j->z = z;
+    j->delta_bias = delta_bias; j->h0 = h0; j->dy = dy; j->dlast = dlast;
+    j->delta_softplus = delta_softplus;
+    j->batch = batch; j->dim = dim; j->dstate = dstate; j->seqlen = seqlen;
+    j->du = du; j->ddelta = ddelta; j->dz = dz; j->dh0 = dh0;
+    j->dA = base; j->dB = base + nA; j->dC = base + nA + nBC;
+    j->dD = base + nA + 2 * nBC; j->dbias = base + nA + 2 * nBC + nd;
+    j->row_begin = rows * w / nthreads;
+    j->row_end = rows * (w + 1) / nthreads;
+    started[w] = 0;
+  }
+  for (int w = 1; w < nthreads; ++w)
+    started[w] = pthread_create(&tids[w], NULL, mamba1_bwd_worker, &jobs[w]) == 0;
+  for (int w = 1; w < nthreads; ++w)
+    if (!started[w]) rc = -2;
+  if (rc == 0 && mamba1_bwd_worker(&jobs[0]) != NULL) rc = -2;
+  for (int w = 1; w < nthreads; ++w) {
+    if (!started[w]) continue;
+    void *ret = NULL;
+    pthread_join(tids[w], &ret);
+    if (ret != NULL) rc = -2;
+  }
+  if (rc == 0) {
+    memset(dA, 0, nA * sizeof(double));
+    memset(dB, 0, nBC * sizeof(double));
+    memset(dC, 0, nBC * sizeof(double));
+    memset(dD, 0, nd * sizeof(double));
+    memset(ddelta_bias, 0, nd * sizeof(double));
+    for (int w = 0; w < nthreads; ++w) {
+      const mamba1_bwd_job *j = &jobs[w];
+      for (size_t i = 0; i < nA; ++i) dA[i] += j->dA[i];
+      for (size_t i = 0; i < nBC; ++i) dB[i] += j->dB[i];
+      for (size_t i = 0; i < nBC; ++i) dC[i] += j->dC[i];
+      for (size_t i = 0; i < nd; ++i) dD[i] += j->dD[i];
+      for (size_t i = 0; i < nd; ++i) ddelta_bias[i] += j->dbias[i];
+    }
+  }
+  free(acc);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Mamba-2 (SSD): scalar A per head, B and C per group, state [P, N].       */
 /* h_t = exp(A_h dt_t) h_{t-1} + dt_t B_t x_t^T   ([CUTILE], recurrence)     */
 /* y_t = C_t . h_t + D_h x_t                                               */
