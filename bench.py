@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--ssd", action="store_true", help="also time the Mamba-2 chunked scan")
+    ap.add_argument("--bwd", action="store_true",
+                    help="also time the backward pass on the same workload")
     ap.add_argument("--decode", action="store_true",
                     help="also time one decode step (state update) at the same batch/dim/dstate")
     return ap.parse_args()
@@ -201,10 +203,56 @@ def main():
         out["ssd"] = bench_ssd(args, torch, ssm, synth)
     if args.decode:
         out["decode"] = bench_decode(args, torch, ssm, synth, cfg)
+    if args.bwd:
+        out["bwd"] = bench_bwd(args, torch, ssm, synth, cfg, io, x)
     if not args.no_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline(x, cfg, oracle)
     print(json.dumps(out), flush=True)
+
+
+def bench_bwd(args, torch, ssm, synth, cfg, io, x):
+    """One ssm_selective_scan_bwd call per step (forward recomputed inside,
+    every gradient written)."""
+    import numpy as np
+    b, d, L = x["u"].shape
+    n = x["A"].shape[1]
+    dev = torch.device("cuda:0")
+    dy = synth.to_device(np.random.default_rng(11).standard_normal((b, d, L)).astype(np.float32),
+                         cfg.dtype, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    du, dd, dz = torch.empty_like(io["u"]), torch.empty_like(io["u"]), torch.empty_like(io["u"])
+    dA = torch.empty((d, n), **f32)
+    dB, dC = torch.empty((b, n, L), **f32), torch.empty((b, n, L), **f32)
+    dD, dbias = torch.empty((d,), **f32), torch.empty((d,), **f32)
+    ws = torch.empty(ssm.ssm_selective_scan_bwd_workspace_size(b, d, n, L), dtype=torch.uint8,
+                     device=dev)
+    handle = ssm.get_handle(0)
+
+    def step():
+        ssm.ssm_selective_scan_bwd(io["u"], io["delta"], io["A"], io["B"], io["C"], io["D"],
+                                   io["z"], io["delta_bias"], cfg.softplus, None, dy, None, du, dd,
+                                   dA, dB, dC, dD, dz, dbias, None, ws, handle=handle)
+
+    steps = max(1, args.steps // 4)
+    for _ in range(max(1, args.warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    es = 2 if cfg.dtype == "bf16" else 4
+    # inputs u, delta, z, dy and outputs du, ddelta, dz once; B, C in, dB, dC (fp32) out
+    nbytes = 7 * b * d * L * es + 2 * b * n * L * es + 2 * b * n * L * 4 + 8 * d * n + 16 * d
+    return {"workload": f"{cfg.name} backward: all gradients, forward recomputed inside",
+            "ms_per_call": round(ms, 4), "workspace_bytes": ws.numel(),
+            "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "state_updates_per_s": round(b * d * L * n / (ms * 1e-3), 1)}
 
 
 def bench_decode(args, torch, ssm, synth, cfg):

@@ -138,6 +138,55 @@ ssm_status ssm_selective_scan_fwd_with_state(
     int64_t seqlen, ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * Workspace size in bytes needed by ssm_selective_scan_bwd for these sizes
+ * (caller-allocated).  Same size checks as ssm_selective_scan_bwd.
+ */
+ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle,
+                                                 int64_t batch, int64_t dim,
+                                                 int64_t dstate, int64_t seqlen,
+                                                 size_t *bytes);
+
+/*
+ * Mamba-1 selective scan, backward ([SPEC]: the backward-pass stage asks
+ * for the gradients of every input; [EXPLAINED] eqs. (5)-(7): the
+ * recurrence differentiated).  Given the forward inputs of
+ * ssm_selective_scan_fwd_with_state and the upstream gradients dy (of y)
+ * and dlast_state (of last_state), computes the gradient of
+ *   sum(dy * y) + sum(dlast_state * last_state)
+ * with respect to u, delta (the raw delta, before bias and softplus), A, B,
+ * C, D, z, delta_bias and initial_state.  The forward is recomputed inside
+ * the call (a state saved every 16 steps in the workspace); nothing needs
+ * to be kept from the forward call.
+ *
+ * Layouts (row-major):
+ *   u, delta, z, dy, du, ddelta, dz : [batch, dim, seqlen]  in_dtype
+ *   B, C                            : [batch, dstate, seqlen] in_dtype
+ *   dB, dC                          : [batch, dstate, seqlen] float32
+ *   A, dA                           : [dim, dstate]  float32
+ *   D, delta_bias, dD, ddelta_bias  : [dim]          float32
+ *   initial_state, dlast_state, dinitial_state : [batch, dim, dstate] float32
+ * Nullable: D, z, delta_bias, initial_state (zero), dlast_state (zero),
+ * dD, ddelta_bias, dinitial_state (not computed); dz is required when z
+ * is given.  workspace: ssm_selective_scan_bwd_workspace_size bytes.
+ * Pointers 16-byte aligned; outputs and the workspace must not overlap
+ * each other or any input.  Every output is overwritten (nothing is
+ * accumulated into).  The result is deterministic (partial sums are added
+ * in a fixed order).
+ *
+ * Limits: as ssm_selective_scan_fwd, and dstate <= 16 (SSM_ERR_UNSUPPORTED
+ * above).
+ */
+ssm_status ssm_selective_scan_bwd(
+    ssm_handle handle, const void *u, const void *delta, const float *A,
+    const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, const float *initial_state,
+    const void *dy, const float *dlast_state, void *du, void *ddelta,
+    float *dA, float *dB, float *dC, float *dD, void *dz,
+    float *ddelta_bias, float *dinitial_state, void *workspace,
+    size_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
+    int64_t seqlen, ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * One decode step of the Mamba-1 recurrence ([SPEC] Stage 1 items 3-4;
  * [EXPLAINED] eqs. (5)-(7); [BLELLOCH] section 1: the sequential form for
  * online inference).  For every row (b, d), with the state updated in place:

@@ -27,7 +27,8 @@ SSM_F32, SSM_BF16 = 0, 1
 # Every symbol declared in include/ssm_scan.h.
 EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
-           "ssm_selective_state_update",
+           "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
+           "ssm_selective_scan_bwd",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
            "ssd_chunk_scan_fwd_with_state")
 
@@ -76,6 +77,14 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_state_update.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
             _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_scan_bwd_workspace_size.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd_workspace_size.argtypes = [
+            _vp, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_selective_scan_bwd.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+            _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_int
         lib.ssd_chunk_scan_workspace_size.argtypes = [
             _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -237,6 +246,74 @@ def ssm_selective_state_update(state, u, delta, A, B, C, D, z, delta_bias, delta
         _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), batch, dim, dstate,
         _dtype_code(u), _stream_ptr(u.device))
     _check("ssm_selective_state_update", st)
+
+
+def ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, handle=None,
+                                          device: int = 0) -> int:
+    if handle is None:
+        handle = get_handle(device)
+    n = ctypes.c_size_t()
+    st = load_library().ssm_selective_scan_bwd_workspace_size(handle, batch, dim, dstate, seqlen,
+                                                              ctypes.byref(n))
+    _check("ssm_selective_scan_bwd_workspace_size", st)
+    return int(n.value)
+
+
+def ssm_selective_scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
+                           dy, dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+                           dinitial_state, workspace, handle=None) -> None:
+    """Enqueue the Mamba-1 backward pass (tensor form of the C entry point;
+    every gradient and the workspace are caller-allocated)."""
+    for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
+                         ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
+                         ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
+                         ("dy", dy, False), ("dlast_state", dlast_state, True),
+                         ("du", du, False), ("ddelta", ddelta, False), ("dA", dA, False),
+                         ("dB", dB, False), ("dC", dC, False), ("dD", dD, True), ("dz", dz, True),
+                         ("ddelta_bias", ddelta_bias, True),
+                         ("dinitial_state", dinitial_state, True),
+                         ("workspace", workspace, False)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssm_selective_scan_bwd(
+        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(dy),
+        _ptr(dlast_state), _ptr(du), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
+        _ptr(dz), _ptr(ddelta_bias), _ptr(dinitial_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), batch, dim, dstate, seqlen,
+        _dtype_code(u), _stream_ptr(u.device))
+    _check("ssm_selective_scan_bwd", st)
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, initial_state=None, dlast_state=None):
+    """Allocating form: returns a dict of gradients (du, ddelta, dz in the
+    input dtype; dA, dB, dC, dD, ddelta_bias, dinitial_state float32; the
+    optional ones are None when their input is None)."""
+    import torch
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    dev = u.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+         "dA": torch.empty((dim, dstate), **f32), "dB": torch.empty((batch, dstate, seqlen), **f32),
+         "dC": torch.empty((batch, dstate, seqlen), **f32),
+         "dD": torch.empty((dim,), **f32) if D is not None else None,
+         "dz": torch.empty_like(u) if z is not None else None,
+         "ddelta_bias": torch.empty((dim,), **f32) if delta_bias is not None else None,
+         "dinitial_state": (torch.empty((batch, dim, dstate), **f32)
+                            if initial_state is not None else None)}
+    nbytes = ssm_selective_scan_bwd_workspace_size(
+        batch, dim, dstate, seqlen, device=dev.index if dev.index is not None else 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ssm_selective_scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state, dy,
+                           dlast_state, g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"],
+                           g["dz"], g["ddelta_bias"], g["dinitial_state"], ws)
+    return g
 
 
 def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,

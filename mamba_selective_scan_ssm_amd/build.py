@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "ssmscan")
 LIB = os.path.join(PKG, "libssmscan.so")
 
-SOURCES = ["api.cpp", "selective_scan.hip", "ssd_chunk_scan.hip", "state_update.hip"]
+SOURCES = ["api.cpp", "selective_scan.hip", "selective_scan_bwd.hip", "ssd_chunk_scan.hip",
+           "state_update.hip"]
 ARCH = "gfx950"
 
 

@@ -203,6 +203,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   ssm::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
   p.delta_bias = delta_bias; p.y = y; p.last_state = last_state; p.h0 = initial_state;
+  p.chunk_states = nullptr;
   p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate; p.seqlen = (int)seqlen;
   p.delta_softplus = delta_softplus ? 1 : 0;
   DeviceGuard guard(handle->device);
@@ -239,6 +240,93 @@ ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, in_dtype,
                              stream);
+}
+
+ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,
+                                                int64_t dstate, int64_t seqlen, size_t* bytes) {
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
+  if (dstate > 16) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 16", (long long)dstate);
+  if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
+  if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
+    return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
+  if (batch * dim > (int64_t(1) << 62) / seqlen / 64)
+    return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  *bytes = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen).total;
+  return ok();
+}
+
+ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* delta,
+                                  const float* A, const void* B, const void* C, const float* D,
+                                  const void* z, const float* delta_bias, int delta_softplus,
+                                  const float* initial_state, const void* dy,
+                                  const float* dlast_state, void* du, void* ddelta, float* dA,
+                                  float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+                                  float* dinitial_state, void* workspace, size_t workspace_bytes,
+                                  int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                  ssm_dtype in_dtype, hipStream_t stream) {
+  if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
+  if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
+  if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
+  if (seqlen <= 0) return fail(SSM_ERR_INVALID_ARG, "seqlen must be >= 1 (got %lld)", (long long)seqlen);
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dstate > 16) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 16", (long long)dstate);
+  if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
+  if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
+    return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
+  if (batch * dim > (int64_t(1) << 62) / seqlen / 64)
+    return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
+  const struct { const char* name; const void* p; } required[] = {
+      {"u", u}, {"delta", delta}, {"A", A}, {"B", B}, {"C", C}, {"dy", dy}, {"du", du},
+      {"ddelta", ddelta}, {"dA", dA}, {"dB", dB}, {"dC", dC}, {"workspace", workspace}};
+  for (const auto& r : required)
+    if (!r.p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", r.name);
+  if (z && !dz) return fail(SSM_ERR_INVALID_ARG, "dz is NULL while z is given");
+  const ssm::BwdLayout lay =
+      ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen);
+  if (workspace_bytes < lay.total)
+    return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                lay.total);
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nrow = (uint64_t)batch * dim * seqlen;
+  const uint64_t nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
+  const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
+                     {"A", A, (uint64_t)dim * dstate * 4}, {"B", B, nbc * es},
+                     {"C", C, nbc * es},           {"D", D, (uint64_t)dim * 4},
+                     {"z", z, nrow * es},          {"delta_bias", delta_bias, (uint64_t)dim * 4},
+                     {"initial_state", initial_state, nst}, {"dy", dy, nrow * es},
+                     {"dlast_state", dlast_state, nst}};
+  const Span out[] = {{"du", du, nrow * es},       {"ddelta", ddelta, nrow * es},
+                      {"dA", dA, (uint64_t)dim * dstate * 4}, {"dB", dB, nbc * 4},
+                      {"dC", dC, nbc * 4},         {"dD", dD, (uint64_t)dim * 4},
+                      {"dz", z ? dz : nullptr, nrow * es},
+                      {"ddelta_bias", ddelta_bias, (uint64_t)dim * 4},
+                      {"dinitial_state", dinitial_state, nst},
+                      {"workspace", workspace, lay.total}};
+  ssm_status st = check_spans(in, 11, out, 10);
+  if (st != SSM_OK) return st;
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+
+  ssm::BwdParams p;
+  ssm::ScanParams& f = p.fwd;
+  f.u = u; f.delta = delta; f.A = A; f.B = B; f.C = C; f.D = D; f.z = z;
+  f.delta_bias = delta_bias; f.y = nullptr; f.last_state = nullptr; f.h0 = initial_state;
+  f.chunk_states = nullptr;
+  f.batch = (int)batch; f.dim = (int)dim; f.dstate = (int)dstate; f.seqlen = (int)seqlen;
+  f.delta_softplus = delta_softplus ? 1 : 0;
+  p.dy = dy; p.dlast = dlast_state; p.du = du; p.ddelta = ddelta; p.dz = z ? dz : nullptr;
+  p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.ddelta_bias = ddelta_bias;
+  p.dh0 = dinitial_state; p.workspace = workspace;
+  DeviceGuard guard(handle->device);
+  if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
+  hipError_t e = ssm::launch_selective_scan_bwd(p, in_dtype == SSM_BF16, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const void* u,

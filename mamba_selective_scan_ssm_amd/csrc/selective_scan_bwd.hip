@@ -1,0 +1,500 @@
+// selective_scan_bwd.hip -- Mamba-1 selective-scan backward pass for gfx950.
+//
+// Sources (web pages; cited by title and section/equation):
+//   [SPEC]      "ТЕХНИЧЕСКОЕ ЗАДАНИЕ: Реализовать selective scan (Mamba)",
+//               Stage 1 items 3-4 (forward: softplus, D skip, silu gate) and
+//               its backward-pass stage (gradients of every input).
+//   [EXPLAINED] "Mamba CUDA 实现解析", eqs. (5)-(7) (the recurrence being
+//               differentiated).
+//
+// Gradients of L(y, last_state) given dy and dlast, by reverse-mode
+// differentiation of the recurrence (per row, t descending):
+//   dyh_t = dy_t silu(z_t);  dz_t = dy_t yh_t silu'(z_t);  dD += dyh_t u_t
+//   lam  = C_t dyh_t + a_{t+1} lam                (lam = dL/dh_t)
+//   dC_t += dyh_t h_t;  dB_t += lam dt_t u_t;  du_t = dyh_t D + sum lam dt_t B_t
+//   ddt_t = sum lam (a_t A h_{t-1} + B_t u_t);  dA += lam a_t dt_t h_{t-1}
+//   ddelta_t = ddt_t sigmoid(delta_t + bias) (softplus) ;  dbias += ddelta_t
+//   dh0 = lam after t = 0.
+//
+// Three launches:
+//   1. the row-parallel forward kernel with 16-step chunks, saving the state
+//      entering every chunk (no y, no last_state);
+//   2. selective_scan_bwd_kernel: per row, chunks in reverse order; each
+//      chunk's states are recomputed from its saved entry state into
+//      registers, then the reverse recurrence runs over the chunk.  The lane
+//      layout is the forward's (a row's states over a DPP lane group, the
+//      group's lanes owning slices of the per-step work).  dB and dC need a
+//      sum over rows: each step's per-lane contributions are summed over
+//      the rows of a 16-lane DPP row with row shifts, the partial sums go
+//      to LDS and are added per workgroup, giving one partial per (batch,
+//      workgroup, state, step) in the workspace; dA, dD and dbias are kept
+//      per row (one partial per batch entry);
+//   3. two small kernels add the partials (over workgroups for dB and dC,
+//      over the batch for dA, dD, dbias) in a fixed order, so the result is
+//      deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_math.h"
+#include "scan_common.h"
+#include "selective_scan_launch.h"
+
+namespace ssm {
+namespace {
+
+using namespace scan;
+
+constexpr int kBwdT = 16;   // steps per chunk (the forward saves a state every kBwdT steps)
+constexpr int kBwdNG = 4;   // states per lane
+
+// Sum of v over the lanes of a 16-lane DPP row that share this lane's slot
+// (lane % LPC); the sum ends up in the last LPC lanes of the row.
+template <int LPC>
+__device__ __forceinline__ float row_sum_same_slot(float v) {
+  if constexpr (LPC <= 1) v += dpp_f<0x111>(v);  // row_shr:1
+  if constexpr (LPC <= 2) v += dpp_f<0x112>(v);  // row_shr:2
+  if constexpr (LPC <= 4) v += dpp_f<0x114>(v);  // row_shr:4
+  v += dpp_f<0x118>(v);                          // row_shr:8
+  return v;
+}
+
+// Sum over the LPC lanes of a row's group (every lane gets the sum).
+template <int LPC>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPC >= 2) v += dpp_f<kSwapPairs>(v);
+  if constexpr (LPC >= 4) v += dpp_f<kSwapHalves>(v);
+  return v;
+}
+
+// Reduce-scatter over the lane group: lane `slot` ends with the sums of the
+// steps slot*TS .. slot*TS + TS-1 (as in the forward kernel).
+template <int LPC, int T>
+__device__ __forceinline__ void group_reduce_scatter(const float (&part)[T], int slot,
+                                                     float (&out)[T / LPC]) {
+  constexpr int TS = T / LPC;
+  if constexpr (LPC == 4) {
+    float s1[T / 2];
+    const bool lo = slot < 2;
+#pragma unroll
+    for (int j = 0; j < T / 2; ++j) {
+      const float keep = lo ? part[j] : part[T / 2 + j];
+      const float send = lo ? part[T / 2 + j] : part[j];
+      s1[j] = keep + dpp_f<kSwapHalves>(send);
+    }
+    const bool ev = (slot & 1) == 0;
+#pragma unroll
+    for (int j = 0; j < TS; ++j) {
+      const float keep = ev ? s1[j] : s1[TS + j];
+      const float send = ev ? s1[TS + j] : s1[j];
+      out[j] = keep + dpp_f<kSwapPairs>(send);
+    }
+  } else if constexpr (LPC == 2) {
+    const bool ev = slot == 0;
+#pragma unroll
+    for (int j = 0; j < TS; ++j) {
+      const float keep = ev ? part[j] : part[TS + j];
+      const float send = ev ? part[TS + j] : part[j];
+      out[j] = keep + dpp_f<kSwapPairs>(send);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TS; ++j) out[j] = part[j];
+  }
+}
+
+template <typename In, int LPC>
+__global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, BwdLayout lay) {
+  constexpr int NG = kBwdNG, T = kBwdT;
+  constexpr int NS = NG * LPC;       // states covered per row
+  constexpr int RPW = 64 / LPC;      // rows per wave
+  constexpr int RPB = 4 * RPW;       // rows per workgroup
+  constexpr int TS = T / LPC;        // steps whose per-step work one lane owns
+  constexpr int EPU = Elem<In>::kPer16B;
+  static_assert(T % EPU == 0, "chunk must hold whole 16-byte units");
+  constexpr int UPR = T / EPU;
+  constexpr int UNITS = 2 * NS * UPR;
+  constexpr int RB = (UNITS + 255) / 256;
+  constexpr int kPad = T * NS + 4;   // LDS stride of one (wave, 16-lane row) partial block
+
+  __shared__ alignas(16) float sB[T][NS];
+  __shared__ alignas(16) float sC[T][NS];
+  __shared__ alignas(16) float sPB[4][4][kPad];  // [wave][16-lane row][t*NS + n]
+  __shared__ alignas(16) float sPC[4][4][kPad];
+
+  const ScanParams& F = P.fwd;
+  const In* __restrict__ u = static_cast<const In*>(F.u);
+  const In* __restrict__ dlt = static_cast<const In*>(F.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(F.B);
+  const In* __restrict__ Cm = static_cast<const In*>(F.C);
+  const In* __restrict__ z = static_cast<const In*>(F.z);
+  const In* __restrict__ dy = static_cast<const In*>(P.dy);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = lane % LPC;
+  const int drow = lane >> 4;
+  const int b = blockIdx.y;
+  const int wg = blockIdx.x;
+  const int d = wg * RPB + wv * RPW + lane / LPC;
+  const bool row_ok = d < F.dim;
+  const bool has_z = z != nullptr;
+  const int L = F.seqlen;
+  const int N = F.dstate;
+  const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
+  const int64_t row_base = row * (int64_t)L;
+  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+
+  float A2[NG], Af[NG], lam[NG], dA_acc[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    const bool ok = row_ok && n < N;
+    Af[k] = ok ? F.A[(int64_t)d * N + n] : 0.0f;
+    A2[k] = Af[k] * kLog2e;
+    lam[k] = (ok && P.dlast) ? P.dlast[row * N + n] : 0.0f;
+    dA_acc[k] = 0.0f;
+  }
+  const float Dd = (row_ok && F.D) ? F.D[d] : 0.0f;
+  const float bias = (row_ok && F.delta_bias) ? F.delta_bias[d] : 0.0f;
+  float dD_acc = 0.0f, dbias_acc = 0.0f;
+  const float* chunk_states = reinterpret_cast<const float*>(
+      static_cast<const char*>(P.workspace) + lay.chunk_states_off);
+  float* part_bc = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off);
+  const int64_t part_c_off = (int64_t)F.batch * lay.nwg * N * L;  // dC partials follow dB's
+
+  for (int ch = lay.nchunks - 1; ch >= 0; --ch) {
+    const int c0 = ch * T;
+    const int ts = c0 + slot * TS;
+    // -- loads: this lane's slice of u, delta, z, dy; B and C of the chunk ----
+    RawSeg<In, TS> ru, rd, rz, rg;
+    if (row_ok) {
+      load_raw<In, TS>(u, row_base, ts, L, ru);
+      load_raw<In, TS>(dlt, row_base, ts, L, rd);
+      load_raw<In, TS>(dy, row_base, ts, L, rg);
+      if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
+    } else {
+#pragma unroll
+      for (int k = 0; k < RawSeg<In, TS>::kWords; ++k) ru.w[k] = rd.w[k] = rg.w[k] = rz.w[k] = 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * 256;
+      if (e < UNITS) {
+        const int n = e % NS, rest = e / NS;
+        const int seg = rest % UPR, x = rest / UPR;
+        RawSeg<In, EPU> r;
+        if (n < N) {
+          load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, r);
+        } else {
+#pragma unroll
+          for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) r.w[k] = 0u;
+        }
+        float v[EPU];
+        decode_raw<In, EPU>(r, v);
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) {
+          if (x) sC[seg * EPU + i][n] = v[i];
+          else sB[seg * EPU + i][n] = v[i];
+        }
+      }
+    }
+    float hs[NG];  // state entering the chunk
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const int n = slot * NG + k;
+      hs[k] = (row_ok && n < N) ? chunk_states[(row * lay.nchunks + ch) * N + n] : 0.0f;
+    }
+    // -- per-step values of this lane's slice ---------------------------------
+    float uk[TS], dl[TS], du[TS], sp[TS], gy[TS], zk[TS];
+    {
+      float dr[TS];
+      decode_raw<In, TS>(ru, uk);
+      decode_raw<In, TS>(rd, dr);
+      decode_raw<In, TS>(rg, gy);
+      if (has_z) {
+        decode_raw<In, TS>(rz, zk);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) zk[j] = 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        sp[j] = dr[j] + bias;
+        dl[j] = F.delta_softplus ? softplus_f(sp[j]) : sp[j];
+        if (ts + j >= L) dl[j] = 0.0f;  // past the end: identity steps
+        du[j] = dl[j] * uk[j];
+      }
+    }
+    __syncthreads();  // sB, sC of this chunk are complete
+
+    // -- forward over the chunk from its saved entry state ---------------------
+    float hist[T][NG], yp[T];
+    {
+      float h[NG];
+#pragma unroll
+      for (int k = 0; k < NG; ++k) h[k] = hs[k];
+      static_for<0, T>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        float dt, dut;
+        if constexpr (LPC > 1) {
+          dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+          dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+        } else {
+          dt = dl[t];
+          dut = du[t];
+        }
+        const float4 bq = *reinterpret_cast<const float4*>(&sB[t][slot * NG]);
+        const float4 cq = *reinterpret_cast<const float4*>(&sC[t][slot * NG]);
+        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+        const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+          const float a = fast_exp2(dt * A2[k]);
+          h[k] = __builtin_fmaf(a, h[k], dut * bv[k]);
+          hist[t][k] = h[k];
+          acc = __builtin_fmaf(cv[k], h[k], acc);
+        }
+        yp[t] = acc;
+      });
+    }
+    // -- output-side gradients for this lane's steps ---------------------------
+    float dyh[TS];
+    {
+      float yo[TS];
+      group_reduce_scatter<LPC, T>(yp, slot, yo);
+      float dzv[TS];
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float yh = __builtin_fmaf(Dd, uk[j], yo[j]);
+        if (has_z) {
+          const float sg = fast_rcp(1.0f + fast_exp2(-zk[j] * kLog2e));
+          dyh[j] = gy[j] * zk[j] * sg;
+          dzv[j] = gy[j] * yh * sg * __builtin_fmaf(zk[j], 1.0f - sg, 1.0f);
+        } else {
+          dyh[j] = gy[j];
+          dzv[j] = 0.0f;
+        }
+        dD_acc = __builtin_fmaf(dyh[j], uk[j], dD_acc);
+      }
+      if (has_z && row_ok) store_seg<In, TS>(static_cast<In*>(P.dz), row_base, ts, L, dzv);
+    }
+
+    // -- reverse recurrence over the chunk -------------------------------------
+    float ddtp[T], dup[T];
+    static_for<0, T>([&](auto rc) {
+      constexpr int t = T - 1 - decltype(rc)::value;
+      float dyt, dt, dut, ut;
+      if constexpr (LPC > 1) {
+        dyt = dpp_f<group_bcast<LPC>(t / TS)>(dyh[t % TS]);
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+        ut = dpp_f<group_bcast<LPC>(t / TS)>(uk[t % TS]);
+      } else {
+        dyt = dyh[t];
+        dt = dl[t];
+        dut = du[t];
+        ut = uk[t];
+      }
+      const float4 bq = *reinterpret_cast<const float4*>(&sB[t][slot * NG]);
+      const float4 cq = *reinterpret_cast<const float4*>(&sC[t][slot * NG]);
+      const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+      const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+      float ddt_p = 0.0f, du_p = 0.0f, cB[NG], cC[NG];
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        lam[k] = __builtin_fmaf(cv[k], dyt, lam[k]);          // lam = dL/dh_t
+        cC[k] = dyt * hist[t][k];
+        const float a = fast_exp2(dt * A2[k]);
+        const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hs[k];
+        ddt_p = __builtin_fmaf(lam[k], __builtin_fmaf(a * Af[k], hp, bv[k] * ut), ddt_p);
+        dA_acc[k] = __builtin_fmaf(lam[k] * a, dt * hp, dA_acc[k]);
+        cB[k] = lam[k] * dut;
+        du_p = __builtin_fmaf(lam[k], dt * bv[k], du_p);
+        lam[k] *= a;                                           // dL/dh_{t-1}
+      }
+      ddtp[t] = ddt_p;
+      dup[t] = du_p;
+      // dB, dC: sum over the rows of this 16-lane DPP row, then to LDS
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        cB[k] = row_sum_same_slot<LPC>(cB[k]);
+        cC[k] = row_sum_same_slot<LPC>(cC[k]);
+      }
+      if ((lane & 15) >= 16 - LPC) {
+        *reinterpret_cast<float4*>(&sPB[wv][drow][t * NS + slot * NG]) =
+            make_float4(cB[0], cB[1], cB[2], cB[3]);
+        *reinterpret_cast<float4*>(&sPC[wv][drow][t * NS + slot * NG]) =
+            make_float4(cC[0], cC[1], cC[2], cC[3]);
+      }
+    });
+
+    // -- input-side gradients for this lane's steps ------------------------------
+    {
+      float ddt_o[TS], du_o[TS];
+      group_reduce_scatter<LPC, T>(ddtp, slot, ddt_o);
+      group_reduce_scatter<LPC, T>(dup, slot, du_o);
+      float dus[TS], dds[TS];
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        dus[j] = __builtin_fmaf(dyh[j], Dd, du_o[j]);
+        float ds = ddt_o[j];
+        if (F.delta_softplus) ds *= fast_rcp(1.0f + fast_exp2(-sp[j] * kLog2e));
+        if (ts + j >= L) ds = 0.0f;
+        dds[j] = ds;
+        dbias_acc += ds;
+      }
+      if (row_ok) {
+        store_seg<In, TS>(static_cast<In*>(P.du), row_base, ts, L, dus);
+        store_seg<In, TS>(static_cast<In*>(P.ddelta), row_base, ts, L, dds);
+      }
+    }
+    __syncthreads();  // sPB, sPC complete; sB, sC free
+    // -- this workgroup's dB, dC partials for the chunk ---------------------------
+    for (int e = tid; e < T * NS; e += 256) {
+      const int t = e / NS, n = e % NS;
+      float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sb += sPB[w][r][e];
+          sc += sPC[w][r][e];
+        }
+      if (n < N && c0 + t < L) {
+        const int64_t o = (((int64_t)b * lay.nwg + wg) * N + n) * L + c0 + t;
+        part_bc[o] = sb;
+        part_bc[part_c_off + o] = sc;
+      }
+    }
+    __syncthreads();  // before the next chunk overwrites the LDS tiles
+  }
+
+  // -- per-row outputs and partials ------------------------------------------------
+  dD_acc = group_sum<LPC>(dD_acc);
+  dbias_acc = group_sum<LPC>(dbias_acc);
+  if (row_ok) {
+    float* part_a = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_a_off);
+    float* part_d = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_d_off);
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const int n = slot * NG + k;
+      if (n < N) {
+        part_a[row * N + n] = dA_acc[k];
+        if (P.dh0) P.dh0[row * N + n] = lam[k];
+      }
+    }
+    if (slot == 0) {
+      part_d[row] = dD_acc;                                // [batch, dim]
+      part_d[(int64_t)F.batch * F.dim + row] = dbias_acc;  // then [batch, dim]
+    }
+  }
+}
+
+// dB[b][n][t] = sum over workgroups of the partials (fixed order).
+__global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdParams P, BwdLayout lay) {
+  const ScanParams& F = P.fwd;
+  const int64_t per = (int64_t)F.dstate * F.seqlen;
+  const int64_t total = (int64_t)F.batch * per;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t b = i / per, r = i % per;
+  const float* part = reinterpret_cast<const float*>(
+      static_cast<const char*>(P.workspace) + lay.part_bc_off);
+  const int64_t part_c_off = (int64_t)F.batch * lay.nwg * per;
+  float sb = 0.0f, sc = 0.0f;
+  for (int w = 0; w < lay.nwg; ++w) {
+    const int64_t o = ((int64_t)b * lay.nwg + w) * per + r;
+    sb += part[o];
+    sc += part[part_c_off + o];
+  }
+  P.dB[i] = sb;
+  P.dC[i] = sc;
+}
+
+// dA[d][n], dD[d], ddelta_bias[d] = sums over the batch (fixed order).
+__global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdParams P, BwdLayout lay) {
+  const ScanParams& F = P.fwd;
+  const int64_t nA = (int64_t)F.dim * F.dstate;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const char* ws = static_cast<const char*>(P.workspace);
+  const float* part_a = reinterpret_cast<const float*>(ws + lay.part_a_off);
+  const float* part_d = reinterpret_cast<const float*>(ws + lay.part_d_off);
+  if (i < nA) {
+    float s = 0.0f;
+    for (int b = 0; b < F.batch; ++b) s += part_a[(int64_t)b * nA + i];
+    P.dA[i] = s;
+  } else if (i < nA + F.dim) {
+    const int64_t dd = i - nA;
+    float sD = 0.0f, sb = 0.0f;
+    for (int b = 0; b < F.batch; ++b) {
+      sD += part_d[(int64_t)b * F.dim + dd];
+      sb += part_d[(int64_t)F.batch * F.dim + (int64_t)b * F.dim + dd];
+    }
+    if (P.dD) P.dD[dd] = sD;
+    if (P.ddelta_bias) P.ddelta_bias[dd] = sb;
+  }
+}
+
+template <typename In, int LPC>
+hipError_t launch_bwd_rows(const BwdParams& p, const BwdLayout& lay, hipStream_t stream) {
+  dim3 grid((unsigned)lay.nwg, (unsigned)p.fwd.batch);
+  hipLaunchKernelGGL((selective_scan_bwd_kernel<In, LPC>), grid, dim3(256), 0, stream, p, lay);
+  return hipGetLastError();
+}
+
+template <typename In>
+hipError_t launch_bwd_typed(const BwdParams& p, const BwdLayout& lay, hipStream_t stream) {
+  if (p.fwd.dstate <= 4) return launch_bwd_rows<In, 1>(p, lay, stream);
+  if (p.fwd.dstate <= 8) return launch_bwd_rows<In, 2>(p, lay, stream);
+  return launch_bwd_rows<In, 4>(p, lay, stream);
+}
+
+int lanes_per_row(int dstate) { return dstate <= 4 ? 1 : dstate <= 8 ? 2 : 4; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen) {
+  BwdLayout l;
+  l.nchunks = (seqlen + kBwdT - 1) / kBwdT;
+  const int rpb = 4 * (64 / lanes_per_row(dstate));
+  l.nwg = (dim + rpb - 1) / rpb;
+  const size_t rows = (size_t)batch * dim;
+  l.chunk_states_off = 0;
+  l.part_bc_off = align256(rows * l.nchunks * dstate * sizeof(float));
+  l.part_a_off = align256(l.part_bc_off +
+                          2 * (size_t)batch * l.nwg * dstate * seqlen * sizeof(float));
+  l.part_d_off = align256(l.part_a_off + rows * dstate * sizeof(float));
+  l.total = align256(l.part_d_off + 2 * rows * sizeof(float));
+  return l;
+}
+
+hipError_t launch_selective_scan_bwd(const BwdParams& p, bool bf16, hipStream_t stream) {
+  const ScanParams& F = p.fwd;
+  const BwdLayout lay = selective_scan_bwd_layout(F.batch, F.dim, F.dstate, F.seqlen);
+  // 1. forward, saving the state entering every chunk
+  ScanParams fs = F;
+  fs.y = nullptr;
+  fs.last_state = nullptr;
+  fs.chunk_states = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.chunk_states_off);
+  hipError_t e = launch_selective_scan_save(fs, bf16, stream);
+  if (e != hipSuccess) return e;
+  // 2. reverse pass
+  e = bf16 ? launch_bwd_typed<uint16_t>(p, lay, stream) : launch_bwd_typed<float>(p, lay, stream);
+  if (e != hipSuccess) return e;
+  // 3. partial sums
+  const int64_t nbc = (int64_t)F.batch * F.dstate * F.seqlen;
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
+                     stream, p, lay);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t np = (int64_t)F.dim * F.dstate + F.dim;
+  hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0,
+                     stream, p, lay);
+  return hipGetLastError();
+}
+
+}  // namespace ssm

@@ -20,6 +20,8 @@ struct ScanParams {
   void* y;
   float* last_state;        // nullable
   const float* h0;          // initial state [batch, dim, dstate], nullable (zero)
+  float* chunk_states;      // nullable: the state entering every time chunk,
+                            // [batch, dim, nchunks, dstate] (backward pass)
   int batch;
   int dim;
   int dstate;
@@ -41,6 +43,35 @@ struct ScanTile {
 
 hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
                                  hipStream_t stream);
+
+// Forward pass that saves the state entering every 16-step chunk into
+// p.chunk_states (dstate <= 16; y and last_state may be null).
+hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream);
+
+// Backward pass (selective_scan_bwd.hip).
+struct BwdParams {
+  ScanParams fwd;           // forward inputs (y, last_state unused); fwd.h0 nullable
+  const void* dy;           // [batch, dim, seqlen] in_dtype
+  const float* dlast;       // [batch, dim, dstate] nullable
+  void* du;                 // [batch, dim, seqlen] in_dtype
+  void* ddelta;             // [batch, dim, seqlen] in_dtype
+  void* dz;                 // [batch, dim, seqlen] in_dtype, required iff z given
+  float* dA;                // [dim, dstate]
+  float* dB;                // [batch, dstate, seqlen]
+  float* dC;                // [batch, dstate, seqlen]
+  float* dD;                // [dim], nullable
+  float* ddelta_bias;       // [dim], nullable
+  float* dh0;               // [batch, dim, dstate], nullable
+  void* workspace;
+};
+
+struct BwdLayout {
+  size_t chunk_states_off, part_bc_off, part_a_off, part_d_off, total;
+  int nchunks, nwg;
+};
+
+BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen);
+hipError_t launch_selective_scan_bwd(const BwdParams& p, bool bf16, hipStream_t stream);
 
 // One decode step (state_update.hip).
 struct StepParams {
