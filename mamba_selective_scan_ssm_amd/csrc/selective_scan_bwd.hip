@@ -23,7 +23,8 @@
 //      chunk's states are recomputed from its saved entry state into
 //      registers, then the reverse recurrence runs over the chunk.  The lane
 //      layout is the forward's (a row's states over a DPP lane group, the
-//      group's lanes owning slices of the per-step work).  dB and dC need a
+//      group's lanes owning slices of the per-step work; per-step sums over
+//      the group are formed at once with DPP adds).  dB and dC need a
 //      sum over rows: each step's per-lane contributions are summed over
 //      the rows of a 16-lane DPP row with row shifts, the partial sums go
 //      to LDS and are added per workgroup, giving one partial per (batch,
@@ -64,42 +65,6 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (LPC >= 2) v += dpp_f<kSwapPairs>(v);
   if constexpr (LPC >= 4) v += dpp_f<kSwapHalves>(v);
   return v;
-}
-
-// Reduce-scatter over the lane group: lane `slot` ends with the sums of the
-// steps slot*TS .. slot*TS + TS-1 (as in the forward kernel).
-template <int LPC, int T>
-__device__ __forceinline__ void group_reduce_scatter(const float (&part)[T], int slot,
-                                                     float (&out)[T / LPC]) {
-  constexpr int TS = T / LPC;
-  if constexpr (LPC == 4) {
-    float s1[T / 2];
-    const bool lo = slot < 2;
-#pragma unroll
-    for (int j = 0; j < T / 2; ++j) {
-      const float keep = lo ? part[j] : part[T / 2 + j];
-      const float send = lo ? part[T / 2 + j] : part[j];
-      s1[j] = keep + dpp_f<kSwapHalves>(send);
-    }
-    const bool ev = (slot & 1) == 0;
-#pragma unroll
-    for (int j = 0; j < TS; ++j) {
-      const float keep = ev ? s1[j] : s1[TS + j];
-      const float send = ev ? s1[TS + j] : s1[j];
-      out[j] = keep + dpp_f<kSwapPairs>(send);
-    }
-  } else if constexpr (LPC == 2) {
-    const bool ev = slot == 0;
-#pragma unroll
-    for (int j = 0; j < TS; ++j) {
-      const float keep = ev ? part[j] : part[TS + j];
-      const float send = ev ? part[TS + j] : part[j];
-      out[j] = keep + dpp_f<kSwapPairs>(send);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < TS; ++j) out[j] = part[j];
-  }
 }
 
 template <typename In, int LPC>
@@ -229,7 +194,11 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
     __syncthreads();  // sB, sC of this chunk are complete
 
     // -- forward over the chunk from its saved entry state ---------------------
-    float hist[T][NG], yp[T];
+    // The readout of step t is summed over the lane group at once and kept
+    // by the lane that owns step t (no per-chunk array of partial sums).
+    float hist[T][NG], yo[TS];
+#pragma unroll
+    for (int j = 0; j < TS; ++j) yo[j] = 0.0f;
     {
       float h[NG];
 #pragma unroll
@@ -256,33 +225,31 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
           hist[t][k] = h[k];
           acc = __builtin_fmaf(cv[k], h[k], acc);
         }
-        yp[t] = acc;
+        acc = group_sum<LPC>(acc);
+        if (slot == t / TS) yo[t % TS] = acc;
+        __builtin_amdgcn_sched_barrier(0);
       });
     }
     // -- output-side gradients for this lane's steps ---------------------------
-    float dyh[TS];
-    {
-      float yo[TS];
-      group_reduce_scatter<LPC, T>(yp, slot, yo);
-      float dzv[TS];
+    float dyh[TS], dzv[TS];
 #pragma unroll
-      for (int j = 0; j < TS; ++j) {
-        const float yh = __builtin_fmaf(Dd, uk[j], yo[j]);
-        if (has_z) {
-          const float sg = fast_rcp(1.0f + fast_exp2(-zk[j] * kLog2e));
-          dyh[j] = gy[j] * zk[j] * sg;
-          dzv[j] = gy[j] * yh * sg * __builtin_fmaf(zk[j], 1.0f - sg, 1.0f);
-        } else {
-          dyh[j] = gy[j];
-          dzv[j] = 0.0f;
-        }
-        dD_acc = __builtin_fmaf(dyh[j], uk[j], dD_acc);
+    for (int j = 0; j < TS; ++j) {
+      const float yh = __builtin_fmaf(Dd, uk[j], yo[j]);
+      if (has_z) {
+        const float sg = fast_rcp(1.0f + fast_exp2(-zk[j] * kLog2e));
+        dyh[j] = gy[j] * zk[j] * sg;
+        dzv[j] = gy[j] * yh * sg * __builtin_fmaf(zk[j], 1.0f - sg, 1.0f);
+      } else {
+        dyh[j] = gy[j];
+        dzv[j] = 0.0f;
       }
-      if (has_z && row_ok) store_seg<In, TS>(static_cast<In*>(P.dz), row_base, ts, L, dzv);
+      dD_acc = __builtin_fmaf(dyh[j], uk[j], dD_acc);
     }
 
     // -- reverse recurrence over the chunk -------------------------------------
-    float ddtp[T], dup[T];
+    float ddt_o[TS], du_o[TS];
+#pragma unroll
+    for (int j = 0; j < TS; ++j) ddt_o[j] = du_o[j] = 0.0f;
     static_for<0, T>([&](auto rc) {
       constexpr int t = T - 1 - decltype(rc)::value;
       float dyt, dt, dut, ut;
@@ -314,8 +281,12 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
         du_p = __builtin_fmaf(lam[k], dt * bv[k], du_p);
         lam[k] *= a;                                           // dL/dh_{t-1}
       }
-      ddtp[t] = ddt_p;
-      dup[t] = du_p;
+      ddt_p = group_sum<LPC>(ddt_p);
+      du_p = group_sum<LPC>(du_p);
+      if (slot == t / TS) {
+        ddt_o[t % TS] = ddt_p;
+        du_o[t % TS] = du_p;
+      }
       // dB, dC: sum over the rows of this 16-lane DPP row, then to LDS
 #pragma unroll
       for (int k = 0; k < NG; ++k) {
@@ -328,13 +299,13 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
         *reinterpret_cast<float4*>(&sPC[wv][drow][t * NS + slot * NG]) =
             make_float4(cC[0], cC[1], cC[2], cC[3]);
       }
+      // keep each step's operands within the step (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
     });
+    if (has_z && row_ok) store_seg<In, TS>(static_cast<In*>(P.dz), row_base, ts, L, dzv);
 
     // -- input-side gradients for this lane's steps ------------------------------
     {
-      float ddt_o[TS], du_o[TS];
-      group_reduce_scatter<LPC, T>(ddtp, slot, ddt_o);
-      group_reduce_scatter<LPC, T>(dup, slot, du_o);
       float dus[TS], dds[TS];
 #pragma unroll
       for (int j = 0; j < TS; ++j) {
