@@ -57,6 +57,11 @@ def _load():
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_selective_scan_grouped_f64.restype = ctypes.c_int
+    lib.oracle_selective_scan_grouped_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
     lib.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
     lib.oracle_selective_scan_bwd_f64.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
@@ -109,8 +114,10 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     """Mamba-1 selective scan in fp64.
 
     u, delta, z: [batch, dim, seqlen]; A: [dim, dstate]; B, C: [batch, dstate,
-    seqlen]; D, delta_bias: [dim]; h0: optional initial state [batch, dim,
-    dstate] (float64; zero when None).  ``rows`` optionally restricts the
+    seqlen], or [batch, ngroups, dstate, seqlen] with channel d reading group
+    d // (dim // ngroups) (ngroups = dim: per-channel B and C);
+    D, delta_bias: [dim]; h0: optional initial state [batch, dim, dstate]
+    (float64; zero when None).  ``rows`` optionally restricts the
     work to flat row indices b*dim+d (outputs then follow that order).
     Returns (y [nrows, seqlen] or None, last_state [nrows, dstate] or None),
     both float64; with rows=None, nrows = batch*dim in (b, d) order.
@@ -119,10 +126,15 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     u = _f32(u)
     batch, dim, seqlen = u.shape
     dstate = np.asarray(A).shape[1]
+    ngroups = np.asarray(B).shape[1] if np.ndim(B) == 4 else 1
     delta = _f32(delta, (batch, dim, seqlen))
     A = _f32(A, (dim, dstate))
-    B = _f32(B, (batch, dstate, seqlen))
-    C = _f32(C, (batch, dstate, seqlen))
+    if np.ndim(B) == 3:
+        B = _f32(B, (batch, dstate, seqlen))
+        C = _f32(C, (batch, dstate, seqlen))
+    else:
+        B = _f32(B, (batch, ngroups, dstate, seqlen))
+        C = _f32(C, (batch, ngroups, dstate, seqlen))
     D = _f32(D, (dim,))
     z = _f32(z, (batch, dim, seqlen))
     delta_bias = _f32(delta_bias, (dim,))
@@ -135,10 +147,10 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     y = np.empty((nrows, seqlen), np.float64) if want_y else None
     st = np.empty((nrows, dstate), np.float64) if want_state else None
     h0 = _f64(h0, (batch, dim, dstate))
-    rc = lib.oracle_selective_scan_h0_f64(
+    rc = lib.oracle_selective_scan_grouped_f64(
         _p32(u), _p32(delta), _p32(A), _p32(B), _p32(C), _p32(D), _p32(z),
         _p32(delta_bias), int(bool(delta_softplus)),
-        None if h0 is None else h0.ctypes.data_as(_f64p), batch, dim, dstate, seqlen,
+        None if h0 is None else h0.ctypes.data_as(_f64p), batch, dim, dstate, seqlen, ngroups,
         None if rows_arr is None else rows_arr.ctypes.data_as(_i64p), nrows,
         None if y is None else y.ctypes.data_as(_f64p),
         None if st is None else st.ctypes.data_as(_f64p),

@@ -53,14 +53,17 @@ static double softplus_d(double x) {
 static double silu_d(double z) { return z / (1.0 + exp(-z)); }
 
 /* ------------------------------------------------------------------------ */
-/* Mamba-1: diagonal A[d,n], B and C shared over channels.                  */
+/* Mamba-1: diagonal A[d,n]; B and C shared over the channels of a group.    */
+/* With one group every channel reads the same B and C; with ngroups = dim  */
+/* each channel has its own, the per-channel form of the [SPEC] reference   */
+/* kernel (B and C indexed by batch, channel and step).                     */
 /* ------------------------------------------------------------------------ */
 
 typedef struct {
   const float *u, *delta, *A, *B, *C, *D, *z, *delta_bias;
   const double *h0; /* initial state [batch, dim, dstate] or NULL (zero) */
   int delta_softplus;
-  int64_t batch, dim, dstate, seqlen;
+  int64_t batch, dim, dstate, seqlen, ngroups;
   const int64_t *rows;
   int64_t nrows;
   double *y, *last_state;
@@ -75,8 +78,11 @@ static void mamba1_one_row(const mamba1_job *j, int64_t out_index, int64_t row,
   const float *dl = j->delta + row * L;
   const float *z = j->z ? j->z + row * L : NULL;
   const float *A = j->A + d * N;            /* A: [dim, dstate] */
-  const float *B = j->B + b * N * L;        /* B, C: [batch, dstate, seqlen] */
-  const float *C = j->C + b * N * L;
+  /* B, C: [batch, ngroups, dstate, seqlen]; channel d is in group
+   * d / (dim / ngroups) */
+  const int64_t g = d / (j->dim / j->ngroups);
+  const float *B = j->B + (b * j->ngroups + g) * N * L;
+  const float *C = j->C + (b * j->ngroups + g) * N * L;
   const double Dd = j->D ? (double)j->D[d] : 0.0;
   const double bias = j->delta_bias ? (double)j->delta_bias[d] : 0.0;
 
@@ -118,19 +124,23 @@ static void *mamba1_worker(void *arg) {
 }
 
 /* Returns 0 on success, -1 on invalid arguments, -2 on thread/alloc failure.
+ * B, C: [batch, ngroups, dstate, seqlen], ngroups dividing dim;
  * rows: optional list of flat row indices b*dim+d (NULL = all rows in order);
  * h0: initial state [batch, dim, dstate] (nullable = zero);
  * y: [nrows, seqlen] (nullable); last_state: [nrows, dstate] (nullable). */
-int oracle_selective_scan_h0_f64(const float *u, const float *delta,
-                                 const float *A, const float *B, const float *C,
-                                 const float *D, const float *z,
-                                 const float *delta_bias, int delta_softplus,
-                                 const double *h0, int64_t batch, int64_t dim,
-                                 int64_t dstate, int64_t seqlen,
-                                 const int64_t *rows, int64_t nrows, double *y,
-                                 double *last_state, int nthreads) {
+int oracle_selective_scan_grouped_f64(const float *u, const float *delta,
+                                      const float *A, const float *B,
+                                      const float *C, const float *D,
+                                      const float *z, const float *delta_bias,
+                                      int delta_softplus, const double *h0,
+                                      int64_t batch, int64_t dim, int64_t dstate,
+                                      int64_t seqlen, int64_t ngroups,
+                                      const int64_t *rows, int64_t nrows,
+                                      double *y, double *last_state,
+                                      int nthreads) {
   if (!u || !delta || !A || !B || !C) return -1;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return -1;
+  if (ngroups <= 0 || dim % ngroups != 0) return -1;
   if (!rows) nrows = batch * dim;
   if (nrows < 0) return -1;
   if (rows)
@@ -150,6 +160,7 @@ int oracle_selective_scan_h0_f64(const float *u, const float *delta,
     j->z = z; j->delta_bias = delta_bias; j->delta_softplus = delta_softplus;
     j->h0 = h0;
     j->batch = batch; j->dim = dim; j->dstate = dstate; j->seqlen = seqlen;
+    j->ngroups = ngroups;
     j->rows = rows; j->nrows = nrows; j->y = y; j->last_state = last_state;
     j->row_begin = nrows * w / nthreads;
     j->row_end = nrows * (w + 1) / nthreads;
@@ -167,6 +178,21 @@ int oracle_selective_scan_h0_f64(const float *u, const float *delta,
     if (ret != NULL) rc = -2;
   }
   return rc;
+}
+
+/* One group: B, C [batch, dstate, seqlen]. */
+int oracle_selective_scan_h0_f64(const float *u, const float *delta,
+                                 const float *A, const float *B, const float *C,
+                                 const float *D, const float *z,
+                                 const float *delta_bias, int delta_softplus,
+                                 const double *h0, int64_t batch, int64_t dim,
+                                 int64_t dstate, int64_t seqlen,
+                                 const int64_t *rows, int64_t nrows, double *y,
+                                 double *last_state, int nthreads) {
+  return oracle_selective_scan_grouped_f64(u, delta, A, B, C, D, z, delta_bias,
+                                           delta_softplus, h0, batch, dim,
+                                           dstate, seqlen, 1, rows, nrows, y,
+                                           last_state, nthreads);
 }
 
 /* Zero initial state. */

@@ -329,6 +329,67 @@ def test_row_subset_matches_full_run():
     np.testing.assert_array_equal(s1, st)
 
 
+def test_groups_reduce_to_one_group_runs():
+    """B and C with a group axis [batch, ngroups, dstate, seqlen]: the
+    channels of group g (a contiguous block of dim/ngroups channels) give the
+    same outputs as a one-group run over that block with B[:, g], C[:, g]
+    (the one-group form is pinned by the closed forms above); every batch
+    entry reads its own groups."""
+    batch, dim, N, L, G = 2, 6, 4, 21, 3
+    x = small_inputs(40, batch=batch, dim=dim, dstate=N, seqlen=L)
+    rng = np.random.default_rng(41)
+    Bg = rng.standard_normal((batch, G, N, L)).astype(np.float32)
+    Cg = rng.standard_normal((batch, G, N, L)).astype(np.float32)
+    xg = dict(x, B=Bg, C=Cg)
+    h0 = rng.standard_normal((batch, dim, N))
+    y, st = oracle.selective_scan(**xg, h0=h0)
+    y = y.reshape(batch, dim, L)
+    st = st.reshape(batch, dim, N)
+    per = dim // G
+    for g in range(G):
+        sl = slice(g * per, (g + 1) * per)
+        xb = dict(u=x["u"][:, sl], delta=x["delta"][:, sl], A=x["A"][sl],
+                  B=Bg[:, g], C=Cg[:, g], D=x["D"][sl], z=x["z"][:, sl],
+                  delta_bias=x["delta_bias"][sl])
+        yb, sb = oracle.selective_scan(**xb, h0=h0[:, sl])
+        np.testing.assert_array_equal(y[:, sl], yb.reshape(batch, per, L))
+        np.testing.assert_array_equal(st[:, sl], sb.reshape(batch, per, N))
+    # one group given with its axis is the plain layout
+    y1, s1 = oracle.selective_scan(**dict(x, B=x["B"][:, None], C=x["C"][:, None]))
+    y0, s0 = oracle.selective_scan(**x)
+    np.testing.assert_array_equal(y1, y0)
+    np.testing.assert_array_equal(s1, s0)
+    with pytest.raises(RuntimeError):  # ngroups must divide dim
+        B4 = np.zeros((batch, 4, N, L), np.float32)
+        oracle.selective_scan(**dict(x, B=B4, C=B4))
+
+
+def test_per_channel_B_C_closed_form():
+    """Per-channel B and C (ngroups = dim), one state: the form of the
+    [SPEC] reference kernel, with A[d], B[b,d,t], C[b,d,t].  With u = 1, a
+    constant step and B[b,d,:] = beta_d the state is the geometric series
+    h_k = dt beta_d (1 - a_d^k) / (1 - a_d), a_d = exp(dt A[d]), and
+    y_t = C[b,d,t] h_t."""
+    batch, dim, L = 2, 5, 40
+    dt = 0.25
+    A = -np.linspace(0.5, 2.5, dim).astype(np.float32)[:, None]
+    beta = np.array([[1.0, -2.0, 0.5, 3.0, -0.75], [2.0, 1.5, -1.0, 0.25, 4.0]], np.float32)
+    B = np.broadcast_to(beta[:, :, None, None], (batch, dim, 1, L)).astype(np.float32)
+    C = np.random.default_rng(42).standard_normal((batch, dim, 1, L)).astype(np.float32)
+    u = np.ones((batch, dim, L), np.float32)
+    delta = np.full((batch, dim, L), dt, np.float32)
+    y, st = oracle.selective_scan(u=u, delta=delta, A=A, B=B, C=C, delta_softplus=False)
+    y = y.reshape(batch, dim, L)
+    k = np.arange(1, L + 1)
+    for b in range(batch):
+        for d in range(dim):
+            a = math.exp(dt * float(A[d, 0]))
+            h = dt * float(beta[b, d]) * (1 - a ** k) / (1 - a)
+            np.testing.assert_allclose(y[b, d], C[b, d, 0].astype(np.float64) * h,
+                                       rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(st.reshape(batch, dim)[b, d], h[-1], rtol=1e-12)
+
+
 def test_invalid_arguments_rejected():
     x = small_inputs(14, batch=1, dim=2, dstate=2, seqlen=4)
     with pytest.raises(RuntimeError):
