@@ -8,7 +8,8 @@ One step = one ssm_selective_scan_fwd call over the whole batch (inputs
 resident in HBM).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--no-cpu-baseline] [--calib-copy] [--ssd]
+                    [--no-cpu-baseline] [--calib-copy] [--ssd] [--bwd] [--decode]
+                    [--grouped]
 
 Algorithmic HBM bytes per call (inputs read once, outputs written once):
     u, delta, z: 3*b*d*L*es   y: b*d*L*es   B, C: 2*b*N*L*es
@@ -59,6 +60,8 @@ def parse():
     ap.add_argument("--ssd", action="store_true", help="also time the Mamba-2 chunked scan")
     ap.add_argument("--bwd", action="store_true",
                     help="also time the backward pass on the same workload")
+    ap.add_argument("--grouped", action="store_true",
+                    help="also time B, C per group of channels: 8 groups and one per channel")
     ap.add_argument("--decode", action="store_true",
                     help="also time one decode step (state update) at the same batch/dim/dstate")
     return ap.parse_args()
@@ -203,6 +206,9 @@ def main():
         out["ssd"] = bench_ssd(args, torch, ssm, synth)
     if args.decode:
         out["decode"] = bench_decode(args, torch, ssm, synth, cfg)
+    if args.grouped:
+        out["grouped"] = [bench_grouped(args, torch, ssm, synth, cfg, io, x, g)
+                          for g in (8, d)]
     if args.bwd:
         out["bwd"] = bench_bwd(args, torch, ssm, synth, cfg, io, x)
     if not args.no_cpu_baseline:
@@ -252,6 +258,49 @@ def bench_bwd(args, torch, ssm, synth, cfg, io, x):
     return {"workload": f"{cfg.name} backward: all gradients, forward recomputed inside",
             "ms_per_call": round(ms, 4), "workspace_bytes": ws.numel(),
             "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "state_updates_per_s": round(b * d * L * n / (ms * 1e-3), 1)}
+
+
+def bench_grouped(args, torch, ssm, synth, cfg, io, x, ngroups):
+    """ssm_selective_scan_fwd_grouped on the same workload with B, C
+    [batch, ngroups, dstate, seqlen] (ngroups = dim: per channel)."""
+    import numpy as np
+    b, d, L = x["u"].shape
+    n = x["A"].shape[1]
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(5)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    Bg = torch.randn((b, ngroups, n, L), generator=gen, device=dev).to(dt)
+    Cg = torch.randn((b, ngroups, n, L), generator=gen, device=dev).to(dt)
+    y = torch.empty_like(io["u"])
+    ls = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    handle = ssm.get_handle(0)
+
+    def step():
+        ssm.ssm_selective_scan_fwd_grouped(io["u"], io["delta"], io["A"], Bg, Cg, io["D"],
+                                           io["z"], io["delta_bias"], cfg.softplus, None, y, ls,
+                                           handle=handle)
+
+    steps = max(1, args.steps // 4)
+    for _ in range(max(1, args.warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    es = 2 if cfg.dtype == "bf16" else 4
+    nbytes = mamba1_bytes(b, d, n, L, es) + 2 * b * (ngroups - 1) * n * L * es
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del Bg, Cg
+    return {"workload": f"{cfg.name} with B, C per group: ngroups {ngroups} "
+                        f"({d // ngroups} channels each)",
+            "ms_per_call": round(ms, 4), "bytes": nbytes, "hbm_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "state_updates_per_s": round(b * d * L * n / (ms * 1e-3), 1)}
 
 

@@ -138,6 +138,28 @@ ssm_status ssm_selective_scan_fwd_with_state(
     int64_t seqlen, ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * ssm_selective_scan_fwd_with_state with B and C given per group of
+ * channels: channel d reads B[b, g, :, :] and C[b, g, :, :] with
+ * g = d / (dim / ngroups).  ngroups = 1 is ssm_selective_scan_fwd_with_state;
+ * ngroups = dim gives every channel its own B and C, the per-channel form
+ * of the [SPEC] reference kernel (B and C indexed by batch, channel and
+ * step, one state per channel there).
+ *
+ *   B, C    : [batch, ngroups, dstate, seqlen] in_dtype, 16-byte aligned
+ *   ngroups : >= 1 and a divisor of dim, else SSM_ERR_INVALID_ARG
+ * Every other argument, layout, limit and error is as for
+ * ssm_selective_scan_fwd_with_state.  When dim / ngroups is a multiple of
+ * the rows one workgroup handles (64 to 256), B and C are staged once per
+ * workgroup as for one group; otherwise each row reads its own B and C.
+ */
+ssm_status ssm_selective_scan_fwd_grouped(
+    ssm_handle handle, const void *u, const void *delta, const float *A,
+    const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, const float *initial_state,
+    void *y, float *last_state, int64_t batch, int64_t dim, int64_t dstate,
+    int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * Workspace size in bytes needed by ssm_selective_scan_bwd for these sizes
  * (caller-allocated).  Same size checks as ssm_selective_scan_bwd.
  */

@@ -27,6 +27,7 @@ SSM_F32, SSM_BF16 = 0, 1
 # Every symbol declared in include/ssm_scan.h.
 EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
+           "ssm_selective_scan_fwd_grouped",
            "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
            "ssm_selective_scan_bwd",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
@@ -73,6 +74,10 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_scan_fwd_with_state.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
             _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_scan_fwd_grouped.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_grouped.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssm_selective_state_update.restype = ctypes.c_int
         lib.ssm_selective_state_update.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
@@ -213,14 +218,43 @@ def ssm_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, delta
     _check("ssm_selective_scan_fwd_with_state", st)
 
 
+def ssm_selective_scan_fwd_grouped(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                   initial_state, y, last_state, handle=None) -> None:
+    """ssm_selective_scan_fwd_with_state with B, C [batch, ngroups, dstate,
+    seqlen]: channel d reads group d // (dim // ngroups)."""
+    for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
+                         ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
+                         ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
+                         ("y", y, False), ("last_state", last_state, True)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    if B.dim() != 4 or C.shape != B.shape or tuple(B.shape) != (batch, B.shape[1], dstate, seqlen):
+        raise ValueError("B and C must be [batch, ngroups, dstate, seqlen], got "
+                         f"{tuple(B.shape)} and {tuple(C.shape)}")
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssm_selective_scan_fwd_grouped(
+        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(y),
+        _ptr(last_state), batch, dim, dstate, seqlen, B.shape[1], _dtype_code(u),
+        _stream_ptr(u.device))
+    _check("ssm_selective_scan_fwd_grouped", st)
+
+
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                        delta_softplus=True, return_last_state=True, initial_state=None):
-    """Allocating form: returns (y, last_state or None)."""
+    """Allocating form: returns (y, last_state or None).  B and C are
+    [batch, dstate, seqlen], or [batch, ngroups, dstate, seqlen] (grouped)."""
     import torch
     y = torch.empty_like(u)
     ls = (torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
                       device=u.device) if return_last_state else None)
-    if initial_state is None:
+    if B.dim() == 4:
+        ssm_selective_scan_fwd_grouped(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                       initial_state, y, ls)
+    elif initial_state is None:
         ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, y, ls)
     else:
         ssm_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, delta_softplus,

@@ -160,12 +160,15 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
                                const void* z, const float* delta_bias, int delta_softplus,
                                const float* initial_state, void* y, float* last_state,
                                int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                               ssm_dtype in_dtype, hipStream_t stream) {
+                               int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream) {
   // ---- sizes -------------------------------------------------------------
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
   if (seqlen <= 0) return fail(SSM_ERR_INVALID_ARG, "seqlen must be >= 1 (got %lld)", (long long)seqlen);
+  if (ngroups <= 0 || dim % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
+                (long long)ngroups, (long long)dim);
   if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
@@ -183,7 +186,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
   const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
-  const uint64_t nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t nbc = (uint64_t)batch * ngroups * dstate * seqlen;
   const uint64_t state_bytes = (uint64_t)batch * dim * dstate * 4;
   // initial_state may be last_state itself (each entry is read once, before
   // the thread that reads it writes it); any other overlap with an output is
@@ -206,10 +209,16 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   p.chunk_states = nullptr;
   p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate; p.seqlen = (int)seqlen;
   p.delta_softplus = delta_softplus ? 1 : 0;
+  p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
   const ssm::ScanTile tile = pick_scan_tile(handle, batch, dim, dstate);
-  hipError_t e = ssm::launch_selective_scan(p, tile, in_dtype == SSM_BF16, stream);
+  const bool bf16 = in_dtype == SSM_BF16;
+  // A group covering whole workgroups of the tile: its B and C are staged
+  // once per workgroup; otherwise every row reads its own.
+  const bool whole = (dim / ngroups) % ssm::scan_tile_rows(tile) == 0;
+  hipError_t e = (ngroups == 1 || whole) ? ssm::launch_selective_scan(p, tile, bf16, stream)
+                                         : ssm::launch_selective_scan_rowbc(p, bf16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -225,7 +234,7 @@ ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* 
                                   int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
                                   hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
-                             nullptr, y, last_state, batch, dim, dstate, seqlen, in_dtype,
+                             nullptr, y, last_state, batch, dim, dstate, seqlen, 1, in_dtype,
                              stream);
 }
 
@@ -238,8 +247,21 @@ ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
                                              int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
                                              hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
-                             initial_state, y, last_state, batch, dim, dstate, seqlen, in_dtype,
+                             initial_state, y, last_state, batch, dim, dstate, seqlen, 1, in_dtype,
                              stream);
+}
+
+ssm_status ssm_selective_scan_fwd_grouped(ssm_handle handle, const void* u, const void* delta,
+                                          const float* A, const void* B, const void* C,
+                                          const float* D, const void* z,
+                                          const float* delta_bias, int delta_softplus,
+                                          const float* initial_state, void* y,
+                                          float* last_state, int64_t batch, int64_t dim,
+                                          int64_t dstate, int64_t seqlen, int64_t ngroups,
+                                          ssm_dtype in_dtype, hipStream_t stream) {
+  return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                             initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
+                             in_dtype, stream);
 }
 
 ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,
@@ -319,6 +341,7 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   f.chunk_states = nullptr;
   f.batch = (int)batch; f.dim = (int)dim; f.dstate = (int)dstate; f.seqlen = (int)seqlen;
   f.delta_softplus = delta_softplus ? 1 : 0;
+  f.ngroups = 1;
   p.dy = dy; p.dlast = dlast_state; p.du = du; p.ddelta = ddelta; p.dz = z ? dz : nullptr;
   p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.ddelta_bias = ddelta_bias;
   p.dh0 = dinitial_state; p.workspace = workspace;

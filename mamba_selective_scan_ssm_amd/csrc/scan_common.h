@@ -113,6 +113,17 @@ __device__ __forceinline__ void decode_raw(const RawSeg<In, K>& r, float (&out)[
   }
 }
 
+// Element I (compile-time) of a raw segment, widened to float.
+template <typename In, int K, int I>
+__device__ __forceinline__ float raw_elem(const RawSeg<In, K>& r) {
+  static_assert(I >= 0 && I < K, "element index");
+  if constexpr (sizeof(In) == 4) {
+    return __uint_as_float(r.w[I]);
+  } else {
+    return __uint_as_float((I & 1) ? (r.w[I / 2] & 0xffff0000u) : (r.w[I / 2] << 16));
+  }
+}
+
 template <typename In, int K>
 __device__ __forceinline__ void store_seg(In* __restrict__ p, int64_t base, int t0, int limit,
                                           const float (&v)[K]) {

@@ -58,7 +58,10 @@ using namespace scan;
 
 // NG: states per lane; LPC: lanes per row (NG*LPC >= dstate); T: steps per
 // time chunk.  Block = 256 threads = 4 waves of 64/LPC rows each.
-template <typename In, int NG, int LPC, int T>
+// RB = false: the workgroup's rows share one group's B and C, staged in LDS.
+// RB = true: every row reads its own group's B and C; each lane loads the
+// chunk of B and C for its own states into registers (no LDS, no barrier).
+template <typename In, int NG, int LPC, int T, bool RB = false>
 __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm) {
   constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
   constexpr int RPW = 64 / LPC;      // rows per wave
@@ -68,10 +71,10 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   static_assert(NG % 4 == 0 && T % EPU == 0 && T % LPC == 0, "tile shape");
   constexpr int UPR = T / EPU;       // 16-byte units per state row of a chunk
   constexpr int UNITS = 2 * NS * UPR;
-  constexpr int RB = (UNITS + 255) / 256;
+  constexpr int RBU = (UNITS + 255) / 256;
 
-  __shared__ alignas(16) float sB[2][T][NS];
-  __shared__ alignas(16) float sC[2][T][NS];
+  __shared__ alignas(16) float sB[RB ? 1 : 2][RB ? 1 : T][RB ? 4 : NS];
+  __shared__ alignas(16) float sC[RB ? 1 : 2][RB ? 1 : T][RB ? 4 : NS];
 
   const In* __restrict__ u = static_cast<const In*>(prm.u);
   const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
@@ -91,7 +94,11 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   const int L = prm.seqlen;
   const int N = prm.dstate;
   const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
-  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  // B, C of group g: [batch, ngroups, dstate, seqlen]; the group of the
+  // workgroup's first row (RB = false) or of this row (RB = true)
+  const int rpg = prm.dim / prm.ngroups;
+  const int grp = RB ? (row_ok ? d : 0) / rpg : (int)(blockIdx.x * RPB) / rpg;
+  const int64_t bc_base = ((int64_t)b * prm.ngroups + grp) * N * (int64_t)L;
 
   // Per-row constants for this lane's states n = slot*NG + k.
   float A2[NG];
@@ -111,9 +118,11 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
     h[k] = (prm.h0 && row_ok && n < N) ? prm.h0[((int64_t)b * prm.dim + d) * N + n] : 0.0f;
   }
 
-  // Raw chunk data, loaded one chunk ahead of its use.
+  // Raw chunk data, loaded one chunk ahead of its use.  RB: this row's B
+  // and C for the lane's states (decoded one element at a time when used).
   RawSeg<In, TS> ru, rd, rz;
-  RawSeg<In, EPU> rbc[RB];
+  RawSeg<In, EPU> rbc[RB ? 1 : RBU];
+  RawSeg<In, T> rBn[RB ? NG : 1], rCn[RB ? NG : 1];
   auto load_chunk = [&](int c0) {
     const int ts = c0 + slot * TS;
     if (row_ok) {
@@ -121,19 +130,34 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
       load_raw<In, TS>(dlt, row_base, ts, L, rd);
       if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
     }
+    if constexpr (RB) {
 #pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      const int e = tid + q * 256;
-      const int n = e % NS, rest = e / NS;
-      const int seg = rest % UPR, x = rest / UPR;
-      if (e < UNITS && n < N) {
-        load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, rbc[q]);
-      } else {
+      for (int k = 0; k < NG; ++k) {
+        const int n = slot * NG + k;
+        if (row_ok && n < N) {
+          load_raw<In, T>(Bm, bc_base + (int64_t)n * L, c0, L, rBn[k]);
+          load_raw<In, T>(Cm, bc_base + (int64_t)n * L, c0, L, rCn[k]);
+        } else {
 #pragma unroll
-        for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
+          for (int w = 0; w < RawSeg<In, T>::kWords; ++w) rBn[k].w[w] = rCn[k].w[w] = 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < RBU; ++q) {
+        const int e = tid + q * 256;
+        const int n = e % NS, rest = e / NS;
+        const int seg = rest % UPR, x = rest / UPR;
+        if (e < UNITS && n < N) {
+          load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, rbc[q]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
+        }
       }
     }
   };
+  RawSeg<In, T> rBr[RB ? NG : 1], rCr[RB ? NG : 1];  // RB: the current chunk's
 
   const int nchunks = (L + T - 1) / T;
   load_chunk(0);
@@ -148,18 +172,26 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
     }
 
     // -- B and C of this chunk into LDS as float32 [t][n] --------------------
+    if constexpr (RB) {
 #pragma unroll
-    for (int q = 0; q < RB; ++q) {
-      const int e = tid + q * 256;
-      if (e < UNITS) {
-        const int n = e % NS, rest = e / NS;
-        const int seg = rest % UPR, x = rest / UPR;
-        float v[EPU];
-        decode_raw<In, EPU>(rbc[q], v);
+      for (int k = 0; k < NG; ++k) {
+        rBr[k] = rBn[k];
+        rCr[k] = rCn[k];
+      }
+    } else {
 #pragma unroll
-        for (int i = 0; i < EPU; ++i) {
-          if (x) sC[buf][seg * EPU + i][n] = v[i];
-          else sB[buf][seg * EPU + i][n] = v[i];
+      for (int q = 0; q < RBU; ++q) {
+        const int e = tid + q * 256;
+        if (e < UNITS) {
+          const int n = e % NS, rest = e / NS;
+          const int seg = rest % UPR, x = rest / UPR;
+          float v[EPU];
+          decode_raw<In, EPU>(rbc[q], v);
+#pragma unroll
+          for (int i = 0; i < EPU; ++i) {
+            if (x) sC[buf][seg * EPU + i][n] = v[i];
+            else sB[buf][seg * EPU + i][n] = v[i];
+          }
         }
       }
     }
@@ -195,7 +227,7 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
       for (int j = 0; j < TS; ++j) du[j] = dl[j] * uk[j];
     }
     if (ch + 1 < nchunks) load_chunk(c0 + T);
-    __syncthreads();
+    if constexpr (!RB) __syncthreads();
 
     // -- recurrence over the chunk ([EXPLAINED] eq. (7)) -----------------------
     float yp[T];
@@ -212,10 +244,19 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
       float acc = 0.0f;
 #pragma unroll
       for (int k4 = 0; k4 < NG; k4 += 4) {
-        const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG + k4]);
-        const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
-        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-        const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+        float bv[4], cv[4];
+        if constexpr (RB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bv[i] = raw_elem<In, T, t>(rBr[k4 + i]);
+            cv[i] = raw_elem<In, T, t>(rCr[k4 + i]);
+          }
+        } else {
+          const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG + k4]);
+          const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
+          bv[0] = bq.x; bv[1] = bq.y; bv[2] = bq.z; bv[3] = bq.w;
+          cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a = fast_exp2(dt * A2[k4 + i]);
@@ -318,7 +359,9 @@ selective_scan_split_kernel(ScanParams prm) {
   const int L = prm.seqlen;
   const int N = prm.dstate;
   const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
-  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  // B, C of the group of the workgroup's rows: [batch, ngroups, dstate, seqlen]
+  const int grp = (int)(blockIdx.x * 64) / (prm.dim / prm.ngroups);
+  const int64_t bc_base = ((int64_t)b * prm.ngroups + grp) * N * (int64_t)L;
 
   // Per-row constants for this wave's states.
   float A2[NG];
@@ -513,11 +556,12 @@ selective_scan_split_kernel(ScanParams prm) {
   }
 }
 
-template <typename In, int NG, int LPC, int T>
+template <typename In, int NG, int LPC, int T, bool RB = false>
 hipError_t launch_rows(const ScanParams& p, hipStream_t stream) {
   constexpr int RPB = 4 * (64 / LPC);
   dim3 grid((unsigned)((p.dim + RPB - 1) / RPB), (unsigned)p.batch);
-  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T>), grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T, RB>), grid, dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
@@ -561,6 +605,30 @@ hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_
 hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
                                  hipStream_t stream) {
   return bf16 ? launch_typed<uint16_t>(p, tile, stream) : launch_typed<float>(p, tile, stream);
+}
+
+int scan_tile_rows(const ScanTile& tile) {
+  switch (tile.id) {
+    case ScanTileId::kN4_Seq: return 256;
+    case ScanTileId::kN8_Seq: return 128;
+    case ScanTileId::kN16_Seq: case ScanTileId::kN64_Seq: return 64;
+    default: return 64;  // time-split kernels: 64 rows per workgroup
+  }
+}
+
+// Per-row B and C: chunks of 16 bf16 / 8 float32 steps for 4 states per
+// lane (the raw B and C of a chunk stay in registers), half that for 16.
+hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream) {
+  if (bf16) {
+    if (p.dstate <= 4) return launch_rows<uint16_t, 4, 1, 16, true>(p, stream);
+    if (p.dstate <= 8) return launch_rows<uint16_t, 4, 2, 16, true>(p, stream);
+    if (p.dstate <= 16) return launch_rows<uint16_t, 4, 4, 16, true>(p, stream);
+    return launch_rows<uint16_t, 16, 4, 8, true>(p, stream);
+  }
+  if (p.dstate <= 4) return launch_rows<float, 4, 1, 8, true>(p, stream);
+  if (p.dstate <= 8) return launch_rows<float, 4, 2, 8, true>(p, stream);
+  if (p.dstate <= 16) return launch_rows<float, 4, 4, 8, true>(p, stream);
+  return launch_rows<float, 16, 4, 4, true>(p, stream);
 }
 
 }  // namespace ssm

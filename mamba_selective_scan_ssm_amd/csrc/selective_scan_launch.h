@@ -27,6 +27,8 @@ struct ScanParams {
   int dstate;
   int seqlen;
   int delta_softplus;
+  int ngroups;              // B, C: [batch, ngroups, dstate, seqlen]; channel d
+                            // reads group d / (dim / ngroups)
 };
 
 // Compiled kernel shapes.  "Seq": each wave runs the whole sequence for its
@@ -43,6 +45,15 @@ struct ScanTile {
 
 hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
                                  hipStream_t stream);
+
+// Rows one workgroup of `tile` covers; with ngroups > 1 the tile's kernels
+// read one group per workgroup, so dim / ngroups must be a multiple of it,
+// else launch_selective_scan_rowbc is used.
+int scan_tile_rows(const ScanTile& tile);
+
+// Row-parallel kernel that reads B and C per row (any ngroups dividing dim,
+// e.g. ngroups = dim: per-channel B and C).
+hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream);
 
 // Forward pass that saves the state entering every 16-step chunk into
 // p.chunk_states (dstate <= 16; y and last_state may be null).

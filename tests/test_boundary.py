@@ -164,3 +164,26 @@ def test_state_update_checks():
     assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg
     st, msg = step(state=P[9] + 4)           # misaligned
     assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg
+
+
+def scan_grouped(ngroups, B=P[3], C=P[4], y=P[5], dim=4, seqlen=8):
+    lib = ssm.load_library()
+    st = lib.ssm_selective_scan_fwd_grouped(None, P[0], P[1], P[2], B, C, None, None, None, 1,
+                                            None, y, None, 2, dim, 4, seqlen, ngroups,
+                                            ssm.SSM_F32, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_grouped_rules():
+    for g in (1, 2, 4):  # divisors of dim pass every check up to the handle
+        st, msg = scan_grouped(g)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, (g, msg)
+    for g in (0, -1, 3, 8):
+        st, msg = scan_grouped(g)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "ngroups" in msg, (g, msg)
+    # B spans batch * ngroups * dstate * seqlen elements: with 4 groups of
+    # 4 states, B (2*4*4*8 floats = 1 KiB) reaches an output 512 bytes on
+    st, msg = scan_grouped(4, y=P[3] + 512)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg, msg
+    st, msg = scan_grouped(1, y=P[3] + 512)  # one group: 512 bytes, no overlap
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, msg

@@ -216,6 +216,65 @@ def test_initial_state(lib, shape, dtype):
     check("last_state", synth.to_host_f64(ls).reshape(b * d, -1), rs, dtype, f32_rel=True)
 
 
+# ---------------------------------------------------------------------------
+# Grouped and per-channel B, C (ssm_selective_scan_fwd_grouped)
+# ---------------------------------------------------------------------------
+
+def grouped_inputs(seed, b, d, n, L, G, dtype):
+    x = make_inputs(seed, b, d, n, L, dtype)
+    rng = np.random.default_rng(seed + 1000)
+    for k in ("B", "C"):
+        v = rng.standard_normal((b, G, n, L)).astype(np.float32)
+        x[k] = synth.round_bf16(v) if dtype == "bf16" else v
+    return x
+
+
+GROUPED = [  # (batch, dim, dstate, seqlen, ngroups, dtype): which kernel
+    ((2, 70, 1, 300, 70), "f32"),     # per channel, one lane per row
+    ((1, 130, 4, 257, 130), "bf16"),  # per channel, one lane per row
+    ((2, 33, 8, 100, 33), "f32"),     # per channel, two lanes per row
+    ((1, 129, 16, 333, 129), "bf16"),  # per channel, four lanes per row
+    ((1, 129, 16, 61, 129), "f32"),
+    ((2, 40, 64, 77, 40), "bf16"),    # per channel, sixteen states per lane
+    ((2, 40, 33, 50, 40), "f32"),
+    ((2, 96, 16, 200, 3), "bf16"),    # groups of 32 rows: per-row reads
+    ((2, 512, 16, 300, 2), "f32"),    # groups of 256 rows, time-split kernel
+    ((8, 2048, 16, 160, 4), "bf16"),  # groups of 512 rows, row-parallel kernel
+    ((16, 4096, 4, 90, 2), "bf16"),   # one lane per row, 256-row workgroups
+]
+
+
+@pytest.mark.parametrize("case", GROUPED)
+def test_grouped_B_C(lib, case):
+    """B, C per group of channels; ngroups = dim is the per-channel form of
+    the task-spec page's reference kernel.  Every y and last_state entry."""
+    (b, d, n, L, G), dtype = case
+    print(f"case grouped {case}", flush=True)
+    x = grouped_inputs(200 + n, b, d, n, L, G, dtype)
+    compare_full(lib, x, dtype, label=f"grouped {case}")
+
+
+def test_grouped_with_initial_state(lib):
+    b, d, n, L, G = 2, 96, 16, 200, 3
+    print("case grouped initial state", flush=True)
+    x = grouped_inputs(77, b, d, n, L, G, "f32")
+    h0 = np.random.default_rng(78).standard_normal((b, d, n)).astype(np.float32)
+    y, ls = run_gpu_h0(lib, x, "f32", h0)
+    ry, rs = oracle.selective_scan(**x, h0=h0.astype(np.float64))
+    check("y", synth.to_host_f64(y).reshape(b * d, L), ry, "f32", f32_rel=True)
+    check("last_state", synth.to_host_f64(ls).reshape(b * d, -1), rs, "f32", f32_rel=True)
+
+
+def test_one_group_axis_is_the_plain_call(lib):
+    """ngroups = 1 through the grouped entry point gives the plain call's
+    bits."""
+    x = make_inputs(91, 4, 300, 16, 130, "bf16")
+    y0, s0 = run_gpu(lib, x, "bf16")
+    xg = dict(x, B=x["B"][:, None], C=x["C"][:, None])
+    y1, s1 = run_gpu(lib, xg, "bf16")
+    assert torch.equal(y0, y1) and torch.equal(s0, s1)
+
+
 @pytest.mark.parametrize("k", [100, 128])
 def test_scan_in_pieces(lib, k):
     """A sequence scanned in two calls, the second starting from the first
