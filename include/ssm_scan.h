@@ -160,6 +160,49 @@ ssm_status ssm_selective_scan_fwd_grouped(
     int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * Bytes of workspace that ssm_selective_scan_fwd_ws can use for these
+ * sizes: 0 when the (batch, channel) rows alone give every SIMD of the
+ * device two waves (then no workspace is needed), else the room for one
+ * aggregate (prod a, v) per (segment, row, state) of a time split
+ * ([EXPLAINED] eqs. (10)-(11)).  Same size checks as
+ * ssm_selective_scan_fwd_grouped; touches no device memory.
+ */
+ssm_status ssm_selective_scan_fwd_workspace_size(ssm_handle handle,
+                                                 int64_t batch, int64_t dim,
+                                                 int64_t dstate, int64_t seqlen,
+                                                 int64_t ngroups,
+                                                 size_t *bytes);
+
+/*
+ * ssm_selective_scan_fwd_grouped with a caller-owned device workspace.
+ * When the workspace size above is non-zero and workspace is given, the
+ * sequence is cut into time segments: a first launch scans every segment
+ * from the identity and stores its aggregate (prod a, v) per (row, state)
+ * in the workspace; a second launch folds, for each segment, the
+ * aggregates before it onto the initial state with the combine operator
+ * of [EXPLAINED] eq. (10) and rescans the segment from that carry-in,
+ * writing y.  This fills the device for small batches and long sequences.
+ * The result equals the unsplit call's up to float32 rounding.
+ *
+ *   workspace       : device memory, 16-byte aligned, nullable (NULL = no
+ *                     split: the call is ssm_selective_scan_fwd_grouped);
+ *                     overwritten; must not overlap any input or output.
+ *   workspace_bytes : its size; below the size above (with workspace
+ *                     given and a split planned) is SSM_ERR_INVALID_ARG.
+ * No split is made when initial_state is last_state (in place), nor when
+ * a group of channels does not cover whole workgroups (64 to 256 rows).
+ * Every other argument, layout, limit and error is as for
+ * ssm_selective_scan_fwd_grouped.
+ */
+ssm_status ssm_selective_scan_fwd_ws(
+    ssm_handle handle, const void *u, const void *delta, const float *A,
+    const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, const float *initial_state,
+    void *y, float *last_state, int64_t batch, int64_t dim, int64_t dstate,
+    int64_t seqlen, int64_t ngroups, void *workspace, size_t workspace_bytes,
+    ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * Workspace size in bytes needed by ssm_selective_scan_bwd for these sizes
  * (caller-allocated).  Same size checks as ssm_selective_scan_bwd.
  */

@@ -27,7 +27,8 @@ SSM_F32, SSM_BF16 = 0, 1
 # Every symbol declared in include/ssm_scan.h.
 EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
-           "ssm_selective_scan_fwd_grouped",
+           "ssm_selective_scan_fwd_grouped", "ssm_selective_scan_fwd_workspace_size",
+           "ssm_selective_scan_fwd_ws",
            "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
            "ssm_selective_scan_bwd",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
@@ -78,6 +79,13 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_scan_fwd_grouped.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
             _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_scan_fwd_workspace_size.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_workspace_size.argtypes = [
+            _vp, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_selective_scan_fwd_ws.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_ws.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_size_t, ctypes.c_int, _vp]
         lib.ssm_selective_state_update.restype = ctypes.c_int
         lib.ssm_selective_state_update.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
@@ -243,14 +251,64 @@ def ssm_selective_scan_fwd_grouped(u, delta, A, B, C, D, z, delta_bias, delta_so
     _check("ssm_selective_scan_fwd_grouped", st)
 
 
+def ssm_selective_scan_fwd_workspace_size(batch, dim, dstate, seqlen, ngroups=1, device=0,
+                                          handle=None) -> int:
+    """Workspace bytes ssm_selective_scan_fwd_ws can use (0: none needed)."""
+    if handle is None:
+        handle = get_handle(device)
+    out = ctypes.c_size_t(0)
+    st = load_library().ssm_selective_scan_fwd_workspace_size(
+        handle, batch, dim, dstate, seqlen, ngroups, ctypes.byref(out))
+    _check("ssm_selective_scan_fwd_workspace_size", st)
+    return int(out.value)
+
+
+def ssm_selective_scan_fwd_ws(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                              initial_state, y, last_state, workspace, handle=None) -> None:
+    """ssm_selective_scan_fwd_grouped with a device workspace (uint8 tensor or
+    None).  B, C: [batch, dstate, seqlen] or [batch, ngroups, dstate, seqlen]."""
+    for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
+                         ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
+                         ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
+                         ("y", y, False), ("last_state", last_state, True),
+                         ("workspace", workspace, True)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    ngroups = B.shape[1] if B.dim() == 4 else 1
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().ssm_selective_scan_fwd_ws(
+        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(y),
+        _ptr(last_state), batch, dim, dstate, seqlen, ngroups, _ptr(workspace), nbytes,
+        _dtype_code(u), _stream_ptr(u.device))
+    _check("ssm_selective_scan_fwd_ws", st)
+
+
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                       delta_softplus=True, return_last_state=True, initial_state=None):
+                       delta_softplus=True, return_last_state=True, initial_state=None,
+                       time_split=True):
     """Allocating form: returns (y, last_state or None).  B and C are
-    [batch, dstate, seqlen], or [batch, ngroups, dstate, seqlen] (grouped)."""
+    [batch, dstate, seqlen], or [batch, ngroups, dstate, seqlen] (grouped).
+    With time_split, a workspace is allocated when the rows alone would
+    leave the device idle (ssm_selective_scan_fwd_ws)."""
     import torch
     y = torch.empty_like(u)
     ls = (torch.empty((u.shape[0], u.shape[1], A.shape[1]), dtype=torch.float32,
                       device=u.device) if return_last_state else None)
+    if time_split:
+        ngroups = B.shape[1] if B.dim() == 4 else 1
+        dev = u.device.index if u.device.index is not None else 0
+        nbytes = ssm_selective_scan_fwd_workspace_size(u.shape[0], u.shape[1], A.shape[1],
+                                                       u.shape[2], ngroups, device=dev)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=u.device)
+            ssm_selective_scan_fwd_ws(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                      initial_state, y, ls, ws)
+            return y, ls
     if B.dim() == 4:
         ssm_selective_scan_fwd_grouped(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                                        initial_state, y, ls)

@@ -160,7 +160,8 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
                                const void* z, const float* delta_bias, int delta_softplus,
                                const float* initial_state, void* y, float* last_state,
                                int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                               int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream) {
+                               int64_t ngroups, void* workspace, size_t workspace_bytes,
+                               ssm_dtype in_dtype, hipStream_t stream) {
   // ---- sizes -------------------------------------------------------------
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
@@ -197,10 +198,21 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
                      {"C", C, nbc * es},           {"D", D, (uint64_t)dim * 4},
                      {"z", z, nrow * es},          {"delta_bias", delta_bias, (uint64_t)dim * 4},
                      {"initial_state", in_place ? nullptr : initial_state, state_bytes}};
-  const Span out[] = {{"y", y, nrow * es}, {"last_state", last_state, state_bytes}};
-  ssm_status st = check_spans(in, 9, out, 2);
+  const Span out[] = {{"y", y, nrow * es}, {"last_state", last_state, state_bytes},
+                      {"workspace", workspace, workspace_bytes}};
+  ssm_status st = check_spans(in, 9, out, 3);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  // time segments when the rows alone leave SIMDs idle and a workspace is
+  // given (groups must cover whole workgroups of the row-parallel kernel)
+  ssm::ScanSegments sg = ssm::plan_scan_segments(batch, dim, dstate, seqlen, handle->num_cus);
+  if (ngroups > 1 && (dim / ngroups) % sg.rows_per_workgroup != 0) sg.nseg = 1;
+  // (not in place: the last segment writes last_state while other segments
+  // may still have to read the initial state)
+  const bool segmented = sg.nseg > 1 && workspace != nullptr && !in_place;
+  if (segmented && workspace_bytes < sg.bytes)
+    return fail(SSM_ERR_INVALID_ARG, "workspace_bytes %zu < %zu needed", workspace_bytes,
+                sg.bytes);
 
   // ---- launch ------------------------------------------------------------
   ssm::ScanParams p;
@@ -217,8 +229,15 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   // A group covering whole workgroups of the tile: its B and C are staged
   // once per workgroup; otherwise every row reads its own.
   const bool whole = (dim / ngroups) % ssm::scan_tile_rows(tile) == 0;
-  hipError_t e = (ngroups == 1 || whole) ? ssm::launch_selective_scan(p, tile, bf16, stream)
-                                         : ssm::launch_selective_scan_rowbc(p, bf16, stream);
+  hipError_t e;
+  if (segmented) {
+    p.seg_agg = static_cast<float*>(workspace);
+    e = ssm::launch_selective_scan_segmented(p, sg, bf16, stream);
+  } else if (ngroups == 1 || whole) {
+    e = ssm::launch_selective_scan(p, tile, bf16, stream);
+  } else {
+    e = ssm::launch_selective_scan_rowbc(p, bf16, stream);
+  }
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -234,8 +253,8 @@ ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* 
                                   int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
                                   hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
-                             nullptr, y, last_state, batch, dim, dstate, seqlen, 1, in_dtype,
-                             stream);
+                             nullptr, y, last_state, batch, dim, dstate, seqlen, 1, nullptr, 0,
+                             in_dtype, stream);
 }
 
 ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
@@ -247,8 +266,8 @@ ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
                                              int64_t dstate, int64_t seqlen, ssm_dtype in_dtype,
                                              hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
-                             initial_state, y, last_state, batch, dim, dstate, seqlen, 1, in_dtype,
-                             stream);
+                             initial_state, y, last_state, batch, dim, dstate, seqlen, 1, nullptr,
+                             0, in_dtype, stream);
 }
 
 ssm_status ssm_selective_scan_fwd_grouped(ssm_handle handle, const void* u, const void* delta,
@@ -261,7 +280,37 @@ ssm_status ssm_selective_scan_fwd_grouped(ssm_handle handle, const void* u, cons
                                           ssm_dtype in_dtype, hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
-                             in_dtype, stream);
+                             nullptr, 0, in_dtype, stream);
+}
+
+ssm_status ssm_selective_scan_fwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,
+                                                 int64_t dstate, int64_t seqlen, int64_t ngroups,
+                                                 size_t* bytes) {
+  if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
+  if (ngroups <= 0 || dim % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
+                (long long)ngroups, (long long)dim);
+  if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  const ssm::ScanSegments sg = ssm::plan_scan_segments(batch, dim, dstate, seqlen, handle->num_cus);
+  if (sg.nseg > 1 && (ngroups == 1 || (dim / ngroups) % sg.rows_per_workgroup == 0))
+    *bytes = sg.bytes;
+  return ok();
+}
+
+ssm_status ssm_selective_scan_fwd_ws(ssm_handle handle, const void* u, const void* delta,
+                                     const float* A, const void* B, const void* C, const float* D,
+                                     const void* z, const float* delta_bias, int delta_softplus,
+                                     const float* initial_state, void* y, float* last_state,
+                                     int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                     int64_t ngroups, void* workspace, size_t workspace_bytes,
+                                     ssm_dtype in_dtype, hipStream_t stream) {
+  return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                             initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
+                             workspace, workspace_bytes, in_dtype, stream);
 }
 
 ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,

@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "device_math.h"
 #include "scan_common.h"
 #include "selective_scan_launch.h"
@@ -61,7 +63,15 @@ using namespace scan;
 // RB = false: the workgroup's rows share one group's B and C, staged in LDS.
 // RB = true: every row reads its own group's B and C; each lane loads the
 // chunk of B and C for its own states into registers (no LDS, no barrier).
-template <typename In, int NG, int LPC, int T, bool RB = false>
+// With prm.seg_len > 0 the sequence is cut into segments of seg_len steps,
+// blockIdx.z selecting one ([EXPLAINED] eq. (11): any regrouping of the
+// combine operator gives the same result):
+//   AGG = true:  scan the segment from the identity (1, 0) and write its
+//                aggregate (prod a, v) per (row, state) to prm.seg_agg;
+//   AGG = false: fold the aggregates of the earlier segments onto the
+//                initial state (the segment's carry-in), then scan the
+//                segment and write its y (and, for the last one, last_state).
+template <typename In, int NG, int LPC, int T, bool RB = false, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm) {
   constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
   constexpr int RPW = 64 / LPC;      // rows per wave
@@ -90,9 +100,15 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   const int b = blockIdx.y;
   const int d = blockIdx.x * RPB + wv * RPW + lane / LPC;
   const bool row_ok = d < prm.dim;
-  const bool has_z = z != nullptr;
+  const bool has_z = !AGG && z != nullptr;
   const int L = prm.seqlen;
   const int N = prm.dstate;
+  // time window of this workgroup: segment blockIdx.z, or the whole sequence
+  const int seg = RB ? 0 : blockIdx.z;  // (per-row B, C is never split in time)
+  const int t_begin = (!RB && prm.seg_len) ? seg * prm.seg_len : 0;
+  const int t_end = (!RB && prm.seg_len) ? min(L, t_begin + prm.seg_len) : L;
+  const int64_t nrows = (int64_t)prm.batch * prm.dim;
+  const int64_t rowi = (int64_t)b * prm.dim + (row_ok ? d : 0);
   const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
   // B, C of group g: [batch, ngroups, dstate, seqlen]; the group of the
   // workgroup's first row (RB = false) or of this row (RB = true)
@@ -110,13 +126,29 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
   const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
 
-  // State: the initial state v_0 of [EXPLAINED] eqs. (8)-(9) when given.
+  // State: the initial state v_0 of [EXPLAINED] eqs. (8)-(9) when given
+  // (a segment's aggregate starts from the identity instead).
   float h[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
     const int n = slot * NG + k;
-    h[k] = (prm.h0 && row_ok && n < N) ? prm.h0[((int64_t)b * prm.dim + d) * N + n] : 0.0f;
+    h[k] = (!AGG && prm.h0 && row_ok && n < N) ? prm.h0[rowi * N + n] : 0.0f;
   }
+  if constexpr (!AGG && !RB) {  // (per-row B, C is never split in time)
+    // carry-in of a later segment: (v_0) (+) agg_0 (+) ... (+) agg_{seg-1},
+    // each step h = P h + V with the combine operator of [EXPLAINED] eq. (10)
+    if (seg > 0 && row_ok) {
+      for (int s2 = 0; s2 < seg; ++s2) {
+        const float* ag = prm.seg_agg + ((int64_t)s2 * nrows + rowi) * N * 2;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+          const int n = slot * NG + k;
+          if (n < N) h[k] = __builtin_fmaf(ag[2 * n], h[k], ag[2 * n + 1]);
+        }
+      }
+    }
+  }
+  float dsum = 0.0f;  // AGG: sum of delta over the segment (prod a = exp2(A2 dsum))
 
   // Raw chunk data, loaded one chunk ahead of its use.  RB: this row's B
   // and C for the lane's states (decoded one element at a time when used).
@@ -159,12 +191,12 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   };
   RawSeg<In, T> rBr[RB ? NG : 1], rCr[RB ? NG : 1];  // RB: the current chunk's
 
-  const int nchunks = (L + T - 1) / T;
-  load_chunk(0);
+  const int nchunks = (t_end - t_begin + T - 1) / T;
+  load_chunk(t_begin);
   for (int ch = 0; ch < nchunks; ++ch) {
-    const int c0 = ch * T;
+    const int c0 = t_begin + ch * T;
     const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
-    if (prm.chunk_states && row_ok) {  // state entering the chunk, for the backward pass
+    if (!AGG && prm.chunk_states && row_ok) {  // state entering the chunk, for the backward pass
       float* cs = prm.chunk_states + (((int64_t)b * prm.dim + d) * nchunks + ch) * N;
 #pragma unroll
       for (int k = 0; k < NG; ++k)
@@ -242,6 +274,7 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
         dut = du[t];
       }
       float acc = 0.0f;
+      if constexpr (AGG) dsum += dt;
 #pragma unroll
       for (int k4 = 0; k4 < NG; k4 += 4) {
         float bv[4], cv[4];
@@ -253,19 +286,22 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
           }
         } else {
           const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG + k4]);
-          const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
           bv[0] = bq.x; bv[1] = bq.y; bv[2] = bq.z; bv[3] = bq.w;
-          cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
+          if constexpr (!AGG) {
+            const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
+            cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a = fast_exp2(dt * A2[k4 + i]);
           h[k4 + i] = __builtin_fmaf(a, h[k4 + i], dut * bv[i]);
-          acc = __builtin_fmaf(cv[i], h[k4 + i], acc);
+          if constexpr (!AGG) acc = __builtin_fmaf(cv[i], h[k4 + i], acc);
         }
       }
       yp[t] = acc;
     });
+    if constexpr (AGG) continue;  // an aggregate has no output
 
     // -- sum the group's partial readouts onto the owners of the steps ---------
     float yo[TS];
@@ -303,8 +339,23 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
     if (row_ok && y) store_seg<In, TS>(y, row_base, ts, L, yo);
   }
 
+  if constexpr (AGG) {
+    // the segment's aggregate (prod a, v) = (exp2(A2 * sum delta), h)
+    if (row_ok) {
+      float* ag = prm.seg_agg + ((int64_t)seg * nrows + rowi) * N * 2;
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        const int n = slot * NG + k;
+        if (n < N) {
+          ag[2 * n] = fast_exp2(A2[k] * dsum);
+          ag[2 * n + 1] = h[k];
+        }
+      }
+    }
+    return;
+  }
   // -- final state -------------------------------------------------------------
-  if (prm.last_state && row_ok) {
+  if (prm.last_state && row_ok && t_end == L) {
     float* ls = prm.last_state + ((int64_t)b * prm.dim + d) * N;
 #pragma unroll
     for (int k = 0; k < NG; ++k)
@@ -556,12 +607,12 @@ selective_scan_split_kernel(ScanParams prm) {
   }
 }
 
-template <typename In, int NG, int LPC, int T, bool RB = false>
-hipError_t launch_rows(const ScanParams& p, hipStream_t stream) {
+template <typename In, int NG, int LPC, int T, bool RB = false, bool AGG = false>
+hipError_t launch_rows(const ScanParams& p, hipStream_t stream, int nz = 1) {
   constexpr int RPB = 4 * (64 / LPC);
-  dim3 grid((unsigned)((p.dim + RPB - 1) / RPB), (unsigned)p.batch);
-  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T, RB>), grid, dim3(256), 0, stream,
-                     p);
+  dim3 grid((unsigned)((p.dim + RPB - 1) / RPB), (unsigned)p.batch, (unsigned)nz);
+  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T, RB, AGG>), grid, dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -605,6 +656,52 @@ hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_
 hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
                                  hipStream_t stream) {
   return bf16 ? launch_typed<uint16_t>(p, tile, stream) : launch_typed<float>(p, tile, stream);
+}
+
+// Row-parallel shape per dstate tier: (NG, LPC, T) = (4,1,16) / (4,2,32) /
+// (4,4,64) / (16,4,32) for dstate <= 4 / 8 / 16 / 64.
+template <typename In, bool AGG>
+hipError_t launch_rows_tier(const ScanParams& p, hipStream_t s, int nz) {
+  if (p.dstate <= 4) return launch_rows<In, 4, 1, 16, false, AGG>(p, s, nz);
+  if (p.dstate <= 8) return launch_rows<In, 4, 2, 32, false, AGG>(p, s, nz);
+  if (p.dstate <= 16) return launch_rows<In, 4, 4, 64, false, AGG>(p, s, nz);
+  return launch_rows<In, 16, 4, 32, false, AGG>(p, s, nz);
+}
+
+ScanSegments plan_scan_segments(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                int num_cus) {
+  const int lpc = dstate <= 4 ? 1 : dstate <= 8 ? 2 : 4;
+  const int T = dstate <= 4 ? 16 : dstate <= 8 ? 32 : dstate <= 16 ? 64 : 32;
+  const int rpb = 256 / lpc;
+  ScanSegments sg{1, 0, rpb, 0};
+  // Split only when the rows leave SIMDs without a wave (the aggregate pass
+  // costs about half a scan of the segments it covers) and the sequence has
+  // at least 8 chunks; aim at two waves per SIMD.
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t waves = batch * ((dim + rpb - 1) / rpb) * 4;
+  const int64_t target = 8 * cus;
+  const int64_t chunks = (seqlen + T - 1) / T;
+  if (waves >= 4 * cus || chunks < 8) return sg;
+  const int64_t want = std::min<int64_t>({(target + waves - 1) / waves, chunks, 64});
+  if (want <= 1) return sg;
+  const int64_t seg_len = ((seqlen + want - 1) / want + T - 1) / T * T;
+  const int64_t nseg = (seqlen + seg_len - 1) / seg_len;
+  if (nseg <= 1) return sg;
+  sg.nseg = (int)nseg;
+  sg.seg_len = (int)seg_len;
+  sg.bytes = (size_t)(nseg - 1) * (size_t)batch * (size_t)dim * (size_t)dstate * 2 * sizeof(float);
+  return sg;
+}
+
+hipError_t launch_selective_scan_segmented(const ScanParams& p0, const ScanSegments& sg, bool bf16,
+                                           hipStream_t stream) {
+  ScanParams p = p0;
+  p.seg_len = sg.seg_len;
+  hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(p, stream, sg.nseg - 1)
+                      : launch_rows_tier<float, true>(p, stream, sg.nseg - 1);
+  if (e != hipSuccess) return e;
+  return bf16 ? launch_rows_tier<uint16_t, false>(p, stream, sg.nseg)
+              : launch_rows_tier<float, false>(p, stream, sg.nseg);
 }
 
 int scan_tile_rows(const ScanTile& tile) {

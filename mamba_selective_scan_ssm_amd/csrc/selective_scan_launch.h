@@ -29,6 +29,8 @@ struct ScanParams {
   int delta_softplus;
   int ngroups;              // B, C: [batch, ngroups, dstate, seqlen]; channel d
                             // reads group d / (dim / ngroups)
+  int seg_len = 0;          // > 0: time segments of this many steps (grid.z)
+  float* seg_agg = nullptr; // [nseg-1, batch*dim, dstate, 2] segment aggregates
 };
 
 // Compiled kernel shapes.  "Seq": each wave runs the whole sequence for its
@@ -54,6 +56,20 @@ int scan_tile_rows(const ScanTile& tile);
 // Row-parallel kernel that reads B and C per row (any ngroups dividing dim,
 // e.g. ngroups = dim: per-channel B and C).
 hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream);
+
+// Time segments for shapes whose rows alone leave SIMDs without a wave:
+// nseg segments of seg_len steps each (nseg = 1: no split), run by the
+// row-parallel kernel in two launches (segment aggregates, then each segment
+// from its carry-in), with `bytes` of workspace for the aggregates.
+struct ScanSegments {
+  int nseg, seg_len, rows_per_workgroup;
+  size_t bytes;
+};
+ScanSegments plan_scan_segments(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                int num_cus);
+// p.seg_agg must point at sg.bytes of workspace.
+hipError_t launch_selective_scan_segmented(const ScanParams& p, const ScanSegments& sg, bool bf16,
+                                           hipStream_t stream);
 
 // Forward pass that saves the state entering every 16-step chunk into
 // p.chunk_states (dstate <= 16; y and last_state may be null).

@@ -37,14 +37,15 @@ def lib():
     return ssm
 
 
-def run_gpu(ssm, x, dtype, softplus=True, want_state=True):
+def run_gpu(ssm, x, dtype, softplus=True, want_state=True, time_split=True):
     dev = "cuda"
     t = {k: (None if v is None else synth.to_device(v, dtype if k in ("u", "delta", "z", "B", "C")
                                                      else "f32", dev))
          for k, v in x.items()}
     y, ls = ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
                                    z=t["z"], delta_bias=t["delta_bias"],
-                                   delta_softplus=softplus, return_last_state=want_state)
+                                   delta_softplus=softplus, return_last_state=want_state,
+                                   time_split=time_split)
     torch.cuda.synchronize()
     return y, ls
 
@@ -69,9 +70,9 @@ def check(name, got, ref, dtype, f32_rel=False):
         assert rel_l2 <= BF16_REL, f"{name}: relative L2 error {rel_l2:.3e}"
 
 
-def compare_full(ssm, x, dtype, softplus=True, label=""):
+def compare_full(ssm, x, dtype, softplus=True, label="", time_split=True):
     print(f"case {label}", flush=True)
-    y, ls = run_gpu(ssm, x, dtype, softplus)
+    y, ls = run_gpu(ssm, x, dtype, softplus, time_split=time_split)
     ry, rs = oracle.selective_scan(**x, delta_softplus=softplus)
     b, d, L = x["u"].shape
     check("y", synth.to_host_f64(y).reshape(b * d, L), ry, dtype)
@@ -91,15 +92,18 @@ def test_tiny_config(lib):
     compare_full(lib, synth.mamba1_inputs(cfg, seed=0), "f32", label="tiny")
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("shape", [tuple(s) for s in SPEC["shapes_batch_dim_seqlen"]])
 @pytest.mark.parametrize("dstate", SPEC["dstates"])
 @pytest.mark.parametrize("gate", [False, True])
-def test_spec_matrix(lib, shape, dstate, gate):
-    """The exercise spec's correctness matrix at its float32 tolerance."""
+def test_spec_matrix(lib, shape, dstate, gate, split):
+    """The exercise spec's correctness matrix at its float32 tolerance, with
+    and without the time split across workgroups (small batches use it)."""
     b, d, L = shape
     x = make_inputs(100 + dstate, b, d, dstate, L, "f32", gate=gate, bias=False,
                     delta_std=1.0)
-    compare_full(lib, x, "f32", label=f"spec {shape} N={dstate} gate={gate}")
+    compare_full(lib, x, "f32", label=f"spec {shape} N={dstate} gate={gate} split={split}",
+                 time_split=split)
 
 
 EDGE = [  # (batch, dim, dstate, seqlen)
@@ -273,6 +277,70 @@ def test_one_group_axis_is_the_plain_call(lib):
     xg = dict(x, B=x["B"][:, None], C=x["C"][:, None])
     y1, s1 = run_gpu(lib, xg, "bf16")
     assert torch.equal(y0, y1) and torch.equal(s0, s1)
+
+
+# ---------------------------------------------------------------------------
+# Time split across workgroups (ssm_selective_scan_fwd_ws)
+# ---------------------------------------------------------------------------
+
+SPLIT = [  # (batch, dim, dstate, seqlen, dtype): every dstate tier, ragged sizes
+    ((1, 256, 16, 2048), "f32"),   # the spec page's speed-up shape
+    ((1, 70, 3, 1000), "bf16"),    # one lane per row, ragged rows
+    ((2, 33, 8, 777), "f32"),      # two lanes per row, odd length
+    ((1, 40, 64, 500), "bf16"),    # sixteen states per lane
+    ((3, 100, 16, 600), "f32"),    # segments of one chunk, a short last one
+    ((1, 5, 16, 520), "f32"),      # last segment of 8 steps
+]
+
+
+@pytest.mark.parametrize("case", SPLIT)
+def test_time_split(lib, case):
+    """Segments scanned from the identity, carried in with the combine
+    operator, rescanned: every y and last_state entry against the oracle.
+    The split regroups the float32 arithmetic, so float32 uses the
+    magnitude-aware bound 1e-5 * (1 + |ref|)."""
+    (b, d, n, L), dtype = case
+    nbytes = lib.ssm_selective_scan_fwd_workspace_size(b, d, n, L)
+    print(f"case time split {case} workspace {nbytes}", flush=True)
+    assert nbytes > 0, "these shapes leave the device idle without a split"
+    x = make_inputs(300 + n, b, d, n, L, dtype)
+    y, ls = run_gpu(lib, x, dtype)
+    ry, rs = oracle.selective_scan(**x)
+    check("y", synth.to_host_f64(y).reshape(b * d, L), ry, dtype, f32_rel=True)
+    check("last_state", synth.to_host_f64(ls).reshape(b * d, -1), rs, dtype, f32_rel=True)
+
+
+def test_time_split_initial_state_and_groups(lib):
+    b, d, n, L, G = 2, 512, 16, 1000, 2
+    print("case time split, initial state, two groups of 256 channels", flush=True)
+    x = grouped_inputs(310, b, d, n, L, G, "f32")
+    assert lib.ssm_selective_scan_fwd_workspace_size(b, d, n, L, G) > 0
+    h0 = np.random.default_rng(311).standard_normal((b, d, n)).astype(np.float32)
+    y, ls = run_gpu_h0(lib, x, "f32", h0)
+    ry, rs = oracle.selective_scan(**x, h0=h0.astype(np.float64))
+    check("y", synth.to_host_f64(y).reshape(b * d, L), ry, "f32", f32_rel=True)
+    check("last_state", synth.to_host_f64(ls).reshape(b * d, -1), rs, "f32", f32_rel=True)
+
+
+def test_time_split_workspace_rules(lib):
+    """No workspace for shapes that fill the device; a too small workspace is
+    rejected; without a workspace the call runs unsplit."""
+    assert lib.ssm_selective_scan_fwd_workspace_size(8, 4096, 16, 2048) == 0
+    b, d, n, L = 1, 64, 16, 512
+    nbytes = lib.ssm_selective_scan_fwd_workspace_size(b, d, n, L)
+    assert nbytes > 0
+    x = make_inputs(320, b, d, n, L, "f32")
+    t = {k: (None if v is None else synth.to_device(v, "f32", "cuda")) for k, v in x.items()}
+    y = torch.empty_like(t["u"])
+    small = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lib.SsmScanError):
+        lib.ssm_selective_scan_fwd_ws(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                      t["z"], t["delta_bias"], True, None, y, None, small)
+    y0, _ = run_gpu(lib, x, "f32", time_split=False)
+    lib.ssm_selective_scan_fwd_ws(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                  t["delta_bias"], True, None, y, None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
 
 
 @pytest.mark.parametrize("k", [100, 128])
