@@ -128,48 +128,57 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
   float* part_bc = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off);
   const int64_t part_c_off = (int64_t)F.batch * lay.nwg * N * L;  // dC partials follow dB's
 
+  // Raw inputs of one chunk (this lane's slice of u, delta, dy, z; its share
+  // of the chunk's B and C; the saved entry state), loaded one chunk ahead of
+  // their use.  Every load is unconditional (clamped indices) so that the
+  // compiler can count the loads in flight instead of waiting for all.
+  RawSeg<In, TS> ru, rd, rz, rg;
+  RawSeg<In, EPU> rbc[RB];
+  float hsr[NG];
+  auto load_chunk = [&](int ch) {
+    const int c0 = ch * T;
+    const int ts = c0 + slot * TS;
+    load_raw<In, TS>(u, row_base, ts, L, ru);
+    load_raw<In, TS>(dlt, row_base, ts, L, rd);
+    load_raw<In, TS>(dy, row_base, ts, L, rg);
+    if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = min(tid + q * 256, UNITS - 1);
+      const int n = e % NS, rest = e / NS;
+      const int seg = rest % UPR, x = rest / UPR;
+      load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)min(n, N - 1) * L, c0 + seg * EPU, L,
+                        rbc[q]);
+    }
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      hsr[k] = chunk_states[(row * lay.nchunks + ch) * N + min(slot * NG + k, N - 1)];
+  };
+
+  load_chunk(lay.nchunks - 1);
   for (int ch = lay.nchunks - 1; ch >= 0; --ch) {
     const int c0 = ch * T;
     const int ts = c0 + slot * TS;
-    // -- loads: this lane's slice of u, delta, z, dy; B and C of the chunk ----
-    RawSeg<In, TS> ru, rd, rz, rg;
-    if (row_ok) {
-      load_raw<In, TS>(u, row_base, ts, L, ru);
-      load_raw<In, TS>(dlt, row_base, ts, L, rd);
-      load_raw<In, TS>(dy, row_base, ts, L, rg);
-      if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
-    } else {
-#pragma unroll
-      for (int k = 0; k < RawSeg<In, TS>::kWords; ++k) ru.w[k] = rd.w[k] = rg.w[k] = rz.w[k] = 0u;
-    }
+    // -- B and C of the chunk into LDS ----------------------------------------
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
       const int e = tid + q * 256;
       if (e < UNITS) {
         const int n = e % NS, rest = e / NS;
         const int seg = rest % UPR, x = rest / UPR;
-        RawSeg<In, EPU> r;
-        if (n < N) {
-          load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, r);
-        } else {
-#pragma unroll
-          for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) r.w[k] = 0u;
-        }
         float v[EPU];
-        decode_raw<In, EPU>(r, v);
+        decode_raw<In, EPU>(rbc[q], v);
 #pragma unroll
         for (int i = 0; i < EPU; ++i) {
-          if (x) sC[seg * EPU + i][n] = v[i];
-          else sB[seg * EPU + i][n] = v[i];
+          const float vv = n < N ? v[i] : 0.0f;
+          if (x) sC[seg * EPU + i][n] = vv;
+          else sB[seg * EPU + i][n] = vv;
         }
       }
     }
     float hs[NG];  // state entering the chunk
 #pragma unroll
-    for (int k = 0; k < NG; ++k) {
-      const int n = slot * NG + k;
-      hs[k] = (row_ok && n < N) ? chunk_states[(row * lay.nchunks + ch) * N + n] : 0.0f;
-    }
+    for (int k = 0; k < NG; ++k) hs[k] = (row_ok && slot * NG + k < N) ? hsr[k] : 0.0f;
     // -- per-step values of this lane's slice ---------------------------------
     float uk[TS], dl[TS], du[TS], sp[TS], gy[TS], zk[TS];
     {
@@ -185,12 +194,14 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
       }
 #pragma unroll
       for (int j = 0; j < TS; ++j) {
+        if (!row_ok) uk[j] = gy[j] = zk[j] = dr[j] = 0.0f;
         sp[j] = dr[j] + bias;
         dl[j] = F.delta_softplus ? softplus_f(sp[j]) : sp[j];
         if (ts + j >= L) dl[j] = 0.0f;  // past the end: identity steps
         du[j] = dl[j] * uk[j];
       }
     }
+    load_chunk(ch > 0 ? ch - 1 : 0);  // the last step reloads chunk 0
     __syncthreads();  // sB, sC of this chunk are complete
 
     // -- forward over the chunk from its saved entry state ---------------------
