@@ -103,6 +103,59 @@ def measured_traffic(name: str, src: str, per: str = "launch"):
     return int(fields[key])
 
 
+def per_call_flushed(torch, step, calls=50, warm=5):
+    """Each call timed on its own with HIP events, after a 1 GiB write that
+    evicts the inputs from L2 and the 256 MB MALL (outside the timed span);
+    returns median, p10 and p90 in microseconds."""
+    import numpy as np
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(warm):
+        step()
+    times = []
+    for _ in range(calls):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    t = np.array(times)
+    return {"calls": calls, "l2_mall_flush": "1 GiB write before each call",
+            "median_us": round(float(np.median(t)), 2),
+            "p10_us": round(float(np.percentile(t, 10)), 2),
+            "p90_us": round(float(np.percentile(t, 90)), 2)}
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of 1 GiB: (bytes read + bytes written) / time."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return round(gbs, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, cfg, oracle, min_seconds=1.0):
     """Time the oracle (as it stands) on the whole workload on the host,
     repeating it until at least `min_seconds` of wall time (about 16 s of CPU
@@ -119,8 +172,15 @@ def cpu_baseline(x, cfg, oracle, min_seconds=1.0):
     b, d, L = x["u"].shape
     n = x["A"].shape[1]
     es = 2 if cfg.dtype == "bf16" else 4
+    # per-core rate: one thread on the first 256 rows
+    rows = list(range(min(256, b * d)))
+    t1 = time.perf_counter()
+    oracle.selective_scan(**x, delta_softplus=cfg.softplus, rows=rows, nthreads=1)
+    one = time.perf_counter() - t1
     return {"value": reps * mamba1_bytes(b, d, n, L, es) / dt / 1e9, "unit": "GB/s",
             "cores": threads, "kind": "oracle", "seconds": round(dt, 3), "repetitions": reps,
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "one_thread_state_updates_per_s": round(len(rows) * L * n / one, 1),
             "sample": f"the whole {cfg.name} workload ({b * d} rows x {L} steps x {n} states, "
                       f"fp64 sequential loop per row, rows over {threads} threads), run {reps}x"}
 
@@ -209,6 +269,10 @@ def main():
                      "traffic": measured_traffic(f"selective_scan_fwd_kernel_{cfg.name}", KERNEL_SRC),
                      "kernel": "selective_scan_fwd_kernel", "flops_per_launch": flops},
     }
+    out["per_call"] = per_call_flushed(torch, step)
+    copy_gbs = copy_bandwidth(torch)
+    out["copy_gbs"] = copy_gbs
+    out["pct_of_copy"] = round(100.0 * hbm_gbs / copy_gbs, 2)
     if args.ssd:
         out["ssd"] = bench_ssd(args, torch, ssm, synth)
     if args.decode:
@@ -384,6 +448,7 @@ def bench_ssd(args, torch, ssm, synth):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    per_call = per_call_flushed(torch, step)
     Q, g = cfg.chunk, cfg.ngroups
     nc = math.ceil(L / Q)
     flops = 2 * b * nc * (g * Q * Q * n + h * Q * Q * p + 2 * h * Q * n * p)
@@ -394,6 +459,7 @@ def bench_ssd(args, torch, ssm, synth):
             "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "mfma_frac_bf16_2500": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4),
             "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "flops": flops, "bytes": nbytes,
+            "per_call": per_call,
             "traffic": measured_traffic("ssd_chunk_scan_ssd", SSD_SRC, per="call")}
 
 
