@@ -9,8 +9,8 @@ resident in HBM; a workspace only for shapes too small to fill the device,
 none at the 1.4B shape).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--no-cpu-baseline] [--calib-copy] [--ssd] [--bwd] [--decode]
-                    [--grouped]
+                    [--no-cpu-baseline] [--no-per-call] [--calib-copy] [--ssd] [--bwd]
+                    [--decode] [--grouped]
 
 Algorithmic HBM bytes per call (inputs read once, outputs written once):
     u, delta, z: 3*b*d*L*es   y: b*d*L*es   B, C: 2*b*N*L*es
@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="m1p4b", choices=["m1p4b", "m130m", "long", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-call", action="store_true",
+                    help="skip the per-call flushed timings and the copy bandwidth (for traces)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--ssd", action="store_true", help="also time the Mamba-2 chunked scan")
@@ -269,10 +271,11 @@ def main():
                      "traffic": measured_traffic(f"selective_scan_fwd_kernel_{cfg.name}", KERNEL_SRC),
                      "kernel": "selective_scan_fwd_kernel", "flops_per_launch": flops},
     }
-    out["per_call"] = per_call_flushed(torch, step)
-    copy_gbs = copy_bandwidth(torch)
-    out["copy_gbs"] = copy_gbs
-    out["pct_of_copy"] = round(100.0 * hbm_gbs / copy_gbs, 2)
+    if not args.no_per_call:
+        out["per_call"] = per_call_flushed(torch, step)
+        copy_gbs = copy_bandwidth(torch)
+        out["copy_gbs"] = copy_gbs
+        out["pct_of_copy"] = round(100.0 * hbm_gbs / copy_gbs, 2)
     if args.ssd:
         out["ssd"] = bench_ssd(args, torch, ssm, synth)
     if args.decode:
@@ -448,7 +451,7 @@ def bench_ssd(args, torch, ssm, synth):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    per_call = per_call_flushed(torch, step)
+    per_call = None if args.no_per_call else per_call_flushed(torch, step)
     Q, g = cfg.chunk, cfg.ngroups
     nc = math.ceil(L / Q)
     flops = 2 * b * nc * (g * Q * Q * n + h * Q * Q * p + 2 * h * Q * n * p)
