@@ -66,6 +66,9 @@ CASES = [  # (batch, seqlen, nheads, headdim, dstate, ngroups, chunk)
     (3, 129, 2, 32, 128, 2, 64),
     (2, 4096, 32, 32, 64, 1, 256),   # several heads per workgroup
     (1, 2048, 16, 64, 128, 2, 128),
+    (1, 300, 2, 128, 256, 1, 128),   # the largest head and state (documented limits)
+    (2, 200, 4, 32, 256, 2, 64),
+    (1, 513, 2, 128, 32, 1, 256),
 ]
 
 
