@@ -247,28 +247,24 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int nh, const GroupRaw<
 // registers PD heads ahead of its use (a ring of PD + 1 register sets,
 // indexed statically by unrolling the head loop by the ring size), so that
 // several heads' loads are in flight while the small per-head product runs.
-template <int P, int NB>
+template <int P, int NB, int QT>
 __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   constexpr int NTHR = 1024, NW = 16;
   constexpr int kRowB = NB + 16;   // LDS row strides (bf16); words = 8 (mod 32) spreads banks
   constexpr int kRowX = P + 16;
-  constexpr bool DB = (size_t)kQMax * (kRowB + 2 * kRowX) * 2 + 2 * kHGMax * kQMax * 4 <= 156 * 1024;
+  constexpr bool DB = (size_t)QT * (kRowB + 2 * kRowX) * 2 + 2 * kHGMax * kQMax * 4 <= 156 * 1024;
   constexpr int NBUF = DB ? 2 : 1;
-  __shared__ alignas(16) uint16_t sB[kQMax][kRowB];         // B[s][n] of one state block
-  __shared__ alignas(16) uint16_t sX[NBUF][kQMax][kRowX];   // (w x)[s][p] of one head
+  __shared__ alignas(16) uint16_t sB[QT][kRowB];         // B[s][n] of one state block
+  __shared__ alignas(16) uint16_t sX[NBUF][QT][kRowX];   // (w x)[s][p] of one head
   __shared__ alignas(16) float sCs2[kHGMax][kQMax];
   __shared__ alignas(16) float sDt[kHGMax][kQMax];
   __shared__ float sTmp[16];
   constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
-  constexpr int XPT = (kQMax * P / 8 + NTHR - 1) / NTHR;
-  constexpr int BPT = (kQMax * NB / 8 + NTHR - 1) / NTHR;
-  constexpr int PD = 6 / XPT < 1 ? 1 : (6 / XPT > 4 ? 4 : 6 / XPT);  // heads of x in flight
-  // When the staging tasks cover the kQMax-row tiles exactly, every task
-  // writes a row that exists (rows past the chunk are never read), so the
-  // staging needs no per-thread condition; a condition there would make the
-  // compiler wait for every outstanding load before the next prefetch.
-  constexpr bool kXExact = kQMax * P / 8 == XPT * NTHR;
-  constexpr bool kBExact = kQMax * NB / 8 == BPT * NTHR;
+  constexpr bool kAllTiles = TILES % NW == 0;  // every wave owns TPW tiles
+  constexpr int XTASKS = QT * P / 8, BTASKS = QT * NB / 8;
+  constexpr int XPT = (XTASKS + NTHR - 1) / NTHR;
+  constexpr int BPT = (BTASKS + NTHR - 1) / NTHR;
+  constexpr int PD = XPT <= 2 ? 2 : 1;  // heads of x in flight
   constexpr int RING = PD + 1;
 
   const int c = blockIdx.x, b = blockIdx.y;
@@ -276,37 +272,38 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   const int h0 = blockIdx.z * a.heads_per_wg_state;
   const int nh = min(a.heads_per_wg_state, a.nheads - h0);
   const int g = h0 / hpg;
-  const int Q = a.chunk, N = a.dstate, L = a.seqlen;
+  const int N = a.dstate, L = a.seqlen;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int r16 = lane & 15, q4 = lane >> 4;
-  const int64_t pos0 = (int64_t)c * Q;
-  const int xtasks = Q * P / 8;
-  const int btasks = Q * NB / 8;
+  const int64_t pos0 = (int64_t)c * QT;
 
+  // Every global load is issued unconditionally (clamped task, position and
+  // head indices): a load under a condition, or a loop whose memory
+  // operations depend on a runtime count, makes the compiler wait for every
+  // load in flight instead of the one it needs.
   uint4 xr[RING][XPT], br[BPT];
   const uint16_t* xsrc[XPT];  // this thread's x pieces of the group's first head
 #pragma unroll
   for (int k = 0; k < XPT; ++k) {
-    const int task = tid + k * NTHR;
+    const int task = min(tid + k * NTHR, XTASKS - 1);
     const int s = task / (P / 8), po = task % (P / 8);
     xsrc[k] = a.x + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.nheads + h0) * P + 8 * po;
   }
-  // x of head hh into ring slot SLOT
+  // x of head hh (clamped to the group) into ring slot SLOT
   auto prefetch = [&](auto slot, int hh) {
     constexpr int SLOT = decltype(slot)::value;
+    const int64_t off = (int64_t)min(hh, nh - 1) * P;
 #pragma unroll
-    for (int k = 0; k < XPT; ++k) xr[SLOT][k] = load16(xsrc[k] + (int64_t)hh * P);
+    for (int k = 0; k < XPT; ++k) xr[SLOT][k] = load16(xsrc[k] + off);
   };
   auto prefetch_first = [&]() {
-    static_for<0, PD>([&](auto jc) {
-      if (decltype(jc)::value < nh) prefetch(jc, decltype(jc)::value);
-    });
+    static_for<0, PD>([&](auto jc) { prefetch(jc, decltype(jc)::value); });
   };
   auto load_b = [&](int nb0) {
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
-      const int task = tid + k * NTHR;
+      const int task = min(tid + k * NTHR, BTASKS - 1);
       const int s = task / (NB / 8), part = task % (NB / 8);
       br[k] = load16(a.B + (((int64_t)b * L + load_pos(pos0 + s, L)) * a.ngroups + g) * N + nb0 +
                      8 * part);
@@ -315,11 +312,11 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   // (w x)[s][p] = x[s][p] exp2(cs_last - cs_s) dt_s, rounded to bf16.
   auto stage = [&](auto slot, int hh, int buf) {
     constexpr int SLOT = decltype(slot)::value;
-    const float cs_last = sCs2[hh][Q - 1];
+    const float cs_last = sCs2[hh][QT - 1];
 #pragma unroll
     for (int k = 0; k < XPT; ++k) {
       const int task = tid + k * NTHR;
-      if (kXExact || task < xtasks) {
+      if (XTASKS % NTHR == 0 || task < XTASKS) {
         const int s = task / (P / 8), po = task % (P / 8);
         const float w = fast_exp2(cs_last - sCs2[hh][s]) * sDt[hh][s];
         const uint32_t e[4] = {xr[SLOT][k].x, xr[SLOT][k].y, xr[SLOT][k].z, xr[SLOT][k].w};
@@ -341,7 +338,7 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   prefetch_first();
   group_log_decay<NTHR>(a, c, nh, graw, sCs2, sDt, sTmp);
   if (tid < nh)
-    a.decay[((int64_t)b * a.nheads + h0 + tid) * a.nchunks + c] = fast_exp2(sCs2[tid][Q - 1]);
+    a.decay[((int64_t)b * a.nheads + h0 + tid) * a.nchunks + c] = fast_exp2(sCs2[tid][QT - 1]);
 
   for (int nb0 = 0; nb0 < N; nb0 += NB) {
     if (nb0 > 0) {
@@ -352,31 +349,31 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int task = tid + k * NTHR;
-      if (kBExact || task < btasks) {
+      if (BTASKS % NTHR == 0 || task < BTASKS) {
         const int s = task / (NB / 8), part = task % (NB / 8);
         *reinterpret_cast<uint4*>(&sB[s][8 * part]) = br[k];
       }
     }
-    for (int hb = 0; hb < nh; hb += RING) static_for<0, RING>([&](auto jc) {
+    // one head: stage its (w x), prefetch the head PD ahead, S_c^T = B^T (w x)
+    auto head = [&](auto jc, int hh) {
       constexpr int J = decltype(jc)::value;
-      const int hh = hb + J;
-      if (hh >= nh) return;
       const int h = h0 + hh;
       const int buf = DB ? (hh & 1) : 0;
       // a single buffer's previous readers are done (the barrier after the
       // last head's product); two buffers alternate
       stage(jc, hh, buf);
-      if (hh + PD < nh) prefetch(std::integral_constant<int, (J + PD) % RING>{}, hh + PD);
+      prefetch(std::integral_constant<int, (J + PD) % RING>{}, hh + PD);
       __syncthreads();
       // S_c^T[n][p] = sum_s B[s][n] (w x)[s][p]
       f32x4 acc[TPW];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int ks = 0; ks < Q / 32; ++ks) {
+#pragma unroll 2
+      for (int ks = 0; ks < QT / 32; ++ks) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
           const int tile = wv + NW * t;
-          if (tile < TILES) {
+          if (kAllTiles || tile < TILES) {
             const int nt = tile / PT, pt = tile % PT;
             const bf16x8 av = lds_kop(&sB[0][0], kRowB, ks * 32, nt * 16);
             const bf16x8 bv = lds_kop(&sX[buf][0][0], kRowX, ks * 32, pt * 16);
@@ -384,13 +381,13 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
           }
         }
       }
-      if (!DB || hh + 1 == nh) __syncthreads();  // readers of sX (and sB) are done
+      if constexpr (!DB) __syncthreads();  // readers of the single sX buffer are done
       // lane holds S_c[p][n .. n+3] with p = pt*16 + r16, n = nt*16 + 4*q4
       uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int tile = wv + NW * t;
-        if (tile < TILES) {
+        if (kAllTiles || tile < TILES) {
           const int nt = tile / PT, pt = tile % PT;
           const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
           uint2 o;
@@ -399,7 +396,14 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
           *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
         }
       }
+    };
+    int hb = 0;
+    for (; hb + RING <= nh; hb += RING)
+      static_for<0, RING>([&](auto jc) { head(jc, hb + decltype(jc)::value); });
+    static_for<0, RING>([&](auto jc) {
+      if (hb + decltype(jc)::value < nh) head(jc, hb + decltype(jc)::value);
     });
+    if constexpr (DB) __syncthreads();  // readers of sX and sB are done
   }
 }
 
@@ -836,7 +840,12 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   // state block: B[chunk][NB] and one head's x[chunk][P] share the LDS
   constexpr int NB = (P == 128 && N >= 128) ? 64 : (N > 128 ? 128 : N);
   dim3 g1(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_state - 1) / a.heads_per_wg_state);
-  hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB>), g1, dim3(1024), 0, stream, a);
+  if (s.chunk == 64)
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB, 64>), g1, dim3(1024), 0, stream, a);
+  else if (s.chunk == 128)
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB, 128>), g1, dim3(1024), 0, stream, a);
+  else
+    hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB, 256>), g1, dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t PN = (int64_t)P * N;
