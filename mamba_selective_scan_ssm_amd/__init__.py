@@ -408,6 +408,59 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
     return g
 
 
+_SCAN_FN = None
+
+
+def _scan_function():
+    """torch.autograd.Function over the forward and backward entry points
+    (built on first use so that importing this module needs no torch)."""
+    global _SCAN_FN
+    if _SCAN_FN is not None:
+        return _SCAN_FN
+    import torch
+
+    class SelectiveScanFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, u, delta, A, B, C, D, z, delta_bias, initial_state, delta_softplus):
+            ins = [None if t is None else t.contiguous()
+                   for t in (u, delta, A, B, C, D, z, delta_bias, initial_state)]
+            y, ls = selective_scan_fwd(*ins[:5], D=ins[5], z=ins[6], delta_bias=ins[7],
+                                       delta_softplus=delta_softplus, initial_state=ins[8])
+            ctx.save_for_backward(*[t if t is not None else torch.empty(0) for t in ins])
+            ctx.present = [t is not None for t in ins]
+            ctx.delta_softplus = delta_softplus
+            return y, ls
+
+        @staticmethod
+        def backward(ctx, dy, dls):
+            ins = [t if p else None for t, p in zip(ctx.saved_tensors, ctx.present)]
+            u, delta, A, B, C, D, z, delta_bias, h0 = ins
+            dy = torch.zeros_like(u) if dy is None else dy.to(u.dtype).contiguous()
+            dls = None if dls is None else dls.float().contiguous()
+            g = selective_scan_bwd(u, delta, A, B, C, dy, D=D, z=z, delta_bias=delta_bias,
+                                   delta_softplus=ctx.delta_softplus, initial_state=h0,
+                                   dlast_state=dls)
+            cast = lambda t, like: None if t is None else t.to(like.dtype)
+            return (g["du"], g["ddelta"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
+                    cast(g["dD"], D) if D is not None else None,
+                    g["dz"] if z is not None else None,
+                    cast(g["ddelta_bias"], delta_bias) if delta_bias is not None else None,
+                    cast(g["dinitial_state"], h0) if h0 is not None else None, None)
+
+    _SCAN_FN = SelectiveScanFn
+    return _SCAN_FN
+
+
+def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                      initial_state=None, return_last_state=False):
+    """Differentiable Mamba-1 selective scan: the forward and backward HIP
+    kernels behind torch.autograd (B, C [batch, dstate, seqlen]; the
+    backward needs dstate <= 16).  Returns y, or (y, last_state)."""
+    y, ls = _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, initial_state,
+                                   bool(delta_softplus))
+    return (y, ls) if return_last_state else y
+
+
 def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
                                   chunk_size, handle=None, device: int = 0) -> int:
     if handle is None:

@@ -130,3 +130,38 @@ def test_backward_repeatable(lib):
     for k in g1:
         if g1[k] is not None:
             assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_function(lib, dtype):
+    """selective_scan_fn under torch.autograd: loss = sum(wy * y) +
+    sum(wl * last_state), .backward(), every input's .grad against the
+    oracle's backward with dy = wy, dlast = wl."""
+    b, d, n, L = 2, 40, 16, 90
+    print(f"case autograd {dtype}", flush=True)
+    cfg = synth.Mamba1Config("ag", b, d, n, L, dtype, 0.0, 0.5, delta_bias=True, gate=True,
+                             use_D=True)
+    x = synth.mamba1_inputs(cfg, seed=55)
+    rng = np.random.default_rng(56)
+    wy = rng.standard_normal((b, d, L)).astype(np.float32)
+    if dtype == "bf16":
+        wy = synth.round_bf16(wy)
+    wl = rng.standard_normal((b, d, n)).astype(np.float32)
+    h0 = rng.standard_normal((b, d, n)).astype(np.float32)
+    dev = "cuda"
+    t = {k: synth.to_device(v, dtype if k in ("u", "delta", "z", "B", "C") else "f32", dev)
+         .requires_grad_(True) for k, v in x.items() if v is not None}
+    h0t = torch.from_numpy(h0).to(dev).requires_grad_(True)
+    y, ls = lib.selective_scan_fn(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], initial_state=h0t,
+                                  return_last_state=True)
+    loss = (y.float() * synth.to_device(wy, "f32", dev)).sum() + \
+        (ls * torch.from_numpy(wl).to(dev)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(**x, dy=wy.astype(np.float64), h0=h0.astype(np.float64),
+                                    dlast=wl.astype(np.float64))
+    for name, rname in (("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC"),
+                        ("D", "dD"), ("z", "dz"), ("delta_bias", "ddelta_bias")):
+        check("grad " + name, synth.to_host_f64(t[name].grad), ref[rname], dtype)
+    check("grad initial_state", synth.to_host_f64(h0t.grad), ref["dh0"], dtype)
