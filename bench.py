@@ -285,9 +285,12 @@ def main():
                           for g in (8, d)]
     if args.bwd:
         out["bwd"] = bench_bwd(args, torch, ssm, synth, cfg, io, x)
+    if not args.no_per_call:
+        out["spec_point"] = bench_spec_point(torch, ssm, synth)
     if not args.no_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline(x, cfg, oracle)
+        out["speedup_vs_oracle"] = round(value / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 
@@ -333,6 +336,41 @@ def bench_bwd(args, torch, ssm, synth, cfg, io, x):
             "ms_per_call": round(ms, 4), "workspace_bytes": ws.numel(),
             "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "state_updates_per_s": round(b * d * L * n / (ms * 1e-3), 1)}
+
+
+def bench_spec_point(torch, ssm, synth):
+    """The task-spec page's speed-up point: batch 1, dim 256, seqlen 2048,
+    float32, dstate 16 (softplus, D, gate), through ssm_selective_scan_fwd_ws
+    (split in time across workgroups at this size)."""
+    cfg = synth.Mamba1Config("spec", 1, 256, 16, 2048, "f32", 0.0, 0.5, delta_bias=True,
+                             gate=True, use_D=True)
+    x = synth.mamba1_inputs(cfg, seed=3)
+    dev = torch.device("cuda:0")
+    io = {k: synth.to_device(v, "f32", dev) for k, v in x.items()}
+    b, d, L = x["u"].shape
+    n = x["A"].shape[1]
+    y = torch.empty_like(io["u"])
+    ls = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    nbytes = ssm.ssm_selective_scan_fwd_workspace_size(b, d, n, L)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+    def step():
+        ssm.ssm_selective_scan_fwd_ws(io["u"], io["delta"], io["A"], io["B"], io["C"], io["D"],
+                                      io["z"], io["delta_bias"], True, None, y, ls, ws)
+
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(100):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 100 * 1e3
+    return {"workload": "batch 1, dim 256, seqlen 2048, dstate 16, f32 (task-spec speed-up point)",
+            "us_per_call": round(us, 2), "workspace_bytes": nbytes,
+            "hbm_gbs": round(mamba1_bytes(b, d, n, L, 4) / (us * 1e-6) / 1e9, 1)}
 
 
 def bench_grouped(args, torch, ssm, synth, cfg, io, x, ngroups):
