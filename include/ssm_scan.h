@@ -104,6 +104,11 @@ ssm_status ssm_scan_destroy(ssm_handle handle);
  * SSM_ERR_INVALID_ARG without touching the device ([SPEC] Definition of
  * Done: batch=0 must not crash).  The initial state is zero (see
  * ssm_selective_scan_fwd_with_state for a given one).
+ *
+ * Performance: when the rows are too few to give every SIMD a wave (e.g.
+ * batch 2, dim 1536), this call splits each time chunk across the waves of
+ * one workgroup only; ssm_selective_scan_fwd_ws with a workspace also
+ * splits the sequence across workgroups and is several times faster there.
  */
 ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void *u,
                                   const void *delta, const float *A,
