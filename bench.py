@@ -10,7 +10,7 @@ none at the 1.4B shape).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
                     [--no-cpu-baseline] [--no-per-call] [--calib-copy] [--ssd] [--bwd]
-                    [--decode] [--grouped]
+                    [--decode] [--grouped] [--seq-table]
 
 Algorithmic HBM bytes per call (inputs read once, outputs written once):
     u, delta, z: 3*b*d*L*es   y: b*d*L*es   B, C: 2*b*N*L*es
@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--ssd", action="store_true", help="also time the Mamba-2 chunked scan")
     ap.add_argument("--bwd", action="store_true",
                     help="also time the backward pass on the same workload")
+    ap.add_argument("--seq-table", action="store_true",
+                    help="also time batch 16, dim 1536, dstate 16, bf16 at seqlen 256..16384")
     ap.add_argument("--grouped", action="store_true",
                     help="also time B, C per group of channels: 8 groups and one per channel")
     ap.add_argument("--decode", action="store_true",
@@ -283,6 +285,8 @@ def main():
     if args.grouped:
         out["grouped"] = [bench_grouped(args, torch, ssm, synth, cfg, io, x, g)
                           for g in (8, d)]
+    if args.seq_table:
+        out["seq_table"] = bench_seq_table(torch, ssm, synth)
     if args.bwd:
         out["bwd"] = bench_bwd(args, torch, ssm, synth, cfg, io, x)
     if not args.no_per_call:
@@ -336,6 +340,45 @@ def bench_bwd(args, torch, ssm, synth, cfg, io, x):
             "ms_per_call": round(ms, 4), "workspace_bytes": ws.numel(),
             "algorithmic_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "state_updates_per_s": round(b * d * L * n / (ms * 1e-3), 1)}
+
+
+def bench_seq_table(torch, ssm, synth):
+    """Batch 16 at seqlen 256, 1024, 4096, 16384 (dim 1536, dstate 16, bf16,
+    softplus, D, gate): the shapes of the Blelloch article's V100 timing
+    table, whose dim and dstate it does not state (context only)."""
+    rows = []
+    dev = torch.device("cuda:0")
+    for L in (256, 1024, 4096, 16384):
+        cfg = synth.Mamba1Config("seq", 16, 1536, 16, L, "bf16", 0.0, 0.5, delta_bias=True,
+                                 gate=True, use_D=True)
+        x = synth.mamba1_inputs(cfg, seed=8)
+        io = {k: synth.to_device(v, "bf16" if k in ("u", "delta", "z", "B", "C") else "f32",
+                                 dev) for k, v in x.items()}
+        b, d, _ = x["u"].shape
+        y = torch.empty_like(io["u"])
+        ls = torch.empty((b, d, 16), dtype=torch.float32, device=dev)
+        nbytes = ssm.ssm_selective_scan_fwd_workspace_size(b, d, 16, L)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+        def step():
+            ssm.ssm_selective_scan_fwd_ws(io["u"], io["delta"], io["A"], io["B"], io["C"],
+                                          io["D"], io["z"], io["delta_bias"], True, None, y, ls,
+                                          ws)
+
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        rows.append({"seqlen": L, "ms_per_call": round(ms, 4),
+                     "hbm_gbs": round(mamba1_bytes(b, d, 16, L, 2) / (ms * 1e-3) / 1e9, 1)})
+        del io, y, ls, ws
+    return rows
 
 
 def bench_spec_point(torch, ssm, synth):
