@@ -28,7 +28,15 @@
 //     group's partial readouts sum_n C h are reduce-scattered back to the
 //     owners of the steps with DPP adds.  No per-step value goes through LDS.
 //
-// selective_scan_split_kernel (too few rows to give every SIMD a wave):
+//   Two variants of it: with per-row B and C (groups of channels smaller
+//   than a workgroup, down to one channel: each lane loads its own states'
+//   B and C into registers), and with the sequence cut into segments across
+//   workgroups (given a workspace: a first launch stores every segment's
+//   aggregate (prod a, v), a second folds the earlier aggregates into each
+//   segment's carry-in with the combine operator and rescans it).
+//
+// selective_scan_split_kernel (too few rows to give every SIMD a wave and no
+// workspace for the segments):
 //   * lane = row (64 rows per wave); G waves split the dstate axis (NG
 //     states each) and share the per-step work through LDS; their partial
 //     readouts are added in LDS;
