@@ -326,7 +326,8 @@ ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batc
   if (batch * dim > (int64_t(1) << 62) / seqlen / 64)
     return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
-  *bytes = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen).total;
+  *bytes = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen,
+                                          handle->num_cus).total;
   return ok();
 }
 
@@ -357,11 +358,6 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   for (const auto& r : required)
     if (!r.p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", r.name);
   if (z && !dz) return fail(SSM_ERR_INVALID_ARG, "dz is NULL while z is given");
-  const ssm::BwdLayout lay =
-      ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen);
-  if (workspace_bytes < lay.total)
-    return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
-                lay.total);
   const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
   const uint64_t nbc = (uint64_t)batch * dstate * seqlen;
@@ -378,10 +374,15 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
                       {"dz", z ? dz : nullptr, nrow * es},
                       {"ddelta_bias", ddelta_bias, (uint64_t)dim * 4},
                       {"dinitial_state", dinitial_state, nst},
-                      {"workspace", workspace, lay.total}};
+                      {"workspace", workspace, workspace_bytes}};
   ssm_status st = check_spans(in, 11, out, 10);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  const ssm::BwdLayout lay = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate,
+                                                            (int)seqlen, handle->num_cus);
+  if (workspace_bytes < lay.total)
+    return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                lay.total);
 
   ssm::BwdParams p;
   ssm::ScanParams& f = p.fwd;
@@ -396,7 +397,7 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   p.dh0 = dinitial_state; p.workspace = workspace;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = ssm::launch_selective_scan_bwd(p, in_dtype == SSM_BF16, stream);
+  hipError_t e = ssm::launch_selective_scan_bwd(p, lay, in_dtype == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -205,7 +205,9 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
     const int c0 = t_begin + ch * T;
     const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
     if (!AGG && prm.chunk_states && row_ok) {  // state entering the chunk, for the backward pass
-      float* cs = prm.chunk_states + (((int64_t)b * prm.dim + d) * nchunks + ch) * N;
+      // global chunk index (segments start on a chunk boundary)
+      const int64_t gch = t_begin / T + ch, gn = (L + T - 1) / T;
+      float* cs = prm.chunk_states + (((int64_t)b * prm.dim + d) * gn + gch) * N;
 #pragma unroll
       for (int k = 0; k < NG; ++k)
         if (slot * NG + k < N) cs[slot * NG + k] = h[k];
@@ -649,23 +651,6 @@ hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream) {
-  // the row-parallel kernel with 16-step chunks: a saved state every 16 steps
-  if (bf16) {
-    if (p.dstate <= 4) return launch_rows<uint16_t, 4, 1, 16>(p, stream);
-    if (p.dstate <= 8) return launch_rows<uint16_t, 4, 2, 16>(p, stream);
-    return launch_rows<uint16_t, 4, 4, 16>(p, stream);
-  }
-  if (p.dstate <= 4) return launch_rows<float, 4, 1, 16>(p, stream);
-  if (p.dstate <= 8) return launch_rows<float, 4, 2, 16>(p, stream);
-  return launch_rows<float, 4, 4, 16>(p, stream);
-}
-
-hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
-                                 hipStream_t stream) {
-  return bf16 ? launch_typed<uint16_t>(p, tile, stream) : launch_typed<float>(p, tile, stream);
-}
-
 // Row-parallel shape per dstate tier: (NG, LPC, T) = (4,1,16) / (4,2,32) /
 // (4,4,64) / (16,4,32) for dstate <= 4 / 8 / 16 / 64.
 template <typename In, bool AGG>
@@ -674,6 +659,33 @@ hipError_t launch_rows_tier(const ScanParams& p, hipStream_t s, int nz) {
   if (p.dstate <= 8) return launch_rows<In, 4, 2, 32, false, AGG>(p, s, nz);
   if (p.dstate <= 16) return launch_rows<In, 4, 4, 64, false, AGG>(p, s, nz);
   return launch_rows<In, 16, 4, 32, false, AGG>(p, s, nz);
+}
+
+hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream) {
+  // the row-parallel kernel with 16-step chunks: a saved state every 16 steps.
+  // With p.seg_len > 0 (a multiple of 64), the segments' aggregates are
+  // computed first (into p.seg_agg) and every segment runs from its carry-in.
+  const int nz = p.seg_len ? (p.seqlen + p.seg_len - 1) / p.seg_len : 1;
+  if (nz > 1) {
+    ScanParams q = p;
+    q.chunk_states = nullptr;
+    const hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(q, stream, nz - 1)
+                              : launch_rows_tier<float, true>(q, stream, nz - 1);
+    if (e != hipSuccess) return e;
+  }
+  if (bf16) {
+    if (p.dstate <= 4) return launch_rows<uint16_t, 4, 1, 16>(p, stream, nz);
+    if (p.dstate <= 8) return launch_rows<uint16_t, 4, 2, 16>(p, stream, nz);
+    return launch_rows<uint16_t, 4, 4, 16>(p, stream, nz);
+  }
+  if (p.dstate <= 4) return launch_rows<float, 4, 1, 16>(p, stream, nz);
+  if (p.dstate <= 8) return launch_rows<float, 4, 2, 16>(p, stream, nz);
+  return launch_rows<float, 4, 4, 16>(p, stream, nz);
+}
+
+hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,
+                                 hipStream_t stream) {
+  return bf16 ? launch_typed<uint16_t>(p, tile, stream) : launch_typed<float>(p, tile, stream);
 }
 
 ScanSegments plan_scan_segments(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,

@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "device_math.h"
 #include "scan_common.h"
 #include "selective_scan_launch.h"
@@ -110,6 +112,12 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
   const int64_t row_base = row * (int64_t)L;
   const int64_t bc_base = (int64_t)b * N * (int64_t)L;
 
+  // time window: segment blockIdx.z of lay.seg_len steps (whole sequence
+  // when there is one segment)
+  const int seg = blockIdx.z;
+  const int t_begin = lay.nseg > 1 ? seg * lay.seg_len : 0;
+  const int t_end = lay.nseg > 1 ? min(L, t_begin + lay.seg_len) : L;
+  const int64_t rows = (int64_t)F.batch * F.dim;
   float A2[NG], Af[NG], lam[NG], dA_acc[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
@@ -119,6 +127,20 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
     A2[k] = Af[k] * kLog2e;
     lam[k] = (ok && P.dlast) ? P.dlast[row * N + n] : 0.0f;
     dA_acc[k] = 0.0f;
+  }
+  // adjoint entering the segment from the right: the later segments'
+  // aggregates (P, V) folded onto dlast, latest first (lam <- P lam + V)
+  if (seg + 1 < lay.nseg && row_ok) {
+    const float* lag = reinterpret_cast<const float*>(
+        static_cast<const char*>(P.workspace) + lay.lam_agg_off);
+    for (int s2 = lay.nseg - 1; s2 > seg; --s2) {
+      const float* ag = lag + ((int64_t)(s2 - 1) * rows + row) * N * 2;
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        const int n = min(slot * NG + k, N - 1);
+        lam[k] = __builtin_fmaf(ag[2 * n], lam[k], ag[2 * n + 1]);
+      }
+    }
   }
   const float Dd = (row_ok && F.D) ? F.D[d] : 0.0f;
   const float bias = (row_ok && F.delta_bias) ? F.delta_bias[d] : 0.0f;
@@ -155,8 +177,9 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
       hsr[k] = chunk_states[(row * lay.nchunks + ch) * N + min(slot * NG + k, N - 1)];
   };
 
-  load_chunk(lay.nchunks - 1);
-  for (int ch = lay.nchunks - 1; ch >= 0; --ch) {
+  const int ch_first = t_begin / T, ch_last = (t_end + T - 1) / T - 1;
+  load_chunk(ch_last);
+  for (int ch = ch_last; ch >= ch_first; --ch) {
     const int c0 = ch * T;
     const int ts = c0 + slot * TS;
     // -- B and C of the chunk into LDS ----------------------------------------
@@ -201,7 +224,7 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
         du[j] = dl[j] * uk[j];
       }
     }
-    load_chunk(ch > 0 ? ch - 1 : 0);  // the last step reloads chunk 0
+    load_chunk(ch > ch_first ? ch - 1 : ch_first);  // the last step reloads its own chunk
     __syncthreads();  // sB, sC of this chunk are complete
 
     // -- forward over the chunk from its saved entry state ---------------------
@@ -363,13 +386,13 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
     for (int k = 0; k < NG; ++k) {
       const int n = slot * NG + k;
       if (n < N) {
-        part_a[row * N + n] = dA_acc[k];
-        if (P.dh0) P.dh0[row * N + n] = lam[k];
+        part_a[((int64_t)seg * rows + row) * N + n] = dA_acc[k];  // [segment, batch, dim, N]
+        if (P.dh0 && seg == 0) P.dh0[row * N + n] = lam[k];
       }
     }
     if (slot == 0) {
-      part_d[row] = dD_acc;                                // [batch, dim]
-      part_d[(int64_t)F.batch * F.dim + row] = dbias_acc;  // then [batch, dim]
+      part_d[(int64_t)(2 * seg) * rows + row] = dD_acc;         // [segment, 2, batch, dim]
+      part_d[(int64_t)(2 * seg + 1) * rows + row] = dbias_acc;
     }
   }
 }
@@ -403,25 +426,160 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdParams P, Bwd
   const char* ws = static_cast<const char*>(P.workspace);
   const float* part_a = reinterpret_cast<const float*>(ws + lay.part_a_off);
   const float* part_d = reinterpret_cast<const float*>(ws + lay.part_d_off);
+  const int64_t rows = (int64_t)F.batch * F.dim;
   if (i < nA) {
     float s = 0.0f;
-    for (int b = 0; b < F.batch; ++b) s += part_a[(int64_t)b * nA + i];
+    for (int sg = 0; sg < lay.nseg; ++sg)
+      for (int b = 0; b < F.batch; ++b) s += part_a[((int64_t)sg * F.batch + b) * nA + i];
     P.dA[i] = s;
   } else if (i < nA + F.dim) {
     const int64_t dd = i - nA;
     float sD = 0.0f, sb = 0.0f;
-    for (int b = 0; b < F.batch; ++b) {
-      sD += part_d[(int64_t)b * F.dim + dd];
-      sb += part_d[(int64_t)F.batch * F.dim + (int64_t)b * F.dim + dd];
-    }
+    for (int sg = 0; sg < lay.nseg; ++sg)
+      for (int b = 0; b < F.batch; ++b) {
+        sD += part_d[(int64_t)(2 * sg) * rows + (int64_t)b * F.dim + dd];
+        sb += part_d[(int64_t)(2 * sg + 1) * rows + (int64_t)b * F.dim + dd];
+      }
     if (P.dD) P.dD[dd] = sD;
     if (P.ddelta_bias) P.ddelta_bias[dd] = sb;
   }
 }
 
+// Aggregate of the adjoint recurrence over segment blockIdx.z + 1 (the
+// segments after the first), from lam = 0, steps descending:
+//   lam += C_t dyh_t;  lam *= a_t        (dyh = dy silu(z), a = exp(delta A))
+// giving (P, V) = (prod a_t = exp2(A2 sum delta), lam) per (row, state): the
+// adjoint leaving the segment to the left is P lam_in + V for an adjoint
+// lam_in entering it from the right ([EXPLAINED] eq. (10), run backwards).
+template <typename In, int LPC>
+__global__ void __launch_bounds__(256) bwd_lambda_agg_kernel(BwdParams P, BwdLayout lay) {
+  constexpr int NG = kBwdNG, T = kBwdT;
+  constexpr int NS = NG * LPC, RPW = 64 / LPC, RPB = 4 * RPW, TS = T / LPC;
+  constexpr int EPU = Elem<In>::kPer16B;
+  constexpr int UPR = T / EPU, UNITS = NS * UPR;
+  constexpr int RB = (UNITS + 255) / 256;
+  __shared__ alignas(16) float sC[T][NS];
+
+  const ScanParams& F = P.fwd;
+  const In* __restrict__ dlt = static_cast<const In*>(F.delta);
+  const In* __restrict__ Cm = static_cast<const In*>(F.C);
+  const In* __restrict__ z = static_cast<const In*>(F.z);
+  const In* __restrict__ dy = static_cast<const In*>(P.dy);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = lane % LPC;
+  const int b = blockIdx.y;
+  const int d = blockIdx.x * RPB + wv * RPW + lane / LPC;
+  const bool row_ok = d < F.dim;
+  const bool has_z = z != nullptr;
+  const int L = F.seqlen, N = F.dstate;
+  const int64_t rows = (int64_t)F.batch * F.dim;
+  const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
+  const int64_t row_base = row * (int64_t)L;
+  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  const int seg = blockIdx.z + 1;
+  const int t_begin = seg * lay.seg_len;
+  const int t_end = min(L, t_begin + lay.seg_len);
+
+  float A2[NG], lam[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    A2[k] = (row_ok && n < N) ? F.A[(int64_t)d * N + n] * kLog2e : 0.0f;
+    lam[k] = 0.0f;
+  }
+  const float bias = (row_ok && F.delta_bias) ? F.delta_bias[d] : 0.0f;
+  float dsum = 0.0f;
+
+  for (int ch = (t_end + T - 1) / T - 1; ch >= t_begin / T; --ch) {
+    const int c0 = ch * T;
+    const int ts = c0 + slot * TS;
+    RawSeg<In, TS> rd, rg, rz;
+    if (row_ok) {
+      load_raw<In, TS>(dlt, row_base, ts, L, rd);
+      load_raw<In, TS>(dy, row_base, ts, L, rg);
+      if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
+    } else {
+#pragma unroll
+      for (int k = 0; k < RawSeg<In, TS>::kWords; ++k) rd.w[k] = rg.w[k] = rz.w[k] = 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * 256;
+      if (e < UNITS) {
+        const int n = e % NS, sg = e / NS;
+        RawSeg<In, EPU> r;
+        if (n < N) {
+          load_raw<In, EPU>(Cm, bc_base + (int64_t)n * L, c0 + sg * EPU, L, r);
+        } else {
+#pragma unroll
+          for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) r.w[k] = 0u;
+        }
+        float v[EPU];
+        decode_raw<In, EPU>(r, v);
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) sC[sg * EPU + i][n] = v[i];
+      }
+    }
+    float dl[TS], dyh[TS];
+    {
+      float dr[TS], gy[TS], zk[TS];
+      decode_raw<In, TS>(rd, dr);
+      decode_raw<In, TS>(rg, gy);
+      if (has_z) decode_raw<In, TS>(rz, zk);
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float sp = dr[j] + bias;
+        dl[j] = F.delta_softplus ? softplus_f(sp) : sp;
+        if (ts + j >= L || !row_ok) dl[j] = 0.0f;  // past the end: identity steps
+        dyh[j] = has_z ? gy[j] * silu_f(zk[j]) : gy[j];
+      }
+    }
+    __syncthreads();  // sC of this chunk is complete
+    static_for<0, T>([&](auto rc) {
+      constexpr int t = T - 1 - decltype(rc)::value;
+      float dt, dyt;
+      if constexpr (LPC > 1) {
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dyt = dpp_f<group_bcast<LPC>(t / TS)>(dyh[t % TS]);
+      } else {
+        dt = dl[t];
+        dyt = dyh[t];
+      }
+      const float4 cq = *reinterpret_cast<const float4*>(&sC[t][slot * NG]);
+      const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        lam[k] = __builtin_fmaf(cv[k], dyt, lam[k]);
+        lam[k] *= fast_exp2(dt * A2[k]);
+      }
+      dsum += dt;
+    });
+    __syncthreads();  // readers of sC are done before the next chunk
+  }
+  if (row_ok) {
+    float* ag = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.lam_agg_off) +
+                ((int64_t)(seg - 1) * rows + row) * N * 2;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      const int n = slot * NG + k;
+      if (n < N) {
+        ag[2 * n] = fast_exp2(A2[k] * dsum);
+        ag[2 * n + 1] = lam[k];
+      }
+    }
+  }
+}
+
 template <typename In, int LPC>
 hipError_t launch_bwd_rows(const BwdParams& p, const BwdLayout& lay, hipStream_t stream) {
-  dim3 grid((unsigned)lay.nwg, (unsigned)p.fwd.batch);
+  if (lay.nseg > 1) {
+    dim3 ga((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)(lay.nseg - 1));
+    hipLaunchKernelGGL((bwd_lambda_agg_kernel<In, LPC>), ga, dim3(256), 0, stream, p, lay);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)lay.nseg);
   hipLaunchKernelGGL((selective_scan_bwd_kernel<In, LPC>), grid, dim3(256), 0, stream, p, lay);
   return hipGetLastError();
 }
@@ -439,29 +597,55 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen) {
+BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus) {
   BwdLayout l;
   l.nchunks = (seqlen + kBwdT - 1) / kBwdT;
   const int rpb = 4 * (64 / lanes_per_row(dstate));
   l.nwg = (dim + rpb - 1) / rpb;
+  // Time segments when the rows leave SIMDs without a wave and the
+  // sequence has at least 8 segments of 64 steps (64: a multiple of the
+  // chunk lengths of every forward and backward kernel involved); aim at
+  // two waves per SIMD.
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t waves = (int64_t)batch * l.nwg * 4;
+  const int64_t c64 = (seqlen + 63) / 64;
+  l.nseg = 1;
+  l.seg_len = 0;
+  if (waves < 4 * cus && c64 >= 8) {
+    const int64_t want = std::min<int64_t>({(8 * cus + waves - 1) / waves, c64, 64});
+    const int64_t seg_len = ((seqlen + want - 1) / want + 63) / 64 * 64;
+    const int64_t nseg = (seqlen + seg_len - 1) / seg_len;
+    if (nseg > 1) {
+      l.nseg = (int)nseg;
+      l.seg_len = (int)seg_len;
+    }
+  }
   const size_t rows = (size_t)batch * dim;
+  const size_t aggs = (size_t)(l.nseg - 1) * rows * dstate * 2 * sizeof(float);
   l.chunk_states_off = 0;
   l.part_bc_off = align256(rows * l.nchunks * dstate * sizeof(float));
   l.part_a_off = align256(l.part_bc_off +
                           2 * (size_t)batch * l.nwg * dstate * seqlen * sizeof(float));
-  l.part_d_off = align256(l.part_a_off + rows * dstate * sizeof(float));
-  l.total = align256(l.part_d_off + 2 * rows * sizeof(float));
+  l.part_d_off = align256(l.part_a_off + (size_t)l.nseg * rows * dstate * sizeof(float));
+  l.fwd_agg_off = align256(l.part_d_off + (size_t)l.nseg * 2 * rows * sizeof(float));
+  l.lam_agg_off = align256(l.fwd_agg_off + aggs);
+  l.total = align256(l.lam_agg_off + aggs);
   return l;
 }
 
-hipError_t launch_selective_scan_bwd(const BwdParams& p, bool bf16, hipStream_t stream) {
+hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
+                                     hipStream_t stream) {
   const ScanParams& F = p.fwd;
-  const BwdLayout lay = selective_scan_bwd_layout(F.batch, F.dim, F.dstate, F.seqlen);
-  // 1. forward, saving the state entering every chunk
+  // 1. forward, saving the state entering every chunk (segmented like the
+  //    backward when it is)
   ScanParams fs = F;
   fs.y = nullptr;
   fs.last_state = nullptr;
   fs.chunk_states = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.chunk_states_off);
+  if (lay.nseg > 1) {
+    fs.seg_len = lay.seg_len;
+    fs.seg_agg = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.fwd_agg_off);
+  }
   hipError_t e = launch_selective_scan_save(fs, bf16, stream);
   if (e != hipSuccess) return e;
   // 2. reverse pass

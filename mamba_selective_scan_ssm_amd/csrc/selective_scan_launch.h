@@ -92,13 +92,18 @@ struct BwdParams {
   void* workspace;
 };
 
+// Workspace of the backward pass.  With nseg > 1 the sequence is cut into
+// nseg segments of seg_len steps (small batches): the forward's segment
+// aggregates, the adjoint's segment aggregates and per-segment partials of
+// dA, dD, ddelta_bias are kept as well.
 struct BwdLayout {
-  size_t chunk_states_off, part_bc_off, part_a_off, part_d_off, total;
-  int nchunks, nwg;
+  size_t chunk_states_off, part_bc_off, part_a_off, part_d_off, fwd_agg_off, lam_agg_off, total;
+  int nchunks, nwg, nseg, seg_len;
 };
 
-BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen);
-hipError_t launch_selective_scan_bwd(const BwdParams& p, bool bf16, hipStream_t stream);
+BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus);
+hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
+                                     hipStream_t stream);
 
 // One decode step (state_update.hip).
 struct StepParams {

@@ -86,6 +86,11 @@ CASES = [  # (b, d, n, L, dtype, gate, bias, softplus, h0, dlast)
     (2, 130, 16, 257, "bf16", True, True, True, False, False),
     (1, 1, 3, 1, "f32", True, True, True, True, True),
     (2, 300, 13, 64, "bf16", False, False, True, True, True),
+    # small batch, long enough to be split in time (segments of 64 steps or more)
+    (1, 100, 16, 700, "f32", True, True, True, True, True),
+    (2, 64, 4, 1000, "bf16", True, True, True, False, True),
+    (1, 40, 8, 600, "f32", False, False, True, True, False),
+    (1, 70, 16, 2048, "bf16", True, True, True, True, False),
 ]
 
 
