@@ -643,7 +643,7 @@ hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
     case ScanTileId::kN64_Seq: return launch_rows<In, 16, 4, 32>(p, s);
     case ScanTileId::kN4_Split: return launch_cfg<In, 4, 1, 8, 8>(p, s);
     case ScanTileId::kN8_Split: return launch_cfg<In, 4, 2, 4, 16>(p, s);
-    case ScanTileId::kN16_Split: return launch_cfg<In, 4, 4, 4, 16>(p, s);
+    case ScanTileId::kN16_Split: return launch_cfg<In, 4, 4, 2, 32>(p, s);
     case ScanTileId::kN64_Split: return launch_cfg<In, 16, 4, 2, 4>(p, s);
   }
   return hipErrorInvalidValue;
