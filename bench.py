@@ -282,6 +282,7 @@ def main():
         out["ssd"] = bench_ssd(args, torch, ssm, synth)
     if args.decode:
         out["decode"] = bench_decode(args, torch, ssm, synth, cfg)
+        out["ssd_decode"] = bench_ssd_decode(args, torch, ssm, synth)
     if args.grouped:
         out["grouped"] = [bench_grouped(args, torch, ssm, synth, cfg, io, x, g)
                           for g in (8, d)]
@@ -501,6 +502,50 @@ def bench_decode(args, torch, ssm, synth, cfg):
                         "updated in place", "timing": f"{args.steps} steps in one HIP graph",
             "us_per_step": round(us, 3),
             "tokens_per_s": round(b / (us * 1e-6), 1),
+            "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
+
+
+def bench_ssd_decode(args, torch, ssm, synth):
+    """One ssd_state_update per step at the SSD shape (batch 4, 24 heads,
+    headdim 64, dstate 128), state updated in place, steps replayed from a
+    HIP graph."""
+    import numpy as np
+    cfg = synth.SSD_CONFIGS["ssd"]
+    s = synth.ssd_inputs(cfg, seed=12, seqlen=1)
+    dev = torch.device("cuda:0")
+    t = {k: synth.to_device(np.ascontiguousarray(s[k][:, 0]), "bf16", dev)
+         for k in ("x", "dt", "B", "C")}
+    f = {k: synth.to_device(s[k], "f32", dev) for k in ("A", "D", "dt_bias")}
+    b, h, p = t["x"].shape
+    n = t["B"].shape[2]
+    state = torch.zeros((b, h, p, n), dtype=torch.float32, device=dev)
+    y = torch.empty_like(t["x"])
+    handle = ssm.get_handle(0)
+
+    def step():
+        ssm.ssd_state_update(state, t["x"], t["dt"], f["A"], t["B"], t["C"], f["D"],
+                             f["dt_bias"], True, y, handle=handle)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    nbytes = 8 * b * h * p * n + 2 * 2 * b * h * p + 2 * b * h + 2 * 2 * b * n + 12 * h
+    return {"workload": f"SSD decode step: batch {b}, heads {h}, headdim {p}, dstate {n}, bf16, "
+                        "fp32 state updated in place", "timing": f"{args.steps} steps in one HIP graph",
+            "us_per_step": round(us, 3), "tokens_per_s": round(b / (us * 1e-6), 1),
             "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
 
 

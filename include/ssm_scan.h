@@ -288,6 +288,41 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float *state,
                                       ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * One decode step of the Mamba-2 (SSD) recurrence: one new token per
+ * (batch, head), the state updated in place ([CUTILE]: the recurrence with
+ * a scalar A per head; [EXPLAINED] eq. (2): the skip term).  For every
+ * (b, head h) with group g = h / (nheads/ngroups) and every p, n:
+ *
+ *   dt = dt[b,h] + dt_bias[h];  softplus if dt_softplus != 0
+ *   state[b,h,p,n] = exp(dt * A[h]) * state[b,h,p,n] + dt * x[b,h,p] * B[b,g,n]
+ *   y[b,h,p] = sum_n C[b,g,n] * state[b,h,p,n] + D[h] * x[b,h,p]
+ *
+ * This equals ssd_chunk_scan_fwd_with_state over a sequence of one token
+ * with initial_state = state and final_state = state; calling it token
+ * after token gives the chunked scan's y and final state (up to float32
+ * rounding).
+ *
+ * Layouts (row-major):
+ *   state       : [batch, nheads, headdim, dstate] float32, read and written
+ *   x, y        : [batch, nheads, headdim]         in_dtype
+ *   dt          : [batch, nheads]                  in_dtype
+ *   B, C        : [batch, ngroups, dstate]         in_dtype
+ *   A, D, dt_bias : [nheads]                       float32
+ * Nullable: D, dt_bias.  Pointers 16-byte aligned; y and state must not
+ * overlap each other or any input.
+ *
+ * Limits: all sizes >= 1; nheads a multiple of ngroups; dstate <= 256;
+ * batch*nheads*headdim <= 2^40.
+ */
+ssm_status ssd_state_update(ssm_handle handle, float *state, const void *x,
+                            const void *dt, const float *A, const void *B,
+                            const void *C, const float *D,
+                            const float *dt_bias, int dt_softplus, void *y,
+                            int64_t batch, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups,
+                            ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * Workspace size in bytes needed by ssd_chunk_scan_fwd for these sizes
  * (the caller allocates it, so the library never allocates device memory).
  * Returns SSM_ERR_INVALID_ARG / SSM_ERR_UNSUPPORTED for sizes that

@@ -32,7 +32,7 @@ EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
            "ssm_selective_scan_bwd",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_fwd_with_state")
+           "ssd_chunk_scan_fwd_with_state", "ssd_state_update")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -86,6 +86,10 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_scan_fwd_ws.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
             _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_size_t, ctypes.c_int, _vp]
+        lib.ssd_state_update.restype = ctypes.c_int
+        lib.ssd_state_update.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+            _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssm_selective_state_update.restype = ctypes.c_int
         lib.ssm_selective_state_update.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
@@ -459,6 +463,26 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
     y, ls = _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, initial_state,
                                    bool(delta_softplus))
     return (y, ls) if return_last_state else y
+
+
+def ssd_state_update(state, x, dt, A, B, C, D, dt_bias, dt_softplus, y, handle=None) -> None:
+    """One SSD decode step in place: state [batch, nheads, headdim, dstate]
+    float32; x, y [batch, nheads, headdim]; dt [batch, nheads]; B, C
+    [batch, ngroups, dstate]; A, D, dt_bias [nheads]."""
+    for name, t, opt in (("state", state, False), ("x", x, False), ("dt", dt, False),
+                         ("A", A, False), ("B", B, False), ("C", C, False), ("D", D, True),
+                         ("dt_bias", dt_bias, True), ("y", y, False)):
+        _need_cuda_contig(name, t, opt)
+    batch, nheads, headdim = x.shape
+    ngroups, dstate = B.shape[1], B.shape[2]
+    dev = x.device.index if x.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssd_state_update(
+        handle, _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), batch, nheads, headdim, dstate,
+        ngroups, _dtype_code(x), _stream_ptr(x.device))
+    _check("ssd_state_update", st)
 
 
 def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,

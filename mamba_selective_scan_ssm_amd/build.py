@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build", "ssmscan")
 LIB = os.path.join(PKG, "libssmscan.so")
 
 SOURCES = ["api.cpp", "selective_scan.hip", "selective_scan_bwd.hip", "ssd_chunk_scan.hip",
-           "state_update.hip"]
+           "state_update.hip", "ssd_state_update.hip"]
 ARCH = "gfx950"
 
 

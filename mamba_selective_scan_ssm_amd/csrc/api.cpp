@@ -447,6 +447,52 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const voi
   return ok();
 }
 
+ssm_status ssd_state_update(ssm_handle handle, float* state, const void* x, const void* dt,
+                            const float* A, const void* B, const void* C, const float* D,
+                            const float* dt_bias, int dt_softplus, void* y, int64_t batch,
+                            int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                            ssm_dtype in_dtype, hipStream_t stream) {
+  if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+    return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
+  if (nheads % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "nheads must be a multiple of ngroups");
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dstate > 256) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 256", (long long)dstate);
+  if (batch > INT32_MAX || nheads > INT32_MAX || headdim > INT32_MAX ||
+      batch * nheads * headdim > (int64_t(1) << 40))
+    return fail(SSM_ERR_UNSUPPORTED, "batch*nheads*headdim too large");
+  const struct { const char* name; const void* p; } required[] = {
+      {"state", state}, {"x", x}, {"dt", dt}, {"A", A}, {"B", B}, {"C", C}, {"y", y}};
+  for (const auto& r : required)
+    if (!r.p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", r.name);
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t nx = (uint64_t)batch * nheads * headdim;
+  const uint64_t nbc = (uint64_t)batch * ngroups * dstate;
+  const Span in[] = {{"x", x, nx * es},
+                     {"dt", dt, (uint64_t)batch * nheads * es},
+                     {"A", A, (uint64_t)nheads * 4},
+                     {"B", B, nbc * es},
+                     {"C", C, nbc * es},
+                     {"D", D, (uint64_t)nheads * 4},
+                     {"dt_bias", dt_bias, (uint64_t)nheads * 4}};
+  const Span out[] = {{"y", y, nx * es}, {"state", state, nx * dstate * 4}};
+  ssm_status st = check_spans(in, 7, out, 2);
+  if (st != SSM_OK) return st;
+  if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+
+  ssm::SsdStepParams p;
+  p.state = state; p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.dt_bias = dt_bias;
+  p.dt_softplus = dt_softplus ? 1 : 0; p.y = y;
+  p.batch = (int)batch; p.nheads = (int)nheads; p.headdim = (int)headdim;
+  p.dstate = (int)dstate; p.ngroups = (int)ngroups;
+  DeviceGuard guard(handle->device);
+  if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
+  hipError_t e = ssm::launch_ssd_state_update(p, in_dtype == SSM_BF16, stream);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch, int64_t seqlen,
                                          int64_t nheads, int64_t headdim, int64_t dstate,
                                          int64_t ngroups, int64_t chunk_size, size_t* bytes) {

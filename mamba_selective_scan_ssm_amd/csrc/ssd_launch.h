@@ -60,4 +60,21 @@ ssm_status ssd_validate_shape(int64_t batch, int64_t seqlen, int64_t nheads, int
 
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
 
+// One decode step of the SSD recurrence (ssd_state_update.hip).
+struct SsdStepParams {
+  float* state;          // [batch, nheads, headdim, dstate], read and written
+  const void* x;         // [batch, nheads, headdim]
+  const void* dt;        // [batch, nheads]
+  const float* A;        // [nheads]
+  const void* B;         // [batch, ngroups, dstate]
+  const void* C;         // [batch, ngroups, dstate]
+  const float* D;        // [nheads], nullable
+  const float* dt_bias;  // [nheads], nullable
+  int dt_softplus;
+  void* y;               // [batch, nheads, headdim]
+  int batch, nheads, headdim, dstate, ngroups;
+};
+
+hipError_t launch_ssd_state_update(const SsdStepParams& p, bool bf16, hipStream_t stream);
+
 }  // namespace ssm

@@ -187,3 +187,28 @@ def test_grouped_rules():
     assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg, msg
     st, msg = scan_grouped(1, y=P[3] + 512)  # one group: 512 bytes, no overlap
     assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, msg
+
+
+def ssd_step(batch=2, nheads=4, headdim=8, dstate=16, ngroups=2, state=P[9], y=P[10], x=P[0]):
+    lib = ssm.load_library()
+    st = lib.ssd_state_update(None, state, x, P[1], P[2], P[3], P[4], None, None, 1, y,
+                              batch, nheads, headdim, dstate, ngroups, ssm.SSM_F32, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_ssd_state_update_rules():
+    st, msg = ssd_step()
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, msg
+    for kw in ({"batch": 0}, {"nheads": -1}, {"headdim": 0}, {"dstate": 0}, {"ngroups": 0}):
+        st, msg = ssd_step(**kw)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "sizes" in msg, (kw, msg)
+    st, msg = ssd_step(ngroups=3)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "ngroups" in msg, msg
+    st, msg = ssd_step(dstate=257)
+    assert st == ssm.SSM_ERR_UNSUPPORTED and "dstate" in msg, msg
+    st, msg = ssd_step(state=None)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "state" in msg, msg
+    st, msg = ssd_step(y=P[0] + 16)  # overlaps x
+    assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg, msg
+    st, msg = ssd_step(state=P[9] + 4)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg, msg

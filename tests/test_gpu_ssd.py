@@ -156,3 +156,66 @@ def test_ssd_scan_in_pieces(lib, k):
     ry, rf = oracle.ssd_scan(**s)
     check("y", synth.to_host_f64(y), ry)
     check("final_state", synth.to_host_f64(state), rf)
+
+
+# ---------------------------------------------------------------------------
+# Decode step (ssd_state_update)
+# ---------------------------------------------------------------------------
+
+def step_inputs(s, t):
+    """Token t of a sequence in the decode layouts."""
+    return {"x": s["x"][:, t], "dt": s["dt"][:, t], "B": s["B"][:, t], "C": s["C"][:, t]}
+
+
+@pytest.mark.parametrize("shape,dtype", [
+    ((2, 4, 64, 128, 2), "bf16"), ((2, 4, 64, 128, 2), "f32"), ((1, 3, 32, 30, 1), "f32"),
+    ((1, 2, 128, 256, 1), "bf16"), ((3, 6, 16, 5, 3), "f32")])
+def test_ssd_state_update_one_step(lib, shape, dtype):
+    """One token from a given state equals the oracle's scan of a one-token
+    sequence started from that state: y and the new state."""
+    b, h, p, n, g = shape
+    print(f"case ssd step {shape} {dtype}", flush=True)
+    s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=120 + n, batch=b, seqlen=1, nheads=h,
+                         headdim=p, dstate=n, ngroups=g)
+    if dtype == "f32":
+        s = {k: (None if v is None else np.asarray(v, np.float32)) for k, v in s.items()}
+    init = np.random.default_rng(n).standard_normal((b, h, p, n)).astype(np.float32)
+    dev = "cuda"
+    one = step_inputs(s, 0)
+    t = {k: synth.to_device(v, dtype, dev) for k, v in one.items()}
+    f = {k: (None if s[k] is None else synth.to_device(s[k], "f32", dev))
+         for k in ("A", "D", "dt_bias")}
+    state = torch.from_numpy(init).to(dev)
+    y = torch.empty_like(t["x"])
+    lib.ssd_state_update(state, t["x"], t["dt"], f["A"], t["B"], t["C"], f["D"], f["dt_bias"],
+                         True, y)
+    torch.cuda.synchronize()
+    ry, rf = oracle.ssd_scan(**s, initial_state=init.astype(np.float64))
+    check("y", synth.to_host_f64(y), ry[:, 0])
+    check("state", synth.to_host_f64(state), rf)
+
+
+def test_ssd_decode_loop_matches_scan(lib):
+    """48 tokens decoded one at a time from a zero state: every token's y and
+    the final state against the oracle's scan of the whole sequence."""
+    b, L, h, p, n, g = 2, 48, 4, 64, 128, 1
+    print("case ssd decode loop", flush=True)
+    s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=131, batch=b, seqlen=L, nheads=h,
+                         headdim=p, dstate=n, ngroups=g)
+    dev = "cuda"
+    f = {k: (None if s[k] is None else synth.to_device(s[k], "f32", dev))
+         for k in ("A", "D", "dt_bias")}
+    state = torch.zeros((b, h, p, n), dtype=torch.float32, device=dev)
+    ys = []
+    for tt in range(L):
+        t = {k: synth.to_device(np.ascontiguousarray(v), "bf16", dev)
+             for k, v in step_inputs(s, tt).items()}
+        y = torch.empty_like(t["x"])
+        lib.ssd_state_update(state, t["x"], t["dt"], f["A"], t["B"], t["C"], f["D"],
+                             f["dt_bias"], True, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    yg = torch.stack(ys, dim=1)
+    ry, rf = oracle.ssd_scan(**s)
+    check("y", synth.to_host_f64(yg), ry)
+    check("final_state", synth.to_host_f64(state), rf)
