@@ -141,6 +141,14 @@ __device__ __forceinline__ void store_seg(In* __restrict__ p, int64_t base, int 
     if (t0 + k < limit) Elem<In>::store(p, base + t0 + k, v[k]);
 }
 
+// softplus for a row of the given input type: exact log1p for float32
+// inputs, the shorter form for bfloat16 inputs.
+template <typename In>
+__device__ __forceinline__ float softplus_in(float x) {
+  if constexpr (sizeof(In) == 2) return softplus_short_f(x);
+  else return softplus_f(x);
+}
+
 // ---- lane-group exchange (DPP) ---------------------------------------------
 
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }

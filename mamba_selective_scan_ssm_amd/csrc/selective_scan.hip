@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
       for (int j = 0; j < TS; ++j) {
         const float v = dr[j] + bias;
-        dl[j] = prm.delta_softplus ? softplus_f(v) : v;
+        dl[j] = prm.delta_softplus ? softplus_in<In>(v) : v;
       }
       // Steps past the end are the identity (delta = 0).  Rows past `dim`
       // compute on zeros and are never stored.
