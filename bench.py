@@ -83,15 +83,26 @@ def calib_copy(torch):
 
 
 CSRC = os.path.join(ROOT, "mamba_selective_scan_ssm_amd", "csrc")
-KERNEL_SRC = os.path.join(CSRC, "selective_scan.hip")
-SSD_SRC = os.path.join(CSRC, "ssd_chunk_scan.hip")
+# The sources each kernel is compiled from (the kernel file and the headers
+# it includes), in a fixed order: their combined sha256 ties a committed
+# counter summary to the code it was taken on.
+KERNEL_SRC = [os.path.join(CSRC, f) for f in
+              ("selective_scan.hip", "scan_common.h", "device_math.h", "selective_scan_launch.h")]
+SSD_SRC = [os.path.join(CSRC, f) for f in ("ssd_chunk_scan.hip", "device_math.h", "ssd_launch.h")]
 
 
-def measured_traffic(name: str, src: str, per: str = "launch"):
+def sources_sha256(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(name: str, srcs, per: str = "launch"):
     """HBM bytes per launch (or per call) from the committed rocprofv3 counter
     summary profiles/<name>_hbm_traffic.md, if it was taken on the kernel
-    source as it is now (else None)."""
-    import hashlib
+    sources as they are now (else None)."""
     path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -100,9 +111,8 @@ def measured_traffic(name: str, src: str, per: str = "launch"):
         if ":" in line and not line.startswith(("#", " ", "|")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     key = f"traffic_bytes_per_{per}"
-    if fields.get("kernel_source_sha256") != sha or key not in fields:
+    if fields.get("kernel_sources_sha256") != sources_sha256(srcs) or key not in fields:
         return None
     return int(fields[key])
 
