@@ -49,6 +49,23 @@ def mamba1_flops(b, d, n, L):
     return b * d * L * (FLOP_PER_UPDATE * n + FLOP_PER_STEP)
 
 
+# Issue-slot view of the ALU bound.  A wave64 VALU instruction occupies a
+# SIMD for 4 cycles (16 lanes per cycle); v_exp_f32 occupies it for two such
+# slots.  The recurrence needs at least 4 VALU (delta*A2, delta*u*B, state
+# FMA, readout FMA) and one exp per state update: 6 lane-slots.
+SLOTS_PER_UPDATE = 6
+LANE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9   # CUs x SIMDs x lanes x clock
+
+
+def alu_floor(updates, kernel_us):
+    """Time the state updates alone need at full VALU issue rate, and the
+    measured kernel's fraction of it (the per-(b, d, t) work and the readout
+    reduce-scatter come on top of this floor)."""
+    floor_us = updates * SLOTS_PER_UPDATE / LANE_SLOTS_PER_S * 1e6
+    return {"slots_per_update": SLOTS_PER_UPDATE, "floor_us": round(floor_us, 1),
+            "frac": round(floor_us / kernel_us, 4)}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +299,7 @@ def main():
                      "frac": round(achieved_tf / VALU_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(f"selective_scan_fwd_kernel_{cfg.name}", KERNEL_SRC),
                      "kernel": "selective_scan_fwd_kernel", "flops_per_launch": flops},
+        "alu_floor": alu_floor(b * d * L * n, ev_ms * 1e3),
     }
     if not args.no_per_call:
         out["per_call"] = per_call_flushed(torch, step)
