@@ -142,20 +142,6 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
     const int n = slot * NG + k;
     h[k] = (!AGG && prm.h0 && row_ok && n < N) ? prm.h0[rowi * N + n] : 0.0f;
   }
-  if constexpr (!AGG && !RB) {  // (per-row B, C is never split in time)
-    // carry-in of a later segment: (v_0) (+) agg_0 (+) ... (+) agg_{seg-1},
-    // each step h = P h + V with the combine operator of [EXPLAINED] eq. (10)
-    if (seg > 0 && row_ok) {
-      for (int s2 = 0; s2 < seg; ++s2) {
-        const float* ag = prm.seg_agg + ((int64_t)s2 * nrows + rowi) * N * 2;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) {
-          const int n = slot * NG + k;
-          if (n < N) h[k] = __builtin_fmaf(ag[2 * n], h[k], ag[2 * n + 1]);
-        }
-      }
-    }
-  }
   float dsum = 0.0f;  // AGG: sum of delta over the segment (prod a = exp2(A2 dsum))
 
   // Raw chunk data, loaded one chunk ahead of its use.  RB: this row's B
@@ -201,6 +187,35 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 
   const int nchunks = (t_end - t_begin + T - 1) / T;
   load_chunk(t_begin);
+  if constexpr (!AGG && !RB) {  // (per-row B, C is never split in time)
+    // carry-in of a later segment: (v_0) (+) agg_0 (+) ... (+) agg_{seg-1},
+    // each step h = P h + V with the combine operator of [EXPLAINED] eq. (10).
+    // The aggregates of FB segments are loaded before any is folded (clamped
+    // indices, no conditional loads), so their latencies overlap each other
+    // and the first chunk's loads issued above.
+    if (seg > 0 && row_ok) {
+      constexpr int FB = NG <= 4 ? 8 : 2;
+      for (int s0 = 0; s0 < seg; s0 += FB) {
+        float2 ag[FB][NG];
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+          const int s2 = min(s0 + i, seg - 1);
+          const float* base = prm.seg_agg + ((int64_t)s2 * nrows + rowi) * N * 2;
+#pragma unroll
+          for (int k = 0; k < NG; ++k)
+            ag[i][k] = *reinterpret_cast<const float2*>(base + 2 * min(slot * NG + k, N - 1));
+        }
+#pragma unroll
+        for (int i = 0; i < FB; ++i) {
+          if (s0 + i < seg) {
+#pragma unroll
+            for (int k = 0; k < NG; ++k)
+              if (slot * NG + k < N) h[k] = __builtin_fmaf(ag[i][k].x, h[k], ag[i][k].y);
+          }
+        }
+      }
+    }
+  }
   for (int ch = 0; ch < nchunks; ++ch) {
     const int c0 = t_begin + ch * T;
     const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
