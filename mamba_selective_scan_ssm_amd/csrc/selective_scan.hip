@@ -632,6 +632,12 @@ selective_scan_split_kernel(ScanParams prm) {
   }
 }
 
+// Time chunk of the row-parallel kernel for 9..16 states when the sequence
+// is cut into segments: segments are a few chunks long, and 32-step chunks
+// keep the kernel at 140 (float32) / 128 (bf16) VGPRs, so three or four
+// waves fit per SIMD (64-step chunks: 228 / 196, two waves).
+constexpr int kTSeg16 = 32;
+
 template <typename In, int NG, int LPC, int T, bool RB = false, bool AGG = false>
 hipError_t launch_rows(const ScanParams& p, hipStream_t stream, int nz = 1) {
   constexpr int RPB = 4 * (64 / LPC);
@@ -672,7 +678,7 @@ template <typename In, bool AGG>
 hipError_t launch_rows_tier(const ScanParams& p, hipStream_t s, int nz) {
   if (p.dstate <= 4) return launch_rows<In, 4, 1, 16, false, AGG>(p, s, nz);
   if (p.dstate <= 8) return launch_rows<In, 4, 2, 32, false, AGG>(p, s, nz);
-  if (p.dstate <= 16) return launch_rows<In, 4, 4, 64, false, AGG>(p, s, nz);
+  if (p.dstate <= 16) return launch_rows<In, 4, 4, kTSeg16, false, AGG>(p, s, nz);
   return launch_rows<In, 16, 4, 32, false, AGG>(p, s, nz);
 }
 
@@ -706,16 +712,17 @@ hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool
 ScanSegments plan_scan_segments(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                 int num_cus) {
   const int lpc = dstate <= 4 ? 1 : dstate <= 8 ? 2 : 4;
-  const int T = dstate <= 4 ? 16 : dstate <= 8 ? 32 : dstate <= 16 ? 64 : 32;
+  const int T = dstate <= 4 ? 16 : dstate <= 8 ? 32 : dstate <= 16 ? kTSeg16 : 32;
   const int rpb = 256 / lpc;
   ScanSegments sg{1, 0, rpb, 0};
   // Split only when the rows leave SIMDs without a wave (the aggregate pass
   // costs about half a scan of the segments it covers) and the sequence has
-  // at least 8 chunks; aim at four waves per SIMD (measured at the 130M
-  // shape: 87 / 80 / 76 us for one, two, four).
+  // at least 8 chunks; aim at three waves per SIMD, the most that stay
+  // resident together (measured at the 130M shape, float32: 67.5 / 66.3 /
+  // 69.3 us for two, three, four; 75.2 us with 64-step chunks at four).
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   const int64_t waves = batch * ((dim + rpb - 1) / rpb) * 4;
-  const int64_t target = 16 * cus;
+  const int64_t target = 12 * cus;
   const int64_t chunks = (seqlen + T - 1) / T;
   if (waves >= 4 * cus || chunks < 8) return sg;
   const int64_t want = std::min<int64_t>({(target + waves - 1) / waves, chunks, 64});
