@@ -632,6 +632,14 @@ selective_scan_split_kernel(ScanParams prm) {
   }
 }
 
+// Time chunk of the row-parallel kernel for 9..16 states over whole rows:
+// the four lanes of a row then read whole 128-byte lines of u, delta, z and
+// write whole lines of y per chunk (64 bf16 or 32 float32 steps), and
+// float32 rows stay at 140 VGPRs (three waves per SIMD; 1.4B shape in
+// float32: 403 -> 362 us against 64-step chunks).
+template <typename In>
+constexpr int t16_rows() { return sizeof(In) == 4 ? 32 : 64; }
+
 // Time chunk of the row-parallel kernel for 9..16 states when the sequence
 // is cut into segments: segments are a few chunks long, and 32-step chunks
 // keep the kernel at 140 (float32) / 128 (bf16) VGPRs, so three or four
@@ -660,7 +668,7 @@ hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
   switch (t.id) {
     case ScanTileId::kN4_Seq: return launch_rows<In, 4, 1, 16>(p, s);
     case ScanTileId::kN8_Seq: return launch_rows<In, 4, 2, 32>(p, s);
-    case ScanTileId::kN16_Seq: return launch_rows<In, 4, 4, 64>(p, s);
+    case ScanTileId::kN16_Seq: return launch_rows<In, 4, 4, t16_rows<In>()>(p, s);
     case ScanTileId::kN64_Seq: return launch_rows<In, 16, 4, 32>(p, s);
     case ScanTileId::kN4_Split: return launch_cfg<In, 4, 1, 8, 8>(p, s);
     case ScanTileId::kN8_Split: return launch_cfg<In, 4, 2, 4, 16>(p, s);
