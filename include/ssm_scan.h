@@ -167,7 +167,9 @@ ssm_status ssm_selective_scan_fwd_grouped(
 /*
  * Bytes of workspace that ssm_selective_scan_fwd_ws can use for these
  * sizes: 0 when the (batch, channel) rows alone give every SIMD of the
- * device two waves (then no workspace is needed), else the room for one
+ * device a wave, or when the sequence is too short to split (fewer than 8
+ * time chunks of the kernel); then no workspace is needed.  Else the room
+ * for one
  * aggregate (prod a, v) per (segment, row, state) of a time split
  * ([EXPLAINED] eqs. (10)-(11)).  Same size checks as
  * ssm_selective_scan_fwd_grouped; touches no device memory.
