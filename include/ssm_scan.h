@@ -169,8 +169,7 @@ ssm_status ssm_selective_scan_fwd_grouped(
  * sizes: 0 when the (batch, channel) rows alone give every SIMD of the
  * device a wave, or when the sequence is too short to split (fewer than 8
  * time chunks of the kernel); then no workspace is needed.  Else the room
- * for one
- * aggregate (prod a, v) per (segment, row, state) of a time split
+ * for one aggregate (prod a, v) per (segment, row, state) of a time split
  * ([EXPLAINED] eqs. (10)-(11)).  Same size checks as
  * ssm_selective_scan_fwd_grouped; touches no device memory.
  */
