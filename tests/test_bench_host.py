@@ -1,0 +1,69 @@
+"""Host logic of bench.py that needs no GPU: the byte and FLOP counts the
+roofline uses, the issue-slot floor, and how a committed counter summary is
+tied to the kernel sources it was taken on."""
+import os
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_and_flops_at_the_1p4b_shape():
+    b, d, n, L = 8, 4096, 16, 2048
+    # u, delta, z read and y written (bf16), B and C read (bf16), A fp32
+    # [d, n], D and delta_bias fp32 [d], last_state fp32 [b, d, n]
+    expect = 4 * b * d * L * 2 + 2 * b * n * L * 2 + 4 * d * n + 8 * d + 4 * b * d * n
+    assert bench.mamba1_bytes(b, d, n, L, 2) == expect == 540_311_552
+    assert bench.mamba1_flops(b, d, n, L) == b * d * L * (7 * n + 12)
+
+
+def test_alu_floor():
+    updates = 8 * 4096 * 2048 * 16
+    f = bench.alu_floor(updates, 272.0)
+    # 6 lane-slots per update at 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+    floor_us = updates * 6 / (256 * 4 * 16 * 2.4e9) * 1e6
+    assert f["slots_per_update"] == 6
+    assert f["floor_us"] == pytest.approx(floor_us, abs=0.05)
+    assert f["frac"] == pytest.approx(floor_us / 272.0, abs=1e-4)
+
+
+def test_sources_sha256_covers_every_file_in_order(tmp_path):
+    a, b = tmp_path / "a.hip", tmp_path / "b.h"
+    a.write_bytes(b"kernel")
+    b.write_bytes(b"header")
+    h1 = bench.sources_sha256([str(a), str(b)])
+    b.write_bytes(b"header changed")
+    assert bench.sources_sha256([str(a), str(b)]) != h1   # a header change counts
+    b.write_bytes(b"header")
+    assert bench.sources_sha256([str(a), str(b)]) == h1
+    assert bench.sources_sha256([str(b), str(a)]) != h1   # order is part of the key
+
+
+def test_measured_traffic_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_bytes(b"v1")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    sha = bench.sources_sha256([str(src)])
+    (prof / "kern_work_hbm_traffic.md").write_text(
+        "# summary\n\n| a | b |\n|---|---|\n\n"
+        f"kernel_sources_sha256: {sha}\n"
+        "traffic_bytes_per_launch: 12345\n"
+        "traffic_bytes_per_call: 678\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("kern_work", [str(src)]) == 12345
+    assert bench.measured_traffic("kern_work", [str(src)], per="call") == 678
+    assert bench.measured_traffic("missing", [str(src)]) is None
+    src.write_bytes(b"v2")  # the kernel changed since the counters were taken
+    assert bench.measured_traffic("kern_work", [str(src)]) is None
+
+
+def test_committed_summaries_name_existing_sources():
+    for name in ("selective_scan_fwd_kernel_m1p4b_hbm_traffic.md",
+                 "ssd_chunk_scan_ssd_hbm_traffic.md"):
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        line = [l for l in text.splitlines() if l.startswith("kernel_sources:")][0]
+        for rel in line.split(":", 1)[1].split(","):
+            assert os.path.exists(os.path.join(ROOT, rel.strip())), rel
