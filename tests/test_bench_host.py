@@ -67,3 +67,12 @@ def test_committed_summaries_name_existing_sources():
         line = [l for l in text.splitlines() if l.startswith("kernel_sources:")][0]
         for rel in line.split(":", 1)[1].split(","):
             assert os.path.exists(os.path.join(ROOT, rel.strip())), rel
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
