@@ -12,6 +12,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// max(x, 0) for a float that is not NaN, as an integer max of its bits
+// (negative floats, -0 included, are negative integers): one instruction,
+// with no canonicalisation of x as a float max may need.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^{-|x|}).
 // log1p(w) for w in (0, 1] is ln(s) + (w - (s - 1)) / s with s = fl(1 + w);
 // the correction term is below 2^-24 and is used without the division by s
@@ -20,7 +27,7 @@ __device__ __forceinline__ float softplus_f(float x) {
   const float w = fast_exp2(-fabsf(x) * kLog2e);
   const float s = 1.0f + w;
   const float corr = w - (s - 1.0f);
-  return fmaxf(x, 0.0f) + __builtin_fmaf(fast_log2(s), kLn2, corr);
+  return relu_bits(x) + __builtin_fmaf(fast_log2(s), kLn2, corr);
 }
 
 // softplus(x) with log1p(w) taken as ln(fl(1 + w)): the rounding of 1 + w
@@ -29,7 +36,7 @@ __device__ __forceinline__ float softplus_f(float x) {
 // whose own resolution is 2^-9 relative; two VALU instructions fewer.
 __device__ __forceinline__ float softplus_short_f(float x) {
   const float w = fast_exp2(-fabsf(x) * kLog2e);
-  return __builtin_fmaf(fast_log2(1.0f + w), kLn2, fmaxf(x, 0.0f));
+  return __builtin_fmaf(fast_log2(1.0f + w), kLn2, relu_bits(x));
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z})

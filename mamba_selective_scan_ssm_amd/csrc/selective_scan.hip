@@ -268,10 +268,13 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
         for (int j = 0; j < TS; ++j) gk[j] = 1.0f;
       }
+      // (the flag is uniform: one branch around the loop, not a select per step)
+      if (prm.delta_softplus) {
 #pragma unroll
-      for (int j = 0; j < TS; ++j) {
-        const float v = dr[j] + bias;
-        dl[j] = prm.delta_softplus ? softplus_in<In>(v) : v;
+        for (int j = 0; j < TS; ++j) dl[j] = softplus_in<In>(dr[j] + bias);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) dl[j] = dr[j] + bias;
       }
       // Steps past the end are the identity (delta = 0).  Rows past `dim`
       // compute on zeros and are never stored.
