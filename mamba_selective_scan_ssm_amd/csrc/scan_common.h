@@ -47,12 +47,10 @@ template <> struct Elem<uint16_t> {  // bfloat16 bit pattern
     return __builtin_bit_cast(uint16_t, h);
   }
   __device__ static void store(uint16_t* p, int64_t i, float x) { p[i] = narrow(x); }
+  // Eight floats -> eight bf16 (round to nearest even), one conversion per pair.
   __device__ static uint4 pack(const float* x) {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = (uint32_t)narrow(x[2 * k]) | ((uint32_t)narrow(x[2 * k + 1]) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                      pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
   }
 };
 

@@ -327,9 +327,8 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = f32_to_bf16_bits(bf16_bits_to_f32(e[i] & 0xffffu) * w);
-          const uint32_t hi = f32_to_bf16_bits(__uint_as_float(e[i] & 0xffff0000u) * w);
-          o[i] = lo | (hi << 16);
+          o[i] = pack_bf16x2(bf16_bits_to_f32(e[i] & 0xffffu) * w,
+                             __uint_as_float(e[i] & 0xffff0000u) * w);
         }
         *reinterpret_cast<uint4*>(&sX[buf][s][8 * po]) = make_uint4(o[0], o[1], o[2], o[3]);
       }
@@ -395,8 +394,8 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
           const int nt = tile / PT, pt = tile % PT;
           const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
           uint2 o;
-          o.x = (uint32_t)f32_to_bf16_bits(acc[t][0]) | ((uint32_t)f32_to_bf16_bits(acc[t][1]) << 16);
-          o.y = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
+          o.x = pack_bf16x2(acc[t][0], acc[t][1]);
+          o.y = pack_bf16x2(acc[t][2], acc[t][3]);
           *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
         }
       }
@@ -436,7 +435,7 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16_bits(S[2 * i]) | ((uint32_t)f32_to_bf16_bits(S[2 * i + 1]) << 16);
+      o[i] = pack_bf16x2(S[2 * i], S[2 * i + 1]);
     *reinterpret_cast<uint4*>(ptr) = make_uint4(o[0], o[1], o[2], o[3]);
     const float dec = a.decay[((int64_t)b * a.nheads + h) * a.nchunks + c];
     const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -777,8 +776,8 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = __builtin_fmaf(Dh, xs[i], yacc[t][pt][i]);
-        yo[t][pt].x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-        yo[t][pt].y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        yo[t][pt].x = pack_bf16x2(v[0], v[1]);
+        yo[t][pt].y = pack_bf16x2(v[2], v[3]);
       }
     }
     auto store_y = [&]() {
