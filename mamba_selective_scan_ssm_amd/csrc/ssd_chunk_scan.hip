@@ -640,21 +640,15 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     }
   }
   // Keep G^T as bf16: a pair holds s-tiles st0 (slots 0-3) and st0+1 (slots 4-7).
+  auto pack_pair = [](const f32x4& lo, const f32x4& hi) {
+    return as_bf16x8(make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
+  };
   bf16x8 gpk[NPN], gdk[2];
 #pragma unroll
-  for (int p = 0; p < NPN; ++p)
+  for (int p = 0; p < NPN; ++p) gpk[p] = pack_pair(gacc[2 * p], gacc[2 * p + 1]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gpk[p][i] = static_cast<__bf16>(gacc[2 * p][i]);
-      gpk[p][4 + i] = static_cast<__bf16>(gacc[2 * p + 1][i]);
-    }
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gdk[t][i] = static_cast<__bf16>(gdacc[2 * t][i]);
-      gdk[t][4 + i] = static_cast<__bf16>(gdacc[2 * t + 1][i]);
-    }
+  for (int t = 0; t < 2; ++t) gdk[t] = pack_pair(gdacc[2 * t], gdacc[2 * t + 1]);
 
   __syncthreads();  // readers of sBs are done before the head buffers reuse its bytes
   stage(0);
@@ -707,7 +701,7 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     // diagonal.
     auto pair_direct = [&](const bf16x8& g, int st0, int l, float cs_l, bool mask,
                            f32x4 (&acc)[PT]) {
-      bf16x8 mop;
+      uint32_t mw[4];  // M^T elements as bf16 pairs
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int s0 = (st0 + half) * 16 + 4 * q4;
@@ -715,14 +709,16 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
         const float4 dt4 = *reinterpret_cast<const float4*>(&sDt[hh][s0 & (kQMax - 1)]);
         const float csv[4] = {cs4.x, cs4.y, cs4.z, cs4.w};
         const float dtv[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = static_cast<float>(g[half * 4 + i]) * fast_exp2(cs_l - csv[i]) * dtv[i];
-          if (mask && s0 + i > l) v = 0.0f;
-          mop[half * 4 + i] = static_cast<__bf16>(v);
+          v[i] = static_cast<float>(g[half * 4 + i]) * fast_exp2(cs_l - csv[i]) * dtv[i];
+          if (mask && s0 + i > l) v[i] = 0.0f;
         }
+        mw[2 * half] = pack_bf16x2(v[0], v[1]);
+        mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
       }
-      pair_mma(mop, st0, acc);
+      pair_mma(as_bf16x8(make_uint4(mw[0], mw[1], mw[2], mw[3])), st0, acc);
     };
     // Factored form for a pair wholly before the output tile when the decay
     // never grows (cs non-increasing): exp2(cs_l - cs_s) = exp2(cs_l - R)
@@ -730,17 +726,19 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
     // in [0, 1]; dt_s exp2(R - cs_s) is sW.
     auto pair_fact = [&](const bf16x8& g, int st0, float cs_l, f32x4 (&acc)[PT]) {
       const float f = fast_exp2(cs_l - sCs2[hh][(16 * st0 + 31) & (kQMax - 1)]);
-      bf16x8 mop;
+      uint32_t mw[4];  // M^T elements as bf16 pairs
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int s0 = (st0 + half) * 16 + 4 * q4;
         const float4 w4 = *reinterpret_cast<const float4*>(&sW[hh][s0 & (kQMax - 1)]);
         const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
+        float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          mop[half * 4 + i] = static_cast<__bf16>(static_cast<float>(g[half * 4 + i]) * (wv4[i] * f));
+        for (int i = 0; i < 4; ++i) v[i] = static_cast<float>(g[half * 4 + i]) * (wv4[i] * f);
+        mw[2 * half] = pack_bf16x2(v[0], v[1]);
+        mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
       }
-      pair_mma(mop, st0, acc);
+      pair_mma(as_bf16x8(make_uint4(mw[0], mw[1], mw[2], mw[3])), st0, acc);
     };
     if (active) {
       if (fact) {
