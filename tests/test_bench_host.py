@@ -76,3 +76,29 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def _profile(name):
+    return open(os.path.join(ROOT, "profiles", name)).read()
+
+
+def test_committed_trace_agrees_with_bench_event_time():
+    """The kernel trace's average duration of the headline kernel agrees with
+    the HIP-event average bench.py measured in the same traced run (the trace
+    also counts the warm-up launches, so a few percent apart)."""
+    import re
+    text = _profile("selective_scan_fwd_kernel_m1p4b_kernel_trace.md")
+    row = [l for l in text.splitlines() if l.startswith("| `selective_scan_fwd_kernel<")][0]
+    trace_us = float(row.split("|")[3]) / 1000.0
+    event_us = float(re.search(r"selective_scan_fwd_kernel ([0-9.]+) us", text).group(1))
+    assert abs(trace_us - event_us) / event_us < 0.05, (trace_us, event_us)
+
+
+def test_committed_traffic_is_close_to_the_algorithmic_bytes():
+    """HBM bytes measured by FETCH_SIZE/WRITE_SIZE for the headline kernel
+    stay within 5% of the bytes the method must move (no wasted re-reads)."""
+    text = _profile("selective_scan_fwd_kernel_m1p4b_hbm_traffic.md")
+    measured = int([l for l in text.splitlines()
+                    if l.startswith("traffic_bytes_per_launch:")][0].split(":")[1])
+    algorithmic = bench.mamba1_bytes(8, 4096, 16, 2048, 2)
+    assert 0.98 <= measured / algorithmic <= 1.05, measured / algorithmic
