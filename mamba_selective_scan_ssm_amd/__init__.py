@@ -183,6 +183,115 @@ def _need_cuda_contig(name, t, allow_none=False):
         raise ValueError(f"{name} must be contiguous")
 
 
+class _Spec:
+    """Expected dtype and shape of the tensors of one call, checked before
+    anything reaches the library (the C ABI sees only pointers and sizes, so
+    a tensor smaller than its sizes say would be read past its end)."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.device = None
+
+    def _fail(self, msg):
+        raise ValueError(f"{self.fn}: {msg}")
+
+    def tensor(self, name, t, dtype=None, shape=None, optional=False):
+        import torch
+        if t is None:
+            if optional:
+                return
+            self._fail(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            self._fail(f"{name} must be a torch.Tensor")
+        if dtype is not None and t.dtype != dtype:
+            self._fail(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+            self._fail(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if self.device is None:
+            self.device = t.device
+        elif t.device != self.device:
+            self._fail(f"{name} is on {t.device}, other tensors on {self.device}")
+
+    def in_dtype(self, name, t):
+        """The input dtype of the call (float32 or bfloat16), from `t`."""
+        import torch
+        self.tensor(name, t)
+        if t.dtype not in (torch.float32, torch.bfloat16):
+            self._fail(f"{name} must be float32 or bfloat16, got {t.dtype}")
+        return t.dtype
+
+    def ndim(self, name, t, n):
+        self.tensor(name, t)
+        if t.dim() != n:
+            self._fail(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+
+
+def _mamba1_spec(fn, u, delta, A, B, C, D, z, delta_bias, y, last_state, initial_state=None,
+                 grouped=None):
+    """Checks the Mamba-1 forward tensors; returns (batch, dim, dstate,
+    seqlen, ngroups).  grouped: True = B, C must be [batch, ngroups, dstate,
+    seqlen]; False = [batch, dstate, seqlen]; None = either."""
+    import torch
+    sp = _Spec(fn)
+    dt = sp.in_dtype("u", u)
+    sp.ndim("u", u, 3)
+    batch, dim, seqlen = (int(v) for v in u.shape)
+    sp.ndim("A", A, 2)
+    dstate = int(A.shape[1])
+    f32 = torch.float32
+    sp.tensor("A", A, f32, (dim, dstate))
+    sp.tensor("delta", delta, dt, u.shape)
+    four = B is not None and B.dim() == 4
+    if grouped is True and not four:
+        sp._fail(f"B must be [batch, ngroups, dstate, seqlen], got {tuple(B.shape)}")
+    if grouped is False and four:
+        sp._fail(f"B must be [batch, dstate, seqlen], got {tuple(B.shape)}")
+    if four:
+        ngroups = int(B.shape[1])
+        if ngroups < 1 or dim % ngroups:
+            sp._fail(f"ngroups {ngroups} must divide dim {dim}")
+        bshape = (batch, ngroups, dstate, seqlen)
+    else:
+        ngroups = 1
+        bshape = (batch, dstate, seqlen)
+    sp.tensor("B", B, dt, bshape)
+    sp.tensor("C", C, dt, bshape)
+    sp.tensor("D", D, f32, (dim,), optional=True)
+    sp.tensor("z", z, dt, u.shape, optional=True)
+    sp.tensor("delta_bias", delta_bias, f32, (dim,), optional=True)
+    sp.tensor("initial_state", initial_state, f32, (batch, dim, dstate), optional=True)
+    sp.tensor("y", y, dt, u.shape)
+    sp.tensor("last_state", last_state, f32, (batch, dim, dstate), optional=True)
+    return batch, dim, dstate, seqlen, ngroups
+
+
+def _ssd_spec(fn, x, dt, A, B, C, D, dt_bias, y, final_state, initial_state=None,
+              workspace=None):
+    """Checks the SSD chunked-scan tensors; returns (batch, seqlen, nheads,
+    headdim, dstate, ngroups)."""
+    import torch
+    sp = _Spec(fn)
+    ty = sp.in_dtype("x", x)
+    sp.ndim("x", x, 4)
+    batch, seqlen, nheads, headdim = (int(v) for v in x.shape)
+    sp.ndim("B", B, 4)
+    ngroups, dstate = int(B.shape[2]), int(B.shape[3])
+    f32 = torch.float32
+    sp.tensor("dt", dt, ty, (batch, seqlen, nheads))
+    sp.tensor("A", A, f32, (nheads,))
+    sp.tensor("B", B, ty, (batch, seqlen, ngroups, dstate))
+    sp.tensor("C", C, ty, (batch, seqlen, ngroups, dstate))
+    sp.tensor("D", D, f32, (nheads,), optional=True)
+    sp.tensor("dt_bias", dt_bias, f32, (nheads,), optional=True)
+    sp.tensor("initial_state", initial_state, f32, (batch, nheads, headdim, dstate),
+              optional=True)
+    sp.tensor("y", y, ty, x.shape)
+    sp.tensor("final_state", final_state, f32, (batch, nheads, headdim, dstate), optional=True)
+    if workspace is not None:
+        sp.tensor("workspace", workspace, torch.uint8)
+    return batch, seqlen, nheads, headdim, dstate, ngroups
+
+
 def _stream_ptr(device) -> int:
     import torch
     return int(torch.cuda.current_stream(device).cuda_stream)
@@ -192,6 +301,8 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, 
                            last_state, handle=None) -> None:
     """Enqueue the Mamba-1 scan on the current stream (tensor form of the C
     entry point of the same name; y and last_state are caller-allocated)."""
+    _mamba1_spec("ssm_selective_scan_fwd", u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                 grouped=False)
     for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
                          ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
                          ("delta_bias", delta_bias, True), ("y", y, False),
@@ -213,6 +324,8 @@ def ssm_selective_scan_fwd_with_state(u, delta, A, B, C, D, z, delta_bias, delta
                                       initial_state, y, last_state, handle=None) -> None:
     """ssm_selective_scan_fwd with an initial state [batch, dim, dstate]
     float32 (None = zero; may be last_state itself for an in-place update)."""
+    _mamba1_spec("ssm_selective_scan_fwd_with_state", u, delta, A, B, C, D, z, delta_bias, y,
+                 last_state, initial_state, grouped=False)
     for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
                          ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
                          ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
@@ -234,6 +347,8 @@ def ssm_selective_scan_fwd_grouped(u, delta, A, B, C, D, z, delta_bias, delta_so
                                    initial_state, y, last_state, handle=None) -> None:
     """ssm_selective_scan_fwd_with_state with B, C [batch, ngroups, dstate,
     seqlen]: channel d reads group d // (dim // ngroups)."""
+    _mamba1_spec("ssm_selective_scan_fwd_grouped", u, delta, A, B, C, D, z, delta_bias, y,
+                 last_state, initial_state, grouped=True)
     for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
                          ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
                          ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
@@ -271,6 +386,12 @@ def ssm_selective_scan_fwd_ws(u, delta, A, B, C, D, z, delta_bias, delta_softplu
                               initial_state, y, last_state, workspace, handle=None) -> None:
     """ssm_selective_scan_fwd_grouped with a device workspace (uint8 tensor or
     None).  B, C: [batch, dstate, seqlen] or [batch, ngroups, dstate, seqlen]."""
+    _mamba1_spec("ssm_selective_scan_fwd_ws", u, delta, A, B, C, D, z, delta_bias, y, last_state,
+                 initial_state)
+    if workspace is not None:
+        import torch
+        if workspace.dtype != torch.uint8:
+            raise ValueError("ssm_selective_scan_fwd_ws: workspace must be a uint8 tensor")
     for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
                          ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
                          ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
@@ -328,6 +449,23 @@ def ssm_selective_state_update(state, u, delta, A, B, C, D, z, delta_bias, delta
                                handle=None) -> None:
     """One decode step, state [batch, dim, dstate] float32 updated in place;
     u, delta, z, y: [batch, dim]; B, C: [batch, dstate]."""
+    import torch
+    sp = _Spec("ssm_selective_state_update")
+    ty = sp.in_dtype("u", u)
+    sp.ndim("u", u, 2)
+    sp.ndim("A", A, 2)
+    batch, dim = (int(v) for v in u.shape)
+    dstate = int(A.shape[1])
+    f32 = torch.float32
+    sp.tensor("A", A, f32, (dim, dstate))
+    sp.tensor("state", state, f32, (batch, dim, dstate))
+    sp.tensor("delta", delta, ty, (batch, dim))
+    sp.tensor("B", B, ty, (batch, dstate))
+    sp.tensor("C", C, ty, (batch, dstate))
+    sp.tensor("D", D, f32, (dim,), optional=True)
+    sp.tensor("z", z, ty, (batch, dim), optional=True)
+    sp.tensor("delta_bias", delta_bias, f32, (dim,), optional=True)
+    sp.tensor("y", y, ty, (batch, dim))
     for name, t, opt in (("state", state, False), ("u", u, False), ("delta", delta, False),
                          ("A", A, False), ("B", B, False), ("C", C, False), ("D", D, True),
                          ("z", z, True), ("delta_bias", delta_bias, True), ("y", y, False)):
@@ -360,6 +498,23 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, 
                            dinitial_state, workspace, handle=None) -> None:
     """Enqueue the Mamba-1 backward pass (tensor form of the C entry point;
     every gradient and the workspace are caller-allocated)."""
+    import torch
+    batch, dim, dstate, seqlen, _ = _mamba1_spec(
+        "ssm_selective_scan_bwd", u, delta, A, B, C, D, z, delta_bias, du, None, initial_state,
+        grouped=False)
+    sp = _Spec("ssm_selective_scan_bwd")
+    f32 = torch.float32
+    sp.tensor("dy", dy, u.dtype, u.shape)
+    sp.tensor("dlast_state", dlast_state, f32, (batch, dim, dstate), optional=True)
+    sp.tensor("ddelta", ddelta, u.dtype, u.shape)
+    sp.tensor("dz", dz, u.dtype, u.shape, optional=z is None)
+    sp.tensor("dA", dA, f32, (dim, dstate))
+    sp.tensor("dB", dB, f32, (batch, dstate, seqlen))
+    sp.tensor("dC", dC, f32, (batch, dstate, seqlen))
+    sp.tensor("dD", dD, f32, (dim,), optional=True)
+    sp.tensor("ddelta_bias", ddelta_bias, f32, (dim,), optional=True)
+    sp.tensor("dinitial_state", dinitial_state, f32, (batch, dim, dstate), optional=True)
+    sp.tensor("workspace", workspace, torch.uint8)
     for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
                          ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
                          ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
@@ -469,6 +624,22 @@ def ssd_state_update(state, x, dt, A, B, C, D, dt_bias, dt_softplus, y, handle=N
     """One SSD decode step in place: state [batch, nheads, headdim, dstate]
     float32; x, y [batch, nheads, headdim]; dt [batch, nheads]; B, C
     [batch, ngroups, dstate]; A, D, dt_bias [nheads]."""
+    import torch
+    sp = _Spec("ssd_state_update")
+    ty = sp.in_dtype("x", x)
+    sp.ndim("x", x, 3)
+    sp.ndim("B", B, 3)
+    batch, nheads, headdim = (int(v) for v in x.shape)
+    ngroups, dstate = int(B.shape[1]), int(B.shape[2])
+    f32 = torch.float32
+    sp.tensor("state", state, f32, (batch, nheads, headdim, dstate))
+    sp.tensor("dt", dt, ty, (batch, nheads))
+    sp.tensor("A", A, f32, (nheads,))
+    sp.tensor("B", B, ty, (batch, ngroups, dstate))
+    sp.tensor("C", C, ty, (batch, ngroups, dstate))
+    sp.tensor("D", D, f32, (nheads,), optional=True)
+    sp.tensor("dt_bias", dt_bias, f32, (nheads,), optional=True)
+    sp.tensor("y", y, ty, x.shape)
     for name, t, opt in (("state", state, False), ("x", x, False), ("dt", dt, False),
                          ("A", A, False), ("B", B, False), ("C", C, False), ("D", D, True),
                          ("dt_bias", dt_bias, True), ("y", y, False)):
@@ -500,6 +671,8 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D, dt_bias, dt_softplus, y, final_state, 
                        chunk_size, handle=None) -> None:
     """Enqueue the Mamba-2 chunked scan on the current stream (tensor form of
     the C entry point; y, final_state and workspace are caller-allocated)."""
+    _ssd_spec("ssd_chunk_scan_fwd", x, dt, A, B, C, D, dt_bias, y, final_state,
+              workspace=workspace)
     for name, t, opt in (("x", x, False), ("dt", dt, False), ("A", A, False), ("B", B, False),
                          ("C", C, False), ("D", D, True), ("dt_bias", dt_bias, True),
                          ("y", y, False), ("final_state", final_state, True),
@@ -522,6 +695,8 @@ def ssd_chunk_scan_fwd_with_state(x, dt, A, B, C, D, dt_bias, dt_softplus, initi
                                   final_state, workspace, chunk_size, handle=None) -> None:
     """ssd_chunk_scan_fwd with an initial state [batch, nheads, headdim,
     dstate] float32 (None = zero; may be final_state itself)."""
+    _ssd_spec("ssd_chunk_scan_fwd_with_state", x, dt, A, B, C, D, dt_bias, y, final_state,
+              initial_state, workspace=workspace)
     for name, t, opt in (("x", x, False), ("dt", dt, False), ("A", A, False), ("B", B, False),
                          ("C", C, False), ("D", D, True), ("dt_bias", dt_bias, True),
                          ("initial_state", initial_state, True), ("y", y, False),

@@ -16,7 +16,19 @@ def test_algorithmic_bytes_and_flops_at_the_1p4b_shape():
     # [d, n], D and delta_bias fp32 [d], last_state fp32 [b, d, n]
     expect = 4 * b * d * L * 2 + 2 * b * n * L * 2 + 4 * d * n + 8 * d + 4 * b * d * n
     assert bench.mamba1_bytes(b, d, n, L, 2) == expect == 540_311_552
-    assert bench.mamba1_flops(b, d, n, L) == b * d * L * (7 * n + 12)
+
+
+def test_ssd_work_and_bytes_at_the_ssd_shape():
+    b, L, h, p, n, g, Q = 4, 4096, 24, 64, 128, 1, 256
+    nc = L // Q
+    # C B^T per (b, chunk, group), masked product, chunk states and
+    # state-to-output per (b, chunk, head)
+    flops = 2 * Q * Q * n * b * nc * g + 2 * Q * Q * p * b * nc * h + 2 * (2 * Q * n * p) * b * nc * h
+    assert bench.ssd_flops(b, L, h, p, n, g, Q) == flops == 26_843_545_600
+    # x, y (bf16), dt (bf16), B, C (bf16), A/D/dt_bias fp32, final_state fp32
+    nbytes = 2 * b * L * h * p * 2 + b * L * h * 2 + 2 * b * L * g * n * 2 + 12 * h + 4 * b * h * p * n
+    assert bench.ssd_bytes(b, L, h, p, n, g) == nbytes
+    assert abs(nbytes - 113.0e6) < 0.1e6
 
 
 def test_alu_floor():
