@@ -209,6 +209,32 @@ ssm_status ssm_selective_scan_fwd_ws(
     ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * ssm_selective_scan_fwd_ws for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc.  It takes no workspace and allocates nothing; when the
+ * time split applies, its aggregates go to a scratch array of
+ * SSM_NOALLOC_SCRATCH_BYTES that the library keeps on each GPU it runs on
+ * (a file-scope device array, held until the process ends).  Every plan of
+ * the time split on a 256-CU gfx950 device fits in it; a plan that would
+ * not returns SSM_ERR_UNSUPPORTED before any device work.
+ *
+ * The scratch is shared by every call on the same GPU and keeps the last
+ * call's contents; no part of it needs to start at zero (a call writes
+ * every entry it reads).  Calls on one GPU whose device work overlaps in
+ * time (different streams, different threads, different handles) race on
+ * it and must be serialised by the caller, e.g. by issuing them on one
+ * stream.  Arguments, layouts, limits, results and every other error are
+ * those of ssm_selective_scan_fwd_ws (with the workspace it would use).
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ssm_status ssm_selective_scan_fwd_noalloc(
+    ssm_handle handle, const void *u, const void *delta, const float *A,
+    const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, const float *initial_state,
+    void *y, float *last_state, int64_t batch, int64_t dim, int64_t dstate,
+    int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * Workspace size in bytes needed by ssm_selective_scan_bwd for these sizes
  * (caller-allocated).  Same size checks as ssm_selective_scan_bwd.
  */

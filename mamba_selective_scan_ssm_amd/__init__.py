@@ -28,7 +28,7 @@ SSM_F32, SSM_BF16 = 0, 1
 EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
            "ssm_selective_scan_fwd_grouped", "ssm_selective_scan_fwd_workspace_size",
-           "ssm_selective_scan_fwd_ws",
+           "ssm_selective_scan_fwd_ws", "ssm_selective_scan_fwd_noalloc",
            "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
            "ssm_selective_scan_bwd",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
@@ -86,6 +86,10 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_scan_fwd_ws.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
             _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_size_t, ctypes.c_int, _vp]
+        lib.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
+        lib.ssm_selective_scan_fwd_noalloc.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssd_state_update.restype = ctypes.c_int
         lib.ssd_state_update.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
@@ -411,6 +415,32 @@ def ssm_selective_scan_fwd_ws(u, delta, A, B, C, D, z, delta_bias, delta_softplu
         _ptr(last_state), batch, dim, dstate, seqlen, ngroups, _ptr(workspace), nbytes,
         _dtype_code(u), _stream_ptr(u.device))
     _check("ssm_selective_scan_fwd_ws", st)
+
+
+def ssm_selective_scan_fwd_noalloc(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                   initial_state, y, last_state, handle=None) -> None:
+    """ssm_selective_scan_fwd_ws without a workspace argument: the time split
+    uses the library's per-GPU scratch array, so the call allocates nothing
+    (calls on one GPU that overlap in time race on that scratch).  B, C:
+    [batch, dstate, seqlen] or [batch, ngroups, dstate, seqlen]."""
+    _, _, _, _, ngroups = _mamba1_spec("ssm_selective_scan_fwd_noalloc", u, delta, A, B, C, D,
+                                       z, delta_bias, y, last_state, initial_state)
+    for name, t, opt in (("u", u, False), ("delta", delta, False), ("A", A, False),
+                         ("B", B, False), ("C", C, False), ("D", D, True), ("z", z, True),
+                         ("delta_bias", delta_bias, True), ("initial_state", initial_state, True),
+                         ("y", y, False), ("last_state", last_state, True)):
+        _need_cuda_contig(name, t, opt)
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    dev = u.device.index if u.device.index is not None else 0
+    if handle is None:
+        handle = get_handle(dev)
+    st = load_library().ssm_selective_scan_fwd_noalloc(
+        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(y),
+        _ptr(last_state), batch, dim, dstate, seqlen, ngroups, _dtype_code(u),
+        _stream_ptr(u.device))
+    _check("ssm_selective_scan_fwd_noalloc", st)
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,

@@ -6,8 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "selective_scan_launch.h"
 #include "ssd_launch.h"
@@ -17,6 +19,7 @@ struct ssm_scan_context {
   int device;
   int num_cus;
   char arch[64];
+  void* scratch;  // device address of this device's no-allocation scratch
 };
 
 namespace {
@@ -35,6 +38,29 @@ ssm_status fail(ssm_status st, const char* fmt, ...) {
 
 ssm_status ok() {
   g_last_error.clear();
+  return SSM_OK;
+}
+
+// Device address of the no-allocation scratch, looked up once per device
+// (hipGetSymbolAddress with that device current) and kept for the process.
+ssm_status scratch_for_device(int device, void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= device) addr.resize(device + 1, nullptr);
+  if (!addr[device]) {
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != device) e = hipSetDevice(device);
+    void* p = nullptr;
+    if (e == hipSuccess) e = ssm::scan_scratch_address(&p);
+    if (prev >= 0 && prev != device) (void)hipSetDevice(prev);
+    if (e != hipSuccess || !p)
+      return fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", device,
+                  hipGetErrorString(e));
+    addr[device] = p;
+  }
+  *out = addr[device];
   return SSM_OK;
 }
 
@@ -137,10 +163,14 @@ ssm_status ssm_scan_create(ssm_handle* out, int hip_device) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(SSM_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
                 hip_device, prop.gcnArchName);
+  void* scratch = nullptr;
+  const ssm_status sst = scratch_for_device(hip_device, &scratch);
+  if (sst != SSM_OK) return sst;
   ssm_scan_context* h = new (std::nothrow) ssm_scan_context;
   if (!h) return fail(SSM_ERR_HIP, "out of host memory");
   h->device = hip_device;
   h->num_cus = prop.multiProcessorCount;
+  h->scratch = scratch;
   std::snprintf(h->arch, sizeof(h->arch), "%s", prop.gcnArchName);
   *out = h;
   return ok();
@@ -161,7 +191,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
                                const float* initial_state, void* y, float* last_state,
                                int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                int64_t ngroups, void* workspace, size_t workspace_bytes,
-                               ssm_dtype in_dtype, hipStream_t stream) {
+                               ssm_dtype in_dtype, hipStream_t stream, bool use_scratch = false) {
   // ---- sizes -------------------------------------------------------------
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
@@ -207,6 +237,13 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   // given (groups must cover whole workgroups of the row-parallel kernel)
   ssm::ScanSegments sg = ssm::plan_scan_segments(batch, dim, dstate, seqlen, handle->num_cus);
   if (ngroups > 1 && (dim / ngroups) % sg.rows_per_workgroup != 0) sg.nseg = 1;
+  if (use_scratch) {  // the device's own scratch array stands in for the workspace
+    workspace = handle->scratch;
+    workspace_bytes = ssm::kNoAllocScratchBytes;
+    if (sg.nseg > 1 && !in_place && sg.bytes > workspace_bytes)
+      return fail(SSM_ERR_UNSUPPORTED, "time split needs %zu bytes of scratch, more than the "
+                  "%zu of the no-allocation entry point", sg.bytes, workspace_bytes);
+  }
   // (not in place: the last segment writes last_state while other segments
   // may still have to read the initial state)
   const bool segmented = sg.nseg > 1 && workspace != nullptr && !in_place;
@@ -311,6 +348,19 @@ ssm_status ssm_selective_scan_fwd_ws(ssm_handle handle, const void* u, const voi
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
                              workspace, workspace_bytes, in_dtype, stream);
+}
+
+ssm_status ssm_selective_scan_fwd_noalloc(ssm_handle handle, const void* u, const void* delta,
+                                          const float* A, const void* B, const void* C,
+                                          const float* D, const void* z,
+                                          const float* delta_bias, int delta_softplus,
+                                          const float* initial_state, void* y,
+                                          float* last_state, int64_t batch, int64_t dim,
+                                          int64_t dstate, int64_t seqlen, int64_t ngroups,
+                                          ssm_dtype in_dtype, hipStream_t stream) {
+  return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                             initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
+                             nullptr, 0, in_dtype, stream, /*use_scratch=*/true);
 }
 
 ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,

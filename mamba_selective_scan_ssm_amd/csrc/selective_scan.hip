@@ -681,7 +681,17 @@ hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Scratch of the no-allocation entry point (the time-split aggregates).
+// Every GPU the library runs on holds its own copy until the process ends.
+// Host code must not pass this name to a kernel: it is a host-side stand-in
+// for the symbol; the device address comes from scan_scratch_address().
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 }  // namespace
+
+hipError_t scan_scratch_address(void** out) {
+  return hipGetSymbolAddress(out, HIP_SYMBOL(scratch));
+}
 
 // Row-parallel shape per dstate tier: (NG, LPC, T) = (4,1,16) / (4,2,32) /
 // (4,4,64) / (16,4,32) for dstate <= 4 / 8 / 16 / 64.

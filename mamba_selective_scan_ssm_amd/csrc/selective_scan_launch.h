@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm_scan.h"
+
 namespace ssm {
 
 // Device pointers and sizes of one ssm_selective_scan_fwd call (already
@@ -70,6 +72,20 @@ ScanSegments plan_scan_segments(int64_t batch, int64_t dim, int64_t dstate, int6
 // p.seg_agg must point at sg.bytes of workspace.
 hipError_t launch_selective_scan_segmented(const ScanParams& p, const ScanSegments& sg, bool bf16,
                                            hipStream_t stream);
+
+// Scratch of ssm_selective_scan_fwd_noalloc: a file-scope device array in
+// selective_scan.hip, one copy per GPU, holding the time-split aggregates.
+// Every plan of plan_scan_segments fits on a 256-CU device: a split is
+// planned only when the rows give W < 4*CUs waves, into nseg <=
+// ceil(12*CUs / W) segments, and the rows of W waves hold at most W*64*NG
+// (row, state) pairs (NG <= 16 states per lane), so the (nseg-1) aggregates
+// of 8 bytes per pair take < (12*CUs + W) * 512 * NG < 8192 * NG * CUs
+// bytes = 32 MiB.
+constexpr size_t kNoAllocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+
+// Device address of that array on the current device (hipGetSymbolAddress;
+// call once per device with the device current).
+hipError_t scan_scratch_address(void** out);
 
 // Forward pass that saves the state entering every 16-step chunk into
 // p.chunk_states (dstate <= 16; y and last_state may be null).

@@ -212,3 +212,48 @@ def test_ssd_state_update_rules():
     assert st == ssm.SSM_ERR_INVALID_ARG and "overlap" in msg, msg
     st, msg = ssd_step(state=P[9] + 4)
     assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg, msg
+
+
+def test_noalloc_entry_checks_arguments_before_the_handle():
+    lib = ssm.load_library()
+    st = lib.ssm_selective_scan_fwd_noalloc(None, P[0], P[1], P[2], P[3], P[4], None, None, None,
+                                            1, None, P[5], None, 0, 4, 4, 8, 1, ssm.SSM_F32,
+                                            None)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "batch" in ssm.ssm_last_error_message()
+    st = lib.ssm_selective_scan_fwd_noalloc(None, P[0], P[1], P[2], P[3], P[4], None, None, None,
+                                            1, None, P[5], None, 2, 4, 4, 8, 1, ssm.SSM_F32,
+                                            None)
+    assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in ssm.ssm_last_error_message()
+
+
+def test_noalloc_scratch_bound_covers_every_plan():
+    """The scratch of the no-allocation entry point (32 MiB) holds the
+    aggregates of every time-split plan on a 256-CU device: the planner's
+    rule replayed here over a sweep of shapes (split only below 4 waves per
+    CU, at most ceil(12 CUs / waves) and 64 segments, segments of whole
+    chunks)."""
+    import math
+    cus, limit = 256, 32 << 20
+    worst = 0
+    for dstate in (1, 4, 5, 8, 9, 16, 17, 33, 64):
+        lpc = 1 if dstate <= 4 else 2 if dstate <= 8 else 4
+        T = 16 if dstate <= 4 else 32
+        rpb = 256 // lpc
+        for batch in (1, 2, 3, 7, 16, 64):
+            for dim in (1, 63, 64, 65, 200, 256, 1000, 1536, 4095, 4096, 16384):
+                waves = batch * math.ceil(dim / rpb) * 4
+                if waves >= 4 * cus:
+                    continue
+                for seqlen in (8 * T, 1000, 4096, 1 << 20):
+                    chunks = math.ceil(seqlen / T)
+                    if chunks < 8:
+                        continue
+                    want = min(math.ceil(12 * cus / waves), chunks, 64)
+                    if want <= 1:
+                        continue
+                    seg_len = math.ceil(math.ceil(seqlen / want) / T) * T
+                    nseg = math.ceil(seqlen / seg_len)
+                    if nseg <= 1:
+                        continue
+                    worst = max(worst, (nseg - 1) * batch * dim * dstate * 8)
+    assert 0 < worst < limit, worst
