@@ -188,32 +188,14 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   const int nchunks = (t_end - t_begin + T - 1) / T;
   load_chunk(t_begin);
   if constexpr (!AGG && !RB) {  // (per-row B, C is never split in time)
-    // carry-in of a later segment: (v_0) (+) agg_0 (+) ... (+) agg_{seg-1},
-    // each step h = P h + V with the combine operator of [EXPLAINED] eq. (10).
-    // The aggregates of FB segments are loaded before any is folded (clamped
-    // indices, no conditional loads), so their latencies overlap each other
-    // and the first chunk's loads issued above.
+    // carry-in of a later segment, (v_0) (+) agg_0 (+) ... (+) agg_{seg-1}
+    // with the combine operator of [EXPLAINED] eq. (10): left in slot seg-1
+    // by segment_carry_kernel.
     if (seg > 0 && row_ok) {
-      constexpr int FB = NG <= 4 ? 8 : 2;
-      for (int s0 = 0; s0 < seg; s0 += FB) {
-        float2 ag[FB][NG];
+      const float* cin = prm.seg_agg + ((int64_t)(seg - 1) * nrows + rowi) * N * 2;
 #pragma unroll
-        for (int i = 0; i < FB; ++i) {
-          const int s2 = min(s0 + i, seg - 1);
-          const float* base = prm.seg_agg + ((int64_t)s2 * nrows + rowi) * N * 2;
-#pragma unroll
-          for (int k = 0; k < NG; ++k)
-            ag[i][k] = *reinterpret_cast<const float2*>(base + 2 * min(slot * NG + k, N - 1));
-        }
-#pragma unroll
-        for (int i = 0; i < FB; ++i) {
-          if (s0 + i < seg) {
-#pragma unroll
-            for (int k = 0; k < NG; ++k)
-              if (slot * NG + k < N) h[k] = __builtin_fmaf(ag[i][k].x, h[k], ag[i][k].y);
-          }
-        }
-      }
+      for (int k = 0; k < NG; ++k)
+        if (slot * NG + k < N) h[k] = cin[2 * (slot * NG + k) + 1];
     }
   }
   for (int ch = 0; ch < nchunks; ++ch) {
@@ -388,6 +370,108 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
     for (int k = 0; k < NG; ++k)
       if (slot * NG + k < N) ls[slot * NG + k] = h[k];
+  }
+}
+
+// ---- carry-ins of the time segments --------------------------------------------
+
+// One step of the inclusive scan below: combine this lane's (a, v) with the
+// pair of the lane CTRL selects (the earlier one, on the left of the combine
+// operator of [EXPLAINED] eq. (10)); lanes without a source, or outside
+// ROW_MASK, take the identity (1, 0).
+template <int CTRL, int ROW_MASK, int K>
+__device__ __forceinline__ void scan_step(float (&a)[K], float (&v)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float ap = __int_as_float(__builtin_amdgcn_update_dpp(
+        __float_as_int(1.0f), __float_as_int(a[k]), CTRL, ROW_MASK, 0xF, false));
+    const float vp = __int_as_float(__builtin_amdgcn_update_dpp(
+        0, __float_as_int(v[k]), CTRL, ROW_MASK, 0xF, false));
+    v[k] = __builtin_fmaf(a[k], vp, v[k]);  // (ap, vp) (+) (a, v) = (a ap, a vp + v)
+    a[k] *= ap;
+  }
+}
+
+// Inclusive scans of K independent sequences of (a, v) pairs, each over the
+// 64 lanes of the wave, lane order = sequence order ([EXPLAINED] eqs.
+// (10)-(12) and the doubling prefix-sum figure): four doubling steps inside
+// each 16-lane row (DPP row_shr by 1, 2, 4, 8), then the totals of rows 0
+// and 2 are combined into rows 1 and 3 (row_bcast:15) and the total of rows
+// 0-1 into rows 2-3 (row_bcast:31).  The K scans are interleaved so that
+// their dependent chains overlap.
+template <int K>
+__device__ __forceinline__ void wave_inclusive_scan(float (&a)[K], float (&v)[K]) {
+  scan_step<0x111, 0xF>(a, v);
+  scan_step<0x112, 0xF>(a, v);
+  scan_step<0x114, 0xF>(a, v);
+  scan_step<0x118, 0xF>(a, v);
+  scan_step<0x142, 0xA>(a, v);
+  scan_step<0x143, 0xC>(a, v);
+}
+
+// Carry-ins of the time segments from their aggregates.  slots[s][pair]
+// holds (prod a, v) of one segment per (row, state) pair, nslots <= 64 of
+// them; on return its v part holds the state entering the neighbouring
+// segment: the exclusive combine-scan of the aggregates, started from
+// init[pair] (or zero).
+//   REV = false (forward scan): slot s holds segment s's aggregate and gets
+//     the carry-in of segment s + 1 = init (+) agg_0 (+) ... (+) agg_s.
+//   REV = true (adjoint, scanned from the right): slot s holds the
+//     aggregate of segment s + 1 and gets the adjoint entering segment s
+//     from the right = init (+) agg_{nslots} (+) ... (+) agg_{s+1}.
+// A workgroup takes 64 pairs: it stages their slots in LDS with coalesced
+// loads (all issued before any is used), each wave scans 16 pairs, eight at
+// a time, with lane = segment, and the carries go back with coalesced
+// stores.
+template <bool REV>
+__global__ void __launch_bounds__(256) segment_carry_kernel(float2* __restrict__ slots, int nslots,
+                                                          int64_t npairs,
+                                                          const float* __restrict__ init) {
+  constexpr int PB = 64, PER = 64 * PB / 256, ILP = 8;
+  __shared__ float2 tile[64][PB + 1];
+  __shared__ float sInit[PB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t p0 = (int64_t)blockIdx.x * PB;
+  const int np = (int)min<int64_t>(PB, npairs - p0);
+  float2 ld[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // clamped indices, no condition on the loads
+    const int e = tid + 256 * i;
+    const int s = min(e / PB, nslots - 1), p = min(e % PB, np - 1);
+    ld[i] = slots[(int64_t)s * npairs + p0 + p];
+  }
+  const float h0 = init ? init[p0 + min(tid & (PB - 1), np - 1)] : 0.0f;
+  if (tid < PB) sInit[tid] = h0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + 256 * i;
+    if (e / PB < nslots) tile[e / PB][e % PB] = ld[i];
+  }
+  __syncthreads();
+  const int s = REV ? nslots - 1 - lane : lane;  // this lane's slot
+  const bool on = lane < nslots;
+#pragma unroll
+  for (int r = 0; r < PB / 4; r += ILP) {
+    float a[ILP], v[ILP];
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+      const int p = wv + 4 * (r + k);  // pairs past np compute on stale tile entries, unused
+      const float2 g = tile[on ? s : 0][p];
+      a[k] = on ? g.x : 1.0f;
+      v[k] = on ? g.y : 0.0f;
+    }
+    wave_inclusive_scan(a, v);
+#pragma unroll
+    for (int k = 0; k < ILP; ++k) {
+      const int p = wv + 4 * (r + k);
+      if (on && p < np) tile[s][p].y = __builtin_fmaf(a[k], sInit[p], v[k]);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nslots * PB; e += 256) {
+    const int s2 = e / PB, p = e % PB;
+    if (p < np) slots[(int64_t)s2 * npairs + p0 + p] = tile[s2][p];
   }
 }
 
@@ -703,6 +787,20 @@ hipError_t launch_rows_tier(const ScanParams& p, hipStream_t s, int nz) {
   return launch_rows<In, 16, 4, 32, false, AGG>(p, s, nz);
 }
 
+hipError_t launch_segment_carry(float* slots, int nslots, int64_t npairs, const float* init,
+                                bool reverse, hipStream_t stream) {
+  if (nslots < 1 || nslots > 64) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((npairs + 63) / 64));
+  float2* s2 = reinterpret_cast<float2*>(slots);
+  if (reverse)
+    hipLaunchKernelGGL(segment_carry_kernel<true>, grid, dim3(256), 0, stream, s2, nslots, npairs,
+                       init);
+  else
+    hipLaunchKernelGGL(segment_carry_kernel<false>, grid, dim3(256), 0, stream, s2, nslots,
+                       npairs, init);
+  return hipGetLastError();
+}
+
 hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream) {
   // the row-parallel kernel with 16-step chunks: a saved state every 16 steps.
   // With p.seg_len > 0 (a multiple of 64), the segments' aggregates are
@@ -711,8 +809,11 @@ hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_
   if (nz > 1) {
     ScanParams q = p;
     q.chunk_states = nullptr;
-    const hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(q, stream, nz - 1)
-                              : launch_rows_tier<float, true>(q, stream, nz - 1);
+    hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(q, stream, nz - 1)
+                        : launch_rows_tier<float, true>(q, stream, nz - 1);
+    if (e != hipSuccess) return e;
+    e = launch_segment_carry(p.seg_agg, nz - 1, (int64_t)p.batch * p.dim * p.dstate, p.h0, false,
+                             stream);
     if (e != hipSuccess) return e;
   }
   if (bf16) {
@@ -763,6 +864,9 @@ hipError_t launch_selective_scan_segmented(const ScanParams& p0, const ScanSegme
   p.seg_len = sg.seg_len;
   hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(p, stream, sg.nseg - 1)
                       : launch_rows_tier<float, true>(p, stream, sg.nseg - 1);
+  if (e != hipSuccess) return e;
+  e = launch_segment_carry(p.seg_agg, sg.nseg - 1, (int64_t)p.batch * p.dim * p.dstate, p.h0,
+                           false, stream);
   if (e != hipSuccess) return e;
   return bf16 ? launch_rows_tier<uint16_t, false>(p, stream, sg.nseg)
               : launch_rows_tier<float, false>(p, stream, sg.nseg);

@@ -129,18 +129,13 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
     dA_acc[k] = 0.0f;
   }
   // adjoint entering the segment from the right: the later segments'
-  // aggregates (P, V) folded onto dlast, latest first (lam <- P lam + V)
+  // aggregates (P, V) combined onto dlast, latest first (lam <- P lam + V),
+  // left in slot seg by the reverse segment_carry_kernel
   if (seg + 1 < lay.nseg && row_ok) {
-    const float* lag = reinterpret_cast<const float*>(
-        static_cast<const char*>(P.workspace) + lay.lam_agg_off);
-    for (int s2 = lay.nseg - 1; s2 > seg; --s2) {
-      const float* ag = lag + ((int64_t)(s2 - 1) * rows + row) * N * 2;
+    const float* cin = reinterpret_cast<const float*>(
+        static_cast<const char*>(P.workspace) + lay.lam_agg_off) + ((int64_t)seg * rows + row) * N * 2;
 #pragma unroll
-      for (int k = 0; k < NG; ++k) {
-        const int n = min(slot * NG + k, N - 1);
-        lam[k] = __builtin_fmaf(ag[2 * n], lam[k], ag[2 * n + 1]);
-      }
-    }
+    for (int k = 0; k < NG; ++k) lam[k] = cin[2 * min(slot * NG + k, N - 1) + 1];
   }
   const float Dd = (row_ok && F.D) ? F.D[d] : 0.0f;
   const float bias = (row_ok && F.delta_bias) ? F.delta_bias[d] : 0.0f;
@@ -576,7 +571,12 @@ hipError_t launch_bwd_rows(const BwdParams& p, const BwdLayout& lay, hipStream_t
   if (lay.nseg > 1) {
     dim3 ga((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)(lay.nseg - 1));
     hipLaunchKernelGGL((bwd_lambda_agg_kernel<In, LPC>), ga, dim3(256), 0, stream, p, lay);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_segment_carry(reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
+                                                      lay.lam_agg_off),
+                             lay.nseg - 1, (int64_t)p.fwd.batch * p.fwd.dim * p.fwd.dstate,
+                             p.dlast, true, stream);
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)lay.nseg);

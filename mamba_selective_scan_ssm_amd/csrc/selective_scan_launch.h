@@ -87,6 +87,15 @@ constexpr size_t kNoAllocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
 // call once per device with the device current).
 hipError_t scan_scratch_address(void** out);
 
+// Carry-ins of the time segments from their aggregates (in place), by a
+// wave-level combine scan per (row, state) pair: slots [nslots][npairs]
+// float2 (prod a, v), 1 <= nslots <= 64; init [npairs] nullable (zero).
+// reverse = false: slot s gets the state entering segment s + 1; true (an
+// adjoint scanned from the right): slot s holds segment s + 1's aggregate
+// and gets the adjoint entering segment s.
+hipError_t launch_segment_carry(float* slots, int nslots, int64_t npairs, const float* init,
+                                bool reverse, hipStream_t stream);
+
 // Forward pass that saves the state entering every 16-step chunk into
 // p.chunk_states (dstate <= 16; y and last_state may be null).
 hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream);
