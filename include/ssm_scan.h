@@ -385,7 +385,11 @@ ssm_status ssd_chunk_scan_workspace_size(ssm_handle handle, int64_t batch,
  * caller-owned, contents need not be initialised; it is overwritten).
  *
  * Limits: nheads % ngroups == 0; chunk_size in {64, 128, 256};
- * headdim in {32, 64, 128}; dstate in {32, 64, 128, 256}; bf16 inputs only.
+ * 1 <= headdim <= 128; 1 <= dstate <= 256; bf16 inputs only (in_dtype
+ * SSM_F32 returns SSM_ERR_UNSUPPORTED).  The kernels' tiles cover headdim
+ * 32, 64, 128 and dstate 32, 64, 128, 256; other sizes run on zero-padded
+ * copies of x, B, C (and the initial state) in the workspace, whose size
+ * then includes them; the result is the same.
  */
 ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void *x, const void *dt,
                               const float *A, const void *B, const void *C,

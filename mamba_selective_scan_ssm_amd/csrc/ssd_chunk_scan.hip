@@ -59,10 +59,8 @@ ssm_status ssd_validate_shape(int64_t batch, int64_t seqlen, int64_t nheads, int
   if (nheads % ngroups != 0) return bad(SSM_ERR_INVALID_ARG, "nheads must be a multiple of ngroups");
   if (chunk != 64 && chunk != 128 && chunk != 256)
     return bad(SSM_ERR_UNSUPPORTED, "chunk_size must be 64, 128 or 256");
-  if (headdim != 32 && headdim != 64 && headdim != 128)
-    return bad(SSM_ERR_UNSUPPORTED, "headdim must be 32, 64 or 128");
-  if (dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
-    return bad(SSM_ERR_UNSUPPORTED, "dstate must be 32, 64, 128 or 256");
+  if (headdim > 128) return bad(SSM_ERR_UNSUPPORTED, "headdim must be <= 128");
+  if (dstate > 256) return bad(SSM_ERR_UNSUPPORTED, "dstate must be <= 256");
   if (batch > 65535 || nheads > 65535 || seqlen > (1 << 30))
     return bad(SSM_ERR_UNSUPPORTED, "batch and nheads must be <= 65535, seqlen <= 2^30");
   out->batch = (int)batch;
@@ -73,6 +71,8 @@ ssm_status ssd_validate_shape(int64_t batch, int64_t seqlen, int64_t nheads, int
   out->ngroups = (int)ngroups;
   out->chunk = (int)chunk;
   out->nchunks = (int)((seqlen + chunk - 1) / chunk);
+  out->kheaddim = headdim <= 32 ? 32 : headdim <= 64 ? 64 : 128;
+  out->kdstate = dstate <= 32 ? 32 : dstate <= 64 ? 64 : dstate <= 128 ? 128 : 256;
   return SSM_OK;
 }
 
@@ -412,7 +412,12 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
 
 // ---- 2. state passing across chunks (the jump formula) ----------------------
 
+// The chunk states of one thread's 8 entries and the chunk decays are
+// loaded RING chunks ahead of their use (clamped chunk index, no condition
+// on the loads), so that the latencies of the loads overlap instead of
+// adding up chunk after chunk.
 __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
+  constexpr int RING = 8;
   const int bh = blockIdx.y;
   const int b = bh / a.nheads, h = bh % a.nheads;
   const int64_t PN = (int64_t)a.headdim * a.dstate;
@@ -429,20 +434,42 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) S[i] = 0.0f;
   }
-  for (int c = 0; c < a.nchunks; ++c) {
-    uint16_t* ptr = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * PN + e0;
-    const uint4 raw = *reinterpret_cast<const uint4*>(ptr);
-    uint32_t o[4];
+  const int nc = a.nchunks;
+  const int64_t cstride = (int64_t)a.nheads * PN;  // elements between chunks
+  uint16_t* base = a.states + ((int64_t)b * nc * a.nheads + h) * PN + e0;
+  const float* dec = a.decay + (int64_t)bh * nc;
+  uint4 raw[RING];
+  float dv[RING];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = pack_bf16x2(S[2 * i], S[2 * i + 1]);
-    *reinterpret_cast<uint4*>(ptr) = make_uint4(o[0], o[1], o[2], o[3]);
-    const float dec = a.decay[((int64_t)b * a.nheads + h) * a.nchunks + c];
-    const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int i = 0; i < RING; ++i) {
+    const int c = min(i, nc - 1);
+    raw[i] = *reinterpret_cast<const uint4*>(base + c * cstride);
+    dv[i] = dec[c];
+  }
+  for (int c0 = 0; c0 < nc; c0 += RING) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      S[2 * i] = __builtin_fmaf(dec, S[2 * i], bf16_bits_to_f32(r[i] & 0xffffu));
-      S[2 * i + 1] = __builtin_fmaf(dec, S[2 * i + 1], __uint_as_float(r[i] & 0xffff0000u));
+    for (int i = 0; i < RING; ++i) {
+      // Chunks past the end (the last ring's tail) are identity steps whose
+      // store is skipped; the loads stay unconditional.
+      const int c = c0 + i;
+      const bool live = c < nc;
+      const uint4 r = raw[i];
+      const float d = live ? dv[i] : 1.0f;
+      // refill this ring slot with chunk c + RING (this thread writes that
+      // chunk's entry only later, after this read)
+      const int cn = min(c + RING, nc - 1);
+      raw[i] = *reinterpret_cast<const uint4*>(base + cn * cstride);
+      dv[i] = dec[cn];
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(S[2 * k], S[2 * k + 1]);
+      if (live) *reinterpret_cast<uint4*>(base + c * cstride) = make_uint4(o[0], o[1], o[2], o[3]);
+      const uint32_t rw[4] = {live ? r.x : 0u, live ? r.y : 0u, live ? r.z : 0u, live ? r.w : 0u};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        S[2 * k] = __builtin_fmaf(d, S[2 * k], bf16_bits_to_f32(rw[k] & 0xffffu));
+        S[2 * k + 1] = __builtin_fmaf(d, S[2 * k + 1], __uint_as_float(rw[k] & 0xffff0000u));
+      }
     }
   }
   if (a.final_state) {
@@ -870,15 +897,76 @@ hipError_t launch_p(const SsdParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-}  // namespace
+// Copy with zero padding or cropping between [outer][ms][ks] (source) and
+// [outer][md][kd] (destination): dst[o][m][k] = src[o][m][k] where m < ms
+// and k < ks, else 0.  One thread per destination element.
+template <typename T>
+__global__ void __launch_bounds__(256) ssd_repack_kernel(const T* __restrict__ src,
+                                                       T* __restrict__ dst, int64_t total,
+                                                       int ms, int ks, int md, int kd) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int k = (int)(i % kd);
+  const int64_t r = i / kd;
+  const int m = (int)(r % md);
+  const int64_t o = r / md;
+  T v = T(0);
+  if (m < ms && k < ks) v = src[(o * ms + m) * ks + k];
+  dst[i] = v;
+}
 
-hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {
+template <typename T>
+hipError_t repack(const void* src, void* dst, int64_t outer, int ms, int ks, int md, int kd,
+                  hipStream_t stream) {
+  const int64_t total = outer * md * kd;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(ssd_repack_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const T*>(src), static_cast<T*>(dst), total, ms, ks, md,
+                     kd);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles(const SsdParams& p, hipStream_t stream) {
   switch (p.shape.headdim) {
     case 32: return launch_p<32>(p, stream);
     case 64: return launch_p<64>(p, stream);
     case 128: return launch_p<128>(p, stream);
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {
+  const SsdShape& s = p.shape;
+  if (!s.padded()) return launch_tiles(p, stream);
+  // Headdim or dstate between the tile sizes: run the kernels on
+  // zero-padded copies in the workspace (see SsdShape).
+  const SsdLayout lay = ssd_layout(s);
+  char* ws = static_cast<char*>(p.workspace);
+  const int P = s.headdim, N = s.dstate, Pk = s.kheaddim, Nk = s.kdstate;
+  const int64_t rows_x = (int64_t)s.batch * s.seqlen * s.nheads;
+  const int64_t rows_bc = (int64_t)s.batch * s.seqlen * s.ngroups;
+  const int64_t bh = (int64_t)s.batch * s.nheads;
+  SsdParams q = p;
+  q.x = ws + lay.x_off;
+  q.y = ws + lay.y_off;
+  q.B = ws + lay.b_off;
+  q.C = ws + lay.c_off;
+  q.initial_state = p.initial_state ? reinterpret_cast<const float*>(ws + lay.init_off) : nullptr;
+  q.final_state = p.final_state ? reinterpret_cast<float*>(ws + lay.final_off) : nullptr;
+  q.shape.headdim = Pk;
+  q.shape.dstate = Nk;
+  hipError_t e = repack<uint16_t>(p.x, ws + lay.x_off, rows_x, 1, P, 1, Pk, stream);
+  if (e == hipSuccess) e = repack<uint16_t>(p.B, ws + lay.b_off, rows_bc, 1, N, 1, Nk, stream);
+  if (e == hipSuccess) e = repack<uint16_t>(p.C, ws + lay.c_off, rows_bc, 1, N, 1, Nk, stream);
+  if (e == hipSuccess && p.initial_state)
+    e = repack<float>(p.initial_state, ws + lay.init_off, bh, P, N, Pk, Nk, stream);
+  if (e == hipSuccess) e = launch_tiles(q, stream);
+  if (e == hipSuccess) e = repack<uint16_t>(ws + lay.y_off, p.y, rows_x, 1, Pk, 1, P, stream);
+  if (e == hipSuccess && p.final_state)
+    e = repack<float>(ws + lay.final_off, p.final_state, bh, Pk, Nk, P, N, stream);
+  return e;
 }
 
 }  // namespace ssm

@@ -13,6 +13,14 @@ namespace ssm {
 struct SsdShape {
   int batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
   int nchunks;  // ceil(seqlen / chunk)
+  // Tile sizes the kernels run at: headdim rounded up to 32, 64 or 128 and
+  // dstate to 32, 64, 128 or 256.  When they differ from headdim / dstate
+  // (padded), x, B, C (and the initial state) are first copied into
+  // zero-padded workspace tensors of the tile sizes, the kernels run on
+  // those, and y (and the final state) are copied back.  Zero padding is
+  // exact: padded states and channels only ever meet zeros.
+  int kheaddim, kdstate;
+  bool padded() const { return kheaddim != headdim || kdstate != dstate; }
 };
 
 struct SsdParams {
@@ -31,22 +39,41 @@ struct SsdParams {
   SsdShape shape;
 };
 
-// Workspace layout (256-byte aligned sections):
-//   states [batch, nchunks, nheads, headdim, dstate] bf16: each chunk's
-//          local state (chunk-state kernel), then, in place, the state
-//          entering that chunk (state-pass kernel)
+// Workspace layout (256-byte aligned sections), with P' = kheaddim and
+// N' = kdstate:
+//   states [batch, nchunks, nheads, P', N'] bf16: each chunk's local state
+//          (chunk-state kernel), then, in place, the state entering that
+//          chunk (state-pass kernel)
 //   decay  [batch, nheads, nchunks] float32: exp(sum of A*dt over the chunk)
+// and only for padded shapes:
+//   x', y' [batch, seqlen, nheads, P'] bf16;  B', C' [batch, seqlen, ngroups, N'] bf16
+//   init', final' [batch, nheads, P', N'] float32
 struct SsdLayout {
-  size_t states_off, decay_off, total;
+  size_t states_off, decay_off, x_off, y_off, b_off, c_off, init_off, final_off, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline SsdLayout ssd_layout(const SsdShape& s) {
   SsdLayout l;
+  const size_t P = s.kheaddim, N = s.kdstate;
   l.states_off = 0;
-  l.decay_off = align256((size_t)s.batch * s.nchunks * s.nheads * s.headdim * s.dstate * 2);
-  l.total = align256(l.decay_off + (size_t)s.batch * s.nheads * s.nchunks * sizeof(float));
+  l.decay_off = align256((size_t)s.batch * s.nchunks * s.nheads * P * N * 2);
+  size_t end = align256(l.decay_off + (size_t)s.batch * s.nheads * s.nchunks * sizeof(float));
+  l.x_off = l.y_off = l.b_off = l.c_off = l.init_off = l.final_off = 0;
+  if (s.padded()) {
+    const size_t rows_x = (size_t)s.batch * s.seqlen * s.nheads;
+    const size_t rows_bc = (size_t)s.batch * s.seqlen * s.ngroups;
+    const size_t st = (size_t)s.batch * s.nheads * P * N * sizeof(float);
+    l.x_off = end;
+    l.y_off = end = align256(l.x_off + rows_x * P * 2);
+    l.b_off = end = align256(l.y_off + rows_x * P * 2);
+    l.c_off = end = align256(l.b_off + rows_bc * N * 2);
+    l.init_off = end = align256(l.c_off + rows_bc * N * 2);
+    l.final_off = end = align256(l.init_off + st);
+    end = align256(l.final_off + st);
+  }
+  l.total = end;
   return l;
 }
 

@@ -94,9 +94,12 @@ def test_ssd_shape_checks():
     assert "handle" in ssd_ws()[1]
     assert ssd_ws(nheads=6, ngroups=4)[0] == ssm.SSM_ERR_INVALID_ARG
     assert ssd_ws(chunk=100)[0] == ssm.SSM_ERR_UNSUPPORTED
-    assert ssd_ws(headdim=48)[0] == ssm.SSM_ERR_UNSUPPORTED
-    assert ssd_ws(dstate=100)[0] == ssm.SSM_ERR_UNSUPPORTED
-    assert ssd_ws(dstate=16)[0] == ssm.SSM_ERR_UNSUPPORTED
+    # any headdim 1..128 and dstate 1..256 (the documented limits) is valid
+    for hd, ds in ((48, 32), (1, 1), (16, 100), (80, 16), (128, 256), (127, 255)):
+        st, msg, _ = ssd_ws(headdim=hd, dstate=ds)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, (hd, ds, msg)
+    assert ssd_ws(headdim=129)[0] == ssm.SSM_ERR_UNSUPPORTED
+    assert ssd_ws(dstate=257)[0] == ssm.SSM_ERR_UNSUPPORTED
     assert ssd_ws(batch=0)[0] == ssm.SSM_ERR_INVALID_ARG
     assert ssd_ws(batch=0)[2] == 0
 

@@ -80,6 +80,50 @@ def test_ssd_shapes(lib, case):
     compare(lib, s, q, f"ssd {case}")
 
 
+ODD = [  # (batch, seqlen, nheads, headdim, dstate, ngroups, chunk): sizes between the tiles
+    (1, 200, 2, 64, 16, 1, 64),      # dstate 16 -> tile 32
+    (2, 300, 4, 32, 48, 2, 128),     # dstate 48 -> 64, two groups
+    (1, 513, 3, 64, 100, 1, 256),    # dstate 100 -> 128, ragged tail
+    (2, 130, 2, 16, 128, 1, 64),     # headdim 16 -> 32
+    (1, 260, 2, 80, 64, 2, 128),     # headdim 80 -> 128
+    (1, 77, 3, 1, 1, 3, 64),         # headdim 1, dstate 1, one head per group
+    (1, 400, 2, 100, 200, 1, 128),   # headdim 100 -> 128, dstate 200 -> 256
+]
+
+
+@pytest.mark.parametrize("case", ODD)
+def test_ssd_odd_sizes(lib, case):
+    """headdim 1..128 and dstate 1..256 off the tile sizes (zero-padded
+    copies in the workspace): every y and final_state entry."""
+    b, L, h, p, n, g, q = case
+    s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=60 + L + p + n, batch=b, seqlen=L,
+                         nheads=h, headdim=p, dstate=n, ngroups=g)
+    compare(lib, s, q, f"ssd odd sizes {case}")
+
+
+def test_ssd_odd_sizes_initial_state_in_place(lib):
+    """An off-tile shape from a given state, updated in place."""
+    b, L, h, p, n, g, q = 2, 300, 4, 48, 40, 2, 128
+    print("case ssd odd sizes, initial state in place", flush=True)
+    s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=71, batch=b, seqlen=L, nheads=h,
+                         headdim=p, dstate=n, ngroups=g)
+    init = np.random.default_rng(72).standard_normal((b, h, p, n)).astype(np.float32)
+    dev = "cuda"
+    t = {k: (None if v is None else
+             synth.to_device(v, "bf16" if k in ("x", "dt", "B", "C") else "f32", dev))
+         for k, v in s.items()}
+    state = torch.from_numpy(init).to(dev)
+    y = torch.empty_like(t["x"])
+    ws = torch.empty(lib.ssd_chunk_scan_workspace_size(b, L, h, p, n, g, q), dtype=torch.uint8,
+                     device=dev)
+    lib.ssd_chunk_scan_fwd_with_state(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                      t["dt_bias"], True, state, y, state, ws, q)
+    torch.cuda.synchronize()
+    ry, rf = oracle.ssd_scan(**s, initial_state=init.astype(np.float64))
+    check("y", synth.to_host_f64(y), ry)
+    check("final_state", synth.to_host_f64(state), rf)
+
+
 def test_ssd_nullable_and_softplus_off(lib):
     s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=7, batch=2, seqlen=200, nheads=2,
                          headdim=64, dstate=64, ngroups=1)
