@@ -99,6 +99,8 @@ struct SsdArgs {
   int dt_softplus;
   int batch, seqlen, nheads, headdim, dstate, ngroups, chunk, nchunks;
   int heads_per_wg_state, heads_per_wg_out;
+  int out_halves;   // output workgroups per (chunk, batch, head group): 1 or 2
+  int out_hgroups;  // head groups of the output kernel
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -157,6 +159,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Most heads per output-kernel workgroup: the largest shape keeps fewer so
 // that its per-head decay tables fit in LDS beside the x and state tiles.
 constexpr int out_heads_max(int P, int N) { return P * N >= 128 * 256 ? 4 : kHGMax; }
+
+// Most heads per workgroup of the four-wave output kernel.
+constexpr int kHGSmall = 6;
 
 // Raw dt for the log-decay of every head of a workgroup's group: NTHR
 // threads form NTHR/256 groups of 256; round r covers heads
@@ -265,6 +270,8 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   __shared__ float sTmp[16];
   constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
   constexpr bool kAllTiles = TILES % NW == 0;  // every wave owns TPW tiles
+  // a wave's tiles come in pairs on the same rows p (16-byte state stores)
+  constexpr bool kPairStores = kAllTiles && TPW % 2 == 0 && NW % PT == 0;
   constexpr int XTASKS = QT * P / 8, BTASKS = QT * NB / 8;
   constexpr int XPT = (XTASKS + NTHR - 1) / NTHR;
   constexpr int BPT = (BTASKS + NTHR - 1) / NTHR;
@@ -387,16 +394,37 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
       if constexpr (!DB) __syncthreads();  // readers of the single sX buffer are done
       // lane holds S_c[p][n .. n+3] with p = pt*16 + r16, n = nt*16 + 4*q4
       uint16_t* st = a.states + (((int64_t)b * a.nchunks + c) * a.nheads + h) * P * N;
+      if constexpr (kPairStores) {
+        // a wave's tiles t = 2j, 2j+1 share their rows p: swapping with the
+        // lane 16 apart (v_permlane16_swap) gives every lane eight
+        // consecutive n of one of them, stored as 16 bytes
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int tile = wv + NW * t;
-        if (kAllTiles || tile < TILES) {
+        for (int j = 0; j < TPW / 2; ++j) {
+          uint2 o[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            o[u].x = pack_bf16x2(acc[2 * j + u][0], acc[2 * j + u][1]);
+            o[u].y = pack_bf16x2(acc[2 * j + u][2], acc[2 * j + u][3]);
+          }
+          const auto lo = __builtin_amdgcn_permlane16_swap(o[0].x, o[1].x, false, false);
+          const auto hi = __builtin_amdgcn_permlane16_swap(o[0].y, o[1].y, false, false);
+          const int tile = wv + NW * (2 * j + (q4 & 1));
           const int nt = tile / PT, pt = tile % PT;
-          const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
-          uint2 o;
-          o.x = pack_bf16x2(acc[t][0], acc[t][1]);
-          o.y = pack_bf16x2(acc[t][2], acc[t][3]);
-          *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
+          const int p = pt * 16 + r16, n = nb0 + nt * 16 + 8 * (q4 >> 1);
+          *reinterpret_cast<uint4*>(st + (int64_t)p * N + n) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const int tile = wv + NW * t;
+          if (kAllTiles || tile < TILES) {
+            const int nt = tile / PT, pt = tile % PT;
+            const int p = pt * 16 + r16, n = nb0 + nt * 16 + 4 * q4;
+            uint2 o;
+            o.x = pack_bf16x2(acc[t][0], acc[t][1]);
+            o.y = pack_bf16x2(acc[t][2], acc[t][3]);
+            *reinterpret_cast<uint2*>(st + (int64_t)p * N + n) = o;
+          }
         }
       }
     };
@@ -492,15 +520,26 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
 // registers loaded while the previous head computed, into one of two LDS
 // buffers when both fit, so a head costs one barrier.  The carried-state
 // product uses C as loaded and is scaled by exp(cs_l) once per column.
-template <int P, int N>
-__global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
+//
+// W = 4 (the shapes whose tiles fit twice in a CU's LDS): the same work with
+// four-wave workgroups, two per (chunk, batch, head group) at Q = 256, each
+// taking half of the chunk's output-tile pairs (workgroup ids i and i + 8 of
+// each block of 16, so both halves run on one XCD and share its L2).  One
+// head buffer and up to 64 states of B per staging round keep a workgroup
+// within half of the LDS, so two workgroups share a CU and one stages or
+// stores while the other computes.
+template <int W>
+constexpr int out_kb(int N) { return W == 8 ? (N < 128 ? N : 128) : (N < 64 ? N : 64); }
+
+template <int P, int N, int W>
+__global__ void __launch_bounds__(64 * W, 8 / W) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr int KN = N / 32;         // contraction steps over the state axis
   constexpr int NPN = kQMax / 32 - 1; // off-diagonal s-tile pairs per wave (at Q = 256)
   constexpr int PT = P / 16;
-  constexpr int KB = N < 128 ? N : 128;  // states of B per staging round
+  constexpr int KB = out_kb<W>(N);   // states of B per staging round
   constexpr int kRowB = KB + 8;
   constexpr int kRowN = N + 8;       // LDS row stride (bf16) of [p][n]
-  constexpr int NTHR = 512;
+  constexpr int NTHR = 64 * W;
   constexpr int kRowX = P + 16;      // LDS row stride (bf16) of x [s][p]
   constexpr int XPT = (kQMax * P / 8 + NTHR - 1) / NTHR;
   constexpr int SPT = (P * N / 8 + NTHR - 1) / NTHR;
@@ -516,9 +555,9 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   constexpr size_t kXtBytes = (size_t)kQMax * kRowX * 2;
   constexpr size_t kSBytes = (size_t)P * kRowN * 2;
   constexpr size_t kBBytes = (size_t)kQMax * kRowB * 2;
-  constexpr int HG = out_heads_max(P, N);  // most heads per workgroup
+  constexpr int HG = W == 8 ? out_heads_max(P, N) : kHGSmall;  // most heads per workgroup
   constexpr size_t kFixed = 3 * HG * kQMax * 4 + 64;
-  constexpr bool DB = 2 * (kXtBytes + kSBytes) + kFixed <= 156 * 1024;
+  constexpr bool DB = W == 8 && 2 * (kXtBytes + kSBytes) + kFixed <= 156 * 1024;
   constexpr int NBUF = DB ? 2 : 1;
   constexpr size_t kBufBytes = NBUF * (kXtBytes + kSBytes);
   constexpr size_t kRawBytes = kBufBytes > kBBytes ? kBufBytes : kBBytes;
@@ -533,13 +572,35 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   auto sBs = reinterpret_cast<uint16_t (*)[kRowB]>(sRaw);
 
   const int Q = a.chunk, L = a.seqlen;
-  const int c = blockIdx.x, b = blockIdx.y;
+  int c, b, zg, half;
+  if constexpr (W == 8) {
+    c = blockIdx.x;
+    b = blockIdx.y;
+    zg = blockIdx.z;
+    half = 0;
+  } else {
+    // one-dimensional grid: (pair of halves) -> (chunk, batch, head group)
+    const int id = blockIdx.x;
+    int pr;
+    if (a.out_halves == 2) {
+      pr = (id / 16) * 8 + id % 8;
+      half = (id / 8) % 2;
+    } else {
+      pr = id;
+      half = 0;
+    }
+    if (pr >= a.nchunks * a.batch * a.out_hgroups) return;  // (uniform per workgroup)
+    c = pr % a.nchunks;
+    b = (pr / a.nchunks) % a.batch;
+    zg = pr / (a.nchunks * a.batch);
+  }
   const int hpg = a.nheads / a.ngroups;
-  const int h0 = blockIdx.z * a.heads_per_wg_out;
+  const int h0 = zg * a.heads_per_wg_out;
   const int nh = min(a.heads_per_wg_out, a.nheads - h0);
   const int g = h0 / hpg;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  // index of this wave's pair of output tiles within the chunk (uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6) + W * half;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int nlt = Q / 16;                    // output tiles in the chunk
   const bool active = wv < nlt / 2;
@@ -612,7 +673,9 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
       cr[t][kk] = load16(crow + kk * 32 + 8 * q4);  // rows past the end feed unstored columns
   }
   load_b(0);
-  prefetch(0);
+  // (the four-wave kernel loads each head right before staging it: its
+  // second workgroup on the CU covers the latency)
+  if constexpr (W == 8) prefetch(0);
   group_log_decay<NTHR>(a, c, nh, graw, sCs2, sDt, sTmp, sW, sHead);
 
   // Pairs of s-tiles: the last pair of each output tile touches its diagonal
@@ -678,8 +741,13 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
   for (int t = 0; t < 2; ++t) gdk[t] = pack_pair(gdacc[2 * t], gdacc[2 * t + 1]);
 
   __syncthreads();  // readers of sBs are done before the head buffers reuse its bytes
-  stage(0);
-  if (nh > 1) prefetch(1);
+  if constexpr (W == 8) {
+    stage(0);
+    if (nh > 1) prefetch(1);
+  } else {
+    prefetch(0);
+    stage(0);
+  }
   __syncthreads();
 
   for (int hh = 0; hh < nh; ++hh) {
@@ -805,24 +873,46 @@ __global__ void __launch_bounds__(512) ssd_chunk_out_kernel(SsdArgs a) {
         yo[t][pt].y = pack_bf16x2(v[2], v[3]);
       }
     }
+    // A lane holds four consecutive p of every 16-wide block of its
+    // position's row; swapping with the lane 16 apart (v_permlane16_swap:
+    // odd 16-lane rows of the first operand with even rows of the second)
+    // gives it runs of eight, so a row is written in 16-byte pieces: for the
+    // block pair (2j, 2j+1) the lane ends with p = 32j + 16 (q4 & 1) +
+    // 8 (q4 >> 1) .. +7.
     auto store_y = [&]() {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        if (!lok[t]) continue;
-        uint16_t* yrow = a.y + (((int64_t)b * L + pos0 + lcol[t]) * a.nheads + h) * P;
+        uint4 run[PT / 2];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-          *reinterpret_cast<uint2*>(yrow + pt * 16 + 4 * q4) = yo[t][pt];
+        for (int j = 0; j < PT / 2; ++j) {
+          const auto lo = __builtin_amdgcn_permlane16_swap(yo[t][2 * j].x, yo[t][2 * j + 1].x,
+                                                          false, false);
+          const auto hi = __builtin_amdgcn_permlane16_swap(yo[t][2 * j].y, yo[t][2 * j + 1].y,
+                                                          false, false);
+          run[j] = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+        }
+        if (!lok[t]) continue;
+        uint16_t* yrow = a.y + (((int64_t)b * L + pos0 + lcol[t]) * a.nheads + h) * P +
+                         16 * (q4 & 1) + 8 * (q4 >> 1);
+#pragma unroll
+        for (int j = 0; j < PT / 2; ++j) *reinterpret_cast<uint4*>(yrow + 32 * j) = run[j];
       }
     };
     // Stage the next head before storing this one, and keep stage, stores
     // and the next prefetch on one path: waiting for the staged loads then
     // never waits for these stores.
     if (hh + 1 < nh) {
-      if (!DB) __syncthreads();  // readers of the single buffer are done
-      stage(DB ? ((hh + 1) & 1) : 0);
-      store_y();
-      if (hh + 2 < nh) prefetch(hh + 2);
+      if constexpr (W == 8) {
+        if (!DB) __syncthreads();  // readers of the single buffer are done
+        stage(DB ? ((hh + 1) & 1) : 0);
+        store_y();
+        if (hh + 2 < nh) prefetch(hh + 2);
+      } else {
+        prefetch(hh + 1);
+        store_y();
+        __syncthreads();  // readers of the single buffer are done
+        stage(0);
+      }
       __syncthreads();
     } else {
       store_y();
@@ -837,6 +927,19 @@ int heads_per_workgroup(int hpg, int nheads, int64_t base_wgs, int64_t target, i
   for (int d = 1; d <= hpg && d <= dmax; ++d)
     if (hpg % d == 0 && base_wgs * (nheads / d) >= target) best = d;
   return best;
+}
+
+// The four-wave output kernel's LDS (one head buffer, B staged 64 states at
+// a time, the decay tables of kHGSmall heads) fits twice in a CU, and its
+// registers fit two waves per SIMD without spilling (up to 128 states: the
+// C operands of a wave's two output tiles take 2 * N / 8 registers).
+template <int P, int N>
+constexpr bool out4_fits() {
+  if (N > 128) return false;
+  constexpr size_t x = (size_t)kQMax * (P + 16) * 2, st = (size_t)P * (N + 8) * 2;
+  constexpr size_t bb = (size_t)kQMax * (out_kb<4>(N) + 8) * 2;
+  constexpr size_t raw = x + st > bb ? x + st : bb;
+  return raw + 3 * kHGSmall * kQMax * 4 + 128 <= 80 * 1024;
 }
 
 template <int P, int N>
@@ -862,8 +965,12 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   const int hpg = s.nheads / s.ngroups;
   a.heads_per_wg_state =
       heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256, kHGMax);
-  a.heads_per_wg_out =
-      heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256, out_heads_max(P, N));
+  constexpr bool kOut4 = out4_fits<P, N>();
+  a.heads_per_wg_out = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256,
+                                           kOut4 ? kHGSmall : out_heads_max(P, N));
+  a.out_hgroups = (s.nheads + a.heads_per_wg_out - 1) / a.heads_per_wg_out;
+  // two four-wave halves when the chunk has more than four output-tile pairs
+  a.out_halves = (kOut4 && s.chunk / 32 > 4) ? 2 : 1;
 
   // state block: B[chunk][NB] and one head's x[chunk][P] share the LDS
   constexpr int NB = (P == 128 && N >= 128) ? 64 : (N > 128 ? 128 : N);
@@ -881,8 +988,15 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(ssd_state_pass_kernel, g2, dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 g3(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_out - 1) / a.heads_per_wg_out);
-  hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N>), g3, dim3(512), 0, stream, a);
+  if constexpr (kOut4) {
+    const int64_t pairs = (int64_t)s.nchunks * s.batch * a.out_hgroups;
+    const int64_t wgs = a.out_halves == 2 ? (pairs + 7) / 8 * 16 : pairs;
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N, 4>), dim3((unsigned)wgs), dim3(256), 0, stream,
+                       a);
+  } else {
+    dim3 g3(s.nchunks, s.batch, a.out_hgroups);
+    hipLaunchKernelGGL((ssd_chunk_out_kernel<P, N, 8>), g3, dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
