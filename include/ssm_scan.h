@@ -270,8 +270,11 @@ ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle,
  * accumulated into).  The result is deterministic (partial sums are added
  * in a fixed order).
  *
- * Limits: as ssm_selective_scan_fwd, and dstate <= 16 (SSM_ERR_UNSUPPORTED
- * above).
+ * Limits: as ssm_selective_scan_fwd (dstate <= 64; SSM_ERR_UNSUPPORTED
+ * above).  For dstate > 16 the states are taken in blocks of 16, each a
+ * backward pass of its own whose per-step sums over its states are added
+ * up across blocks (the workspace then also holds three float32
+ * [batch, dim, seqlen] accumulators); the result is the same.
  */
 ssm_status ssm_selective_scan_bwd(
     ssm_handle handle, const void *u, const void *delta, const float *A,

@@ -644,7 +644,7 @@ def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_
                       initial_state=None, return_last_state=False):
     """Differentiable Mamba-1 selective scan: the forward and backward HIP
     kernels behind torch.autograd (B, C [batch, dstate, seqlen]; the
-    backward needs dstate <= 16).  Returns y, or (y, last_state)."""
+    backward takes dstate <= 64).  Returns y, or (y, last_state)."""
     y, ls = _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, initial_state,
                                    bool(delta_softplus))
     return (y, ls) if return_last_state else y

@@ -369,7 +369,7 @@ ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batc
   *bytes = 0;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0)
     return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
-  if (dstate > 16) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 16", (long long)dstate);
+  if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 64", (long long)dstate);
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
     return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
@@ -396,7 +396,7 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   if (seqlen <= 0) return fail(SSM_ERR_INVALID_ARG, "seqlen must be >= 1 (got %lld)", (long long)seqlen);
   if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
-  if (dstate > 16) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 16", (long long)dstate);
+  if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 64", (long long)dstate);
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
     return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");

@@ -331,6 +331,24 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
       // keep each step's operands within the step (register pressure)
       __builtin_amdgcn_sched_barrier(0);
     });
+    if (P.acc_y) {
+      // state block of a larger dstate: this block's per-step sums over its
+      // states (readout, d/d delta, d/d u) go to the float32 accumulators;
+      // the finishing kernel forms du, ddelta and dz from their totals
+      if (row_ok) {
+        float* ay = P.acc_y + row_base;
+        float* at = P.acc_ddt + row_base;
+        float* au = P.acc_du + row_base;
+#pragma unroll
+        for (int j = 0; j < TS; ++j) {
+          if (ts + j < L) {
+            ay[ts + j] = P.acc_init ? yo[j] : ay[ts + j] + yo[j];
+            at[ts + j] = P.acc_init ? ddt_o[j] : at[ts + j] + ddt_o[j];
+            au[ts + j] = P.acc_init ? du_o[j] : au[ts + j] + du_o[j];
+          }
+        }
+      }
+    } else {
     if (has_z && row_ok) store_seg<In, TS>(static_cast<In*>(P.dz), row_base, ts, L, dzv);
 
     // -- input-side gradients for this lane's steps ------------------------------
@@ -349,6 +367,7 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
         store_seg<In, TS>(static_cast<In*>(P.du), row_base, ts, L, dus);
         store_seg<In, TS>(static_cast<In*>(P.ddelta), row_base, ts, L, dds);
       }
+    }
     }
     __syncthreads();  // sPB, sPC complete; sB, sC free
     // -- this workgroup's dB, dC partials for the chunk ---------------------------
@@ -597,8 +616,33 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus) {
+BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus,
+                                    int in_bytes) {
+  if (dstate > 16) {
+    // blocks of 16 states, each run as a 16-state backward pass
+    BwdLayout l = selective_scan_bwd_layout(batch, dim, 16, seqlen, num_cus, in_bytes);
+    l.nblocks = (dstate + 15) / 16;
+    const size_t rows = (size_t)batch * dim, steps = rows * seqlen;
+    const size_t bc = (size_t)batch * 16 * seqlen;
+    size_t end = l.total;
+    l.acc_off = end;
+    l.a_off = end = align256(l.acc_off + 3 * steps * sizeof(float));
+    l.b_off = end = align256(l.a_off + (size_t)dim * 16 * sizeof(float));
+    l.c_off = end = align256(l.b_off + bc * in_bytes);
+    l.h0_off = end = align256(l.c_off + bc * in_bytes);
+    l.dl_off = end = align256(l.h0_off + rows * 16 * sizeof(float));
+    l.da_off = end = align256(l.dl_off + rows * 16 * sizeof(float));
+    l.db_off = end = align256(l.da_off + (size_t)dim * 16 * sizeof(float));
+    l.dc_off = end = align256(l.db_off + bc * sizeof(float));
+    l.dh0_off = end = align256(l.dc_off + bc * sizeof(float));
+    l.prow_off = end = align256(l.dh0_off + rows * 16 * sizeof(float));
+    l.total = align256(l.prow_off + 2 * rows * sizeof(float));
+    return l;
+  }
   BwdLayout l;
+  l.nblocks = 1;
+  l.acc_off = l.a_off = l.b_off = l.c_off = l.h0_off = l.dl_off = 0;
+  l.da_off = l.db_off = l.dc_off = l.dh0_off = l.prow_off = 0;
   l.nchunks = (seqlen + kBwdT - 1) / kBwdT;
   const int rpb = 4 * (64 / lanes_per_row(dstate));
   l.nwg = (dim + rpb - 1) / rpb;
@@ -633,8 +677,200 @@ BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, 
   return l;
 }
 
+namespace {
+
+// dst[o * dst_stride + dst_off + j] = src[o * src_stride + src_off + j] for
+// j < width (elements of `bytes` bytes): the gathers and scatters of one
+// state block's columns.
+__global__ void __launch_bounds__(256) bwd_copy_cols_kernel(const char* __restrict__ src,
+                                                          int64_t src_stride, int64_t src_off,
+                                                          char* __restrict__ dst,
+                                                          int64_t dst_stride, int64_t dst_off,
+                                                          int64_t outer, int64_t width,
+                                                          int bytes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= outer * width) return;
+  const int64_t o = i / width, j = i % width;
+  const char* s = src + (o * src_stride + src_off + j) * bytes;
+  char* d = dst + (o * dst_stride + dst_off + j) * bytes;
+  if (bytes == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+  else *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+}
+
+hipError_t copy_cols(const void* src, int64_t src_stride, int64_t src_off, void* dst,
+                     int64_t dst_stride, int64_t dst_off, int64_t outer, int64_t width, int bytes,
+                     hipStream_t stream) {
+  const int64_t total = outer * width;
+  if (total == 0 || !src || !dst) return hipSuccess;
+  hipLaunchKernelGGL(bwd_copy_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const char*>(src), src_stride, src_off,
+                     static_cast<char*>(dst), dst_stride, dst_off, outer, width, bytes);
+  return hipGetLastError();
+}
+
+// Per-step gradients from the state blocks' summed partials, one workgroup
+// per row (b, d):
+//   yh = acc_y + D u;  dyh = dy silu(z);  dz = dy yh silu'(z)
+//   du = dyh D + acc_du;  ddelta = acc_ddt * softplus'(delta + bias)
+// and the row's sums of dyh u (for dD) and ddelta (for ddelta_bias).
+template <typename In>
+__global__ void __launch_bounds__(256) bwd_finish_blocks_kernel(BwdParams P, BwdLayout lay) {
+  const ScanParams& F = P.fwd;
+  const int64_t row = blockIdx.x;
+  const int d = (int)(row % F.dim);
+  const int L = F.seqlen;
+  const int64_t base = row * L;
+  const int64_t steps = (int64_t)F.batch * F.dim * L;
+  const float* acc = reinterpret_cast<const float*>(static_cast<const char*>(P.workspace) +
+                                                    lay.acc_off);
+  const In* u = static_cast<const In*>(F.u);
+  const In* dlt = static_cast<const In*>(F.delta);
+  const In* z = static_cast<const In*>(F.z);
+  const In* dy = static_cast<const In*>(P.dy);
+  const float Dd = F.D ? F.D[d] : 0.0f;
+  const float bias = F.delta_bias ? F.delta_bias[d] : 0.0f;
+  float sD = 0.0f, sB = 0.0f;
+  for (int t = threadIdx.x; t < L; t += 256) {
+    const int64_t i = base + t;
+    const float uu = Elem<In>::load(u, i), g = Elem<In>::load(dy, i);
+    const float yh = __builtin_fmaf(Dd, uu, acc[i]);
+    float dyh = g;
+    if (z) {
+      const float zz = Elem<In>::load(z, i);
+      const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+      dyh = g * zz * sg;
+      Elem<In>::store(static_cast<In*>(P.dz), i, g * yh * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
+    }
+    Elem<In>::store(static_cast<In*>(P.du), i, __builtin_fmaf(dyh, Dd, acc[2 * steps + i]));
+    float ds = acc[steps + i];
+    if (F.delta_softplus) {
+      const float sp = Elem<In>::load(dlt, i) + bias;
+      ds *= fast_rcp(1.0f + fast_exp2(-sp * kLog2e));
+    }
+    Elem<In>::store(static_cast<In*>(P.ddelta), i, ds);
+    sD = __builtin_fmaf(dyh, uu, sD);
+    sB += ds;
+  }
+  __shared__ float red[2][256];
+  red[0][threadIdx.x] = sD;
+  red[1][threadIdx.x] = sB;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float* prow = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.prow_off);
+    const int64_t rows = (int64_t)F.batch * F.dim;
+    prow[row] = red[0][0];
+    prow[rows + row] = red[1][0];
+  }
+}
+
+// dD[d], ddelta_bias[d] = sums of the per-row sums over the batch (fixed order).
+__global__ void __launch_bounds__(256) bwd_finish_params_kernel(BwdParams P, BwdLayout lay) {
+  const ScanParams& F = P.fwd;
+  const int d = blockIdx.x * 256 + threadIdx.x;
+  if (d >= F.dim) return;
+  const float* prow = reinterpret_cast<const float*>(static_cast<const char*>(P.workspace) +
+                                                     lay.prow_off);
+  const int64_t rows = (int64_t)F.batch * F.dim;
+  float sD = 0.0f, sB = 0.0f;
+  for (int b = 0; b < F.batch; ++b) {
+    sD += prow[(int64_t)b * F.dim + d];
+    sB += prow[rows + (int64_t)b * F.dim + d];
+  }
+  if (P.dD) P.dD[d] = sD;
+  if (P.ddelta_bias) P.ddelta_bias[d] = sB;
+}
+
+hipError_t launch_bwd_one(const BwdParams& p, const BwdLayout& lay, bool bf16,
+                          hipStream_t stream);
+
+// dstate > 16: the backward pass of each block of 16 states on copies of
+// that block's columns (A, B, C, initial state, dlast), its per-step sums
+// over the block's states added up across blocks, its state gradients
+// (dA, dB, dC, dinitial_state) scattered back; then the per-step gradients
+// from the totals.  Every state-indexed quantity of the recurrence belongs
+// to one block; only the per-step sums over n couple them.
+hipError_t launch_bwd_blocks(const BwdParams& p, const BwdLayout& lay, bool bf16,
+                             hipStream_t stream) {
+  const ScanParams& F = p.fwd;
+  char* ws = static_cast<char*>(p.workspace);
+  const int N = F.dstate, L = F.seqlen, es = bf16 ? 2 : 4;
+  const int64_t rows = (int64_t)F.batch * F.dim, steps = rows * L;
+  hipError_t e = hipSuccess;
+  for (int k = 0; k < lay.nblocks && e == hipSuccess; ++k) {
+    const int n0 = 16 * k, nk = std::min(16, N - n0);
+    BwdParams q = p;
+    ScanParams& f = q.fwd;
+    f.dstate = nk;
+    f.A = reinterpret_cast<const float*>(ws + lay.a_off);
+    f.B = ws + lay.b_off;
+    f.C = ws + lay.c_off;
+    f.h0 = F.h0 ? reinterpret_cast<const float*>(ws + lay.h0_off) : nullptr;
+    q.dlast = p.dlast ? reinterpret_cast<const float*>(ws + lay.dl_off) : nullptr;
+    q.dA = reinterpret_cast<float*>(ws + lay.da_off);
+    q.dB = reinterpret_cast<float*>(ws + lay.db_off);
+    q.dC = reinterpret_cast<float*>(ws + lay.dc_off);
+    q.dh0 = p.dh0 ? reinterpret_cast<float*>(ws + lay.dh0_off) : nullptr;
+    q.dD = nullptr;
+    q.ddelta_bias = nullptr;
+    q.acc_y = reinterpret_cast<float*>(ws + lay.acc_off);
+    q.acc_ddt = q.acc_y + steps;
+    q.acc_du = q.acc_y + 2 * steps;
+    q.acc_init = k == 0;
+    e = copy_cols(F.A, N, n0, ws + lay.a_off, nk, 0, F.dim, nk, 4, stream);
+    if (e == hipSuccess)
+      e = copy_cols(F.B, (int64_t)N * L, (int64_t)n0 * L, ws + lay.b_off, (int64_t)nk * L, 0,
+                    F.batch, (int64_t)nk * L, es, stream);
+    if (e == hipSuccess)
+      e = copy_cols(F.C, (int64_t)N * L, (int64_t)n0 * L, ws + lay.c_off, (int64_t)nk * L, 0,
+                    F.batch, (int64_t)nk * L, es, stream);
+    if (e == hipSuccess && F.h0)
+      e = copy_cols(F.h0, N, n0, ws + lay.h0_off, nk, 0, rows, nk, 4, stream);
+    if (e == hipSuccess && p.dlast)
+      e = copy_cols(p.dlast, N, n0, ws + lay.dl_off, nk, 0, rows, nk, 4, stream);
+    if (e == hipSuccess) e = launch_bwd_one(q, lay, bf16, stream);
+    if (e == hipSuccess) e = copy_cols(ws + lay.da_off, nk, 0, p.dA, N, n0, F.dim, nk, 4, stream);
+    if (e == hipSuccess)
+      e = copy_cols(ws + lay.db_off, (int64_t)nk * L, 0, p.dB, (int64_t)N * L, (int64_t)n0 * L,
+                    F.batch, (int64_t)nk * L, 4, stream);
+    if (e == hipSuccess)
+      e = copy_cols(ws + lay.dc_off, (int64_t)nk * L, 0, p.dC, (int64_t)N * L, (int64_t)n0 * L,
+                    F.batch, (int64_t)nk * L, 4, stream);
+    if (e == hipSuccess && p.dh0)
+      e = copy_cols(ws + lay.dh0_off, nk, 0, p.dh0, N, n0, rows, nk, 4, stream);
+  }
+  if (e != hipSuccess) return e;
+  if (bf16)
+    hipLaunchKernelGGL(bwd_finish_blocks_kernel<uint16_t>, dim3((unsigned)rows), dim3(256), 0,
+                       stream, p, lay);
+  else
+    hipLaunchKernelGGL(bwd_finish_blocks_kernel<float>, dim3((unsigned)rows), dim3(256), 0, stream,
+                       p, lay);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_finish_params_kernel, dim3((unsigned)((F.dim + 255) / 256)), dim3(256),
+                     0, stream, p, lay);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
                                      hipStream_t stream) {
+  if (lay.nblocks > 1) return launch_bwd_blocks(p, lay, bf16, stream);
+  return launch_bwd_one(p, lay, bf16, stream);
+}
+
+namespace {
+
+hipError_t launch_bwd_one(const BwdParams& p, const BwdLayout& lay, bool bf16,
+                          hipStream_t stream) {
   const ScanParams& F = p.fwd;
   // 1. forward, saving the state entering every chunk (segmented like the
   //    backward when it is)
@@ -662,5 +898,7 @@ hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, b
                      stream, p, lay);
   return hipGetLastError();
 }
+
+}  // namespace
 
 }  // namespace ssm

@@ -115,6 +115,15 @@ struct BwdParams {
   float* ddelta_bias;       // [dim], nullable
   float* dh0;               // [batch, dim, dstate], nullable
   void* workspace;
+  // State-block mode (set by the driver for dstate > 16, null otherwise):
+  // the kernel adds its per-step sums over its states -- readout, d/d delta
+  // before the softplus derivative, d/d u without the skip term -- to these
+  // float32 [batch, dim, seqlen] arrays (writes them when acc_init) and
+  // writes neither du, ddelta, dz nor the dD / ddelta_bias partials.
+  float* acc_y = nullptr;
+  float* acc_ddt = nullptr;
+  float* acc_du = nullptr;
+  int acc_init = 0;
 };
 
 // Workspace of the backward pass.  With nseg > 1 the sequence is cut into
@@ -124,9 +133,19 @@ struct BwdParams {
 struct BwdLayout {
   size_t chunk_states_off, part_bc_off, part_a_off, part_d_off, fwd_agg_off, lam_agg_off, total;
   int nchunks, nwg, nseg, seg_len;
+  // dstate > 16: the states are taken in blocks of 16 (nblocks of them),
+  // each a backward pass of its own whose workspace is the layout above (at
+  // offset 0, for 16 states); after it: the float32 per-step accumulators
+  // acc[3][batch, dim, seqlen], the block's inputs and gradients (A, dA
+  // [dim, 16]; B, C [batch, 16, seqlen] in the input type; dB, dC float32;
+  // initial state, dlast, dinitial_state [batch, dim, 16]) and per-row
+  // dD, ddelta_bias sums [2][batch, dim].
+  int nblocks;
+  size_t acc_off, a_off, b_off, c_off, h0_off, dl_off, da_off, db_off, dc_off, dh0_off, prow_off;
 };
 
-BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus);
+BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus,
+                                    int in_bytes = 4);
 hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
                                      hipStream_t stream);
 

@@ -92,6 +92,12 @@ CASES = [  # (b, d, n, L, dtype, gate, bias, softplus, h0, dlast)
     (2, 130, 16, 257, "bf16", True, True, True, False, False),
     (1, 1, 3, 1, "f32", True, True, True, True, True),
     (2, 300, 13, 64, "bf16", False, False, True, True, True),
+    # dstate above 16: blocks of 16 states, per-step sums added across blocks
+    (2, 70, 32, 100, "f32", True, True, True, True, True),
+    (2, 130, 64, 257, "bf16", True, True, True, False, True),
+    (1, 40, 33, 77, "f32", False, True, True, True, False),
+    (3, 64, 48, 50, "f32", True, False, False, True, True),
+    (1, 100, 64, 700, "f32", True, True, True, True, True),   # blocks and time split
     # small batch, long enough to be split in time (segments of 64 steps or more)
     (1, 100, 16, 700, "f32", True, True, True, True, True),
     (2, 64, 4, 1000, "bf16", True, True, True, False, True),
@@ -133,9 +139,10 @@ def test_backward_1p4b_shape_short(lib):
     compare(g, ref, "bf16", True, True, False)
 
 
-def test_backward_repeatable(lib):
-    g1, _ = run_case(lib, 7, 2, 200, 16, 96, "bf16")
-    g2, _ = run_case(lib, 7, 2, 200, 16, 96, "bf16")
+@pytest.mark.parametrize("n", [16, 48])
+def test_backward_repeatable(lib, n):
+    g1, _ = run_case(lib, 7, 2, 200, n, 96, "bf16")
+    g2, _ = run_case(lib, 7, 2, 200, n, 96, "bf16")
     for k in g1:
         if g1[k] is not None:
             assert torch.equal(g1[k], g2[k]), k
