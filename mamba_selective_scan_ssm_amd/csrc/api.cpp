@@ -123,12 +123,15 @@ ssm::ScanTile pick_scan_tile(const ssm_scan_context* h, int64_t batch, int64_t d
   const int64_t row_tiles = batch * ((dim + 63) / 64);
   const int64_t simds = 4 * (int64_t)(h->num_cus > 0 ? h->num_cus : 256);
   using ssm::ScanTileId;
+  // Too few rows: up to 16 states, the waves of a workgroup take
+  // consecutive time slots of the same rows (the row-parallel lane layout);
+  // above, lane = row with the states split over waves.
   if (dstate <= 4) {
-    return {row_tiles >= simds ? ScanTileId::kN4_Seq : ScanTileId::kN4_Split};
+    return {row_tiles >= simds ? ScanTileId::kN4_Seq : ScanTileId::kN4_Slot};
   } else if (dstate <= 8) {
-    return {row_tiles * 2 >= simds ? ScanTileId::kN8_Seq : ScanTileId::kN8_Split};
+    return {row_tiles * 2 >= simds ? ScanTileId::kN8_Seq : ScanTileId::kN8_Slot};
   } else if (dstate <= 16) {
-    return {row_tiles * 4 >= simds ? ScanTileId::kN16_Seq : ScanTileId::kN16_Split};
+    return {row_tiles * 4 >= simds ? ScanTileId::kN16_Seq : ScanTileId::kN16_Slot};
   }
   return {row_tiles * 4 >= simds ? ScanTileId::kN64_Seq : ScanTileId::kN64_Split};
 }

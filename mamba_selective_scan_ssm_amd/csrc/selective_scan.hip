@@ -373,6 +373,277 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   }
 }
 
+// ---- time-sliced row kernel --------------------------------------------------
+
+// NG: states per lane; LPC: lanes per row (NG*LPC >= dstate); T: steps per
+// time slot; W: time slots per chunk = waves per workgroup.  Block = 64*W
+// threads, all W waves on the same 64/LPC rows (the row kernel's lane
+// layout: a row's states over a group of LPC lanes, its per-step work over
+// their slices of the slot), wave w taking the steps [c0 + w T, c0 + (w+1) T)
+// of every chunk of W T steps.  Per chunk, each wave
+//   1. scans its slot from the identity, keeping the slot's decays
+//      a_t = exp2(delta_t A2) in registers, and publishes the slot's
+//      aggregate (prod a, v) = (exp2(A2 sum delta), h) per (row, state);
+//   2. folds the aggregates of the earlier slots onto the running carry of
+//      the chunks before ([EXPLAINED] eqs. (10)-(11)) -- its carry-in -- and
+//      all W of them into the next chunk's carry;
+//   3. rescans the slot from its carry-in with the cached decays, reads out
+//      y, reduce-scatters the partial readouts over the row's lanes, adds
+//      the skip term, gates and stores.
+// For shapes whose rows alone give too few waves, without any workspace:
+// the rows of a wave are spread over W times as many waves (the rescan
+// costs about three issue slots per state update on top of the scan).
+template <typename In, int NG, int LPC, int T, int W>
+__global__ void __launch_bounds__(64 * W) selective_scan_slot_kernel(ScanParams prm) {
+  constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
+  constexpr int RPB = 64 / LPC;      // rows per workgroup (shared by its waves)
+  constexpr int TS = T / LPC;        // steps of the slot whose per-step work one lane owns
+  constexpr int TC = W * T;          // steps per chunk
+  constexpr int NTHR = 64 * W;
+  constexpr int EPU = Elem<In>::kPer16B;
+  static_assert(NG % 4 == 0 && T % LPC == 0 && TC % EPU == 0, "tile shape");
+  constexpr int UPR = TC / EPU;      // 16-byte units per state row of a chunk
+  constexpr int UNITS = 2 * NS * UPR;
+  constexpr int RBU = (UNITS + NTHR - 1) / NTHR;
+
+  __shared__ alignas(16) float sB[2][TC][NS];
+  __shared__ alignas(16) float sC[2][TC][NS];
+  __shared__ alignas(16) float2 sAgg[W][RPB][NS];  // slot aggregates per (row, state)
+
+  const In* __restrict__ u = static_cast<const In*>(prm.u);
+  const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(prm.B);
+  const In* __restrict__ Cm = static_cast<const In*>(prm.C);
+  const In* __restrict__ z = static_cast<const In*>(prm.z);
+  In* __restrict__ y = static_cast<In*>(prm.y);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // time slot of this wave
+  const int slot = lane % LPC;       // position in the row's lane group
+  const int r = lane / LPC;          // row within the workgroup
+  const int b = blockIdx.y;
+  const int d = blockIdx.x * RPB + r;
+  const bool row_ok = d < prm.dim;
+  const bool has_z = z != nullptr;
+  const int L = prm.seqlen;
+  const int N = prm.dstate;
+  const int64_t rowi = (int64_t)b * prm.dim + (row_ok ? d : 0);
+  const int64_t row_base = rowi * (int64_t)L;
+  // B, C of the group of the workgroup's rows: [batch, ngroups, dstate, seqlen]
+  const int grp = (int)(blockIdx.x * RPB) / (prm.dim / prm.ngroups);
+  const int64_t bc_base = ((int64_t)b * prm.ngroups + grp) * N * (int64_t)L;
+
+  float A2[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    A2[k] = (row_ok && n < N) ? prm.A[(int64_t)d * N + n] * kLog2e : 0.0f;
+  }
+  const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
+  const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
+  // running carry: the state entering the chunk (v_0 of [EXPLAINED] eqs.
+  // (8)-(9) when an initial state is given)
+  float carry[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    carry[k] = (prm.h0 && row_ok && n < N) ? prm.h0[rowi * N + n] : 0.0f;
+  }
+
+  RawSeg<In, TS> ru, rd, rz;
+  RawSeg<In, EPU> rbc[RBU];
+  auto load_chunk = [&](int c0) {
+    const int ts = c0 + w * T + slot * TS;
+    if (row_ok) {
+      load_raw<In, TS>(u, row_base, ts, L, ru);
+      load_raw<In, TS>(dlt, row_base, ts, L, rd);
+      if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
+    }
+#pragma unroll
+    for (int q = 0; q < RBU; ++q) {
+      const int e = tid + q * NTHR;
+      const int n = e % NS, rest = e / NS;
+      const int sg = rest % UPR, x = rest / UPR;
+      if (e < UNITS && n < N) {
+        load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + sg * EPU, L, rbc[q]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
+      }
+    }
+  };
+
+  const int nchunks = (L + TC - 1) / TC;
+  load_chunk(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * TC;
+    const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
+    // -- B and C of this chunk into LDS as float32 [t][n] ----------------------
+#pragma unroll
+    for (int q = 0; q < RBU; ++q) {
+      const int e = tid + q * NTHR;
+      if (e < UNITS) {
+        const int n = e % NS, rest = e / NS;
+        const int sg = rest % UPR, x = rest / UPR;
+        float v[EPU];
+        decode_raw<In, EPU>(rbc[q], v);
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) {
+          if (x) sC[buf][sg * EPU + i][n] = v[i];
+          else sB[buf][sg * EPU + i][n] = v[i];
+        }
+      }
+    }
+    // -- per-step work for this lane's slice of the slot ------------------------
+    const int ts = c0 + w * T + slot * TS;
+    float uk[TS], gk[TS], dl[TS], du[TS];
+    {
+      float dr[TS];
+      decode_raw<In, TS>(ru, uk);
+      decode_raw<In, TS>(rd, dr);
+      if (has_z) {
+        float zk[TS];
+        decode_raw<In, TS>(rz, zk);
+#pragma unroll
+        for (int j = 0; j < TS; ++j) gk[j] = silu_f(zk[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) gk[j] = 1.0f;
+      }
+      if (prm.delta_softplus) {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) dl[j] = softplus_in<In>(dr[j] + bias);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TS; ++j) dl[j] = dr[j] + bias;
+      }
+      // steps past the end are the identity (delta = 0)
+      if (ts + TS > L) {
+#pragma unroll
+        for (int j = 0; j < TS; ++j)
+          if (ts + j >= L) dl[j] = 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < TS; ++j) du[j] = dl[j] * uk[j];
+    }
+    if (ch + 1 < nchunks) load_chunk(c0 + TC);
+    __syncthreads();  // B, C of this chunk staged; last chunk's aggregates read
+
+    // -- 1. the slot from the identity: decays and aggregate ---------------------
+    float acache[T][NG], v[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) v[k] = 0.0f;
+    float dsum = 0.0f;
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      float dt, dut;
+      if constexpr (LPC > 1) {
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+      } else {
+        dt = dl[t];
+        dut = du[t];
+      }
+      dsum += dt;
+#pragma unroll
+      for (int k4 = 0; k4 < NG; k4 += 4) {
+        const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][w * T + t][slot * NG + k4]);
+        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = fast_exp2(dt * A2[k4 + i]);
+          acache[t][k4 + i] = a;
+          v[k4 + i] = __builtin_fmaf(a, v[k4 + i], dut * bv[i]);
+        }
+      }
+    });
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      sAgg[w][r][slot * NG + k] = make_float2(fast_exp2(A2[k] * dsum), v[k]);
+    __syncthreads();  // every slot's aggregate published
+
+    // -- 2. carry-in of this slot and the next chunk's carry ---------------------
+    float h[NG];
+    for (int s2 = 0; s2 < W; ++s2) {  // (uniform per wave)
+      if (s2 == w) {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) h[k] = carry[k];
+      }
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        const float2 g = sAgg[s2][r][slot * NG + k];
+        carry[k] = __builtin_fmaf(g.x, carry[k], g.y);
+      }
+    }
+
+    // -- 3. rescan with the cached decays, read out ------------------------------
+    float yp[T];
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      float dut;
+      if constexpr (LPC > 1) dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+      else dut = du[t];
+      float acc = 0.0f;
+#pragma unroll
+      for (int k4 = 0; k4 < NG; k4 += 4) {
+        const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][w * T + t][slot * NG + k4]);
+        const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][w * T + t][slot * NG + k4]);
+        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+        const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[k4 + i] = __builtin_fmaf(acache[t][k4 + i], h[k4 + i], dut * bv[i]);
+          acc = __builtin_fmaf(cv[i], h[k4 + i], acc);
+        }
+      }
+      yp[t] = acc;
+    });
+
+    // -- sum the group's partial readouts onto the owners of the steps ---------
+    float yo[TS];
+    if constexpr (LPC == 4) {
+      float s1[T / 2];
+      const bool lo = slot < 2;
+#pragma unroll
+      for (int j = 0; j < T / 2; ++j) {
+        const float keep = lo ? yp[j] : yp[T / 2 + j];
+        const float send = lo ? yp[T / 2 + j] : yp[j];
+        s1[j] = keep + dpp_f<kSwapHalves>(send);
+      }
+      const bool ev = (slot & 1) == 0;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float keep = ev ? s1[j] : s1[TS + j];
+        const float send = ev ? s1[TS + j] : s1[j];
+        yo[j] = keep + dpp_f<kSwapPairs>(send);
+      }
+    } else if constexpr (LPC == 2) {
+      const bool ev = slot == 0;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float keep = ev ? yp[j] : yp[TS + j];
+        const float send = ev ? yp[TS + j] : yp[j];
+        yo[j] = keep + dpp_f<kSwapPairs>(send);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TS; ++j) yo[j] = yp[j];
+    }
+#pragma unroll
+    for (int j = 0; j < TS; ++j) yo[j] = __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j];
+    if (row_ok && y) store_seg<In, TS>(y, row_base, ts, L, yo);
+  }
+  // -- final state: the carry after the last chunk (steps past the end are
+  //    identity steps) -----------------------------------------------------------
+  if (prm.last_state && row_ok && w == 0) {
+    float* ls = prm.last_state + rowi * N;
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      if (slot * NG + k < N) ls[slot * NG + k] = carry[k];
+  }
+}
+
 // ---- carry-ins of the time segments --------------------------------------------
 
 // One step of the inclusive scan below: combine this lane's (a, v) with the
@@ -752,6 +1023,15 @@ hipError_t launch_cfg(const ScanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename In, int NG, int LPC, int T, int W>
+hipError_t launch_slot(const ScanParams& p, hipStream_t stream) {
+  constexpr int RPB = 64 / LPC;
+  dim3 grid((unsigned)((p.dim + RPB - 1) / RPB), (unsigned)p.batch);
+  hipLaunchKernelGGL((selective_scan_slot_kernel<In, NG, LPC, T, W>), grid, dim3(64 * W), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <typename In>
 hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
   switch (t.id) {
@@ -763,6 +1043,9 @@ hipError_t launch_typed(const ScanParams& p, const ScanTile& t, hipStream_t s) {
     case ScanTileId::kN8_Split: return launch_cfg<In, 4, 2, 4, 16>(p, s);
     case ScanTileId::kN16_Split: return launch_cfg<In, 4, 4, 2, 32>(p, s);
     case ScanTileId::kN64_Split: return launch_cfg<In, 16, 4, 2, 4>(p, s);
+    case ScanTileId::kN4_Slot: return launch_slot<In, 4, 1, 16, 8>(p, s);
+    case ScanTileId::kN8_Slot: return launch_slot<In, 4, 2, 16, 8>(p, s);
+    case ScanTileId::kN16_Slot: return launch_slot<In, 4, 4, 16, 8>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -879,6 +1162,9 @@ int scan_tile_rows(const ScanTile& tile) {
     case ScanTileId::kN4_Seq: return 256;
     case ScanTileId::kN8_Seq: return 128;
     case ScanTileId::kN16_Seq: case ScanTileId::kN64_Seq: return 64;
+    case ScanTileId::kN4_Slot: return 64;
+    case ScanTileId::kN8_Slot: return 32;
+    case ScanTileId::kN16_Slot: return 16;
     default: return 64;  // time-split kernels: 64 rows per workgroup
   }
 }

@@ -37,10 +37,13 @@ struct ScanParams {
 
 // Compiled kernel shapes.  "Seq": each wave runs the whole sequence for its
 // rows (no time split).  "Split": each time chunk is split over several
-// waves whose carries are combined with the associative operator.
+// waves whose carries are combined with the associative operator (lane =
+// row).  "Slot": the row-parallel lane layout with the waves of a workgroup
+// on consecutive time slots of the same rows.
 enum class ScanTileId : int {
   kN4_Seq, kN8_Seq, kN16_Seq, kN64_Seq,
   kN4_Split, kN8_Split, kN16_Split, kN64_Split,
+  kN4_Slot, kN8_Slot, kN16_Slot,
 };
 
 struct ScanTile {
