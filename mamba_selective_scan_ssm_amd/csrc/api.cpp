@@ -258,7 +258,6 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   ssm::ScanParams p;
   p.u = u; p.delta = delta; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z;
   p.delta_bias = delta_bias; p.y = y; p.last_state = last_state; p.h0 = initial_state;
-  p.chunk_states = nullptr;
   p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate; p.seqlen = (int)seqlen;
   p.delta_softplus = delta_softplus ? 1 : 0;
   p.ngroups = (int)ngroups;
@@ -441,7 +440,6 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   ssm::ScanParams& f = p.fwd;
   f.u = u; f.delta = delta; f.A = A; f.B = B; f.C = C; f.D = D; f.z = z;
   f.delta_bias = delta_bias; f.y = nullptr; f.last_state = nullptr; f.h0 = initial_state;
-  f.chunk_states = nullptr;
   f.batch = (int)batch; f.dim = (int)dim; f.dstate = (int)dstate; f.seqlen = (int)seqlen;
   f.delta_softplus = delta_softplus ? 1 : 0;
   f.ngroups = 1;

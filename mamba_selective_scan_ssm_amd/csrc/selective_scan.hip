@@ -201,14 +201,6 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   for (int ch = 0; ch < nchunks; ++ch) {
     const int c0 = t_begin + ch * T;
     const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
-    if (!AGG && prm.chunk_states && row_ok) {  // state entering the chunk, for the backward pass
-      // global chunk index (segments start on a chunk boundary)
-      const int64_t gch = t_begin / T + ch, gn = (L + T - 1) / T;
-      float* cs = prm.chunk_states + (((int64_t)b * prm.dim + d) * gn + gch) * N;
-#pragma unroll
-      for (int k = 0; k < NG; ++k)
-        if (slot * NG + k < N) cs[slot * NG + k] = h[k];
-    }
 
     // -- B and C of this chunk into LDS as float32 [t][n] --------------------
     if constexpr (RB) {
@@ -1086,29 +1078,16 @@ hipError_t launch_segment_carry(float* slots, int nslots, int64_t npairs, const 
   return hipGetLastError();
 }
 
-hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream) {
-  // the row-parallel kernel with 16-step chunks: a saved state every 16 steps.
-  // With p.seg_len > 0 (a multiple of 64), the segments' aggregates are
-  // computed first (into p.seg_agg) and every segment runs from its carry-in.
-  const int nz = p.seg_len ? (p.seqlen + p.seg_len - 1) / p.seg_len : 1;
-  if (nz > 1) {
-    ScanParams q = p;
-    q.chunk_states = nullptr;
-    hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(q, stream, nz - 1)
-                        : launch_rows_tier<float, true>(q, stream, nz - 1);
-    if (e != hipSuccess) return e;
-    e = launch_segment_carry(p.seg_agg, nz - 1, (int64_t)p.batch * p.dim * p.dstate, p.h0, false,
-                             stream);
-    if (e != hipSuccess) return e;
-  }
-  if (bf16) {
-    if (p.dstate <= 4) return launch_rows<uint16_t, 4, 1, 16>(p, stream, nz);
-    if (p.dstate <= 8) return launch_rows<uint16_t, 4, 2, 16>(p, stream, nz);
-    return launch_rows<uint16_t, 4, 4, 16>(p, stream, nz);
-  }
-  if (p.dstate <= 4) return launch_rows<float, 4, 1, 16>(p, stream, nz);
-  if (p.dstate <= 8) return launch_rows<float, 4, 2, 16>(p, stream, nz);
-  return launch_rows<float, 4, 4, 16>(p, stream, nz);
+hipError_t launch_selective_scan_carries(const ScanParams& p, bool bf16, hipStream_t stream) {
+  // every segment but the last scanned from the identity (its aggregate into
+  // p.seg_agg), then the combine scan of the aggregates in place
+  const int nz = (p.seqlen + p.seg_len - 1) / p.seg_len;
+  if (nz <= 1) return hipSuccess;
+  hipError_t e = bf16 ? launch_rows_tier<uint16_t, true>(p, stream, nz - 1)
+                      : launch_rows_tier<float, true>(p, stream, nz - 1);
+  if (e != hipSuccess) return e;
+  return launch_segment_carry(p.seg_agg, nz - 1, (int64_t)p.batch * p.dim * p.dstate, p.h0, false,
+                              stream);
 }
 
 hipError_t launch_selective_scan(const ScanParams& p, const ScanTile& tile, bool bf16,

@@ -16,23 +16,27 @@
 //   ddelta_t = ddt_t sigmoid(delta_t + bias) (softplus) ;  dbias += ddelta_t
 //   dh0 = lam after t = 0.
 //
-// Three launches:
-//   1. the row-parallel forward kernel with 16-step chunks, saving the state
-//      entering every chunk (no y, no last_state);
-//   2. selective_scan_bwd_kernel: per row, chunks in reverse order; each
-//      chunk's states are recomputed from its saved entry state into
-//      registers, then the reverse recurrence runs over the chunk.  The lane
-//      layout is the forward's (a row's states over a DPP lane group, the
+// Launches (dstate <= 16; larger dstate runs this per block of 16 states):
+//   1. bwd_fwd_sweep_kernel: the recurrence forward, per row, saving the
+//      state entering every 16-step chunk, with the gradients that need h_t
+//      but not the adjoint (dz, dD, the dC partials);
+//   2. bwd_rev_sweep_kernel: per row, 16-step chunks in reverse order; each
+//      chunk's decayed states a_t h_{t-1} are recomputed from its saved
+//      entry state into registers, then the adjoint runs backwards over the
+//      chunk (du, ddelta, dA, dinitial_state, the dB partials).  Both use
+//      the forward's lane layout (a row's states over a DPP lane group, the
 //      group's lanes owning slices of the per-step work; per-step sums over
-//      the group are formed at once with DPP adds).  dB and dC need a
-//      sum over rows: each step's per-lane contributions are summed over
-//      the rows of a 16-lane DPP row with row shifts, the partial sums go
-//      to LDS and are added per workgroup, giving one partial per (batch,
-//      workgroup, state, step) in the workspace; dA, dD and dbias are kept
-//      per row (one partial per batch entry);
+//      the group formed with DPP adds).  dB and dC are sums over rows: each
+//      step's per-lane terms are summed over the rows of a 16-lane DPP row
+//      with row shifts, the partial sums go to LDS and are added per
+//      workgroup, giving one partial per (batch, workgroup, state, step);
+//      dA, dD and dbias are kept per row (one partial per batch entry);
 //   3. two small kernels add the partials (over workgroups for dB and dC,
 //      over the batch for dA, dD, dbias) in a fixed order, so the result is
 //      deterministic.
+// Small batches split the sequence into segments: the forward's carry-ins
+// (aggregate pass and combine scan) come before 1, the adjoint's carry-ins
+// (bwd_lambda_agg_kernel and the same scan from the right) between 1 and 2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,8 +56,12 @@ constexpr int kBwdNG = 4;   // states per lane
 
 // Sum of v over the lanes of a 16-lane DPP row that share this lane's slot
 // (lane % LPC); the sum ends up in the last LPC lanes of the row.
+// (No contraction of these adds with the products that feed them: an add of
+// a DPP-moved value folds into one v_add_f32_dpp, while a contracted fma
+// needs the move on its own and keeps the broadcasts from folding too.)
 template <int LPC>
 __device__ __forceinline__ float row_sum_same_slot(float v) {
+#pragma clang fp contract(off)
   if constexpr (LPC <= 1) v += dpp_f<0x111>(v);  // row_shr:1
   if constexpr (LPC <= 2) v += dpp_f<0x112>(v);  // row_shr:2
   if constexpr (LPC <= 4) v += dpp_f<0x114>(v);  // row_shr:4
@@ -64,29 +72,44 @@ __device__ __forceinline__ float row_sum_same_slot(float v) {
 // Sum over the LPC lanes of a row's group (every lane gets the sum).
 template <int LPC>
 __device__ __forceinline__ float group_sum(float v) {
+#pragma clang fp contract(off)
   if constexpr (LPC >= 2) v += dpp_f<kSwapPairs>(v);
   if constexpr (LPC >= 4) v += dpp_f<kSwapHalves>(v);
   return v;
 }
 
-template <typename In, int LPC>
-__global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, BwdLayout lay) {
-  constexpr int NG = kBwdNG, T = kBwdT;
+// Per-chunk layout shared by the two sweeps: a row's states over a group of
+// LPC lanes (NG = 4 each), its per-step work over their slices of TS = T/LPC
+// steps; B and C of the chunk staged in LDS as float32 [t][n].
+//
+// ---- forward sweep -------------------------------------------------------------
+// Per row, t ascending from the initial state (or the segment's carry-in):
+// the recurrence, the state entering every kBwdT-step chunk saved for the
+// reverse sweep, and every gradient that needs h_t but not the adjoint:
+//   yh_t = C_t . h_t + D u_t,  dz_t = dy_t yh_t silu'(z_t),  dD += dyh_t u_t,
+//   dC_t += dyh_t h_t  (a sum over rows: summed over the rows of a 16-lane
+//   DPP row with row shifts, then over the workgroup's 16 such partials in
+//   LDS, one partial per (batch, workgroup, state, step) in the workspace).
+// In state-block mode the readout sum over the block's states goes to acc_y
+// instead (dz and dD are formed from the totals by the finishing kernel).
+template <typename In, int LPC, int T>
+__global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayout lay) {
+  constexpr int NG = kBwdNG;
   constexpr int NS = NG * LPC;       // states covered per row
   constexpr int RPW = 64 / LPC;      // rows per wave
   constexpr int RPB = 4 * RPW;       // rows per workgroup
   constexpr int TS = T / LPC;        // steps whose per-step work one lane owns
   constexpr int EPU = Elem<In>::kPer16B;
-  static_assert(T % EPU == 0, "chunk must hold whole 16-byte units");
+  static_assert(T % EPU == 0 && T % kBwdT == 0, "chunk must hold whole 16-byte units");
   constexpr int UPR = T / EPU;
   constexpr int UNITS = 2 * NS * UPR;
   constexpr int RB = (UNITS + 255) / 256;
   constexpr int kPad = T * NS + 4;   // LDS stride of one (wave, 16-lane row) partial block
 
-  __shared__ alignas(16) float sB[T][NS];
-  __shared__ alignas(16) float sC[T][NS];
-  __shared__ alignas(16) float sPB[4][4][kPad];  // [wave][16-lane row][t*NS + n]
-  __shared__ alignas(16) float sPC[4][4][kPad];
+  __shared__ alignas(16) float sB[2][T][NS];
+  __shared__ alignas(16) float sC[2][T][NS];
+  __shared__ alignas(16) float sPC[4][4][kPad];  // [wave][16-lane row][t*NS + n]
+  __shared__ alignas(16) float sJunk[T * NS + 64];
 
   const ScanParams& F = P.fwd;
   const In* __restrict__ u = static_cast<const In*>(F.u);
@@ -106,18 +129,282 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
   const int d = wg * RPB + wv * RPW + lane / LPC;
   const bool row_ok = d < F.dim;
   const bool has_z = z != nullptr;
+  const bool block_mode = P.acc_y != nullptr;
+  const int L = F.seqlen;
+  const int N = F.dstate;
+  const int64_t rows = (int64_t)F.batch * F.dim;
+  const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
+  const int64_t row_base = row * (int64_t)L;
+  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  const int seg = blockIdx.z;
+  const int t_begin = lay.nseg > 1 ? seg * lay.seg_len : 0;
+  const int t_end = lay.nseg > 1 ? min(L, t_begin + lay.seg_len) : L;
+
+  float A2[NG], h[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) {
+    const int n = slot * NG + k;
+    const bool ok = row_ok && n < N;
+    A2[k] = ok ? F.A[(int64_t)d * N + n] * kLog2e : 0.0f;
+    h[k] = (ok && F.h0) ? F.h0[row * N + n] : 0.0f;
+  }
+  // carry-in of a later segment, left in slot seg - 1 by segment_carry_kernel
+  if (seg > 0 && row_ok) {
+    const float* cin = reinterpret_cast<const float*>(
+        static_cast<const char*>(P.workspace) + lay.fwd_agg_off) + ((int64_t)(seg - 1) * rows + row) * N * 2;
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      if (slot * NG + k < N) h[k] = cin[2 * (slot * NG + k) + 1];
+  }
+  const float Dd = (row_ok && F.D) ? F.D[d] : 0.0f;
+  const float bias = (row_ok && F.delta_bias) ? F.delta_bias[d] : 0.0f;
+  float dD_acc = 0.0f;
+  // Where this lane stores its row sums of step t (at + t * NS): the sums sit
+  // in the last LPC lanes of each 16-lane row; the other lanes write to a
+  // scratch block that is never read (no branch around the store).
+  float* const pc_base = (lane & 15) >= 16 - LPC ? &sPC[wv][drow][slot * NG]
+                                                 : &sJunk[(lane & 15) * 4];
+  float* chunk_states = reinterpret_cast<float*>(static_cast<char*>(P.workspace) +
+                                                 lay.chunk_states_off);
+  float* part_c = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off) +
+                  (int64_t)F.batch * lay.nwg * N * L;  // dC partials follow dB's
+
+  // Raw inputs of one chunk, loaded one chunk ahead of their use; every load
+  // is unconditional (clamped indices).
+  RawSeg<In, TS> ru, rd, rz, rg;
+  RawSeg<In, EPU> rbc[RB];
+  auto load_chunk = [&](int c0) {
+    const int ts = c0 + slot * TS;
+    load_raw<In, TS>(u, row_base, ts, L, ru);
+    load_raw<In, TS>(dlt, row_base, ts, L, rd);
+    load_raw<In, TS>(dy, row_base, ts, L, rg);
+    if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = min(tid + q * 256, UNITS - 1);
+      const int n = e % NS, rest = e / NS;
+      const int sg = rest % UPR, x = rest / UPR;
+      load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)min(n, N - 1) * L, c0 + sg * EPU, L,
+                        rbc[q]);
+    }
+  };
+
+  const int nch = (t_end - t_begin + T - 1) / T;
+  load_chunk(t_begin);
+  for (int ch = 0; ch < nch; ++ch) {
+    const int c0 = t_begin + ch * T;
+    const int buf = ch & 1;  // its last readers were two chunks ago, before a barrier
+    const int ts = c0 + slot * TS;
+    // -- B and C of the chunk into LDS ----------------------------------------
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int e = tid + q * 256;
+      if (e < UNITS) {
+        const int n = e % NS, rest = e / NS;
+        const int sg = rest % UPR, x = rest / UPR;
+        float v[EPU];
+        decode_raw<In, EPU>(rbc[q], v);
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) {
+          const float vv = n < N ? v[i] : 0.0f;
+          if (x) sC[buf][sg * EPU + i][n] = vv;
+          else sB[buf][sg * EPU + i][n] = vv;
+        }
+      }
+    }
+    // -- per-step values of this lane's slice ---------------------------------
+    float uk[TS], dl[TS], du[TS], gy[TS], zk[TS], sgz[TS], dyh[TS];
+    {
+      float dr[TS];
+      decode_raw<In, TS>(ru, uk);
+      decode_raw<In, TS>(rd, dr);
+      decode_raw<In, TS>(rg, gy);
+      if (has_z) decode_raw<In, TS>(rz, zk);
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        if (!row_ok) uk[j] = gy[j] = dr[j] = 0.0f;
+        if (!has_z || !row_ok) zk[j] = 0.0f;
+        const float x = dr[j] + bias;
+        dl[j] = F.delta_softplus ? softplus_in<In>(x) : x;
+        if (ts + j >= L) dl[j] = 0.0f;  // past the end: identity steps
+        du[j] = dl[j] * uk[j];
+        sgz[j] = has_z ? fast_rcp(1.0f + fast_exp2(-zk[j] * kLog2e)) : 1.0f;
+        dyh[j] = has_z ? gy[j] * zk[j] * sgz[j] : gy[j];
+      }
+    }
+    if (ch + 1 < nch) load_chunk(c0 + T);
+    __syncthreads();  // sB, sC of this chunk complete; sPC of the last chunk read
+
+    // -- recurrence over the chunk ----------------------------------------------
+    float yp[T];
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      float dt, dut, dyt;
+      if constexpr (LPC > 1) {
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+        dyt = dpp_f<group_bcast<LPC>(t / TS)>(dyh[t % TS]);
+      } else {
+        dt = dl[t];
+        dut = du[t];
+        dyt = dyh[t];
+      }
+      if constexpr (t % kBwdT == 0) {  // the state entering this kBwdT-step piece
+        if (row_ok && c0 + t < L) {
+          float* cs = chunk_states + (row * lay.nchunks + (c0 + t) / kBwdT) * N;
+#pragma unroll
+          for (int k = 0; k < NG; ++k)
+            if (slot * NG + k < N) cs[slot * NG + k] = h[k];
+        }
+      }
+      const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG]);
+      const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG]);
+      const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
+      const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
+      float acc = 0.0f, cC[NG];
+#pragma unroll
+      for (int k = 0; k < NG; ++k) {
+        const float a = fast_exp2(dt * A2[k]);
+        h[k] = __builtin_fmaf(a, h[k], dut * bv[k]);
+        acc = __builtin_fmaf(cv[k], h[k], acc);
+        cC[k] = dyt * h[k];
+      }
+      yp[t] = acc;
+#pragma unroll
+      for (int k = 0; k < NG; ++k) cC[k] = row_sum_same_slot<LPC>(cC[k]);
+      *reinterpret_cast<float4*>(pc_base + t * NS) = make_float4(cC[0], cC[1], cC[2], cC[3]);
+    });
+
+    // -- the group's partial readouts onto the owners of the steps --------------
+    float yo[TS];
+    if constexpr (LPC == 4) {
+      float s1[T / 2];
+      const bool lo = slot < 2;
+#pragma unroll
+      for (int j = 0; j < T / 2; ++j) {
+        const float keep = lo ? yp[j] : yp[T / 2 + j];
+        const float send = lo ? yp[T / 2 + j] : yp[j];
+        s1[j] = keep + dpp_f<kSwapHalves>(send);
+      }
+      const bool ev = (slot & 1) == 0;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float keep = ev ? s1[j] : s1[TS + j];
+        const float send = ev ? s1[TS + j] : s1[j];
+        yo[j] = keep + dpp_f<kSwapPairs>(send);
+      }
+    } else if constexpr (LPC == 2) {
+      const bool ev = slot == 0;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const float keep = ev ? yp[j] : yp[TS + j];
+        const float send = ev ? yp[TS + j] : yp[j];
+        yo[j] = keep + dpp_f<kSwapPairs>(send);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < TS; ++j) yo[j] = yp[j];
+    }
+    // -- output-side gradients of this lane's steps -----------------------------
+    if (block_mode) {
+      if (row_ok) {
+        float* ay = P.acc_y + row_base;
+#pragma unroll
+        for (int j = 0; j < TS; ++j)
+          if (ts + j < L) ay[ts + j] = P.acc_init ? yo[j] : ay[ts + j] + yo[j];
+      }
+    } else {
+      if (has_z) {
+        float dzv[TS];
+#pragma unroll
+        for (int j = 0; j < TS; ++j) {
+          const float yh = __builtin_fmaf(Dd, uk[j], yo[j]);
+          dzv[j] = gy[j] * yh * sgz[j] * __builtin_fmaf(zk[j], 1.0f - sgz[j], 1.0f);
+        }
+        if (row_ok) store_seg<In, TS>(static_cast<In*>(P.dz), row_base, ts, L, dzv);
+      }
+#pragma unroll
+      for (int j = 0; j < TS; ++j) dD_acc = __builtin_fmaf(dyh[j], uk[j], dD_acc);
+    }
+    __syncthreads();  // sPC complete
+    // -- this workgroup's dC partials for the chunk --------------------------------
+    for (int e = tid; e < T * NS; e += 256) {
+      const int t = e / NS, n = e % NS;
+      float sc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc += sPC[w][r][e];
+      if (n < N && c0 + t < t_end)
+        part_c[(((int64_t)b * lay.nwg + wg) * N + n) * L + c0 + t] = sc;
+    }
+  }
+  dD_acc = group_sum<LPC>(dD_acc);
+  if (row_ok && slot == 0) {
+    float* part_d = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_d_off);
+    part_d[(int64_t)(2 * seg) * rows + row] = dD_acc;  // [segment, 2, batch, dim]
+  }
+}
+
+// ---- reverse sweep -------------------------------------------------------------
+// Per row, chunks of kBwdT steps in reverse order.  A chunk's decayed states
+// q_t = a_t h_{t-1} are recomputed from its saved entry state into
+// registers; then the adjoint lam = dL/dh_t runs backwards over the chunk
+// (lam += C_t dyh_t; ...; lam *= a_t) and, since dh_t/d delta_t =
+// A q_t + B_t u_t and dh_t/dA = delta_t q_t:
+//   ddelta_t = (sum_n A_n lam_n q_n + u_t sum_n lam_n B_n) softplus'
+//   du_t = dyh_t D + delta_t sum_n lam_n B_n,  dA_n += lam_n delta_t q_n,
+//   dB_t += lam delta_t u_t  (summed over rows like dC in the forward sweep).
+// In state-block mode the per-step sums over the block's states go to
+// acc_ddt, acc_du instead.
+template <typename In, int LPC>
+__global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayout lay) {
+  constexpr int NG = kBwdNG, T = kBwdT;
+  constexpr int NS = NG * LPC;
+  constexpr int RPW = 64 / LPC;
+  constexpr int RPB = 4 * RPW;
+  constexpr int TS = T / LPC;
+  constexpr int EPU = Elem<In>::kPer16B;
+  static_assert(T % EPU == 0, "chunk must hold whole 16-byte units");
+  constexpr int UPR = T / EPU;
+  constexpr int UNITS = 2 * NS * UPR;
+  constexpr int RB = (UNITS + 255) / 256;
+  constexpr int kPad = T * NS + 4;
+
+  __shared__ alignas(16) float sB[T][NS];
+  __shared__ alignas(16) float sC[T][NS];
+  __shared__ alignas(16) float sPB[4][4][kPad];
+  __shared__ alignas(16) float sJunk[T * NS + 64];
+
+  const ScanParams& F = P.fwd;
+  const In* __restrict__ u = static_cast<const In*>(F.u);
+  const In* __restrict__ dlt = static_cast<const In*>(F.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(F.B);
+  const In* __restrict__ Cm = static_cast<const In*>(F.C);
+  const In* __restrict__ z = static_cast<const In*>(F.z);
+  const In* __restrict__ dy = static_cast<const In*>(P.dy);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = lane % LPC;
+  const int drow = lane >> 4;
+  const int b = blockIdx.y;
+  const int wg = blockIdx.x;
+  const int d = wg * RPB + wv * RPW + lane / LPC;
+  const bool row_ok = d < F.dim;
+  const bool has_z = z != nullptr;
+  const bool block_mode = P.acc_y != nullptr;
   const int L = F.seqlen;
   const int N = F.dstate;
   const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
   const int64_t row_base = row * (int64_t)L;
   const int64_t bc_base = (int64_t)b * N * (int64_t)L;
-
-  // time window: segment blockIdx.z of lay.seg_len steps (whole sequence
-  // when there is one segment)
   const int seg = blockIdx.z;
   const int t_begin = lay.nseg > 1 ? seg * lay.seg_len : 0;
   const int t_end = lay.nseg > 1 ? min(L, t_begin + lay.seg_len) : L;
   const int64_t rows = (int64_t)F.batch * F.dim;
+
   float A2[NG], Af[NG], lam[NG], dA_acc[NG];
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
@@ -139,16 +426,14 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
   }
   const float Dd = (row_ok && F.D) ? F.D[d] : 0.0f;
   const float bias = (row_ok && F.delta_bias) ? F.delta_bias[d] : 0.0f;
-  float dD_acc = 0.0f, dbias_acc = 0.0f;
+  float dbias_acc = 0.0f;
+  // row sums of step t at pb_base + t * NS (as in the forward sweep)
+  float* const pb_base = (lane & 15) >= 16 - LPC ? &sPB[wv][drow][slot * NG]
+                                                 : &sJunk[(lane & 15) * 4];
   const float* chunk_states = reinterpret_cast<const float*>(
       static_cast<const char*>(P.workspace) + lay.chunk_states_off);
-  float* part_bc = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off);
-  const int64_t part_c_off = (int64_t)F.batch * lay.nwg * N * L;  // dC partials follow dB's
+  float* part_b = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off);
 
-  // Raw inputs of one chunk (this lane's slice of u, delta, dy, z; its share
-  // of the chunk's B and C; the saved entry state), loaded one chunk ahead of
-  // their use.  Every load is unconditional (clamped indices) so that the
-  // compiler can count the loads in flight instead of waiting for all.
   RawSeg<In, TS> ru, rd, rz, rg;
   RawSeg<In, EPU> rbc[RB];
   float hsr[NG];
@@ -163,8 +448,8 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
     for (int q = 0; q < RB; ++q) {
       const int e = min(tid + q * 256, UNITS - 1);
       const int n = e % NS, rest = e / NS;
-      const int seg = rest % UPR, x = rest / UPR;
-      load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)min(n, N - 1) * L, c0 + seg * EPU, L,
+      const int sg = rest % UPR, x = rest / UPR;
+      load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)min(n, N - 1) * L, c0 + sg * EPU, L,
                         rbc[q]);
     }
 #pragma unroll
@@ -177,182 +462,134 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
   for (int ch = ch_last; ch >= ch_first; --ch) {
     const int c0 = ch * T;
     const int ts = c0 + slot * TS;
-    // -- B and C of the chunk into LDS ----------------------------------------
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
       const int e = tid + q * 256;
       if (e < UNITS) {
         const int n = e % NS, rest = e / NS;
-        const int seg = rest % UPR, x = rest / UPR;
+        const int sg = rest % UPR, x = rest / UPR;
         float v[EPU];
         decode_raw<In, EPU>(rbc[q], v);
 #pragma unroll
         for (int i = 0; i < EPU; ++i) {
           const float vv = n < N ? v[i] : 0.0f;
-          if (x) sC[seg * EPU + i][n] = vv;
-          else sB[seg * EPU + i][n] = vv;
+          if (x) sC[sg * EPU + i][n] = vv;
+          else sB[sg * EPU + i][n] = vv;
         }
       }
     }
-    float hs[NG];  // state entering the chunk
+    float h[NG];  // state entering the chunk
 #pragma unroll
-    for (int k = 0; k < NG; ++k) hs[k] = (row_ok && slot * NG + k < N) ? hsr[k] : 0.0f;
+    for (int k = 0; k < NG; ++k) h[k] = (row_ok && slot * NG + k < N) ? hsr[k] : 0.0f;
     // -- per-step values of this lane's slice ---------------------------------
-    float uk[TS], dl[TS], du[TS], sp[TS], gy[TS], zk[TS];
+    float uk[TS], dl[TS], du[TS], sp[TS], dyh[TS];
     {
-      float dr[TS];
+      float dr[TS], gy[TS], zk[TS];
       decode_raw<In, TS>(ru, uk);
       decode_raw<In, TS>(rd, dr);
       decode_raw<In, TS>(rg, gy);
-      if (has_z) {
-        decode_raw<In, TS>(rz, zk);
-      } else {
-#pragma unroll
-        for (int j = 0; j < TS; ++j) zk[j] = 0.0f;
-      }
+      if (has_z) decode_raw<In, TS>(rz, zk);
 #pragma unroll
       for (int j = 0; j < TS; ++j) {
-        if (!row_ok) uk[j] = gy[j] = zk[j] = dr[j] = 0.0f;
+        if (!row_ok) uk[j] = gy[j] = dr[j] = 0.0f;
+        if (!has_z || !row_ok) zk[j] = 0.0f;
         sp[j] = dr[j] + bias;
-        dl[j] = F.delta_softplus ? softplus_f(sp[j]) : sp[j];
+        dl[j] = F.delta_softplus ? softplus_in<In>(sp[j]) : sp[j];
         if (ts + j >= L) dl[j] = 0.0f;  // past the end: identity steps
         du[j] = dl[j] * uk[j];
+        dyh[j] = has_z ? gy[j] * silu_f(zk[j]) : gy[j];
       }
     }
     load_chunk(ch > ch_first ? ch - 1 : ch_first);  // the last step reloads its own chunk
-    __syncthreads();  // sB, sC of this chunk are complete
+    __syncthreads();  // sB, sC of this chunk complete; sPB of the last chunk read
 
-    // -- forward over the chunk from its saved entry state ---------------------
-    // The readout of step t is summed over the lane group at once and kept
-    // by the lane that owns step t (no per-chunk array of partial sums).
-    float hist[T][NG], yo[TS];
+    // -- decayed states of the chunk, q_t = a_t h_{t-1} ---------------------------
+    float qh[T][NG];
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      float dt, dut;
+      if constexpr (LPC > 1) {
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
+      } else {
+        dt = dl[t];
+        dut = du[t];
+      }
+      const float4 bq = *reinterpret_cast<const float4*>(&sB[t][slot * NG]);
+      const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
 #pragma unroll
-    for (int j = 0; j < TS; ++j) yo[j] = 0.0f;
-    {
-      float h[NG];
-#pragma unroll
-      for (int k = 0; k < NG; ++k) h[k] = hs[k];
-      static_for<0, T>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        float dt, dut;
-        if constexpr (LPC > 1) {
-          dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
-          dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
-        } else {
-          dt = dl[t];
-          dut = du[t];
-        }
-        const float4 bq = *reinterpret_cast<const float4*>(&sB[t][slot * NG]);
-        const float4 cq = *reinterpret_cast<const float4*>(&sC[t][slot * NG]);
-        const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-        const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) {
-          const float a = fast_exp2(dt * A2[k]);
-          h[k] = __builtin_fmaf(a, h[k], dut * bv[k]);
-          hist[t][k] = h[k];
-          acc = __builtin_fmaf(cv[k], h[k], acc);
-        }
-        acc = group_sum<LPC>(acc);
-        if (slot == t / TS) yo[t % TS] = acc;
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
-    // -- output-side gradients for this lane's steps ---------------------------
-    float dyh[TS], dzv[TS];
+      for (int k = 0; k < NG; ++k) {
+        qh[t][k] = fast_exp2(dt * A2[k]) * h[k];
+        h[k] = __builtin_fmaf(dut, bv[k], qh[t][k]);
+      }
+    });
+
+    // -- reverse recurrence over the chunk -----------------------------------------
+    // The decays are recomputed: an empty asm makes delta opaque here, so that
+    // the compiler does not keep the chunk's 16 x NG decays from the loop
+    // above alive in registers instead (measured: 286 VGPRs, one wave per
+    // SIMD, 1.89 ms at the 1.4B shape, against 223 VGPRs and 1.58 ms).
+    float dlr[TS];
 #pragma unroll
     for (int j = 0; j < TS; ++j) {
-      const float yh = __builtin_fmaf(Dd, uk[j], yo[j]);
-      if (has_z) {
-        const float sg = fast_rcp(1.0f + fast_exp2(-zk[j] * kLog2e));
-        dyh[j] = gy[j] * zk[j] * sg;
-        dzv[j] = gy[j] * yh * sg * __builtin_fmaf(zk[j], 1.0f - sg, 1.0f);
-      } else {
-        dyh[j] = gy[j];
-        dzv[j] = 0.0f;
-      }
-      dD_acc = __builtin_fmaf(dyh[j], uk[j], dD_acc);
+      dlr[j] = dl[j];
+      asm volatile("" : "+v"(dlr[j]));
     }
-
-    // -- reverse recurrence over the chunk -------------------------------------
     float ddt_o[TS], du_o[TS];
 #pragma unroll
     for (int j = 0; j < TS; ++j) ddt_o[j] = du_o[j] = 0.0f;
     static_for<0, T>([&](auto rc) {
       constexpr int t = T - 1 - decltype(rc)::value;
-      float dyt, dt, dut, ut;
+      float dyt, dt, dut;
       if constexpr (LPC > 1) {
         dyt = dpp_f<group_bcast<LPC>(t / TS)>(dyh[t % TS]);
-        dt = dpp_f<group_bcast<LPC>(t / TS)>(dl[t % TS]);
+        dt = dpp_f<group_bcast<LPC>(t / TS)>(dlr[t % TS]);
         dut = dpp_f<group_bcast<LPC>(t / TS)>(du[t % TS]);
-        ut = dpp_f<group_bcast<LPC>(t / TS)>(uk[t % TS]);
       } else {
         dyt = dyh[t];
-        dt = dl[t];
+        dt = dlr[t];
         dut = du[t];
-        ut = uk[t];
       }
       const float4 bq = *reinterpret_cast<const float4*>(&sB[t][slot * NG]);
       const float4 cq = *reinterpret_cast<const float4*>(&sC[t][slot * NG]);
       const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
       const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
-      float ddt_p = 0.0f, du_p = 0.0f, cB[NG], cC[NG];
+      float ddt_p = 0.0f, lb_p = 0.0f, cB[NG];
 #pragma unroll
       for (int k = 0; k < NG; ++k) {
-        lam[k] = __builtin_fmaf(cv[k], dyt, lam[k]);          // lam = dL/dh_t
-        cC[k] = dyt * hist[t][k];
-        const float a = fast_exp2(dt * A2[k]);
-        const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hs[k];
-        ddt_p = __builtin_fmaf(lam[k], __builtin_fmaf(a * Af[k], hp, bv[k] * ut), ddt_p);
-        dA_acc[k] = __builtin_fmaf(lam[k] * a, dt * hp, dA_acc[k]);
+        lam[k] = __builtin_fmaf(cv[k], dyt, lam[k]);           // lam = dL/dh_t
+        const float lq = lam[k] * qh[t][k];
+        dA_acc[k] = __builtin_fmaf(lq, dt, dA_acc[k]);
+        ddt_p = __builtin_fmaf(lq, Af[k], ddt_p);
+        lb_p = __builtin_fmaf(lam[k], bv[k], lb_p);
         cB[k] = lam[k] * dut;
-        du_p = __builtin_fmaf(lam[k], dt * bv[k], du_p);
-        lam[k] *= a;                                           // dL/dh_{t-1}
+        lam[k] *= fast_exp2(dt * A2[k]);                       // dL/dh_{t-1}
       }
       ddt_p = group_sum<LPC>(ddt_p);
-      du_p = group_sum<LPC>(du_p);
-      if (slot == t / TS) {
-        ddt_o[t % TS] = ddt_p;
-        du_o[t % TS] = du_p;
+      lb_p = group_sum<LPC>(lb_p);
+      {  // the owner of step t keeps the sums (selects, no branch)
+        const bool own = slot == t / TS;
+        ddt_o[t % TS] = own ? __builtin_fmaf(uk[t % TS], lb_p, ddt_p) : ddt_o[t % TS];
+        du_o[t % TS] = own ? dl[t % TS] * lb_p : du_o[t % TS];
       }
-      // dB, dC: sum over the rows of this 16-lane DPP row, then to LDS
 #pragma unroll
-      for (int k = 0; k < NG; ++k) {
-        cB[k] = row_sum_same_slot<LPC>(cB[k]);
-        cC[k] = row_sum_same_slot<LPC>(cC[k]);
-      }
-      if ((lane & 15) >= 16 - LPC) {
-        *reinterpret_cast<float4*>(&sPB[wv][drow][t * NS + slot * NG]) =
-            make_float4(cB[0], cB[1], cB[2], cB[3]);
-        *reinterpret_cast<float4*>(&sPC[wv][drow][t * NS + slot * NG]) =
-            make_float4(cC[0], cC[1], cC[2], cC[3]);
-      }
-      // keep each step's operands within the step (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < NG; ++k) cB[k] = row_sum_same_slot<LPC>(cB[k]);
+      *reinterpret_cast<float4*>(pb_base + t * NS) = make_float4(cB[0], cB[1], cB[2], cB[3]);
     });
-    if (P.acc_y) {
-      // state block of a larger dstate: this block's per-step sums over its
-      // states (readout, d/d delta, d/d u) go to the float32 accumulators;
-      // the finishing kernel forms du, ddelta and dz from their totals
+    // -- input-side gradients of this lane's steps ----------------------------------
+    if (block_mode) {
       if (row_ok) {
-        float* ay = P.acc_y + row_base;
         float* at = P.acc_ddt + row_base;
         float* au = P.acc_du + row_base;
 #pragma unroll
         for (int j = 0; j < TS; ++j) {
           if (ts + j < L) {
-            ay[ts + j] = P.acc_init ? yo[j] : ay[ts + j] + yo[j];
             at[ts + j] = P.acc_init ? ddt_o[j] : at[ts + j] + ddt_o[j];
             au[ts + j] = P.acc_init ? du_o[j] : au[ts + j] + du_o[j];
           }
         }
       }
     } else {
-    if (has_z && row_ok) store_seg<In, TS>(static_cast<In*>(P.dz), row_base, ts, L, dzv);
-
-    // -- input-side gradients for this lane's steps ------------------------------
-    {
       float dus[TS], dds[TS];
 #pragma unroll
       for (int j = 0; j < TS; ++j) {
@@ -368,30 +605,19 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
         store_seg<In, TS>(static_cast<In*>(P.ddelta), row_base, ts, L, dds);
       }
     }
-    }
-    __syncthreads();  // sPB, sPC complete; sB, sC free
-    // -- this workgroup's dB, dC partials for the chunk ---------------------------
+    __syncthreads();  // sPB complete; sB, sC free
     for (int e = tid; e < T * NS; e += 256) {
       const int t = e / NS, n = e % NS;
-      float sb = 0.0f, sc = 0.0f;
+      float sb = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sb += sPB[w][r][e];
-          sc += sPC[w][r][e];
-        }
-      if (n < N && c0 + t < L) {
-        const int64_t o = (((int64_t)b * lay.nwg + wg) * N + n) * L + c0 + t;
-        part_bc[o] = sb;
-        part_bc[part_c_off + o] = sc;
-      }
+        for (int r = 0; r < 4; ++r) sb += sPB[w][r][e];
+      if (n < N && c0 + t < L)
+        part_b[(((int64_t)b * lay.nwg + wg) * N + n) * L + c0 + t] = sb;
     }
-    __syncthreads();  // before the next chunk overwrites the LDS tiles
   }
 
-  // -- per-row outputs and partials ------------------------------------------------
-  dD_acc = group_sum<LPC>(dD_acc);
   dbias_acc = group_sum<LPC>(dbias_acc);
   if (row_ok) {
     float* part_a = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_a_off);
@@ -404,10 +630,7 @@ __global__ void __launch_bounds__(256) selective_scan_bwd_kernel(BwdParams P, Bw
         if (P.dh0 && seg == 0) P.dh0[row * N + n] = lam[k];
       }
     }
-    if (slot == 0) {
-      part_d[(int64_t)(2 * seg) * rows + row] = dD_acc;         // [segment, 2, batch, dim]
-      part_d[(int64_t)(2 * seg + 1) * rows + row] = dbias_acc;
-    }
+    if (slot == 0) part_d[(int64_t)(2 * seg + 1) * rows + row] = dbias_acc;
   }
 }
 
@@ -544,7 +767,7 @@ __global__ void __launch_bounds__(256) bwd_lambda_agg_kernel(BwdParams P, BwdLay
 #pragma unroll
       for (int j = 0; j < TS; ++j) {
         const float sp = dr[j] + bias;
-        dl[j] = F.delta_softplus ? softplus_f(sp) : sp;
+        dl[j] = F.delta_softplus ? softplus_in<In>(sp) : sp;
         if (ts + j >= L || !row_ok) dl[j] = 0.0f;  // past the end: identity steps
         dyh[j] = has_z ? gy[j] * silu_f(zk[j]) : gy[j];
       }
@@ -585,12 +808,23 @@ __global__ void __launch_bounds__(256) bwd_lambda_agg_kernel(BwdParams P, BwdLay
   }
 }
 
+// Chunk length of the forward sweep: 16 steps (124 VGPRs at four lanes per
+// row; 32-step chunks need 279, whose state save in mid-chunk splits the
+// step loop).
+template <int LPC>
+constexpr int fwd_sweep_t() { return 16; }
+
 template <typename In, int LPC>
 hipError_t launch_bwd_rows(const BwdParams& p, const BwdLayout& lay, hipStream_t stream) {
+  const dim3 grid((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)lay.nseg);
+  hipLaunchKernelGGL((bwd_fwd_sweep_kernel<In, LPC, fwd_sweep_t<LPC>()>), grid, dim3(256), 0,
+                     stream, p, lay);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (lay.nseg > 1) {
     dim3 ga((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)(lay.nseg - 1));
     hipLaunchKernelGGL((bwd_lambda_agg_kernel<In, LPC>), ga, dim3(256), 0, stream, p, lay);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_segment_carry(reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
                                                       lay.lam_agg_off),
@@ -598,8 +832,7 @@ hipError_t launch_bwd_rows(const BwdParams& p, const BwdLayout& lay, hipStream_t
                              p.dlast, true, stream);
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)lay.nwg, (unsigned)p.fwd.batch, (unsigned)lay.nseg);
-  hipLaunchKernelGGL((selective_scan_bwd_kernel<In, LPC>), grid, dim3(256), 0, stream, p, lay);
+  hipLaunchKernelGGL((bwd_rev_sweep_kernel<In, LPC>), grid, dim3(256), 0, stream, p, lay);
   return hipGetLastError();
 }
 
@@ -872,19 +1105,19 @@ namespace {
 hipError_t launch_bwd_one(const BwdParams& p, const BwdLayout& lay, bool bf16,
                           hipStream_t stream) {
   const ScanParams& F = p.fwd;
-  // 1. forward, saving the state entering every chunk (segmented like the
-  //    backward when it is)
-  ScanParams fs = F;
-  fs.y = nullptr;
-  fs.last_state = nullptr;
-  fs.chunk_states = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.chunk_states_off);
+  // 1. the forward's segment carry-ins (time split only): aggregates of the
+  //    segments, then their combine scan
+  hipError_t e = hipSuccess;
   if (lay.nseg > 1) {
+    ScanParams fs = F;
+    fs.y = nullptr;
+    fs.last_state = nullptr;
     fs.seg_len = lay.seg_len;
     fs.seg_agg = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.fwd_agg_off);
+    e = launch_selective_scan_carries(fs, bf16, stream);
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_selective_scan_save(fs, bf16, stream);
-  if (e != hipSuccess) return e;
-  // 2. reverse pass
+  // 2. forward sweep, adjoint carry-ins (time split only), reverse sweep
   e = bf16 ? launch_bwd_typed<uint16_t>(p, lay, stream) : launch_bwd_typed<float>(p, lay, stream);
   if (e != hipSuccess) return e;
   // 3. partial sums

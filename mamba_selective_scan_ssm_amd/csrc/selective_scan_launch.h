@@ -22,8 +22,6 @@ struct ScanParams {
   void* y;
   float* last_state;        // nullable
   const float* h0;          // initial state [batch, dim, dstate], nullable (zero)
-  float* chunk_states;      // nullable: the state entering every time chunk,
-                            // [batch, dim, nchunks, dstate] (backward pass)
   int batch;
   int dim;
   int dstate;
@@ -99,9 +97,11 @@ hipError_t scan_scratch_address(void** out);
 hipError_t launch_segment_carry(float* slots, int nslots, int64_t npairs, const float* init,
                                 bool reverse, hipStream_t stream);
 
-// Forward pass that saves the state entering every 16-step chunk into
-// p.chunk_states (dstate <= 16; y and last_state may be null).
-hipError_t launch_selective_scan_save(const ScanParams& p, bool bf16, hipStream_t stream);
+// Carry-ins of the time segments of p (p.seg_len > 0, a multiple of 64;
+// dstate <= 16): the aggregate pass over every segment but the last, then
+// segment_carry_kernel; slot s of p.seg_agg then holds the state entering
+// segment s + 1.
+hipError_t launch_selective_scan_carries(const ScanParams& p, bool bf16, hipStream_t stream);
 
 // Backward pass (selective_scan_bwd.hip).
 struct BwdParams {
