@@ -97,6 +97,11 @@ struct SsdArgs {
   uint16_t* states;
   float* decay;
   int dt_softplus;
+  // nheads counts the heads the kernels see; with hshift = 1 a head of 128
+  // channels runs as two heads of 64 (x, y and the states are the same
+  // bytes), whose dt, A, D and dt_bias are those of head >> hshift of the
+  // dt_heads real heads.
+  int hshift, dt_heads;
   int batch, seqlen, nheads, headdim, dstate, ngroups, chunk, nchunks;
   int heads_per_wg_state, heads_per_wg_out;
   int out_halves;   // output workgroups per (chunk, batch, head group): 1 or 2
@@ -184,10 +189,11 @@ __device__ __forceinline__ void load_group_dt(const SsdArgs& a, int b, int c, in
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int hh = min(NGRP * r + grp, nh - 1);  // the consumer skips hh >= nh
-    g.dt[r] = a.dt[((int64_t)b * a.seqlen + load_pos(pos, a.seqlen)) * a.nheads + h0 + hh];
-    g.A[r] = a.A[h0 + hh];
-    g.bias[r] = a.dt_bias ? a.dt_bias[h0 + hh] : 0.0f;
-    g.D[r] = a.D ? a.D[h0 + hh] : 0.0f;
+    const int hr = (h0 + hh) >> a.hshift;        // the real head
+    g.dt[r] = a.dt[((int64_t)b * a.seqlen + load_pos(pos, a.seqlen)) * a.dt_heads + hr];
+    g.A[r] = a.A[hr];
+    g.bias[r] = a.dt_bias ? a.dt_bias[hr] : 0.0f;
+    g.D[r] = a.D ? a.D[hr] : 0.0f;
   }
 }
 
@@ -446,15 +452,15 @@ __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
 // adding up chunk after chunk.
 __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
   constexpr int RING = 8;
-  const int bh = blockIdx.y;
-  const int b = bh / a.nheads, h = bh % a.nheads;
+  const int64_t bh = blockIdx.x;
+  const int b = (int)(bh / a.nheads), h = (int)(bh % a.nheads);
   const int64_t PN = (int64_t)a.headdim * a.dstate;
-  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t e0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
   if (e0 >= PN) return;
   // the state entering the sequence: the given initial state, else zero
   float S[8];
   if (a.init) {
-    const float4* s0 = reinterpret_cast<const float4*>(a.init + (int64_t)bh * PN + e0);
+    const float4* s0 = reinterpret_cast<const float4*>(a.init + bh * PN + e0);
     const float4 lo = s0[0], hi = s0[1];
     S[0] = lo.x; S[1] = lo.y; S[2] = lo.z; S[3] = lo.w;
     S[4] = hi.x; S[5] = hi.y; S[6] = hi.z; S[7] = hi.w;
@@ -465,7 +471,7 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
   const int nc = a.nchunks;
   const int64_t cstride = (int64_t)a.nheads * PN;  // elements between chunks
   uint16_t* base = a.states + ((int64_t)b * nc * a.nheads + h) * PN + e0;
-  const float* dec = a.decay + (int64_t)bh * nc;
+  const float* dec = a.decay + bh * nc;
   uint4 raw[RING];
   float dv[RING];
 #pragma unroll
@@ -501,7 +507,7 @@ __global__ void __launch_bounds__(256) ssd_state_pass_kernel(SsdArgs a) {
     }
   }
   if (a.final_state) {
-    float4* f = reinterpret_cast<float4*>(a.final_state + (int64_t)bh * PN + e0);
+    float4* f = reinterpret_cast<float4*>(a.final_state + bh * PN + e0);
     f[0] = make_float4(S[0], S[1], S[2], S[3]);
     f[1] = make_float4(S[4], S[5], S[6], S[7]);
   }
@@ -960,6 +966,8 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.states = reinterpret_cast<uint16_t*>(static_cast<char*>(p.workspace) + lay.states_off);
   a.decay = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + lay.decay_off);
   a.dt_softplus = p.dt_softplus;
+  a.hshift = p.hshift;
+  a.dt_heads = s.nheads >> p.hshift;
   a.batch = s.batch; a.seqlen = s.seqlen; a.nheads = s.nheads; a.headdim = s.headdim;
   a.dstate = s.dstate; a.ngroups = s.ngroups; a.chunk = s.chunk; a.nchunks = s.nchunks;
   const int hpg = s.nheads / s.ngroups;
@@ -973,7 +981,7 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.out_halves = (kOut4 && s.chunk / 32 > 4) ? 2 : 1;
 
   // state block: B[chunk][NB] and one head's x[chunk][P] share the LDS
-  constexpr int NB = (P == 128 && N >= 128) ? 64 : (N > 128 ? 128 : N);
+  constexpr int NB = N > 128 ? 128 : N;
   dim3 g1(s.nchunks, s.batch, (s.nheads + a.heads_per_wg_state - 1) / a.heads_per_wg_state);
   if (s.chunk == 64)
     hipLaunchKernelGGL((ssd_chunk_state_kernel<P, NB, 64>), g1, dim3(1024), 0, stream, a);
@@ -984,7 +992,7 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t PN = (int64_t)P * N;
-  dim3 g2((unsigned)((PN / 8 + 255) / 256), (unsigned)(s.batch * s.nheads));
+  dim3 g2((unsigned)(s.batch * s.nheads), (unsigned)((PN / 8 + 255) / 256));
   hipLaunchKernelGGL(ssd_state_pass_kernel, g2, dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1006,45 +1014,98 @@ hipError_t launch_p(const SsdParams& p, hipStream_t stream) {
     case 32: return launch_pn<P, 32>(p, stream);
     case 64: return launch_pn<P, 64>(p, stream);
     case 128: return launch_pn<P, 128>(p, stream);
-    case 256: return launch_pn<P, 256>(p, stream);
+    case 256:
+      if constexpr (P == 32) return launch_pn<32, 256>(p, stream);
+      break;
   }
   return hipErrorInvalidValue;
 }
 
 // Copy with zero padding or cropping between [outer][ms][ks] (source) and
 // [outer][md][kd] (destination): dst[o][m][k] = src[o][m][k] where m < ms
-// and k < ks, else 0.  One thread per destination element.
+// and k < ks, else 0.  One thread per 8 consecutive destination elements of
+// a row; when kd is a multiple of 8 (e.g. a tile size) they are written as
+// one 16- or 32-byte store, else one by one.
 template <typename T>
 __global__ void __launch_bounds__(256) ssd_repack_kernel(const T* __restrict__ src,
-                                                       T* __restrict__ dst, int64_t total,
+                                                       T* __restrict__ dst, int64_t groups,
                                                        int ms, int ks, int md, int kd) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const int k = (int)(i % kd);
-  const int64_t r = i / kd;
+  if (i >= groups) return;
+  const int gpr = (kd + 7) / 8;            // groups per destination row
+  const int64_t r = i / gpr;               // destination row: o * md + m
+  const int k0 = (int)(i - r * gpr) * 8;
   const int m = (int)(r % md);
   const int64_t o = r / md;
-  T v = T(0);
-  if (m < ms && k < ks) v = src[(o * ms + m) * ks + k];
-  dst[i] = v;
+  T v[8];
+  const T* s = src + (o * ms + m) * ks;
+  if (ks % 8 == 0 && m < ms && k0 + 8 <= ks) {  // whole, aligned source run
+    if constexpr (sizeof(T) == 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(s + k0);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = (T)(ww[j] & 0xffffu);
+        v[2 * j + 1] = (T)(ww[j] >> 16);
+      }
+    } else {
+      const float4 lo = reinterpret_cast<const float4*>(s + k0)[0];
+      const float4 hi = reinterpret_cast<const float4*>(s + k0)[1];
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (m < ms && k0 + j < ks) ? s[k0 + j] : T(0);
+  }
+  T* d = dst + r * kd + k0;
+  if (kd % 8 != 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < kd) d[j] = v[j];
+    return;
+  }
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)v[2 * j] | ((uint32_t)v[2 * j + 1] << 16);
+    *reinterpret_cast<uint4*>(d) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    reinterpret_cast<float4*>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
 }
 
 template <typename T>
 hipError_t repack(const void* src, void* dst, int64_t outer, int ms, int ks, int md, int kd,
                   hipStream_t stream) {
-  const int64_t total = outer * md * kd;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(ssd_repack_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, static_cast<const T*>(src), static_cast<T*>(dst), total, ms, ks, md,
+  const int64_t groups = outer * md * ((kd + 7) / 8);
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(ssd_repack_kernel<T>, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const T*>(src), static_cast<T*>(dst), groups, ms, ks, md,
                      kd);
   return hipGetLastError();
 }
 
 hipError_t launch_tiles(const SsdParams& p, hipStream_t stream) {
-  switch (p.shape.headdim) {
-    case 32: return launch_p<32>(p, stream);
-    case 64: return launch_p<64>(p, stream);
-    case 128: return launch_p<128>(p, stream);
+  // Heads wider than the kernels' tile run as 2 or 4 narrower heads: every
+  // channel's recurrence is separate, and x, y, the chunk states and the
+  // initial and final states of head h, channels vp j .. vp j + vp - 1, are
+  // the bytes of head (P / vp) h + j of the vp-channel layout.  The narrower
+  // tiles keep the output kernel within its registers (the 128-channel
+  // tiles, and 64 channels with 256 states, needed more than 256 VGPRs).
+  const int vp = ssd_tile_headdim(p.shape.headdim, p.shape.dstate);
+  SsdParams q = p;
+  while (q.shape.headdim > vp) {
+    q.shape.nheads *= 2;
+    q.shape.headdim /= 2;
+    q.hshift += 1;
+  }
+  q.shape.kheaddim = q.shape.headdim;
+  switch (q.shape.headdim) {
+    case 32: return launch_p<32>(q, stream);
+    case 64: return launch_p<64>(q, stream);
   }
   return hipErrorInvalidValue;
 }

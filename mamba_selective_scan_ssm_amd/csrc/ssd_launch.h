@@ -37,6 +37,7 @@ struct SsdParams {
   const float* initial_state;  // [b, h, P, N], nullable (zero)
   void* workspace;
   SsdShape shape;
+  int hshift = 0;        // internal: set when 128-channel heads run as pairs of 64
 };
 
 // Workspace layout (256-byte aligned sections), with P' = kheaddim and
@@ -44,7 +45,8 @@ struct SsdParams {
 //   states [batch, nchunks, nheads, P', N'] bf16: each chunk's local state
 //          (chunk-state kernel), then, in place, the state entering that
 //          chunk (state-pass kernel)
-//   decay  [batch, nheads, nchunks] float32: exp(sum of A*dt over the chunk)
+//   decay  [batch, nheads', nchunks] float32: exp(sum of A*dt over the chunk),
+//          nheads' = nheads P' / ssd_tile_headdim(P', N') (heads the kernels see)
 // and only for padded shapes:
 //   x', y' [batch, seqlen, nheads, P'] bf16;  B', C' [batch, seqlen, ngroups, N'] bf16
 //   init', final' [batch, nheads, P', N'] float32
@@ -54,12 +56,18 @@ struct SsdLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Channels per head of the kernels' tiles for a (padded) head of P channels
+// and N states: 32 with 256 states, else up to 64; wider heads run as
+// P / tile heads of the tile's width.
+inline int ssd_tile_headdim(int P, int N) { return N > 128 ? 32 : (P < 64 ? P : 64); }
+
 inline SsdLayout ssd_layout(const SsdShape& s) {
   SsdLayout l;
   const size_t P = s.kheaddim, N = s.kdstate;
   l.states_off = 0;
   l.decay_off = align256((size_t)s.batch * s.nchunks * s.nheads * P * N * 2);
-  size_t end = align256(l.decay_off + (size_t)s.batch * s.nheads * s.nchunks * sizeof(float));
+  const size_t hk = (size_t)s.nheads * (P / ssd_tile_headdim((int)P, (int)N));
+  size_t end = align256(l.decay_off + (size_t)s.batch * hk * s.nchunks * sizeof(float));
   l.x_off = l.y_off = l.b_off = l.c_off = l.init_off = l.final_off = 0;
   if (s.padded()) {
     const size_t rows_x = (size_t)s.batch * s.seqlen * s.nheads;

@@ -150,9 +150,14 @@ def test_ssd_repeatable(lib):
 
 
 @pytest.mark.parametrize("case", [(2, 300, 4, 64, 64, 2, 128), (1, 512, 6, 64, 128, 1, 256),
-                                  (2, 200, 2, 32, 32, 1, 64)])
+                                  (2, 200, 2, 32, 32, 1, 64),
+                                  (1, 300, 3, 128, 128, 1, 128),  # heads run as two of 64
+                                  (2, 260, 2, 128, 256, 2, 256),  # ... as four of 32
+                                  (1, 200, 2, 64, 256, 1, 64)])   # ... as two of 32
 def test_ssd_initial_state(lib, case):
-    """S starts at a given state; every y and final_state entry."""
+    """S starts at a given state; every y and final_state entry.  Heads wider
+    than the kernels' tiles are split into narrower heads, the initial and
+    final states included."""
     b, L, h, p, n, g, q = case
     print(f"case ssd initial state {case}", flush=True)
     s = synth.ssd_inputs(synth.SSD_CONFIGS["ssd"], seed=80 + L, batch=b, seqlen=L, nheads=h,
