@@ -655,21 +655,22 @@ __device__ __forceinline__ void scan_step(float (&a)[K], float (&v)[K]) {
   }
 }
 
-// Inclusive scans of K independent sequences of (a, v) pairs, each over the
-// 64 lanes of the wave, lane order = sequence order ([EXPLAINED] eqs.
-// (10)-(12) and the doubling prefix-sum figure): four doubling steps inside
-// each 16-lane row (DPP row_shr by 1, 2, 4, 8), then the totals of rows 0
-// and 2 are combined into rows 1 and 3 (row_bcast:15) and the total of rows
-// 0-1 into rows 2-3 (row_bcast:31).  The K scans are interleaved so that
-// their dependent chains overlap.
-template <int K>
+// Inclusive scans of K independent sequences of (a, v) pairs, each over
+// 16 RPP consecutive lanes (RPP = 1, 2 or 4 16-lane rows), lane order =
+// sequence order ([EXPLAINED] eqs. (10)-(12) and the doubling prefix-sum
+// figure): four doubling steps inside each 16-lane row (DPP row_shr by 1,
+// 2, 4, 8); for RPP >= 2 the totals of rows 0 and 2 are combined into rows
+// 1 and 3 (row_bcast:15), and for RPP = 4 the total of rows 0-1 into rows
+// 2-3 (row_bcast:31).  So a wave holds 4 / RPP sequences side by side, and
+// the K scans are interleaved so that their dependent chains overlap.
+template <int RPP, int K>
 __device__ __forceinline__ void wave_inclusive_scan(float (&a)[K], float (&v)[K]) {
   scan_step<0x111, 0xF>(a, v);
   scan_step<0x112, 0xF>(a, v);
   scan_step<0x114, 0xF>(a, v);
   scan_step<0x118, 0xF>(a, v);
-  scan_step<0x142, 0xA>(a, v);
-  scan_step<0x143, 0xC>(a, v);
+  if constexpr (RPP >= 2) scan_step<0x142, 0xA>(a, v);
+  if constexpr (RPP == 4) scan_step<0x143, 0xC>(a, v);
 }
 
 // Carry-ins of the time segments from their aggregates.  slots[s][pair]
@@ -682,18 +683,23 @@ __device__ __forceinline__ void wave_inclusive_scan(float (&a)[K], float (&v)[K]
 //   REV = true (adjoint, scanned from the right): slot s holds the
 //     aggregate of segment s + 1 and gets the adjoint entering segment s
 //     from the right = init (+) agg_{nslots} (+) ... (+) agg_{s+1}.
-// A workgroup takes 16 pairs: it stages their slots in LDS with loads of
-// 128 contiguous bytes per segment (all issued before any is used), each
-// wave scans 4 pairs at once with lane = segment, and the carries go back
+// With nslots <= 16 RPP, a pair's slots take 16 RPP lanes (lane = slot), so
+// one wave scan covers 4 / RPP pairs, and a workgroup takes PB = 16 pairs
+// per wave scan width (16, 32 or 64 pairs): it stages their slots in LDS
+// with loads of PB * 8 contiguous bytes per segment (all issued before any
+// is used), each wave runs 4 interleaved scans, and the carries go back
 // with stores of the same shape.  (Small workgroups: the pass is a few
-// microseconds of latency, and more workgroups overlap more of it; 64 pairs
-// per workgroup took 6.4 us at batch 1, dim 256, 64 segments, 16 pairs 4.7.)
-template <bool REV>
+// microseconds of latency, and more workgroups overlap more of it.)
+template <bool REV, int RPP>
 __global__ void __launch_bounds__(256) segment_carry_kernel(float2* __restrict__ slots, int nslots,
                                                           int64_t npairs,
                                                           const float* __restrict__ init) {
-  constexpr int PB = 16, PER = 64 * PB / 256, ILP = PB / 4;
-  __shared__ float2 tile[64][PB + 1];
+  constexpr int SL = 16 * RPP;         // lanes (slots) per pair
+  constexpr int PPS = 4 / RPP;         // pairs per wave scan
+  constexpr int ILP = 4;               // interleaved scans per wave
+  constexpr int PB = 4 * PPS * ILP;    // pairs per workgroup
+  constexpr int PER = SL * PB / 256;   // staged entries per thread
+  __shared__ float2 tile[SL][PB + 1];
   __shared__ float sInit[PB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -706,32 +712,30 @@ __global__ void __launch_bounds__(256) segment_carry_kernel(float2* __restrict__
     const int s = min(e / PB, nslots - 1), p = min(e % PB, np - 1);
     ld[i] = slots[(int64_t)s * npairs + p0 + p];
   }
-  const float h0 = init ? init[p0 + min(tid & (PB - 1), np - 1)] : 0.0f;
-  if (tid < PB) sInit[tid] = h0;
+  if (tid < PB) sInit[tid] = init ? init[p0 + min(tid, np - 1)] : 0.0f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = tid + 256 * i;
     if (e / PB < nslots) tile[e / PB][e % PB] = ld[i];
   }
   __syncthreads();
-  const int s = REV ? nslots - 1 - lane : lane;  // this lane's slot
-  const bool on = lane < nslots;
+  const int sub = lane / SL;                      // pair of the scan this lane is in
+  const int sl = lane % SL;
+  const int s = REV ? nslots - 1 - sl : sl;       // this lane's slot
+  const bool on = sl < nslots;
+  float a[ILP], v[ILP];
 #pragma unroll
-  for (int r = 0; r < PB / 4; r += ILP) {
-    float a[ILP], v[ILP];
+  for (int k = 0; k < ILP; ++k) {
+    const int p = (wv * ILP + k) * PPS + sub;     // pairs past np compute on stale entries, unused
+    const float2 g = tile[on ? s : 0][p];
+    a[k] = on ? g.x : 1.0f;
+    v[k] = on ? g.y : 0.0f;
+  }
+  wave_inclusive_scan<RPP>(a, v);
 #pragma unroll
-    for (int k = 0; k < ILP; ++k) {
-      const int p = wv + 4 * (r + k);  // pairs past np compute on stale tile entries, unused
-      const float2 g = tile[on ? s : 0][p];
-      a[k] = on ? g.x : 1.0f;
-      v[k] = on ? g.y : 0.0f;
-    }
-    wave_inclusive_scan(a, v);
-#pragma unroll
-    for (int k = 0; k < ILP; ++k) {
-      const int p = wv + 4 * (r + k);
-      if (on && p < np) tile[s][p].y = __builtin_fmaf(a[k], sInit[p], v[k]);
-    }
+  for (int k = 0; k < ILP; ++k) {
+    const int p = (wv * ILP + k) * PPS + sub;
+    if (on && p < np) tile[s][p].y = __builtin_fmaf(a[k], sInit[p], v[k]);
   }
   __syncthreads();
   for (int e = tid; e < nslots * PB; e += 256) {
@@ -1064,17 +1068,28 @@ hipError_t launch_rows_tier(const ScanParams& p, hipStream_t s, int nz) {
   return launch_rows<In, 16, 4, 32, false, AGG>(p, s, nz);
 }
 
+template <bool REV, int RPP>
+void launch_carry_rpp(float2* slots, int nslots, int64_t npairs, const float* init,
+                      hipStream_t stream) {
+  constexpr int PB = 64 / RPP;  // pairs per workgroup (as in the kernel)
+  hipLaunchKernelGGL((segment_carry_kernel<REV, RPP>), dim3((unsigned)((npairs + PB - 1) / PB)),
+                     dim3(256), 0, stream, slots, nslots, npairs, init);
+}
+
+template <bool REV>
+void launch_carry(float2* slots, int nslots, int64_t npairs, const float* init,
+                  hipStream_t stream) {
+  if (nslots <= 16) launch_carry_rpp<REV, 1>(slots, nslots, npairs, init, stream);
+  else if (nslots <= 32) launch_carry_rpp<REV, 2>(slots, nslots, npairs, init, stream);
+  else launch_carry_rpp<REV, 4>(slots, nslots, npairs, init, stream);
+}
+
 hipError_t launch_segment_carry(float* slots, int nslots, int64_t npairs, const float* init,
                                 bool reverse, hipStream_t stream) {
   if (nslots < 1 || nslots > 64) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((npairs + 15) / 16));  // 16 pairs per workgroup
   float2* s2 = reinterpret_cast<float2*>(slots);
-  if (reverse)
-    hipLaunchKernelGGL(segment_carry_kernel<true>, grid, dim3(256), 0, stream, s2, nslots, npairs,
-                       init);
-  else
-    hipLaunchKernelGGL(segment_carry_kernel<false>, grid, dim3(256), 0, stream, s2, nslots,
-                       npairs, init);
+  if (reverse) launch_carry<true>(s2, nslots, npairs, init, stream);
+  else launch_carry<false>(s2, nslots, npairs, init, stream);
   return hipGetLastError();
 }
 

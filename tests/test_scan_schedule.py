@@ -36,13 +36,14 @@ def dpp_step(vals, src_of, rows_enabled):
     return out
 
 
-def wave_scan(vals):
+def wave_scan(vals, rpp=4):
+    """rpp: 16-lane rows per sequence (1, 2 or 4), 4 // rpp sequences side by side."""
     for off in (1, 2, 4, 8):                  # row_shr:off, all rows
         vals = dpp_step(vals, lambda i, o=off: i - o if (i % 16) >= o else None, {0, 1, 2, 3})
-    # row_bcast:15 -> rows 1 and 3 read lane 15 of the row before
-    vals = dpp_step(vals, lambda i: (i // 16) * 16 - 1, {1, 3})
-    # row_bcast:31 -> rows 2 and 3 read lane 31
-    vals = dpp_step(vals, lambda i: 31, {2, 3})
+    if rpp >= 2:  # row_bcast:15 -> rows 1 and 3 read lane 15 of the row before
+        vals = dpp_step(vals, lambda i: (i // 16) * 16 - 1, {1, 3})
+    if rpp == 4:  # row_bcast:31 -> rows 2 and 3 read lane 31
+        vals = dpp_step(vals, lambda i: 31, {2, 3})
     return vals
 
 
@@ -77,3 +78,25 @@ def test_carry_from_initial_state_reversed_order():
             lam = a * lam + v
         a, v = got[j]
         assert a * init + v == lam
+
+
+@pytest.mark.parametrize("rpp,active", [(1, 1), (1, 5), (1, 15), (1, 16),
+                                         (2, 1), (2, 16), (2, 17), (2, 31), (2, 32)])
+def test_side_by_side_sequences(rpp, active):
+    """Shorter sequences (at most 16 or 32 segments) packed 4 or 2 to a wave:
+    each sequence's lanes get its own sequential prefix, untouched by its
+    neighbours."""
+    width = 16 * rpp
+    rng = random.Random(100 * rpp + active)
+    seqs = [[(Fraction(rng.randint(1, 9), rng.randint(1, 9)),
+              Fraction(rng.randint(-9, 9), rng.randint(1, 9))) for _ in range(active)]
+            for _ in range(4 // rpp)]
+    lanes = []
+    for sq in seqs:
+        lanes += sq + [IDENT] * (width - active)
+    got = wave_scan(lanes, rpp)
+    for j, sq in enumerate(seqs):
+        acc = IDENT
+        for i in range(active):
+            acc = combine(acc, sq[i])
+            assert got[j * width + i] == acc, (j, i)
