@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
   constexpr int RPB = 4 * RPW;       // rows per workgroup
   constexpr int TS = T / LPC;        // steps whose per-step work one lane owns
   constexpr int EPU = Elem<In>::kPer16B;
-  static_assert(T % EPU == 0 && T % kBwdT == 0, "chunk must hold whole 16-byte units");
+  static_assert(T % EPU == 0 && (T == kBwdT || T == 2 * kBwdT), "chunk shape");
   constexpr int UPR = T / EPU;
   constexpr int UNITS = 2 * NS * UPR;
   constexpr int RB = (UNITS + 255) / 256;
@@ -189,6 +189,17 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
     }
   };
 
+  // The state entering step t0 (a multiple of kBwdT) for the reverse sweep;
+  // steps outside this segment and rows past dim go to the row's spare slot
+  // (index nchunks), which is never read.
+  float hmid[NG];
+#pragma unroll
+  for (int k = 0; k < NG; ++k) hmid[k] = 0.0f;
+  auto save_state = [&](int t0, const float (&hv)[NG]) {
+    const int64_t ci = (row_ok && t0 >= t_begin && t0 < t_end) ? t0 / kBwdT : lay.nchunks;
+    *reinterpret_cast<float4*>(chunk_states + (row * (lay.nchunks + 1) + ci) * NS + slot * NG) =
+        make_float4(hv[0], hv[1], hv[2], hv[3]);
+  };
   const int nch = (t_end - t_begin + T - 1) / T;
   load_chunk(t_begin);
   for (int ch = 0; ch < nch; ++ch) {
@@ -249,13 +260,16 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
         dut = du[t];
         dyt = dyh[t];
       }
-      if constexpr (t % kBwdT == 0) {  // the state entering this kBwdT-step piece
-        if (row_ok && c0 + t < L) {
-          float* cs = chunk_states + (row * lay.nchunks + (c0 + t) / kBwdT) * N;
+      if constexpr (t == 0) {
+        // the state entering this chunk, and the one entering the second
+        // half of the last chunk (kept in registers: a store in mid-chunk
+        // costs the step loop ~90 VGPRs): 16-byte stores, no branch
+        save_state(c0, h);
+        if constexpr (T > kBwdT) save_state(c0 - T + kBwdT, hmid);
+      }
+      if constexpr (T > kBwdT && t == kBwdT) {
 #pragma unroll
-          for (int k = 0; k < NG; ++k)
-            if (slot * NG + k < N) cs[slot * NG + k] = h[k];
-        }
+        for (int k = 0; k < NG; ++k) hmid[k] = h[k];
       }
       const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG]);
       const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG]);
@@ -339,6 +353,7 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
         part_c[(((int64_t)b * lay.nwg + wg) * N + n) * L + c0 + t] = sc;
     }
   }
+  if constexpr (T > kBwdT) save_state(t_begin + nch * T - T + kBwdT, hmid);  // the last one
   dD_acc = group_sum<LPC>(dD_acc);
   if (row_ok && slot == 0) {
     float* part_d = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_d_off);
@@ -452,9 +467,11 @@ __global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayo
       load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)min(n, N - 1) * L, c0 + sg * EPU, L,
                         rbc[q]);
     }
-#pragma unroll
-    for (int k = 0; k < NG; ++k)
-      hsr[k] = chunk_states[(row * lay.nchunks + ch) * N + min(slot * NG + k, N - 1)];
+    {
+      const float4 v = *reinterpret_cast<const float4*>(
+          chunk_states + (row * (lay.nchunks + 1) + ch) * NS + slot * NG);
+      hsr[0] = v.x; hsr[1] = v.y; hsr[2] = v.z; hsr[3] = v.w;
+    }
   };
 
   const int ch_first = t_begin / T, ch_last = (t_end + T - 1) / T - 1;
@@ -808,11 +825,12 @@ __global__ void __launch_bounds__(256) bwd_lambda_agg_kernel(BwdParams P, BwdLay
   }
 }
 
-// Chunk length of the forward sweep: 16 steps (124 VGPRs at four lanes per
-// row; 32-step chunks need 279, whose state save in mid-chunk splits the
-// step loop).
+// Chunk length of the forward sweep: 32 steps for four lanes per row (193
+// VGPRs; the state entering the second half is stored at the next chunk's
+// start, since a store in mid-chunk cost ~90 more), 16 otherwise (fewer
+// per-step registers per lane).
 template <int LPC>
-constexpr int fwd_sweep_t() { return 16; }
+constexpr int fwd_sweep_t() { return LPC == 4 ? 32 : 16; }
 
 template <typename In, int LPC>
 hipError_t launch_bwd_rows(const BwdParams& p, const BwdLayout& lay, hipStream_t stream) {
@@ -900,7 +918,9 @@ BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, 
   const size_t rows = (size_t)batch * dim;
   const size_t aggs = (size_t)(l.nseg - 1) * rows * dstate * 2 * sizeof(float);
   l.chunk_states_off = 0;
-  l.part_bc_off = align256(rows * l.nchunks * dstate * sizeof(float));
+  // chunk states: [row][nchunks + 1][4 * lanes per row] (a spare slot per
+  // row takes the forward sweep's stores past the end; padded states)
+  l.part_bc_off = align256(rows * (l.nchunks + 1) * 4 * lanes_per_row(dstate) * sizeof(float));
   l.part_a_off = align256(l.part_bc_off +
                           2 * (size_t)batch * l.nwg * dstate * seqlen * sizeof(float));
   l.part_d_off = align256(l.part_a_off + (size_t)l.nseg * rows * dstate * sizeof(float));
