@@ -39,6 +39,12 @@ __device__ __forceinline__ float softplus_short_f(float x) {
   return __builtin_fmaf(fast_log2(1.0f + w), kLn2, relu_bits(x));
 }
 
+// log2(e) softplus(x) from x2 = log2(e) x: max(x2, 0) + log2(fl(1 + 2^{-|x2|}))
+// (the bfloat16 form above in log2 units: the same rounding of 1 + w).
+__device__ __forceinline__ float softplus_log2_short(float x2) {
+  return relu_bits(x2) + fast_log2(1.0f + fast_exp2(-fabsf(x2)));
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z})
 __device__ __forceinline__ float silu_f(float z) {
   return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));

@@ -90,6 +90,13 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   constexpr int UPR = T / EPU;       // 16-byte units per state row of a chunk
   constexpr int UNITS = 2 * NS * UPR;
   constexpr int RBU = (UNITS + 255) / 256;
+  // bfloat16 rows with shared B, C keep delta in log2 units: delta' =
+  // log2(e) delta (the bias add becomes an fma that scales it, softplus
+  // takes its log2 form), so that exp(delta A) = exp2(delta' A) with A as
+  // given, and B is staged as ln(2) B so that delta' u B' = delta u B.  Two
+  // VALU fewer per (b, d, t) than scaling A; float32 rows keep delta and
+  // pre-scale A (the exact form of the float32 parity bound).
+  constexpr bool L2U = sizeof(In) == 2 && !RB;
 
   __shared__ alignas(16) float sB[RB ? 1 : 2][RB ? 1 : T][RB ? 4 : NS];
   __shared__ alignas(16) float sC[RB ? 1 : 2][RB ? 1 : T][RB ? 4 : NS];
@@ -129,10 +136,10 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
   for (int k = 0; k < NG; ++k) {
     const int n = slot * NG + k;
-    A2[k] = (row_ok && n < N) ? prm.A[(int64_t)d * N + n] * kLog2e : 0.0f;
+    A2[k] = (row_ok && n < N) ? prm.A[(int64_t)d * N + n] * (L2U ? 1.0f : kLog2e) : 0.0f;
   }
   const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
-  const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
+  const float bias = ((row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f) * (L2U ? kLog2e : 1.0f);
 
   // State: the initial state v_0 of [EXPLAINED] eqs. (8)-(9) when given
   // (a segment's aggregate starts from the identity instead).
@@ -221,7 +228,7 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
           for (int i = 0; i < EPU; ++i) {
             if (x) sC[buf][seg * EPU + i][n] = v[i];
-            else sB[buf][seg * EPU + i][n] = v[i];
+            else sB[buf][seg * EPU + i][n] = L2U ? v[i] * kLn2 : v[i];
           }
         }
       }
@@ -242,13 +249,23 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
         for (int j = 0; j < TS; ++j) gk[j] = 1.0f;
       }
-      // (the flag is uniform: one branch around the loop, not a select per step)
-      if (prm.delta_softplus) {
+      // (the flag is uniform: one branch around the loop, not a select per
+      // step; delta + bias is formed once, before it, or the compiler forms
+      // it on both sides)
+      if constexpr (L2U) {
 #pragma unroll
-        for (int j = 0; j < TS; ++j) dl[j] = softplus_in<In>(dr[j] + bias);
+        for (int j = 0; j < TS; ++j) dl[j] = __builtin_fmaf(dr[j], kLog2e, bias);
+        if (prm.delta_softplus) {
+#pragma unroll
+          for (int j = 0; j < TS; ++j) dl[j] = softplus_log2_short(dl[j]);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < TS; ++j) dl[j] = dr[j] + bias;
+        if (prm.delta_softplus) {
+#pragma unroll
+          for (int j = 0; j < TS; ++j) dl[j] = softplus_in<In>(dl[j]);
+        }
       }
       // Steps past the end are the identity (delta = 0).  Rows past `dim`
       // compute on zeros and are never stored.
@@ -503,12 +520,11 @@ __global__ void __launch_bounds__(64 * W) selective_scan_slot_kernel(ScanParams 
 #pragma unroll
         for (int j = 0; j < TS; ++j) gk[j] = 1.0f;
       }
+#pragma unroll
+      for (int j = 0; j < TS; ++j) dl[j] = dr[j] + bias;  // (formed once, outside the branch)
       if (prm.delta_softplus) {
 #pragma unroll
-        for (int j = 0; j < TS; ++j) dl[j] = softplus_in<In>(dr[j] + bias);
-      } else {
-#pragma unroll
-        for (int j = 0; j < TS; ++j) dl[j] = dr[j] + bias;
+        for (int j = 0; j < TS; ++j) dl[j] = softplus_in<In>(dl[j]);
       }
       // steps past the end are the identity (delta = 0)
       if (ts + TS > L) {
