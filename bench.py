@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--no-ssd", action="store_true", help="leave out the Mamba-2 chunked scan")
     ap.add_argument("--ssd", action="store_true", help=argparse.SUPPRESS)  # (now the default)
     ap.add_argument("--bwd", action="store_true",
-                    help="also time the backward pass on the same workload")
+                    help="time the backward pass on the same workload also with --no-per-call")
     ap.add_argument("--seq-table", action="store_true",
                     help="also time batch 16, dim 1536, dstate 16, bf16 at seqlen 256..16384")
     ap.add_argument("--grouped", action="store_true",
@@ -344,7 +344,7 @@ def main():
                           for g in (8, d)]
     if args.seq_table:
         out["seq_table"] = bench_seq_table(torch, ssm, synth)
-    if args.bwd:
+    if args.bwd or not args.no_per_call:
         out["bwd"] = bench_bwd(args, torch, ssm, synth, cfg, io, x)
     if not args.no_per_call or args.spec_point:
         out["spec_point"] = bench_spec_point(torch, ssm, synth)
