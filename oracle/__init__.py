@@ -62,6 +62,12 @@ def _load():
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int, _f64p,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
         _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_selective_scan_bwd_grouped_f64.restype = ctypes.c_int
+    lib.oracle_selective_scan_bwd_grouped_f64.argtypes = [
+        _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
+        _f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int64,
+        _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
     lib.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
     lib.oracle_selective_scan_bwd_f64.argtypes = [
         _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int,
@@ -166,18 +172,24 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
     differentiation of the sequential loop, for upstream gradients dy
     [batch, dim, seqlen] and dlast [batch, dim, dstate] (None = zero).
 
+    B, C may be [batch, ngroups, dstate, seqlen] (channel d in group
+    d // (dim // ngroups)); dB, dC then have that shape too.
+
     Returns a dict: du, ddelta, dz (None without z) [batch, dim, seqlen];
-    dA [dim, dstate]; dB, dC [batch, dstate, seqlen]; dD, ddelta_bias [dim];
-    dh0 [batch, dim, dstate].
+    dA [dim, dstate]; dB, dC [batch, dstate, seqlen] (or grouped); dD,
+    ddelta_bias [dim]; dh0 [batch, dim, dstate].
     """
     lib = _load()
     u = _f32(u)
     batch, dim, seqlen = u.shape
     dstate = np.asarray(A).shape[1]
+    grouped = np.ndim(B) == 4
+    ngroups = np.asarray(B).shape[1] if grouped else 1
+    bc_shape = (batch, ngroups, dstate, seqlen) if grouped else (batch, dstate, seqlen)
     delta = _f32(delta, (batch, dim, seqlen))
     A = _f32(A, (dim, dstate))
-    B = _f32(B, (batch, dstate, seqlen))
-    C = _f32(C, (batch, dstate, seqlen))
+    B = _f32(B, bc_shape)
+    C = _f32(C, bc_shape)
     D = _f32(D, (dim,))
     z = _f32(z, (batch, dim, seqlen))
     delta_bias = _f32(delta_bias, (dim,))
@@ -186,13 +198,14 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
     dlast = _f64(dlast, (batch, dim, dstate))
     out = {k: np.empty(shape, np.float64) for k, shape in (
         ("du", (batch, dim, seqlen)), ("ddelta", (batch, dim, seqlen)),
-        ("dA", (dim, dstate)), ("dB", (batch, dstate, seqlen)), ("dC", (batch, dstate, seqlen)),
+        ("dA", (dim, dstate)), ("dB", bc_shape), ("dC", bc_shape),
         ("dD", (dim,)), ("ddelta_bias", (dim,)), ("dh0", (batch, dim, dstate)))}
     out["dz"] = np.empty((batch, dim, seqlen), np.float64) if z is not None else None
     p64 = lambda a: None if a is None else a.ctypes.data_as(_f64p)
-    rc = lib.oracle_selective_scan_bwd_f64(
+    rc = lib.oracle_selective_scan_bwd_grouped_f64(
         _p32(u), _p32(delta), _p32(A), _p32(B), _p32(C), _p32(D), _p32(z), _p32(delta_bias),
         int(bool(delta_softplus)), p64(h0), p64(dy), p64(dlast), batch, dim, dstate, seqlen,
+        ngroups,
         p64(out["du"]), p64(out["ddelta"]), p64(out["dA"]), p64(out["dB"]), p64(out["dC"]),
         p64(out["dD"]), p64(out["dz"]), p64(out["ddelta_bias"]), p64(out["dh0"]),
         int(nthreads or default_threads()))

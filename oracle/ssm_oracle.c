@@ -235,7 +235,7 @@ typedef struct {
   const float *u, *delta, *A, *B, *C, *D, *z, *delta_bias;
   const double *h0, *dy, *dlast;
   int delta_softplus;
-  int64_t batch, dim, dstate, seqlen;
+  int64_t batch, dim, dstate, seqlen, ngroups;
   /* per-row outputs (disjoint between workers) */
   double *du, *ddelta, *dz, *dh0;
   /* this worker's private accumulators for the shared-parameter gradients */
@@ -260,7 +260,9 @@ static void *mamba1_bwd_worker(void *arg) {
     const float *u = j->u + row * L, *dl = j->delta + row * L;
     const float *z = j->z ? j->z + row * L : NULL;
     const float *A = j->A + d * N;
-    const float *B = j->B + b * N * L, *C = j->C + b * N * L;
+    /* channel d reads group g's B and C (and accumulates into its dB, dC) */
+    const int64_t bg = b * j->ngroups + d / (j->dim / j->ngroups);
+    const float *B = j->B + bg * N * L, *C = j->C + bg * N * L;
     const double Dd = j->D ? (double)j->D[d] : 0.0;
     const double bias = j->delta_bias ? (double)j->delta_bias[d] : 0.0;
     const double *dy = j->dy + row * L;
@@ -293,12 +295,12 @@ static void *mamba1_bwd_worker(void *arg) {
       for (int64_t n = 0; n < N; ++n) {
         /* lam currently holds a_{t+1} lam_{t+1} (or dlast); add the readout */
         lam[n] += (double)C[n * L + t] * dyh;
-        j->dC[(b * N + n) * L + t] += dyh * h[n];
+        j->dC[(bg * N + n) * L + t] += dyh * h[n];
         const double a = exp(dt * (double)A[n]);
         const double bt = (double)B[n * L + t];
         ddt += lam[n] * (a * (double)A[n] * hp[n] + bt * ut);
         j->dA[d * N + n] += lam[n] * a * dt * hp[n];
-        j->dB[(b * N + n) * L + t] += lam[n] * dt * ut;
+        j->dB[(bg * N + n) * L + t] += lam[n] * dt * ut;
         du += lam[n] * dt * bt;
         lam[n] *= a; /* now dL/dh_{t-1} */
       }
@@ -315,33 +317,32 @@ static void *mamba1_bwd_worker(void *arg) {
   return NULL;
 }
 
-/* Gradients of oracle_selective_scan_h0_f64's outputs (y, last_state) with
- * upstream gradients dy [batch, dim, seqlen] and dlast [batch, dim, dstate]
- * (nullable = zero).  Outputs (all written, float64): du, ddelta, dz (dz only
- * when z is given, else may be NULL) [batch, dim, seqlen]; dA [dim, dstate];
- * dB, dC [batch, dstate, seqlen]; dD, ddelta_bias [dim]; dh0 [batch, dim,
- * dstate] (nullable).  Shared-parameter gradients are summed per worker and
- * then over workers in a fixed order.  Returns 0, -1 (arguments) or -2. */
-int oracle_selective_scan_bwd_f64(const float *u, const float *delta,
-                                  const float *A, const float *B, const float *C,
-                                  const float *D, const float *z,
-                                  const float *delta_bias, int delta_softplus,
-                                  const double *h0, const double *dy,
-                                  const double *dlast, int64_t batch,
-                                  int64_t dim, int64_t dstate, int64_t seqlen,
-                                  double *du, double *ddelta, double *dA,
-                                  double *dB, double *dC, double *dD,
-                                  double *dz, double *ddelta_bias, double *dh0,
-                                  int nthreads) {
+/* Gradients of oracle_selective_scan_grouped_f64's outputs (y, last_state)
+ * with upstream gradients dy [batch, dim, seqlen] and dlast [batch, dim,
+ * dstate] (nullable = zero).  B, C and dB, dC: [batch, ngroups, dstate,
+ * seqlen], channel d in group d / (dim / ngroups).  Outputs (all written,
+ * float64): du, ddelta, dz (dz only when z is given, else may be NULL)
+ * [batch, dim, seqlen]; dA [dim, dstate]; dB, dC; dD, ddelta_bias [dim];
+ * dh0 [batch, dim, dstate] (nullable).  Shared-parameter gradients are
+ * summed per worker and then over workers in a fixed order.  Returns 0, -1
+ * (arguments) or -2. */
+int oracle_selective_scan_bwd_grouped_f64(
+    const float *u, const float *delta, const float *A, const float *B, const float *C,
+    const float *D, const float *z, const float *delta_bias, int delta_softplus,
+    const double *h0, const double *dy, const double *dlast, int64_t batch, int64_t dim,
+    int64_t dstate, int64_t seqlen, int64_t ngroups, double *du, double *ddelta, double *dA,
+    double *dB, double *dC, double *dD, double *dz, double *ddelta_bias, double *dh0,
+    int nthreads) {
   if (!u || !delta || !A || !B || !C || !dy) return -1;
   if (!du || !ddelta || !dA || !dB || !dC || !dD || !ddelta_bias) return -1;
   if (z && !dz) return -1;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return -1;
+  if (ngroups <= 0 || dim % ngroups != 0) return -1;
   const int64_t rows = batch * dim, N = dstate, L = seqlen;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 64) nthreads = 64;
   if ((int64_t)nthreads > rows) nthreads = (int)rows;
-  const size_t nA = (size_t)(dim * N), nBC = (size_t)(batch * N * L), nd = (size_t)dim;
+  const size_t nA = (size_t)(dim * N), nBC = (size_t)(batch * ngroups * N * L), nd = (size_t)dim;
   const size_t per = nA + 2 * nBC + 2 * nd;
   double *acc = (double *)calloc((size_t)nthreads * per, sizeof(double));
   if (!acc) return -2;
@@ -356,6 +357,7 @@ int oracle_selective_scan_bwd_f64(const float *u, const float *delta,
     j->delta_bias = delta_bias; j->h0 = h0; j->dy = dy; j->dlast = dlast;
     j->delta_softplus = delta_softplus;
     j->batch = batch; j->dim = dim; j->dstate = dstate; j->seqlen = seqlen;
+    j->ngroups = ngroups;
     j->du = du; j->ddelta = ddelta; j->dz = dz; j->dh0 = dh0;
     j->dA = base; j->dB = base + nA; j->dC = base + nA + nBC;
     j->dD = base + nA + 2 * nBC; j->dbias = base + nA + 2 * nBC + nd;
@@ -391,6 +393,24 @@ int oracle_selective_scan_bwd_f64(const float *u, const float *delta,
   }
   free(acc);
   return rc;
+}
+
+/* One group: B, C, dB, dC [batch, dstate, seqlen]. */
+int oracle_selective_scan_bwd_f64(const float *u, const float *delta,
+                                  const float *A, const float *B, const float *C,
+                                  const float *D, const float *z,
+                                  const float *delta_bias, int delta_softplus,
+                                  const double *h0, const double *dy,
+                                  const double *dlast, int64_t batch,
+                                  int64_t dim, int64_t dstate, int64_t seqlen,
+                                  double *du, double *ddelta, double *dA,
+                                  double *dB, double *dC, double *dD,
+                                  double *dz, double *ddelta_bias, double *dh0,
+                                  int nthreads) {
+  return oracle_selective_scan_bwd_grouped_f64(u, delta, A, B, C, D, z, delta_bias,
+                                               delta_softplus, h0, dy, dlast, batch, dim,
+                                               dstate, seqlen, 1, du, ddelta, dA, dB, dC, dD,
+                                               dz, ddelta_bias, dh0, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -95,3 +95,41 @@ def test_backward_threads_do_not_change_results():
     for k in g1:
         if g1[k] is not None:
             np.testing.assert_allclose(g1[k], g4[k], rtol=1e-13, atol=1e-13, err_msg=k)
+
+
+def test_grouped_backward_equals_finite_differences():
+    """B and C per group of channels ([batch, ngroups, dstate, seqlen], channel
+    d in group d // (dim // ngroups)): every gradient, dB and dC per group
+    included, equals a central difference of the oracle's grouped forward."""
+    rng = np.random.default_rng(21)
+    b, d, n, L, g = 2, 4, 3, 10, 2
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    x = dict(u=f(b, d, L), delta=(0.5 * f(b, d, L)).astype(np.float32),
+             A=(-np.abs(f(d, n)) - 0.2).astype(np.float32), B=f(b, g, n, L), C=f(b, g, n, L),
+             D=f(d), z=f(b, d, L), delta_bias=(0.3 * f(d)).astype(np.float32))
+    h0 = rng.standard_normal((b, d, n))
+    dy = rng.standard_normal((b, d, L))
+    dlast = rng.standard_normal((b, d, n))
+    got = oracle.selective_scan_bwd(**x, dy=dy, delta_softplus=True, h0=h0, dlast=dlast,
+                                    nthreads=2)
+    assert got["dB"].shape == (b, g, n, L)
+    for name, gname in [("B", "dB"), ("C", "dC"), ("u", "du"), ("delta", "ddelta"),
+                        ("A", "dA"), ("z", "dz")]:
+        want = fd_grad(x, name, True, h0, dy, dlast)
+        np.testing.assert_allclose(got[gname], want, rtol=2e-5, atol=2e-6, err_msg=gname)
+
+
+def test_per_channel_groups_split_the_one_group_gradient():
+    """With B, C repeated into every group, the per-group dB, dC add up over
+    the groups to the one-group gradient (the groups' channels partition the
+    sum over channels); the other gradients are unchanged."""
+    x = inputs(8, batch=2, dim=6, dstate=3, seqlen=9)
+    rng = np.random.default_rng(3)
+    dy = rng.standard_normal((2, 6, 9))
+    one = oracle.selective_scan_bwd(**x, dy=dy, nthreads=1)
+    xg = dict(x, B=np.repeat(x["B"][:, None], 3, axis=1), C=np.repeat(x["C"][:, None], 3, axis=1))
+    grp = oracle.selective_scan_bwd(**xg, dy=dy, nthreads=3)
+    np.testing.assert_allclose(grp["dB"].sum(axis=1), one["dB"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(grp["dC"].sum(axis=1), one["dC"], rtol=1e-12, atol=1e-12)
+    for k in ("du", "ddelta", "dA", "dD", "dz", "ddelta_bias"):
+        np.testing.assert_allclose(grp[k], one[k], rtol=1e-12, atol=1e-12, err_msg=k)
