@@ -289,6 +289,42 @@ ssm_status ssm_selective_scan_bwd(
     int64_t seqlen, ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * Workspace size of ssm_selective_scan_bwd_grouped (as
+ * ssm_selective_scan_bwd_workspace_size, for ngroups groups of B and C).
+ * Same size and group checks as ssm_selective_scan_bwd_grouped.
+ */
+ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle,
+                                                        int64_t batch, int64_t dim,
+                                                        int64_t dstate, int64_t seqlen,
+                                                        int64_t ngroups, size_t *bytes);
+
+/*
+ * ssm_selective_scan_bwd for B and C given per group of channels, as in
+ * ssm_selective_scan_fwd_grouped ([SPEC] backward-pass stage; channel d
+ * reads group d / (dim / ngroups)):
+ *   B, C   : [batch, ngroups, dstate, seqlen] in_dtype
+ *   dB, dC : [batch, ngroups, dstate, seqlen] float32, each group's
+ *            gradient summed over its channels only
+ *   workspace: ssm_selective_scan_bwd_grouped_workspace_size bytes.
+ * ngroups >= 1 must divide dim (else SSM_ERR_INVALID_ARG), and with
+ * ngroups > 1, dim / ngroups must be a multiple of the channels one
+ * workgroup of the backward kernels handles (64 for dstate 9..64, 128 for
+ * 5..8, 256 for 1..4), else SSM_ERR_UNSUPPORTED (per-channel B and C, for
+ * instance, are not supported by the backward pass).  ngroups = 1 is
+ * ssm_selective_scan_bwd.  Every other argument, layout, limit and error
+ * is as for ssm_selective_scan_bwd.
+ */
+ssm_status ssm_selective_scan_bwd_grouped(
+    ssm_handle handle, const void *u, const void *delta, const float *A,
+    const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, const float *initial_state,
+    const void *dy, const float *dlast_state, void *du, void *ddelta,
+    float *dA, float *dB, float *dC, float *dD, void *dz,
+    float *ddelta_bias, float *dinitial_state, void *workspace,
+    size_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
+    int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream);
+
+/*
  * One decode step of the Mamba-1 recurrence ([SPEC] Stage 1 items 3-4;
  * [EXPLAINED] eqs. (5)-(7); [BLELLOCH] section 1: the sequential form for
  * online inference).  For every row (b, d), with the state updated in place:

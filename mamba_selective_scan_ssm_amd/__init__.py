@@ -30,7 +30,8 @@ EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_selective_scan_fwd_grouped", "ssm_selective_scan_fwd_workspace_size",
            "ssm_selective_scan_fwd_ws", "ssm_selective_scan_fwd_noalloc",
            "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
-           "ssm_selective_scan_bwd",
+           "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_grouped_workspace_size",
+           "ssm_selective_scan_bwd_grouped",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
            "ssd_chunk_scan_fwd_with_state", "ssd_state_update")
 
@@ -106,6 +107,14 @@ def load_library() -> ctypes.CDLL:
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
             _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_scan_bwd_grouped_workspace_size.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd_grouped_workspace_size.argtypes = [
+            _vp, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssm_selective_scan_bwd_grouped.restype = ctypes.c_int
+        lib.ssm_selective_scan_bwd_grouped.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+            _i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_int
         lib.ssd_chunk_scan_workspace_size.argtypes = [
             _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -523,24 +532,54 @@ def ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, handle=Non
     return int(n.value)
 
 
+def ssm_selective_scan_bwd_grouped_workspace_size(batch, dim, dstate, seqlen, ngroups,
+                                                  handle=None, device: int = 0) -> int:
+    if handle is None:
+        handle = get_handle(device)
+    n = ctypes.c_size_t()
+    st = load_library().ssm_selective_scan_bwd_grouped_workspace_size(
+        handle, batch, dim, dstate, seqlen, ngroups, ctypes.byref(n))
+    _check("ssm_selective_scan_bwd_grouped_workspace_size", st)
+    return int(n.value)
+
+
 def ssm_selective_scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
                            dy, dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
                            dinitial_state, workspace, handle=None) -> None:
     """Enqueue the Mamba-1 backward pass (tensor form of the C entry point;
     every gradient and the workspace are caller-allocated)."""
+    _bwd_call("ssm_selective_scan_bwd", False, u, delta, A, B, C, D, z, delta_bias,
+              delta_softplus, initial_state, dy, dlast_state, du, ddelta, dA, dB, dC, dD, dz,
+              ddelta_bias, dinitial_state, workspace, handle)
+
+
+def ssm_selective_scan_bwd_grouped(u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                   initial_state, dy, dlast_state, du, ddelta, dA, dB, dC, dD,
+                                   dz, ddelta_bias, dinitial_state, workspace,
+                                   handle=None) -> None:
+    """The backward pass with B, C (and dB, dC) [batch, ngroups, dstate,
+    seqlen]."""
+    _bwd_call("ssm_selective_scan_bwd_grouped", True, u, delta, A, B, C, D, z, delta_bias,
+              delta_softplus, initial_state, dy, dlast_state, du, ddelta, dA, dB, dC, dD, dz,
+              ddelta_bias, dinitial_state, workspace, handle)
+
+
+def _bwd_call(fn, grouped, u, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state,
+              dy, dlast_state, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state,
+              workspace, handle):
     import torch
-    batch, dim, dstate, seqlen, _ = _mamba1_spec(
-        "ssm_selective_scan_bwd", u, delta, A, B, C, D, z, delta_bias, du, None, initial_state,
-        grouped=False)
-    sp = _Spec("ssm_selective_scan_bwd")
+    batch, dim, dstate, seqlen, ngroups = _mamba1_spec(
+        fn, u, delta, A, B, C, D, z, delta_bias, du, None, initial_state, grouped=grouped)
+    bc_shape = (batch, ngroups, dstate, seqlen) if grouped else (batch, dstate, seqlen)
+    sp = _Spec(fn)
     f32 = torch.float32
     sp.tensor("dy", dy, u.dtype, u.shape)
     sp.tensor("dlast_state", dlast_state, f32, (batch, dim, dstate), optional=True)
     sp.tensor("ddelta", ddelta, u.dtype, u.shape)
     sp.tensor("dz", dz, u.dtype, u.shape, optional=z is None)
     sp.tensor("dA", dA, f32, (dim, dstate))
-    sp.tensor("dB", dB, f32, (batch, dstate, seqlen))
-    sp.tensor("dC", dC, f32, (batch, dstate, seqlen))
+    sp.tensor("dB", dB, f32, bc_shape)
+    sp.tensor("dC", dC, f32, bc_shape)
     sp.tensor("dD", dD, f32, (dim,), optional=True)
     sp.tensor("ddelta_bias", ddelta_bias, f32, (dim,), optional=True)
     sp.tensor("dinitial_state", dinitial_state, f32, (batch, dim, dstate), optional=True)
@@ -555,45 +594,50 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, 
                          ("dinitial_state", dinitial_state, True),
                          ("workspace", workspace, False)):
         _need_cuda_contig(name, t, opt)
-    batch, dim, seqlen = u.shape
-    dstate = A.shape[1]
     dev = u.device.index if u.device.index is not None else 0
     if handle is None:
         handle = get_handle(dev)
-    st = load_library().ssm_selective_scan_bwd(
-        handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(dy),
-        _ptr(dlast_state), _ptr(du), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
-        _ptr(dz), _ptr(ddelta_bias), _ptr(dinitial_state), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), batch, dim, dstate, seqlen,
-        _dtype_code(u), _stream_ptr(u.device))
-    _check("ssm_selective_scan_bwd", st)
+    args = [handle, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state), _ptr(dy),
+            _ptr(dlast_state), _ptr(du), _ptr(ddelta), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
+            _ptr(dz), _ptr(ddelta_bias), _ptr(dinitial_state), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), batch, dim, dstate, seqlen]
+    if grouped:
+        args.append(ngroups)
+    st = getattr(load_library(), fn)(*args, _dtype_code(u), _stream_ptr(u.device))
+    _check(fn, st)
 
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                        delta_softplus=True, initial_state=None, dlast_state=None):
     """Allocating form: returns a dict of gradients (du, ddelta, dz in the
     input dtype; dA, dB, dC, dD, ddelta_bias, dinitial_state float32; the
-    optional ones are None when their input is None)."""
+    optional ones are None when their input is None).  B, C may be
+    [batch, ngroups, dstate, seqlen] (the grouped entry point; dB, dC then
+    have that shape)."""
     import torch
     batch, dim, seqlen = u.shape
     dstate = A.shape[1]
     dev = u.device
+    grouped = B.dim() == 4
+    ngroups = int(B.shape[1]) if grouped else 1
+    bc_shape = (batch, ngroups, dstate, seqlen) if grouped else (batch, dstate, seqlen)
     f32 = dict(dtype=torch.float32, device=dev)
     g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
-         "dA": torch.empty((dim, dstate), **f32), "dB": torch.empty((batch, dstate, seqlen), **f32),
-         "dC": torch.empty((batch, dstate, seqlen), **f32),
+         "dA": torch.empty((dim, dstate), **f32), "dB": torch.empty(bc_shape, **f32),
+         "dC": torch.empty(bc_shape, **f32),
          "dD": torch.empty((dim,), **f32) if D is not None else None,
          "dz": torch.empty_like(u) if z is not None else None,
          "ddelta_bias": torch.empty((dim,), **f32) if delta_bias is not None else None,
          "dinitial_state": (torch.empty((batch, dim, dstate), **f32)
                             if initial_state is not None else None)}
-    nbytes = ssm_selective_scan_bwd_workspace_size(
-        batch, dim, dstate, seqlen, device=dev.index if dev.index is not None else 0)
+    nbytes = ssm_selective_scan_bwd_grouped_workspace_size(
+        batch, dim, dstate, seqlen, ngroups, device=dev.index if dev.index is not None else 0)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    ssm_selective_scan_bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state, dy,
-                           dlast_state, g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"],
-                           g["dz"], g["ddelta_bias"], g["dinitial_state"], ws)
+    call = ssm_selective_scan_bwd_grouped if grouped else ssm_selective_scan_bwd
+    call(u, delta, A, B, C, D, z, delta_bias, delta_softplus, initial_state, dy, dlast_state,
+         g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"], g["ddelta_bias"],
+         g["dinitial_state"], ws)
     return g
 
 
@@ -643,8 +687,9 @@ def _scan_function():
 def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                       initial_state=None, return_last_state=False):
     """Differentiable Mamba-1 selective scan: the forward and backward HIP
-    kernels behind torch.autograd (B, C [batch, dstate, seqlen]; the
-    backward takes dstate <= 64).  Returns y, or (y, last_state)."""
+    kernels behind torch.autograd (B, C [batch, dstate, seqlen] or grouped
+    [batch, ngroups, dstate, seqlen]; the backward takes dstate <= 64 and
+    groups of whole backward workgroups).  Returns y, or (y, last_state)."""
     y, ls = _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, initial_state,
                                    bool(delta_softplus))
     return (y, ls) if return_last_state else y

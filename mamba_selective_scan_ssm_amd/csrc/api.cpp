@@ -365,13 +365,41 @@ ssm_status ssm_selective_scan_fwd_noalloc(ssm_handle handle, const void* u, cons
                              nullptr, 0, in_dtype, stream, /*use_scratch=*/true);
 }
 
+namespace {
+
+// The grouped backward's condition on ngroups (the kernels sum dB, dC of a
+// group over whole workgroups).
+ssm_status check_bwd_groups(int64_t dim, int64_t dstate, int64_t ngroups) {
+  if (ngroups <= 0 || dim % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
+                (long long)ngroups, (long long)dim);
+  const int rpw = ssm::selective_scan_bwd_rows_per_workgroup((int)dstate);
+  if (ngroups > 1 && (dim / ngroups) % rpw != 0)
+    return fail(SSM_ERR_UNSUPPORTED,
+                "backward: dim / ngroups = %lld must be a multiple of %d at dstate %lld",
+                (long long)(dim / ngroups), rpw, (long long)dstate);
+  return SSM_OK;
+}
+
+}  // namespace
+
 ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,
                                                 int64_t dstate, int64_t seqlen, size_t* bytes) {
+  return ssm_selective_scan_bwd_grouped_workspace_size(handle, batch, dim, dstate, seqlen, 1,
+                                                       bytes);
+}
+
+ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle, int64_t batch,
+                                                        int64_t dim, int64_t dstate,
+                                                        int64_t seqlen, int64_t ngroups,
+                                                        size_t* bytes) {
   if (!bytes) return fail(SSM_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = 0;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0)
     return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 64", (long long)dstate);
+  ssm_status gs = check_bwd_groups(dim, dstate, ngroups);
+  if (gs != SSM_OK) return gs;
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
     return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
@@ -379,7 +407,7 @@ ssm_status ssm_selective_scan_bwd_workspace_size(ssm_handle handle, int64_t batc
     return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
   *bytes = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen,
-                                          handle->num_cus).total;
+                                          handle->num_cus, 4, (int)ngroups).total;
   return ok();
 }
 
@@ -392,6 +420,20 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
                                   float* dinitial_state, void* workspace, size_t workspace_bytes,
                                   int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                   ssm_dtype in_dtype, hipStream_t stream) {
+  return ssm_selective_scan_bwd_grouped(handle, u, delta, A, B, C, D, z, delta_bias,
+                                        delta_softplus, initial_state, dy, dlast_state, du,
+                                        ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state,
+                                        workspace, workspace_bytes, batch, dim, dstate, seqlen, 1,
+                                        in_dtype, stream);
+}
+
+ssm_status ssm_selective_scan_bwd_grouped(
+    ssm_handle handle, const void* u, const void* delta, const float* A, const void* B,
+    const void* C, const float* D, const void* z, const float* delta_bias, int delta_softplus,
+    const float* initial_state, const void* dy, const float* dlast_state, void* du,
+    void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+    float* dinitial_state, void* workspace, size_t workspace_bytes, int64_t batch, int64_t dim,
+    int64_t dstate, int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream) {
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
@@ -404,6 +446,8 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
     return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
   if (batch * dim > (int64_t(1) << 62) / seqlen / 64)
     return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
+  ssm_status gs = check_bwd_groups(dim, dstate, ngroups);
+  if (gs != SSM_OK) return gs;
   const struct { const char* name; const void* p; } required[] = {
       {"u", u}, {"delta", delta}, {"A", A}, {"B", B}, {"C", C}, {"dy", dy}, {"du", du},
       {"ddelta", ddelta}, {"dA", dA}, {"dB", dB}, {"dC", dC}, {"workspace", workspace}};
@@ -412,7 +456,7 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   if (z && !dz) return fail(SSM_ERR_INVALID_ARG, "dz is NULL while z is given");
   const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
-  const uint64_t nbc = (uint64_t)batch * dstate * seqlen;
+  const uint64_t nbc = (uint64_t)batch * ngroups * dstate * seqlen;
   const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
   const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
                      {"A", A, (uint64_t)dim * dstate * 4}, {"B", B, nbc * es},
@@ -430,8 +474,8 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   ssm_status st = check_spans(in, 11, out, 10);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
-  const ssm::BwdLayout lay = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate,
-                                                            (int)seqlen, handle->num_cus);
+  const ssm::BwdLayout lay = ssm::selective_scan_bwd_layout(
+      (int)batch, (int)dim, (int)dstate, (int)seqlen, handle->num_cus, 4, (int)ngroups);
   if (workspace_bytes < lay.total)
     return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
                 lay.total);
@@ -442,7 +486,7 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
   f.delta_bias = delta_bias; f.y = nullptr; f.last_state = nullptr; f.h0 = initial_state;
   f.batch = (int)batch; f.dim = (int)dim; f.dstate = (int)dstate; f.seqlen = (int)seqlen;
   f.delta_softplus = delta_softplus ? 1 : 0;
-  f.ngroups = 1;
+  f.ngroups = (int)ngroups;
   p.dy = dy; p.dlast = dlast_state; p.du = du; p.ddelta = ddelta; p.dz = z ? dz : nullptr;
   p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.ddelta_bias = ddelta_bias;
   p.dh0 = dinitial_state; p.workspace = workspace;

@@ -135,7 +135,10 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
   const int64_t rows = (int64_t)F.batch * F.dim;
   const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
   const int64_t row_base = row * (int64_t)L;
-  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  // B, C of the group of the workgroup's rows: [batch, ngroups, dstate, seqlen]
+  // (a group's channels are a whole number of workgroups)
+  const int64_t bc_base = ((int64_t)b * F.ngroups +
+                           (int64_t)(blockIdx.x * RPB) / (F.dim / F.ngroups)) * N * (int64_t)L;
   const int seg = blockIdx.z;
   const int t_begin = lay.nseg > 1 ? seg * lay.seg_len : 0;
   const int t_end = lay.nseg > 1 ? min(L, t_begin + lay.seg_len) : L;
@@ -414,7 +417,10 @@ __global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayo
   const int N = F.dstate;
   const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
   const int64_t row_base = row * (int64_t)L;
-  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  // B, C of the group of the workgroup's rows: [batch, ngroups, dstate, seqlen]
+  // (a group's channels are a whole number of workgroups)
+  const int64_t bc_base = ((int64_t)b * F.ngroups +
+                           (int64_t)(blockIdx.x * RPB) / (F.dim / F.ngroups)) * N * (int64_t)L;
   const int seg = blockIdx.z;
   const int t_begin = lay.nseg > 1 ? seg * lay.seg_len : 0;
   const int t_end = lay.nseg > 1 ? min(L, t_begin + lay.seg_len) : L;
@@ -651,19 +657,22 @@ __global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayo
   }
 }
 
-// dB[b][n][t] = sum over workgroups of the partials (fixed order).
+// dB[b][g][n][t] = sum over the workgroups of group g of the partials
+// (fixed order; a group's channels are a whole number of workgroups).
 __global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(BwdParams P, BwdLayout lay) {
   const ScanParams& F = P.fwd;
   const int64_t per = (int64_t)F.dstate * F.seqlen;
-  const int64_t total = (int64_t)F.batch * per;
+  const int64_t total = (int64_t)F.batch * F.ngroups * per;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
-  const int64_t b = i / per, r = i % per;
+  const int64_t bg = i / per, r = i % per;
+  const int64_t b = bg / F.ngroups, g = bg % F.ngroups;
+  const int wpg = lay.nwg / F.ngroups;  // workgroups per group
   const float* part = reinterpret_cast<const float*>(
       static_cast<const char*>(P.workspace) + lay.part_bc_off);
   const int64_t part_c_off = (int64_t)F.batch * lay.nwg * per;
   float sb = 0.0f, sc = 0.0f;
-  for (int w = 0; w < lay.nwg; ++w) {
+  for (int w = (int)g * wpg; w < (int)(g + 1) * wpg; ++w) {
     const int64_t o = ((int64_t)b * lay.nwg + w) * per + r;
     sb += part[o];
     sc += part[part_c_off + o];
@@ -730,7 +739,10 @@ __global__ void __launch_bounds__(256) bwd_lambda_agg_kernel(BwdParams P, BwdLay
   const int64_t rows = (int64_t)F.batch * F.dim;
   const int64_t row = (int64_t)b * F.dim + (row_ok ? d : 0);
   const int64_t row_base = row * (int64_t)L;
-  const int64_t bc_base = (int64_t)b * N * (int64_t)L;
+  // B, C of the group of the workgroup's rows: [batch, ngroups, dstate, seqlen]
+  // (a group's channels are a whole number of workgroups)
+  const int64_t bc_base = ((int64_t)b * F.ngroups +
+                           (int64_t)(blockIdx.x * RPB) / (F.dim / F.ngroups)) * N * (int64_t)L;
   const int seg = blockIdx.z + 1;
   const int t_begin = seg * lay.seg_len;
   const int t_end = min(L, t_begin + lay.seg_len);
@@ -867,14 +879,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
+int selective_scan_bwd_rows_per_workgroup(int dstate) {
+  return 4 * (64 / lanes_per_row(dstate > 16 ? 16 : dstate));
+}
+
 BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus,
-                                    int in_bytes) {
+                                    int in_bytes, int ngroups) {
   if (dstate > 16) {
     // blocks of 16 states, each run as a 16-state backward pass
-    BwdLayout l = selective_scan_bwd_layout(batch, dim, 16, seqlen, num_cus, in_bytes);
+    BwdLayout l = selective_scan_bwd_layout(batch, dim, 16, seqlen, num_cus, in_bytes, ngroups);
     l.nblocks = (dstate + 15) / 16;
     const size_t rows = (size_t)batch * dim, steps = rows * seqlen;
-    const size_t bc = (size_t)batch * 16 * seqlen;
+    const size_t bc = (size_t)batch * ngroups * 16 * seqlen;
     size_t end = l.total;
     l.acc_off = end;
     l.a_off = end = align256(l.acc_off + 3 * steps * sizeof(float));
@@ -1077,12 +1093,13 @@ hipError_t launch_bwd_blocks(const BwdParams& p, const BwdLayout& lay, bool bf16
     q.acc_du = q.acc_y + 2 * steps;
     q.acc_init = k == 0;
     e = copy_cols(F.A, N, n0, ws + lay.a_off, nk, 0, F.dim, nk, 4, stream);
+    const int64_t bgs = (int64_t)F.batch * F.ngroups;  // (batch, group) rows of B, C
     if (e == hipSuccess)
       e = copy_cols(F.B, (int64_t)N * L, (int64_t)n0 * L, ws + lay.b_off, (int64_t)nk * L, 0,
-                    F.batch, (int64_t)nk * L, es, stream);
+                    bgs, (int64_t)nk * L, es, stream);
     if (e == hipSuccess)
       e = copy_cols(F.C, (int64_t)N * L, (int64_t)n0 * L, ws + lay.c_off, (int64_t)nk * L, 0,
-                    F.batch, (int64_t)nk * L, es, stream);
+                    bgs, (int64_t)nk * L, es, stream);
     if (e == hipSuccess && F.h0)
       e = copy_cols(F.h0, N, n0, ws + lay.h0_off, nk, 0, rows, nk, 4, stream);
     if (e == hipSuccess && p.dlast)
@@ -1091,10 +1108,10 @@ hipError_t launch_bwd_blocks(const BwdParams& p, const BwdLayout& lay, bool bf16
     if (e == hipSuccess) e = copy_cols(ws + lay.da_off, nk, 0, p.dA, N, n0, F.dim, nk, 4, stream);
     if (e == hipSuccess)
       e = copy_cols(ws + lay.db_off, (int64_t)nk * L, 0, p.dB, (int64_t)N * L, (int64_t)n0 * L,
-                    F.batch, (int64_t)nk * L, 4, stream);
+                    bgs, (int64_t)nk * L, 4, stream);
     if (e == hipSuccess)
       e = copy_cols(ws + lay.dc_off, (int64_t)nk * L, 0, p.dC, (int64_t)N * L, (int64_t)n0 * L,
-                    F.batch, (int64_t)nk * L, 4, stream);
+                    bgs, (int64_t)nk * L, 4, stream);
     if (e == hipSuccess && p.dh0)
       e = copy_cols(ws + lay.dh0_off, nk, 0, p.dh0, N, n0, rows, nk, 4, stream);
   }
@@ -1141,7 +1158,7 @@ hipError_t launch_bwd_one(const BwdParams& p, const BwdLayout& lay, bool bf16,
   e = bf16 ? launch_bwd_typed<uint16_t>(p, lay, stream) : launch_bwd_typed<float>(p, lay, stream);
   if (e != hipSuccess) return e;
   // 3. partial sums
-  const int64_t nbc = (int64_t)F.batch * F.dstate * F.seqlen;
+  const int64_t nbc = (int64_t)F.batch * F.ngroups * F.dstate * F.seqlen;
   hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
                      stream, p, lay);
   e = hipGetLastError();

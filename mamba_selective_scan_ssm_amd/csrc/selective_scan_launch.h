@@ -118,6 +118,8 @@ struct BwdParams {
   float* ddelta_bias;       // [dim], nullable
   float* dh0;               // [batch, dim, dstate], nullable
   void* workspace;
+  // fwd.ngroups: B, C, dB, dC are [batch, ngroups, dstate, seqlen]; a group's
+  // channels are a whole number of the kernels' workgroups.
   // State-block mode (set by the driver for dstate > 16, null otherwise):
   // the kernel adds its per-step sums over its states -- readout, d/d delta
   // before the softplus derivative, d/d u without the skip term -- to these
@@ -140,7 +142,7 @@ struct BwdLayout {
   // each a backward pass of its own whose workspace is the layout above (at
   // offset 0, for 16 states); after it: the float32 per-step accumulators
   // acc[3][batch, dim, seqlen], the block's inputs and gradients (A, dA
-  // [dim, 16]; B, C [batch, 16, seqlen] in the input type; dB, dC float32;
+  // [dim, 16]; B, C [batch, ngroups, 16, seqlen] in the input type; dB, dC float32;
   // initial state, dlast, dinitial_state [batch, dim, 16]) and per-row
   // dD, ddelta_bias sums [2][batch, dim].
   int nblocks;
@@ -148,7 +150,11 @@ struct BwdLayout {
 };
 
 BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, int num_cus,
-                                    int in_bytes = 4);
+                                    int in_bytes = 4, int ngroups = 1);
+// Channels per workgroup of the backward kernels for this dstate (64 for
+// dstate 9..64, 128 for 5..8, 256 for 1..4): with ngroups > 1, dim / ngroups
+// must be a multiple of it.
+int selective_scan_bwd_rows_per_workgroup(int dstate);
 hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
                                      hipStream_t stream);
 

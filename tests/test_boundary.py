@@ -260,3 +260,33 @@ def test_noalloc_scratch_bound_covers_every_plan():
                         continue
                     worst = max(worst, (nseg - 1) * batch * dim * dstate * 8)
     assert 0 < worst < limit, worst
+
+
+def bwd_grouped(ngroups, dim=256, dstate=16, handle=None, dB=P[13]):
+    lib = ssm.load_library()
+    st = lib.ssm_selective_scan_bwd_grouped(
+        handle, P[0], P[1], P[2], P[3], P[4], None, None, None, 1, None, P[5], None,
+        P[6], P[7], P[8], dB, P[9], None, None, None, None, P[10], 1 << 20,
+        2, dim, dstate, 8, ngroups, ssm.SSM_F32, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_grouped_backward_rules():
+    """Groups must divide dim, and (the kernels sum a group's dB, dC over
+    whole workgroups) hold a multiple of the backward's channels per
+    workgroup: 64 at dstate 9..64, 128 at 5..8, 256 at 1..4."""
+    for g, dim, n in ((1, 256, 16), (2, 256, 16), (4, 256, 16), (2, 256, 8), (1, 100, 4),
+                      (2, 128, 64)):
+        st, msg = bwd_grouped(g, dim, n)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, (g, dim, n, msg)
+    for g, dim, n in ((3, 256, 16), (0, 256, 16)):
+        st, msg = bwd_grouped(g, dim, n)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "ngroups" in msg, (g, msg)
+    for g, dim, n in ((8, 256, 16), (4, 256, 8), (2, 256, 4), (256, 256, 16)):
+        st, msg = bwd_grouped(g, dim, n)
+        assert st == ssm.SSM_ERR_UNSUPPORTED and "multiple" in msg, (g, dim, n, msg)
+    n = ctypes.c_size_t(1)
+    lib = ssm.load_library()
+    st = lib.ssm_selective_scan_bwd_grouped_workspace_size(None, 2, 256, 16, 8, 8,
+                                                           ctypes.byref(n))
+    assert st == ssm.SSM_ERR_UNSUPPORTED and n.value == 0

@@ -41,10 +41,15 @@ def check(name, got, ref, dtype):
 
 
 def run_case(ssm, seed, b, d, n, L, dtype, gate=True, bias=True, softplus=True, h0=False,
-             dlast=False):
+             dlast=False, groups=0):
     cfg = synth.Mamba1Config("bwd", b, d, n, L, dtype, 0.0, 0.5, delta_bias=bias, gate=gate,
                              use_D=True)
     x = synth.mamba1_inputs(cfg, seed=seed)
+    if groups:  # B, C per group of channels: [b, groups, n, L]
+        grng = np.random.default_rng(seed + 500)
+        for k in ("B", "C"):
+            v = grng.standard_normal((b, groups, n, L)).astype(np.float32)
+            x[k] = synth.round_bf16(v) if dtype == "bf16" else v
     if not softplus:
         # without softplus the raw delta is the step size: keep it positive
         # and small, as a softplus output would be
@@ -181,3 +186,48 @@ def test_autograd_function(lib, dtype):
                         ("D", "dD"), ("z", "dz"), ("delta_bias", "ddelta_bias")):
         check("grad " + name, synth.to_host_f64(t[name].grad), ref[rname], dtype)
     check("grad initial_state", synth.to_host_f64(h0t.grad), ref["dh0"], dtype)
+
+
+GROUPED = [  # (b, d, n, L, dtype, groups, h0, dlast): a group is whole backward workgroups
+    (2, 128, 16, 100, "f32", 2, True, True),     # 64 channels per workgroup
+    (1, 256, 8, 300, "bf16", 2, False, True),     # 128 per workgroup (two lanes per row)
+    (2, 512, 4, 90, "f32", 2, True, False),       # 256 per workgroup (one lane per row)
+    (2, 192, 32, 77, "f32", 3, True, True),       # blocks of 16 states
+    (1, 128, 16, 700, "f32", 2, True, True),      # split in time
+    (1, 256, 48, 600, "bf16", 4, False, True),    # blocks and time split
+]
+
+
+@pytest.mark.parametrize("case", GROUPED)
+def test_grouped_backward_matches_oracle(lib, case):
+    """B, C per group of channels: dB and dC per group, every other gradient
+    as for one group; against the oracle's grouped backward."""
+    b, d, n, L, dtype, groups, h0, dlast = case
+    print(f"case bwd grouped {case}", flush=True)
+    g, ref = run_case(lib, 300 + n, b, d, n, L, dtype, True, True, True, h0, dlast, groups)
+    assert tuple(g["dB"].shape) == (b, groups, n, L)
+    compare(g, ref, dtype, True, True, h0)
+
+
+def test_grouped_backward_through_autograd(lib):
+    """selective_scan_fn with grouped B, C: torch.autograd reaches the grouped
+    backward, and its gradients equal the oracle's."""
+    b, d, n, L, groups = 2, 128, 16, 64, 2
+    print("case bwd grouped autograd", flush=True)
+    cfg = synth.Mamba1Config("bwd", b, d, n, L, "f32", 0.0, 0.5, delta_bias=True, gate=True,
+                             use_D=True)
+    x = synth.mamba1_inputs(cfg, seed=41)
+    rng = np.random.default_rng(42)
+    for k in ("B", "C"):
+        x[k] = rng.standard_normal((b, groups, n, L)).astype(np.float32)
+    dy = rng.standard_normal((b, d, L)).astype(np.float32)
+    t = {k: torch.from_numpy(v).cuda().requires_grad_(True) for k, v in x.items()
+         if v is not None}
+    y = lib.selective_scan_fn(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                              delta_bias=t["delta_bias"])
+    y.backward(torch.from_numpy(dy).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(**x, dy=dy.astype(np.float64))
+    for name, rname in (("u", "du"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"),
+                        ("C", "dC"), ("D", "dD"), ("z", "dz"), ("delta_bias", "ddelta_bias")):
+        check(name, t[name].grad.double().cpu().numpy(), ref[rname], "f32")
