@@ -78,6 +78,18 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Scratch destination of a lane that holds no row sum (lane % 16 < 16 - LPC)
+// when the row sums of its 16-lane row go to `real` (LPC 16-byte units):
+// unit (u + LPC + lane % 16) mod 16 of the 256-byte aligned scratch block,
+// u = the unit of `real` modulo 256 bytes, so that the 16 lanes' stores fall
+// on 16 different bank groups.  (The low 32 bits of a generic LDS address
+// are its LDS offset.)
+template <int LPC>
+__device__ __forceinline__ float* junk_slot(const float* real, float* junk, int lane) {
+  const int u = (int)((uint32_t)reinterpret_cast<uintptr_t>(real) >> 4) & 15;
+  return junk + 4 * ((u + LPC + (lane & 15)) & 15);
+}
+
 // Per-chunk layout shared by the two sweeps: a row's states over a group of
 // LPC lanes (NG = 4 each), its per-step work over their slices of TS = T/LPC
 // steps; B and C of the chunk staged in LDS as float32 [t][n].
@@ -109,7 +121,7 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
   __shared__ alignas(16) float sB[2][T][NS];
   __shared__ alignas(16) float sC[2][T][NS];
   __shared__ alignas(16) float sPC[4][4][kPad];  // [wave][16-lane row][t*NS + n]
-  __shared__ alignas(16) float sJunk[T * NS + 64];
+  __shared__ alignas(256) float sJunk[T * NS + 64];
 
   const ScanParams& F = P.fwd;
   const In* __restrict__ u = static_cast<const In*>(F.u);
@@ -164,9 +176,11 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
   float dD_acc = 0.0f;
   // Where this lane stores its row sums of step t (at + t * NS): the sums sit
   // in the last LPC lanes of each 16-lane row; the other lanes write to a
-  // scratch block that is never read (no branch around the store).
+  // scratch block that is never read (no branch around the store), at the
+  // 16-byte units that the real sums of their 16-lane row leave free modulo
+  // 256 bytes, so the store has no bank conflict.
   float* const pc_base = (lane & 15) >= 16 - LPC ? &sPC[wv][drow][slot * NG]
-                                                 : &sJunk[(lane & 15) * 4];
+                                                 : junk_slot<LPC>(&sPC[wv][drow][0], sJunk, lane);
   float* chunk_states = reinterpret_cast<float*>(static_cast<char*>(P.workspace) +
                                                  lay.chunk_states_off);
   float* part_c = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off) +
@@ -392,7 +406,7 @@ __global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayo
   __shared__ alignas(16) float sB[T][NS];
   __shared__ alignas(16) float sC[T][NS];
   __shared__ alignas(16) float sPB[4][4][kPad];
-  __shared__ alignas(16) float sJunk[T * NS + 64];
+  __shared__ alignas(256) float sJunk[T * NS + 64];
 
   const ScanParams& F = P.fwd;
   const In* __restrict__ u = static_cast<const In*>(F.u);
@@ -450,7 +464,7 @@ __global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayo
   float dbias_acc = 0.0f;
   // row sums of step t at pb_base + t * NS (as in the forward sweep)
   float* const pb_base = (lane & 15) >= 16 - LPC ? &sPB[wv][drow][slot * NG]
-                                                 : &sJunk[(lane & 15) * 4];
+                                                 : junk_slot<LPC>(&sPB[wv][drow][0], sJunk, lane);
   const float* chunk_states = reinterpret_cast<const float*>(
       static_cast<const char*>(P.workspace) + lay.chunk_states_off);
   float* part_b = reinterpret_cast<float*>(static_cast<char*>(P.workspace) + lay.part_bc_off);
