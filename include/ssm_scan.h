@@ -109,8 +109,8 @@ ssm_status ssm_scan_destroy(ssm_handle handle);
  * batch 2, dim 1536), this call splits each time chunk across the waves of
  * one workgroup only (73 us at batch 2, dim 1536, dstate 16, seqlen 2048,
  * float32); ssm_selective_scan_fwd_ws with a workspace also splits the
- * sequence across workgroups (65 us there, and far faster for a single
- * short row block such as batch 1, dim 256: 17 against 68 us).
+ * sequence across workgroups (63 us there, and far faster for a single
+ * short row block such as batch 1, dim 256: 16 against 68 us).
  */
 ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void *u,
                                   const void *delta, const float *A,
