@@ -152,6 +152,7 @@ __device__ __forceinline__ bf16x8 lds_kop(const uint16_t* tile, int stride, int 
 }
 
 constexpr int kHGMax = 8;           // most heads one workgroup handles
+constexpr int kHGState = 6;         // most heads per chunk-state workgroup
 
 template <int I, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -261,18 +262,20 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int nh, const GroupRaw<
 template <int P, int NB, int QT>
 __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
   constexpr int NTHR = 1024, NW = 16;
-  // LDS row strides (bf16): 8 elements of padding per row (16 bytes, so rows
-  // stay 16-byte aligned for the staging stores); small enough that at P = 64,
-  // NB = 128, Q = 256 the x tile is double-buffered within 156 KB (measured:
-  // 27.0 -> 23.0 us per call against 16 elements of padding, single buffer).
-  constexpr int kRowB = NB + 8;
+  // LDS row strides (bf16), in bytes 32 and 16 modulo 128 past the row
+  // (B: NB + 16 elements; x: P + 8): the four rows that a 16-lane group of
+  // the transposing read touches then fall on disjoint bank groups of B and
+  // x; rows stay 16-byte aligned for the staging stores.  With the decay
+  // tables of at most kHGState heads the x tile stays double-buffered within
+  // 156 KB at P = 64, NB = 128, Q = 256.
+  constexpr int kRowB = NB + 16;
   constexpr int kRowX = P + 8;
-  constexpr bool DB = (size_t)QT * (kRowB + 2 * kRowX) * 2 + 2 * kHGMax * kQMax * 4 <= 156 * 1024;
+  constexpr bool DB = (size_t)QT * (kRowB + 2 * kRowX) * 2 + 2 * kHGState * kQMax * 4 <= 156 * 1024;
   constexpr int NBUF = DB ? 2 : 1;
   __shared__ alignas(16) uint16_t sB[QT][kRowB];         // B[s][n] of one state block
   __shared__ alignas(16) uint16_t sX[NBUF][QT][kRowX];   // (w x)[s][p] of one head
-  __shared__ alignas(16) float sCs2[kHGMax][kQMax];
-  __shared__ alignas(16) float sDt[kHGMax][kQMax];
+  __shared__ alignas(16) float sCs2[kHGState][kQMax];
+  __shared__ alignas(16) float sDt[kHGState][kQMax];
   __shared__ float sTmp[16];
   constexpr int NT = NB / 16, PT = P / 16, TILES = NT * PT, TPW = (TILES + NW - 1) / NW;
   constexpr bool kAllTiles = TILES % NW == 0;  // every wave owns TPW tiles
@@ -972,7 +975,7 @@ hipError_t launch_pn(const SsdParams& p, hipStream_t stream) {
   a.dstate = s.dstate; a.ngroups = s.ngroups; a.chunk = s.chunk; a.nchunks = s.nchunks;
   const int hpg = s.nheads / s.ngroups;
   a.heads_per_wg_state =
-      heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256, kHGMax);
+      heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256, kHGState);
   constexpr bool kOut4 = out4_fits<P, N>();
   a.heads_per_wg_out = heads_per_workgroup(hpg, s.nheads, (int64_t)s.nchunks * s.batch, 256,
                                            kOut4 ? kHGSmall : out_heads_max(P, N));
