@@ -27,6 +27,7 @@ is alu_floor: the issue slots the recurrence needs at full VALU rate.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -286,6 +287,12 @@ def main():
                                       io["z"], io["delta_bias"], cfg.softplus, None, y, ls, ws,
                                       handle=handle)
 
+    # The steps are launched from Python: a cyclic garbage collection in the
+    # middle of the timed loop has stalled the launches for tens of
+    # milliseconds (seen in kernel traces as one gap between two launches),
+    # so the collector runs now and stays off for the GPU measurements.
+    gc.collect()
+    gc.disable()
     warm = clock_warmup(torch, step, args.warmup_seconds)
     for _ in range(args.warmup):
         step()
