@@ -122,6 +122,16 @@ def test_edge_shapes(lib, shape, dtype):
     compare_full(lib, x, dtype, label=f"edge {shape} {dtype}")
 
 
+@pytest.mark.parametrize("dtype,split", [("f32", True), ("f32", False), ("bf16", True)])
+def test_very_long_sequence_few_rows(lib, dtype, split):
+    """One batch entry, 8 channels, 2^18 steps: with a workspace the time
+    split at its limit of 64 segments (4096 steps each), without one the
+    time-sliced row kernel over 2048 chunks; every y and last_state entry."""
+    x = make_inputs(78, 1, 8, 16, 1 << 18, dtype)
+    compare_full(lib, x, dtype, label=f"very long (1, 8, 16, 2^18) {dtype} split={split}",
+                 time_split=split)
+
+
 def test_softplus_off_and_nullable_inputs(lib):
     x = make_inputs(21, 2, 40, 16, 100, "f32", gate=False, bias=False, D=False)
     x["delta"] = np.abs(x["delta"]).astype(np.float32)
