@@ -108,6 +108,7 @@ CASES = [  # (b, d, n, L, dtype, gate, bias, softplus, h0, dlast)
     (2, 64, 4, 1000, "bf16", True, True, True, False, True),
     (1, 40, 8, 600, "f32", False, False, True, True, False),
     (1, 70, 16, 2048, "bf16", True, True, True, True, False),
+    (1, 8, 16, 1 << 16, "f32", True, True, True, True, True),   # 2^16 steps, 64 segments
 ]
 
 
