@@ -382,6 +382,191 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   }
 }
 
+// ---- per-row B, C: one state per lane -------------------------------------------
+
+// For B and C read per row (groups of channels smaller than a row-parallel
+// workgroup, e.g. one per channel) with 9..16 states.  B, C are
+// [batch, ngroups, dstate, seqlen]: each (row, state) is its own sequence of
+// seqlen elements, so a lane that holds several states of a row, reading a
+// short piece of each per chunk, touches a 128-byte line four times in four
+// chunks, long after the L2 has dropped it (measured: 4x the algorithmic HBM
+// bytes).  Here a row's 16 states take the 16 lanes of a DPP row, one state
+// per lane, and a chunk is T = 128 bytes of steps (64 bf16, 32 float32), so
+// every lane reads whole lines of its state's B and C, loaded one chunk
+// ahead into registers.  Step t of a chunk belongs to lane t % 16 of the
+// row (its delta, softplus, delta*u, gate, skip term and y); its delta and
+// delta*u reach the row's lanes through a DPP row broadcast folded into the
+// multiplies.  Each lane's partial readout C h of a step goes to LDS; after
+// every 16 steps each lane adds the 16 partials of its step of the block
+// ([EXPLAINED] eq. (7) per state; the readout sum of [SPEC] Stage 1 item 3).
+// Block = 256 threads = 4 waves of 4 rows.
+// LOAD: how B and C of the next chunk are loaded.  Rows a whole number of
+// 16-byte units long: 16-byte loads after the chunk (kChanLoadAfter), or
+// each unit reloaded with the next chunk's as soon as its last step has been
+// used (kChanLoadSpread: the loads spread over the chunk, no second set of
+// registers; float32 3.0 against 4.1 ms at 4096 channels of 2048 steps,
+// bfloat16 1.5 against 1.1 ms, so bfloat16 loads after the chunk).  Other
+// rows: element loads after the chunk (kChanLoadElem).
+constexpr int kChanLoadElem = 0, kChanLoadAfter = 1, kChanLoadSpread = 2;
+template <typename In, int LOAD>
+__global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm) {
+  constexpr bool VEC = LOAD != kChanLoadElem;
+  constexpr int EPU = Elem<In>::kPer16B;
+  constexpr int T = 128 / (int)sizeof(In);  // steps per chunk: one 128-byte line per state
+  constexpr int NB = T / 16;                // 16-step blocks per chunk
+  constexpr int kRowP = 16 * 20 + 16;       // LDS floats per row of partials
+  // partials of step tt of the block from state n at [rw][tt][n], rows of 20
+  // floats and row groups 16 floats apart modulo 64 banks: the stores of a
+  // step (16 consecutive floats per row) and each lane's four 16-byte reads
+  // of its step (16 lanes 80 bytes apart) meet no bank twice
+  __shared__ alignas(16) float sP[4][4 * kRowP];
+
+  const In* __restrict__ u = static_cast<const In*>(prm.u);
+  const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(prm.B);
+  const In* __restrict__ Cm = static_cast<const In*>(prm.C);
+  const In* __restrict__ z = static_cast<const In*>(prm.z);
+  In* __restrict__ y = static_cast<In*>(prm.y);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = lane >> 4;   // row within the wave
+  const int l = lane & 15;    // state n of this lane, and the owner index of steps
+  const int b = blockIdx.y;
+  const int d = blockIdx.x * 16 + wv * 4 + rw;
+  const bool row_ok = d < prm.dim;
+  const int L = prm.seqlen;
+  const int N = prm.dstate;
+  const bool st_ok = row_ok && l < N;
+  const bool has_z = z != nullptr;
+  const int64_t rowi = (int64_t)b * prm.dim + (row_ok ? d : 0);
+  const int64_t row_base = rowi * (int64_t)L;
+  const int rpg = prm.dim / prm.ngroups;
+  const int64_t bc_row = (((int64_t)b * prm.ngroups + (row_ok ? d : 0) / rpg) * N +
+                          (st_ok ? l : 0)) * (int64_t)L;
+
+  const float A2 = st_ok ? prm.A[(int64_t)d * N + l] * kLog2e : 0.0f;
+  const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
+  const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
+  float h = (st_ok && prm.h0) ? prm.h0[rowi * N + l] : 0.0f;
+
+  // B, C of this lane's state for the steps c0 .. c0 + T - 1.  Steps past
+  // the end read the row's last elements instead (finite values that meet
+  // delta = 0 there: the state does not move and their readout is not
+  // stored), so every load is unconditional (lanes of states past dstate
+  // read state 0 and use zeros).
+  RawSeg<In, T> rB, rC;
+  auto load_unit = [&](const In* __restrict__ p, int c0, int k, RawSeg<In, T>& r) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + bc_row + min(c0 + EPU * k, L - EPU));
+    r.w[4 * k] = st_ok ? v.x : 0u;
+    r.w[4 * k + 1] = st_ok ? v.y : 0u;
+    r.w[4 * k + 2] = st_ok ? v.z : 0u;
+    r.w[4 * k + 3] = st_ok ? v.w : 0u;
+  };
+  auto load_line = [&](const In* __restrict__ p, int c0, RawSeg<In, T>& r) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < T / EPU; ++k) load_unit(p, c0, k, r);
+    } else if constexpr (sizeof(In) == 4) {
+#pragma unroll
+      for (int k = 0; k < T; ++k)
+        r.w[k] = reinterpret_cast<const uint32_t*>(p)[bc_row + min(c0 + k, L - 1)];
+    } else {
+#pragma unroll
+      for (int k = 0; k < T / 2; ++k)
+        r.w[k] = (uint32_t)p[bc_row + min(c0 + 2 * k, L - 1)] |
+                 ((uint32_t)p[bc_row + min(c0 + 2 * k + 1, L - 1)] << 16);
+    }
+  };
+  auto load_bc = [&](int c0, RawSeg<In, T>& rb, RawSeg<In, T>& rc) {
+    load_line(Bm, c0, rb);
+    load_line(Cm, c0, rc);
+    if (!VEC && !st_ok) {
+#pragma unroll
+      for (int w = 0; w < RawSeg<In, T>::kWords; ++w) rb.w[w] = rc.w[w] = 0u;
+    }
+  };
+  float* const prow = &sP[wv][rw * kRowP];
+
+  auto to_f32 = [](In v) {
+    if constexpr (sizeof(In) == 4) return (float)v;
+    else return __uint_as_float((uint32_t)v << 16);
+  };
+  // this lane's steps c0 + 16 j + l of u, delta, z, loaded one chunk ahead
+  // (B and C are loaded after their last use in the previous chunk: the
+  // registers of one chunk, not two, leave room for four waves per SIMD)
+  In ru[NB], rd[NB], rz[NB];
+  auto load_own = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int t = min(c0 + 16 * j + l, L - 1);
+      ru[j] = u[row_base + t];
+      rd[j] = dlt[row_base + t];
+      rz[j] = has_z ? z[row_base + t] : In(0);
+    }
+  };
+  const int nchunks = (L + T - 1) / T;
+  load_bc(0, rB, rC);
+  load_own(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * T;
+    // -- this lane's steps c0 + 16 j + l: delta, softplus, delta*u, gate --------
+    float dl[NB], du[NB], uk[NB], gk[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bool in = row_ok && c0 + 16 * j + l < L;
+      uk[j] = in ? to_f32(ru[j]) : 0.0f;
+      const float dr = in ? to_f32(rd[j]) : 0.0f;
+      const float zz = (in && has_z) ? to_f32(rz[j]) : 0.0f;
+      float dd = dr + bias;
+      if (prm.delta_softplus) dd = softplus_in<In>(dd);
+      dl[j] = in ? dd : 0.0f;  // steps past the end are the identity
+      du[j] = dl[j] * uk[j];
+      gk[j] = has_z ? silu_f(zz) : 1.0f;
+    }
+    if (ch + 1 < nchunks) load_own(c0 + T);
+
+    float yo[NB];
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      constexpr int own = t % 16, j = t / 16;
+      const float dt = dpp_f<0x150 + own>(dl[j]);    // row broadcast of lane `own`
+      const float dut = dpp_f<0x150 + own>(du[j]);
+      const float a = fast_exp2(dt * A2);
+      h = __builtin_fmaf(a, h, dut * raw_elem<In, T, t>(rB));
+      prow[own * 20 + l] = raw_elem<In, T, t>(rC) * h;
+      if constexpr (LOAD == kChanLoadSpread && (t + 1) % EPU == 0) {  // unit used up: the next chunk's
+        load_unit(Bm, c0 + T, t / EPU, rB);
+        load_unit(Cm, c0 + T, t / EPU, rC);
+      }
+      if constexpr (own == 15) {
+        // the 16 partials of this lane's step of the block, in a fixed order
+        // (the lanes of a row share a wave, whose LDS accesses complete in
+        // program order: no barrier)
+        __builtin_amdgcn_wave_barrier();
+        const float4 q0 = *reinterpret_cast<const float4*>(prow + l * 20);
+        const float4 q1 = *reinterpret_cast<const float4*>(prow + l * 20 + 4);
+        const float4 q2 = *reinterpret_cast<const float4*>(prow + l * 20 + 8);
+        const float4 q3 = *reinterpret_cast<const float4*>(prow + l * 20 + 12);
+        __builtin_amdgcn_wave_barrier();
+        yo[j] = (((q0.x + q0.y) + (q0.z + q0.w)) + ((q1.x + q1.y) + (q1.z + q1.w))) +
+                (((q2.x + q2.y) + (q2.z + q2.w)) + ((q3.x + q3.y) + (q3.z + q3.w)));
+      }
+    });
+    // -- skip term, gate ([SPEC] Stage 1 item 4), store -------------------------------
+    if (row_ok && y) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int t = c0 + 16 * j + l;
+        if (t < L) Elem<In>::store(y, row_base + t, __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j]);
+      }
+    }
+    if (LOAD != kChanLoadSpread && ch + 1 < nchunks) load_bc(c0 + T, rB, rC);
+  }
+  if (prm.last_state && st_ok) prm.last_state[rowi * N + l] = h;
+}
+
 // ---- time-sliced row kernel --------------------------------------------------
 
 // NG: states per lane; LPC: lanes per row (NG*LPC >= dstate); T: steps per
@@ -1181,7 +1366,22 @@ int scan_tile_rows(const ScanTile& tile) {
 
 // Per-row B and C: chunks of 16 bf16 / 8 float32 steps for 4 states per
 // lane (the raw B and C of a chunk stay in registers), half that for 16.
+template <typename In>
+hipError_t launch_chan(const ScanParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)((p.dim + 15) / 16), (unsigned)p.batch);
+  constexpr int kVec = sizeof(In) == 4 ? kChanLoadSpread : kChanLoadAfter;
+  if (p.seqlen % Elem<In>::kPer16B == 0)
+    hipLaunchKernelGGL((selective_scan_chan_kernel<In, kVec>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((selective_scan_chan_kernel<In, kChanLoadElem>), grid, dim3(256), 0, stream,
+                       p);
+  return hipGetLastError();
+}
+
 hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream) {
+  // 9..16 states: one state per lane, whole 128-byte lines of B and C
+  if (p.dstate > 8 && p.dstate <= 16)
+    return bf16 ? launch_chan<uint16_t>(p, stream) : launch_chan<float>(p, stream);
   if (bf16) {
     if (p.dstate <= 4) return launch_rows<uint16_t, 4, 1, 16, true>(p, stream);
     if (p.dstate <= 8) return launch_rows<uint16_t, 4, 2, 16, true>(p, stream);

@@ -253,6 +253,11 @@ GROUPED = [  # (batch, dim, dstate, seqlen, ngroups, dtype): which kernel
     ((2, 40, 64, 77, 40), "bf16"),    # per channel, sixteen states per lane
     ((2, 40, 33, 50, 40), "f32"),
     ((2, 96, 16, 200, 3), "bf16"),    # groups of 32 rows: per-row reads
+    ((1, 70, 12, 100, 70), "f32"),    # per channel, one state per lane
+    ((2, 50, 9, 77, 50), "bf16"),     # rows not a multiple of 16 bytes: element reads
+    ((1, 33, 16, 1, 33), "bf16"),     # one step
+    ((3, 20, 13, 129, 4), "f32"),     # groups of 5 rows, ragged length
+    ((1, 24, 16, 1000, 24), "bf16"),  # 16 chunks of 64 steps, a partial last one
     ((2, 512, 16, 300, 2), "f32"),    # groups of 256 rows, time-split kernel
     ((8, 2048, 16, 160, 4), "bf16"),  # groups of 512 rows, row-parallel kernel
     ((16, 4096, 4, 90, 2), "bf16"),   # one lane per row, 256-row workgroups
