@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 // ---- per-row B, C: one state per lane -------------------------------------------
 
 // For B and C read per row (groups of channels smaller than a row-parallel
-// workgroup, e.g. one per channel) with 9..16 states.  B, C are
+// workgroup, e.g. one per channel) with up to 16 states.  B, C are
 // [batch, ngroups, dstate, seqlen]: each (row, state) is its own sequence of
 // seqlen elements, so a lane that holds several states of a row, reading a
 // short piece of each per chunk, touches a 128-byte line four times in four
@@ -1379,19 +1379,14 @@ hipError_t launch_chan(const ScanParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream) {
-  // 9..16 states: one state per lane, whole 128-byte lines of B and C
-  if (p.dstate > 8 && p.dstate <= 16)
+  // up to 16 states: one state per lane, whole 128-byte lines of B and C
+  // (per channel at the 1.4B shape, bf16 / f32: 16 states 2.50 / 5.21 ->
+  // 1.2 / 2.9 ms against four states per lane and 32-byte pieces; 4 states
+  // 0.95 / 2.13 -> 0.59 / 0.80 ms; 1 state 0.48 / 1.27 -> 0.52 / 0.56 ms)
+  if (p.dstate <= 16)
     return bf16 ? launch_chan<uint16_t>(p, stream) : launch_chan<float>(p, stream);
-  if (bf16) {
-    if (p.dstate <= 4) return launch_rows<uint16_t, 4, 1, 16, true>(p, stream);
-    if (p.dstate <= 8) return launch_rows<uint16_t, 4, 2, 16, true>(p, stream);
-    if (p.dstate <= 16) return launch_rows<uint16_t, 4, 4, 16, true>(p, stream);
-    return launch_rows<uint16_t, 16, 4, 8, true>(p, stream);
-  }
-  if (p.dstate <= 4) return launch_rows<float, 4, 1, 8, true>(p, stream);
-  if (p.dstate <= 8) return launch_rows<float, 4, 2, 8, true>(p, stream);
-  if (p.dstate <= 16) return launch_rows<float, 4, 4, 8, true>(p, stream);
-  return launch_rows<float, 16, 4, 4, true>(p, stream);
+  return bf16 ? launch_rows<uint16_t, 16, 4, 8, true>(p, stream)
+              : launch_rows<float, 16, 4, 4, true>(p, stream);
 }
 
 }  // namespace ssm
