@@ -567,6 +567,184 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
   if (prm.last_state && st_ok) prm.last_state[rowi * N + l] = h;
 }
 
+// Per-row B, C with 17..64 states: the same one-state-per-lane layout with
+// S = 32 or 64 lanes per row (two rows or one per wave; lanes past dstate
+// idle).  A row now spans more than one DPP row, so the delta and delta*u of
+// step t come from its owner lane (t mod S of the row) with v_readlane into
+// a scalar register, one per row of the wave (a select between the two rows
+// when S = 32): a few instructions per step of the wave, not per state.
+// Partial readouts go to LDS ([row][step][state], rows of S + 4 floats) and
+// after the chunk the owner of each step adds its S partials.
+template <typename In, int S, int LOAD>
+__global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams prm) {
+  constexpr bool VEC = LOAD != kChanLoadElem;
+  constexpr int EPU = Elem<In>::kPer16B;
+  constexpr int T = 128 / (int)sizeof(In);  // steps per chunk: one 128-byte line per state
+  constexpr int RPW = 64 / S;               // rows per wave
+  constexpr int NOWN = (T + S - 1) / S;     // steps of a chunk owned per lane (some lanes
+                                            // own none when T < S)
+  constexpr int kRowT = S + 4;              // LDS floats per step of a row
+  // the two rows of a wave (S = 32) 32 floats apart modulo 64 banks, so the
+  // 64 lanes' stores of a step meet no bank twice
+  constexpr int kRowR = T * kRowT + 32;
+  static_assert(S == 32 || S == 64, "lanes per row");
+  __shared__ alignas(16) float sP[4][RPW * kRowR];
+
+  const In* __restrict__ u = static_cast<const In*>(prm.u);
+  const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
+  const In* __restrict__ Bm = static_cast<const In*>(prm.B);
+  const In* __restrict__ Cm = static_cast<const In*>(prm.C);
+  const In* __restrict__ z = static_cast<const In*>(prm.z);
+  In* __restrict__ y = static_cast<In*>(prm.y);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = lane / S;   // row within the wave
+  const int l = lane % S;    // state n of this lane, and the owner index of steps
+  const int b = blockIdx.y;
+  const int d = blockIdx.x * (4 * RPW) + wv * RPW + rw;
+  const bool row_ok = d < prm.dim;
+  const int L = prm.seqlen;
+  const int N = prm.dstate;
+  const bool st_ok = row_ok && l < N;
+  const bool has_z = z != nullptr;
+  const int64_t rowi = (int64_t)b * prm.dim + (row_ok ? d : 0);
+  const int64_t row_base = rowi * (int64_t)L;
+  const int rpg = prm.dim / prm.ngroups;
+  const int64_t bc_row = (((int64_t)b * prm.ngroups + (row_ok ? d : 0) / rpg) * N +
+                          (st_ok ? l : 0)) * (int64_t)L;
+
+  const float A2 = st_ok ? prm.A[(int64_t)d * N + l] * kLog2e : 0.0f;
+  const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
+  const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
+  float h = (st_ok && prm.h0) ? prm.h0[rowi * N + l] : 0.0f;
+
+  // B, C of this lane's state, steps past the end reading the row's last
+  // elements (as in selective_scan_chan_kernel)
+  RawSeg<In, T> rB, rC;
+  auto load_unit = [&](const In* __restrict__ p, int c0, int k, RawSeg<In, T>& r) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + bc_row + min(c0 + EPU * k, L - EPU));
+    r.w[4 * k] = st_ok ? v.x : 0u;
+    r.w[4 * k + 1] = st_ok ? v.y : 0u;
+    r.w[4 * k + 2] = st_ok ? v.z : 0u;
+    r.w[4 * k + 3] = st_ok ? v.w : 0u;
+  };
+  auto load_line = [&](const In* __restrict__ p, int c0, RawSeg<In, T>& r) {
+    if constexpr (VEC) {
+#pragma unroll
+      for (int k = 0; k < T / EPU; ++k) load_unit(p, c0, k, r);
+    } else if constexpr (sizeof(In) == 4) {
+#pragma unroll
+      for (int k = 0; k < T; ++k)
+        r.w[k] = reinterpret_cast<const uint32_t*>(p)[bc_row + min(c0 + k, L - 1)];
+    } else {
+#pragma unroll
+      for (int k = 0; k < T / 2; ++k)
+        r.w[k] = (uint32_t)p[bc_row + min(c0 + 2 * k, L - 1)] |
+                 ((uint32_t)p[bc_row + min(c0 + 2 * k + 1, L - 1)] << 16);
+    }
+  };
+  auto load_bc = [&](int c0) {
+    load_line(Bm, c0, rB);
+    load_line(Cm, c0, rC);
+    if (!VEC && !st_ok) {
+#pragma unroll
+      for (int w = 0; w < RawSeg<In, T>::kWords; ++w) rB.w[w] = rC.w[w] = 0u;
+    }
+  };
+  auto to_f32 = [](In v) {
+    if constexpr (sizeof(In) == 4) return (float)v;
+    else return __uint_as_float((uint32_t)v << 16);
+  };
+  // this lane's steps c0 + S j + l of u, delta, z, loaded one chunk ahead
+  In ru[NOWN], rd[NOWN], rz[NOWN];
+  auto load_own = [&](int c0) {
+#pragma unroll
+    for (int j = 0; j < NOWN; ++j) {
+      const int t = min(c0 + S * j + l, L - 1);
+      ru[j] = u[row_base + t];
+      rd[j] = dlt[row_base + t];
+      rz[j] = has_z ? z[row_base + t] : In(0);
+    }
+  };
+  float* const prow = &sP[wv][rw * kRowR];
+  // the value of lane `own` of each row of the wave, for this lane's row
+  auto from_owner = [&](float v, auto ownc) {
+    constexpr int own = decltype(ownc)::value;
+    const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), own));
+    if constexpr (RPW == 1) {
+      return s0;
+    } else {
+      const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), S + own));
+      return rw == 0 ? s0 : s1;
+    }
+  };
+
+  const int nchunks = (L + T - 1) / T;
+  load_bc(0);
+  load_own(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * T;
+    float dl[NOWN], du[NOWN], uk[NOWN], gk[NOWN];
+#pragma unroll
+    for (int j = 0; j < NOWN; ++j) {
+      const bool in = row_ok && S * j + l < T && c0 + S * j + l < L;
+      uk[j] = in ? to_f32(ru[j]) : 0.0f;
+      const float dr = in ? to_f32(rd[j]) : 0.0f;
+      const float zz = (in && has_z) ? to_f32(rz[j]) : 0.0f;
+      float dd = dr + bias;
+      if (prm.delta_softplus) dd = softplus_in<In>(dd);
+      dl[j] = in ? dd : 0.0f;  // steps past the end are the identity
+      du[j] = dl[j] * uk[j];
+      gk[j] = has_z ? silu_f(zz) : 1.0f;
+    }
+    if (ch + 1 < nchunks) load_own(c0 + T);
+
+    static_for<0, T>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      constexpr int own = t % S, j = t / S;
+      const float dt = from_owner(dl[j], std::integral_constant<int, own>{});
+      const float dut = from_owner(du[j], std::integral_constant<int, own>{});
+      const float a = fast_exp2(dt * A2);
+      h = __builtin_fmaf(a, h, dut * raw_elem<In, T, t>(rB));
+      prow[t * kRowT + l] = raw_elem<In, T, t>(rC) * h;
+      if constexpr (LOAD == kChanLoadSpread && (t + 1) % EPU == 0) {
+        load_unit(Bm, c0 + T, t / EPU, rB);
+        load_unit(Cm, c0 + T, t / EPU, rC);
+      }
+    });
+    // -- each owner adds the S partials of its steps, skip term, gate, store --
+    // (the lanes of a row share a wave, whose LDS accesses complete in
+    // program order: no barrier)
+    __builtin_amdgcn_wave_barrier();
+    float yo[NOWN];
+#pragma unroll
+    for (int j = 0; j < NOWN; ++j) {
+      const int t = (S * j + l) < T ? S * j + l : T - 1;
+      const float* q = prow + t * kRowT;
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < S / 4; ++k) {
+        const float4 v = *reinterpret_cast<const float4*>(q + 4 * k);
+        acc[k & 3] += (v.x + v.y) + (v.z + v.w);
+      }
+      yo[j] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (row_ok && y) {
+#pragma unroll
+      for (int j = 0; j < NOWN; ++j) {
+        const int t = c0 + S * j + l;
+        if (S * j + l < T && t < L)
+          Elem<In>::store(y, row_base + t, __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j]);
+      }
+    }
+    if (LOAD != kChanLoadSpread && ch + 1 < nchunks) load_bc(c0 + T);
+  }
+  if (prm.last_state && st_ok) prm.last_state[rowi * N + l] = h;
+}
+
 // ---- time-sliced row kernel --------------------------------------------------
 
 // NG: states per lane; LPC: lanes per row (NG*LPC >= dstate); T: steps per
@@ -1378,6 +1556,18 @@ hipError_t launch_chan(const ScanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename In, int S>
+hipError_t launch_chanw(const ScanParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)((p.dim + 4 * (64 / S) - 1) / (4 * (64 / S))), (unsigned)p.batch);
+  constexpr int kVec = sizeof(In) == 4 ? kChanLoadSpread : kChanLoadAfter;
+  if (p.seqlen % Elem<In>::kPer16B == 0)
+    hipLaunchKernelGGL((selective_scan_chanw_kernel<In, S, kVec>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((selective_scan_chanw_kernel<In, S, kChanLoadElem>), grid, dim3(256), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream) {
   // up to 16 states: one state per lane, whole 128-byte lines of B and C
   // (per channel at the 1.4B shape, bf16 / f32: 16 states 2.50 / 5.21 ->
@@ -1385,8 +1575,9 @@ hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream
   // 0.95 / 2.13 -> 0.59 / 0.80 ms; 1 state 0.48 / 1.27 -> 0.52 / 0.56 ms)
   if (p.dstate <= 16)
     return bf16 ? launch_chan<uint16_t>(p, stream) : launch_chan<float>(p, stream);
-  return bf16 ? launch_rows<uint16_t, 16, 4, 8, true>(p, stream)
-              : launch_rows<float, 16, 4, 4, true>(p, stream);
+  if (p.dstate <= 32)
+    return bf16 ? launch_chanw<uint16_t, 32>(p, stream) : launch_chanw<float, 32>(p, stream);
+  return bf16 ? launch_chanw<uint16_t, 64>(p, stream) : launch_chanw<float, 64>(p, stream);
 }
 
 }  // namespace ssm

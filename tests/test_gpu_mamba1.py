@@ -258,6 +258,10 @@ GROUPED = [  # (batch, dim, dstate, seqlen, ngroups, dtype): which kernel
     ((1, 33, 16, 1, 33), "bf16"),     # one step
     ((3, 20, 13, 129, 4), "f32"),     # groups of 5 rows, ragged length
     ((1, 24, 16, 1000, 24), "bf16"),  # 16 chunks of 64 steps, a partial last one
+    ((1, 50, 24, 200, 50), "bf16"),   # per channel, 17-32 states: two rows per wave
+    ((2, 30, 64, 333, 30), "f32"),    # per channel, 64 states: one row per wave
+    ((1, 20, 48, 128, 5), "bf16"),    # groups of 4 rows, 48 states
+    ((1, 16, 40, 77, 16), "f32"),     # rows not a multiple of 16 bytes, 40 states
     ((2, 512, 16, 300, 2), "f32"),    # groups of 256 rows, time-split kernel
     ((8, 2048, 16, 160, 4), "bf16"),  # groups of 512 rows, row-parallel kernel
     ((16, 4096, 4, 90, 2), "bf16"),   # one lane per row, 256-row workgroups
