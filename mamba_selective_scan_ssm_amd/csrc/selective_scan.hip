@@ -68,9 +68,8 @@ using namespace scan;
 
 // NG: states per lane; LPC: lanes per row (NG*LPC >= dstate); T: steps per
 // time chunk.  Block = 256 threads = 4 waves of 64/LPC rows each.
-// RB = false: the workgroup's rows share one group's B and C, staged in LDS.
-// RB = true: every row reads its own group's B and C; each lane loads the
-// chunk of B and C for its own states into registers (no LDS, no barrier).
+// The workgroup's rows share one group's B and C, staged in LDS (per-row
+// B and C: selective_scan_chan_kernel / selective_scan_chanw_kernel).
 // With prm.seg_len > 0 the sequence is cut into segments of seg_len steps,
 // blockIdx.z selecting one ([EXPLAINED] eq. (11): any regrouping of the
 // combine operator gives the same result):
@@ -79,7 +78,7 @@ using namespace scan;
 //   AGG = false: fold the aggregates of the earlier segments onto the
 //                initial state (the segment's carry-in), then scan the
 //                segment and write its y (and, for the last one, last_state).
-template <typename In, int NG, int LPC, int T, bool RB = false, bool AGG = false>
+template <typename In, int NG, int LPC, int T, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm) {
   constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
   constexpr int RPW = 64 / LPC;      // rows per wave
@@ -96,10 +95,10 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   // given, and B is staged as ln(2) B so that delta' u B' = delta u B.  Two
   // VALU fewer per (b, d, t) than scaling A; float32 rows keep delta and
   // pre-scale A (the exact form of the float32 parity bound).
-  constexpr bool L2U = sizeof(In) == 2 && !RB;
+  constexpr bool L2U = sizeof(In) == 2;
 
-  __shared__ alignas(16) float sB[RB ? 1 : 2][RB ? 1 : T][RB ? 4 : NS];
-  __shared__ alignas(16) float sC[RB ? 1 : 2][RB ? 1 : T][RB ? 4 : NS];
+  __shared__ alignas(16) float sB[2][T][NS];
+  __shared__ alignas(16) float sC[2][T][NS];
 
   const In* __restrict__ u = static_cast<const In*>(prm.u);
   const In* __restrict__ dlt = static_cast<const In*>(prm.delta);
@@ -119,16 +118,16 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   const int L = prm.seqlen;
   const int N = prm.dstate;
   // time window of this workgroup: segment blockIdx.z, or the whole sequence
-  const int seg = RB ? 0 : blockIdx.z;  // (per-row B, C is never split in time)
-  const int t_begin = (!RB && prm.seg_len) ? seg * prm.seg_len : 0;
-  const int t_end = (!RB && prm.seg_len) ? min(L, t_begin + prm.seg_len) : L;
+  const int seg = blockIdx.z;
+  const int t_begin = prm.seg_len ? seg * prm.seg_len : 0;
+  const int t_end = prm.seg_len ? min(L, t_begin + prm.seg_len) : L;
   const int64_t nrows = (int64_t)prm.batch * prm.dim;
   const int64_t rowi = (int64_t)b * prm.dim + (row_ok ? d : 0);
   const int64_t row_base = ((int64_t)b * prm.dim + (row_ok ? d : 0)) * (int64_t)L;
   // B, C of group g: [batch, ngroups, dstate, seqlen]; the group of the
-  // workgroup's first row (RB = false) or of this row (RB = true)
+  // workgroup's rows (a group covers whole workgroups)
   const int rpg = prm.dim / prm.ngroups;
-  const int grp = RB ? (row_ok ? d : 0) / rpg : (int)(blockIdx.x * RPB) / rpg;
+  const int grp = (int)(blockIdx.x * RPB) / rpg;
   const int64_t bc_base = ((int64_t)b * prm.ngroups + grp) * N * (int64_t)L;
 
   // Per-row constants for this lane's states n = slot*NG + k.
@@ -151,11 +150,9 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
   }
   float dsum = 0.0f;  // AGG: sum of delta over the segment (prod a = exp2(A2 dsum))
 
-  // Raw chunk data, loaded one chunk ahead of its use.  RB: this row's B
-  // and C for the lane's states (decoded one element at a time when used).
+  // Raw chunk data, loaded one chunk ahead of its use.
   RawSeg<In, TS> ru, rd, rz;
-  RawSeg<In, EPU> rbc[RB ? 1 : RBU];
-  RawSeg<In, T> rBn[RB ? NG : 1], rCn[RB ? NG : 1];
+  RawSeg<In, EPU> rbc[RBU];
   auto load_chunk = [&](int c0) {
     const int ts = c0 + slot * TS;
     if (row_ok) {
@@ -163,38 +160,23 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
       load_raw<In, TS>(dlt, row_base, ts, L, rd);
       if (has_z) load_raw<In, TS>(z, row_base, ts, L, rz);
     }
-    if constexpr (RB) {
 #pragma unroll
-      for (int k = 0; k < NG; ++k) {
-        const int n = slot * NG + k;
-        if (row_ok && n < N) {
-          load_raw<In, T>(Bm, bc_base + (int64_t)n * L, c0, L, rBn[k]);
-          load_raw<In, T>(Cm, bc_base + (int64_t)n * L, c0, L, rCn[k]);
-        } else {
+    for (int q = 0; q < RBU; ++q) {
+      const int e = tid + q * 256;
+      const int n = e % NS, rest = e / NS;
+      const int seg = rest % UPR, x = rest / UPR;
+      if (e < UNITS && n < N) {
+        load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, rbc[q]);
+      } else {
 #pragma unroll
-          for (int w = 0; w < RawSeg<In, T>::kWords; ++w) rBn[k].w[w] = rCn[k].w[w] = 0u;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < RBU; ++q) {
-        const int e = tid + q * 256;
-        const int n = e % NS, rest = e / NS;
-        const int seg = rest % UPR, x = rest / UPR;
-        if (e < UNITS && n < N) {
-          load_raw<In, EPU>(x ? Cm : Bm, bc_base + (int64_t)n * L, c0 + seg * EPU, L, rbc[q]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
-        }
+        for (int k = 0; k < RawSeg<In, EPU>::kWords; ++k) rbc[q].w[k] = 0u;
       }
     }
   };
-  RawSeg<In, T> rBr[RB ? NG : 1], rCr[RB ? NG : 1];  // RB: the current chunk's
 
   const int nchunks = (t_end - t_begin + T - 1) / T;
   load_chunk(t_begin);
-  if constexpr (!AGG && !RB) {  // (per-row B, C is never split in time)
+  if constexpr (!AGG) {
     // carry-in of a later segment, (v_0) (+) agg_0 (+) ... (+) agg_{seg-1}
     // with the combine operator of [EXPLAINED] eq. (10): left in slot seg-1
     // by segment_carry_kernel.
@@ -210,26 +192,18 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
     const int buf = ch & 1;  // its last readers were two chunks ago, before the last barrier
 
     // -- B and C of this chunk into LDS as float32 [t][n] --------------------
-    if constexpr (RB) {
 #pragma unroll
-      for (int k = 0; k < NG; ++k) {
-        rBr[k] = rBn[k];
-        rCr[k] = rCn[k];
-      }
-    } else {
+    for (int q = 0; q < RBU; ++q) {
+      const int e = tid + q * 256;
+      if (e < UNITS) {
+        const int n = e % NS, rest = e / NS;
+        const int seg = rest % UPR, x = rest / UPR;
+        float v[EPU];
+        decode_raw<In, EPU>(rbc[q], v);
 #pragma unroll
-      for (int q = 0; q < RBU; ++q) {
-        const int e = tid + q * 256;
-        if (e < UNITS) {
-          const int n = e % NS, rest = e / NS;
-          const int seg = rest % UPR, x = rest / UPR;
-          float v[EPU];
-          decode_raw<In, EPU>(rbc[q], v);
-#pragma unroll
-          for (int i = 0; i < EPU; ++i) {
-            if (x) sC[buf][seg * EPU + i][n] = v[i];
-            else sB[buf][seg * EPU + i][n] = L2U ? v[i] * kLn2 : v[i];
-          }
+        for (int i = 0; i < EPU; ++i) {
+          if (x) sC[buf][seg * EPU + i][n] = v[i];
+          else sB[buf][seg * EPU + i][n] = L2U ? v[i] * kLn2 : v[i];
         }
       }
     }
@@ -278,7 +252,7 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
       for (int j = 0; j < TS; ++j) du[j] = dl[j] * uk[j];
     }
     if (ch + 1 < nchunks) load_chunk(c0 + T);
-    if constexpr (!RB) __syncthreads();
+    __syncthreads();
 
     // -- recurrence over the chunk ([EXPLAINED] eq. (7)) -----------------------
     float yp[T];
@@ -297,19 +271,11 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 #pragma unroll
       for (int k4 = 0; k4 < NG; k4 += 4) {
         float bv[4], cv[4];
-        if constexpr (RB) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bv[i] = raw_elem<In, T, t>(rBr[k4 + i]);
-            cv[i] = raw_elem<In, T, t>(rCr[k4 + i]);
-          }
-        } else {
-          const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG + k4]);
-          bv[0] = bq.x; bv[1] = bq.y; bv[2] = bq.z; bv[3] = bq.w;
-          if constexpr (!AGG) {
-            const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
-            cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
-          }
+        const float4 bq = *reinterpret_cast<const float4*>(&sB[buf][t][slot * NG + k4]);
+        bv[0] = bq.x; bv[1] = bq.y; bv[2] = bq.z; bv[3] = bq.w;
+        if constexpr (!AGG) {
+          const float4 cq = *reinterpret_cast<const float4*>(&sC[buf][t][slot * NG + k4]);
+          cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1381,11 +1347,11 @@ constexpr int t16_rows() { return sizeof(In) == 4 ? 32 : 64; }
 // waves fit per SIMD (64-step chunks: 228 / 196, two waves).
 constexpr int kTSeg16 = 32;
 
-template <typename In, int NG, int LPC, int T, bool RB = false, bool AGG = false>
+template <typename In, int NG, int LPC, int T, bool AGG = false>
 hipError_t launch_rows(const ScanParams& p, hipStream_t stream, int nz = 1) {
   constexpr int RPB = 4 * (64 / LPC);
   dim3 grid((unsigned)((p.dim + RPB - 1) / RPB), (unsigned)p.batch, (unsigned)nz);
-  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T, RB, AGG>), grid, dim3(256), 0,
+  hipLaunchKernelGGL((selective_scan_fwd_kernel<In, NG, LPC, T, AGG>), grid, dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -1441,10 +1407,10 @@ hipError_t scan_scratch_address(void** out) {
 // (4,4,64) / (16,4,32) for dstate <= 4 / 8 / 16 / 64.
 template <typename In, bool AGG>
 hipError_t launch_rows_tier(const ScanParams& p, hipStream_t s, int nz) {
-  if (p.dstate <= 4) return launch_rows<In, 4, 1, 16, false, AGG>(p, s, nz);
-  if (p.dstate <= 8) return launch_rows<In, 4, 2, 32, false, AGG>(p, s, nz);
-  if (p.dstate <= 16) return launch_rows<In, 4, 4, kTSeg16, false, AGG>(p, s, nz);
-  return launch_rows<In, 16, 4, 32, false, AGG>(p, s, nz);
+  if (p.dstate <= 4) return launch_rows<In, 4, 1, 16, AGG>(p, s, nz);
+  if (p.dstate <= 8) return launch_rows<In, 4, 2, 32, AGG>(p, s, nz);
+  if (p.dstate <= 16) return launch_rows<In, 4, 4, kTSeg16, AGG>(p, s, nz);
+  return launch_rows<In, 16, 4, 32, AGG>(p, s, nz);
 }
 
 template <bool REV, int RPP>
