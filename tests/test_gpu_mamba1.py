@@ -278,15 +278,20 @@ def test_grouped_B_C(lib, case):
     compare_full(lib, x, dtype, label=f"grouped {case}")
 
 
-def test_grouped_with_initial_state(lib):
-    b, d, n, L, G = 2, 96, 16, 200, 3
-    print("case grouped initial state", flush=True)
-    x = grouped_inputs(77, b, d, n, L, G, "f32")
+@pytest.mark.parametrize("case", [
+    ((2, 96, 16, 200, 3), "f32"),     # per-row B, C, one state per lane
+    ((1, 40, 48, 150, 40), "bf16"),   # per channel, 64 lanes per row
+    ((1, 30, 20, 77, 30), "f32"),     # per channel, 32 lanes per row, element reads
+])
+def test_grouped_with_initial_state(lib, case):
+    (b, d, n, L, G), dtype = case
+    print(f"case grouped initial state {case}", flush=True)
+    x = grouped_inputs(77, b, d, n, L, G, dtype)
     h0 = np.random.default_rng(78).standard_normal((b, d, n)).astype(np.float32)
-    y, ls = run_gpu_h0(lib, x, "f32", h0)
+    y, ls = run_gpu_h0(lib, x, dtype, h0)
     ry, rs = oracle.selective_scan(**x, h0=h0.astype(np.float64))
-    check("y", synth.to_host_f64(y).reshape(b * d, L), ry, "f32", f32_rel=True)
-    check("last_state", synth.to_host_f64(ls).reshape(b * d, -1), rs, "f32", f32_rel=True)
+    check("y", synth.to_host_f64(y).reshape(b * d, L), ry, dtype, f32_rel=True)
+    check("last_state", synth.to_host_f64(ls).reshape(b * d, -1), rs, dtype, f32_rel=True)
 
 
 def test_one_group_axis_is_the_plain_call(lib):
