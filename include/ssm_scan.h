@@ -169,8 +169,9 @@ ssm_status ssm_selective_scan_fwd_grouped(
 /*
  * Bytes of workspace that ssm_selective_scan_fwd_ws can use for these
  * sizes: 0 when the (batch, channel) rows alone give every SIMD of the
- * device a wave, or when the sequence is too short to split (fewer than 8
- * time chunks of the kernel); then no workspace is needed.  Else the room
+ * device a wave (with per-row B, C, see below: every CU a wave), or when
+ * the sequence is too short to split (fewer than 8 time chunks of the
+ * kernel); then no workspace is needed.  Else the room
  * for one aggregate (prod a, v) per (segment, row, state) of a time split
  * ([EXPLAINED] eqs. (10)-(11)).  Same size checks as
  * ssm_selective_scan_fwd_grouped; touches no device memory.
@@ -197,9 +198,11 @@ ssm_status ssm_selective_scan_fwd_workspace_size(ssm_handle handle,
  *                     overwritten; must not overlap any input or output.
  *   workspace_bytes : its size; below the size above (with workspace
  *                     given and a split planned) is SSM_ERR_INVALID_ARG.
- * No split is made when initial_state is last_state (in place), nor when
- * a group of channels does not cover whole workgroups (64 to 256 rows).
- * Every other argument, layout, limit and error is as for
+ * No split is made when initial_state is last_state (in place).  When a
+ * group of channels does not cover whole workgroups (64 to 256 rows), each
+ * row reads its own B, C rows and the split is made only when the rows
+ * give fewer waves than the device has CUs (the aggregate launch reads the
+ * B rows a second time).  Every other argument, layout, limit and error is as for
  * ssm_selective_scan_fwd_grouped.
  */
 ssm_status ssm_selective_scan_fwd_ws(

@@ -236,10 +236,16 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   ssm_status st = check_spans(in, 9, out, 3);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
-  // time segments when the rows alone leave SIMDs idle and a workspace is
-  // given (groups must cover whole workgroups of the row-parallel kernel)
-  ssm::ScanSegments sg = ssm::plan_scan_segments(batch, dim, dstate, seqlen, handle->num_cus);
-  if (ngroups > 1 && (dim / ngroups) % sg.rows_per_workgroup != 0) sg.nseg = 1;
+  // Per-row B, C when the groups cover no whole workgroup of the kernel the
+  // rows pick (each row then reads its own B and C).  Time segments when the
+  // rows alone leave SIMDs idle and a workspace is given (shared B, C:
+  // groups must also cover whole workgroups of the segmented kernel).
+  const ssm::ScanTile tile = pick_scan_tile(handle, batch, dim, dstate);
+  const bool per_row = ngroups > 1 && (dim / ngroups) % ssm::scan_tile_rows(tile) != 0;
+  ssm::ScanSegments sg =
+      per_row ? ssm::plan_scan_segments_rowbc(batch, dim, dstate, seqlen, handle->num_cus)
+              : ssm::plan_scan_segments(batch, dim, dstate, seqlen, handle->num_cus);
+  if (!per_row && ngroups > 1 && (dim / ngroups) % sg.rows_per_workgroup != 0) sg.nseg = 1;
   if (use_scratch) {  // the device's own scratch array stands in for the workspace
     workspace = handle->scratch;
     workspace_bytes = ssm::kNoAllocScratchBytes;
@@ -263,16 +269,13 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  const ssm::ScanTile tile = pick_scan_tile(handle, batch, dim, dstate);
   const bool bf16 = in_dtype == SSM_BF16;
-  // A group covering whole workgroups of the tile: its B and C are staged
-  // once per workgroup; otherwise every row reads its own.
-  const bool whole = (dim / ngroups) % ssm::scan_tile_rows(tile) == 0;
   hipError_t e;
   if (segmented) {
     p.seg_agg = static_cast<float*>(workspace);
-    e = ssm::launch_selective_scan_segmented(p, sg, bf16, stream);
-  } else if (ngroups == 1 || whole) {
+    e = per_row ? ssm::launch_selective_scan_rowbc_segmented(p, sg, bf16, stream)
+                : ssm::launch_selective_scan_segmented(p, sg, bf16, stream);
+  } else if (!per_row) {
     e = ssm::launch_selective_scan(p, tile, bf16, stream);
   } else {
     e = ssm::launch_selective_scan_rowbc(p, bf16, stream);
@@ -334,6 +337,14 @@ ssm_status ssm_selective_scan_fwd_workspace_size(ssm_handle handle, int64_t batc
                 (long long)ngroups, (long long)dim);
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  const ssm::ScanTile tile = pick_scan_tile(handle, batch, dim, dstate);
+  const bool per_row = ngroups > 1 && (dim / ngroups) % ssm::scan_tile_rows(tile) != 0;
+  if (per_row) {
+    const ssm::ScanSegments sg =
+        ssm::plan_scan_segments_rowbc(batch, dim, dstate, seqlen, handle->num_cus);
+    if (sg.nseg > 1) *bytes = sg.bytes;
+    return ok();
+  }
   const ssm::ScanSegments sg = ssm::plan_scan_segments(batch, dim, dstate, seqlen, handle->num_cus);
   if (sg.nseg > 1 && (ngroups == 1 || (dim / ngroups) % sg.rows_per_workgroup == 0))
     *bytes = sg.bytes;

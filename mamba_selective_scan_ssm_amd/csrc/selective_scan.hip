@@ -374,7 +374,11 @@ __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm)
 // bfloat16 1.5 against 1.1 ms, so bfloat16 loads after the chunk).  Other
 // rows: element loads after the chunk (kChanLoadElem).
 constexpr int kChanLoadElem = 0, kChanLoadAfter = 1, kChanLoadSpread = 2;
-template <typename In, int LOAD>
+// With prm.seg_len > 0, blockIdx.z selects a time segment as in the
+// row-parallel kernel: AGG = true scans it from the identity and writes its
+// aggregate (prod a, v) per (row, state); AGG = false starts from the
+// carry-in the combine scan left for it.
+template <typename In, int LOAD, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm) {
   constexpr bool VEC = LOAD != kChanLoadElem;
   constexpr int EPU = Elem<In>::kPer16B;
@@ -415,7 +419,15 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
   const float A2 = st_ok ? prm.A[(int64_t)d * N + l] * kLog2e : 0.0f;
   const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
   const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
-  float h = (st_ok && prm.h0) ? prm.h0[rowi * N + l] : 0.0f;
+  // time window: segment blockIdx.z, or the whole sequence
+  const int seg = blockIdx.z;
+  const int t_begin = prm.seg_len ? seg * prm.seg_len : 0;
+  const int t_end = prm.seg_len ? min(L, t_begin + prm.seg_len) : L;
+  const int64_t nrows = (int64_t)prm.batch * prm.dim;
+  float h = (!AGG && st_ok && prm.h0) ? prm.h0[rowi * N + l] : 0.0f;
+  if (!AGG && seg > 0 && st_ok)  // carry-in left in slot seg - 1 by segment_carry_kernel
+    h = prm.seg_agg[(((int64_t)(seg - 1) * nrows + rowi) * N + l) * 2 + 1];
+  float dsum = 0.0f;  // AGG: sum of delta over the segment (prod a = exp2(A2 dsum))
 
   // B, C of this lane's state for the steps c0 .. c0 + T - 1.  Steps past
   // the end read the row's last elements instead (finite values that meet
@@ -472,16 +484,16 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
       rz[j] = has_z ? z[row_base + t] : In(0);
     }
   };
-  const int nchunks = (L + T - 1) / T;
-  load_bc(0, rB, rC);
-  load_own(0);
+  const int nchunks = (t_end - t_begin + T - 1) / T;
+  load_bc(t_begin, rB, rC);
+  load_own(t_begin);
   for (int ch = 0; ch < nchunks; ++ch) {
-    const int c0 = ch * T;
+    const int c0 = t_begin + ch * T;
     // -- this lane's steps c0 + 16 j + l: delta, softplus, delta*u, gate --------
     float dl[NB], du[NB], uk[NB], gk[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const bool in = row_ok && c0 + 16 * j + l < L;
+      const bool in = row_ok && c0 + 16 * j + l < t_end;
       uk[j] = in ? to_f32(ru[j]) : 0.0f;
       const float dr = in ? to_f32(rd[j]) : 0.0f;
       const float zz = (in && has_z) ? to_f32(rz[j]) : 0.0f;
@@ -493,7 +505,7 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
     }
     if (ch + 1 < nchunks) load_own(c0 + T);
 
-    float yo[NB];
+    float yo[NB] = {};
     static_for<0, T>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
       constexpr int own = t % 16, j = t / 16;
@@ -501,12 +513,13 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
       const float dut = dpp_f<0x150 + own>(du[j]);
       const float a = fast_exp2(dt * A2);
       h = __builtin_fmaf(a, h, dut * raw_elem<In, T, t>(rB));
-      prow[own * 20 + l] = raw_elem<In, T, t>(rC) * h;
+      if constexpr (AGG) dsum += dt;
+      else prow[own * 20 + l] = raw_elem<In, T, t>(rC) * h;
       if constexpr (LOAD == kChanLoadSpread && (t + 1) % EPU == 0) {  // unit used up: the next chunk's
         load_unit(Bm, c0 + T, t / EPU, rB);
         load_unit(Cm, c0 + T, t / EPU, rC);
       }
-      if constexpr (own == 15) {
+      if constexpr (!AGG && own == 15) {
         // the 16 partials of this lane's step of the block, in a fixed order
         // (the lanes of a row share a wave, whose LDS accesses complete in
         // program order: no barrier)
@@ -521,16 +534,24 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
       }
     });
     // -- skip term, gate ([SPEC] Stage 1 item 4), store -------------------------------
-    if (row_ok && y) {
+    if (!AGG && row_ok && y) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int t = c0 + 16 * j + l;
-        if (t < L) Elem<In>::store(y, row_base + t, __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j]);
+        if (t < t_end) Elem<In>::store(y, row_base + t, __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j]);
       }
     }
     if (LOAD != kChanLoadSpread && ch + 1 < nchunks) load_bc(c0 + T, rB, rC);
   }
-  if (prm.last_state && st_ok) prm.last_state[rowi * N + l] = h;
+  if constexpr (AGG) {
+    if (st_ok) {
+      float* ag = prm.seg_agg + (((int64_t)seg * nrows + rowi) * N + l) * 2;
+      ag[0] = fast_exp2(A2 * dsum);
+      ag[1] = h;
+    }
+  } else if (prm.last_state && st_ok && t_end == L) {
+    prm.last_state[rowi * N + l] = h;
+  }
 }
 
 // Per-row B, C with 17..64 states: the same one-state-per-lane layout with
@@ -541,7 +562,7 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
 // when S = 32): a few instructions per step of the wave, not per state.
 // Partial readouts go to LDS ([row][step][state], rows of S + 4 floats) and
 // after the chunk the owner of each step adds its S partials.
-template <typename In, int S, int LOAD>
+template <typename In, int S, int LOAD, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams prm) {
   constexpr bool VEC = LOAD != kChanLoadElem;
   constexpr int EPU = Elem<In>::kPer16B;
@@ -584,7 +605,15 @@ __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams pr
   const float A2 = st_ok ? prm.A[(int64_t)d * N + l] * kLog2e : 0.0f;
   const float Dd = (row_ok && prm.D) ? prm.D[d] : 0.0f;
   const float bias = (row_ok && prm.delta_bias) ? prm.delta_bias[d] : 0.0f;
-  float h = (st_ok && prm.h0) ? prm.h0[rowi * N + l] : 0.0f;
+  // time window: segment blockIdx.z, or the whole sequence
+  const int seg = blockIdx.z;
+  const int t_begin = prm.seg_len ? seg * prm.seg_len : 0;
+  const int t_end = prm.seg_len ? min(L, t_begin + prm.seg_len) : L;
+  const int64_t nrows = (int64_t)prm.batch * prm.dim;
+  float h = (!AGG && st_ok && prm.h0) ? prm.h0[rowi * N + l] : 0.0f;
+  if (!AGG && seg > 0 && st_ok)  // carry-in left in slot seg - 1 by segment_carry_kernel
+    h = prm.seg_agg[(((int64_t)(seg - 1) * nrows + rowi) * N + l) * 2 + 1];
+  float dsum = 0.0f;  // AGG: sum of delta over the segment (prod a = exp2(A2 dsum))
 
   // B, C of this lane's state, steps past the end reading the row's last
   // elements (as in selective_scan_chan_kernel)
@@ -647,15 +676,15 @@ __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams pr
     }
   };
 
-  const int nchunks = (L + T - 1) / T;
-  load_bc(0);
-  load_own(0);
+  const int nchunks = (t_end - t_begin + T - 1) / T;
+  load_bc(t_begin);
+  load_own(t_begin);
   for (int ch = 0; ch < nchunks; ++ch) {
-    const int c0 = ch * T;
+    const int c0 = t_begin + ch * T;
     float dl[NOWN], du[NOWN], uk[NOWN], gk[NOWN];
 #pragma unroll
     for (int j = 0; j < NOWN; ++j) {
-      const bool in = row_ok && S * j + l < T && c0 + S * j + l < L;
+      const bool in = row_ok && S * j + l < T && c0 + S * j + l < t_end;
       uk[j] = in ? to_f32(ru[j]) : 0.0f;
       const float dr = in ? to_f32(rd[j]) : 0.0f;
       const float zz = (in && has_z) ? to_f32(rz[j]) : 0.0f;
@@ -674,7 +703,8 @@ __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams pr
       const float dut = from_owner(du[j], std::integral_constant<int, own>{});
       const float a = fast_exp2(dt * A2);
       h = __builtin_fmaf(a, h, dut * raw_elem<In, T, t>(rB));
-      prow[t * kRowT + l] = raw_elem<In, T, t>(rC) * h;
+      if constexpr (AGG) dsum += dt;
+      else prow[t * kRowT + l] = raw_elem<In, T, t>(rC) * h;
       if constexpr (LOAD == kChanLoadSpread && (t + 1) % EPU == 0) {
         load_unit(Bm, c0 + T, t / EPU, rB);
         load_unit(Cm, c0 + T, t / EPU, rC);
@@ -687,6 +717,7 @@ __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams pr
     float yo[NOWN];
 #pragma unroll
     for (int j = 0; j < NOWN; ++j) {
+      if constexpr (AGG) { yo[j] = 0.0f; continue; }
       const int t = (S * j + l) < T ? S * j + l : T - 1;
       const float* q = prow + t * kRowT;
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -698,17 +729,25 @@ __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams pr
       yo[j] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     __builtin_amdgcn_wave_barrier();
-    if (row_ok && y) {
+    if (!AGG && row_ok && y) {
 #pragma unroll
       for (int j = 0; j < NOWN; ++j) {
         const int t = c0 + S * j + l;
-        if (S * j + l < T && t < L)
+        if (S * j + l < T && t < t_end)
           Elem<In>::store(y, row_base + t, __builtin_fmaf(Dd, uk[j], yo[j]) * gk[j]);
       }
     }
     if (LOAD != kChanLoadSpread && ch + 1 < nchunks) load_bc(c0 + T);
   }
-  if (prm.last_state && st_ok) prm.last_state[rowi * N + l] = h;
+  if constexpr (AGG) {
+    if (st_ok) {
+      float* ag = prm.seg_agg + (((int64_t)seg * nrows + rowi) * N + l) * 2;
+      ag[0] = fast_exp2(A2 * dsum);
+      ag[1] = h;
+    }
+  } else if (prm.last_state && st_ok && t_end == L) {
+    prm.last_state[rowi * N + l] = h;
+  }
 }
 
 // ---- time-sliced row kernel --------------------------------------------------
@@ -1510,28 +1549,38 @@ int scan_tile_rows(const ScanTile& tile) {
 
 // Per-row B and C: chunks of 16 bf16 / 8 float32 steps for 4 states per
 // lane (the raw B and C of a chunk stay in registers), half that for 16.
-template <typename In>
-hipError_t launch_chan(const ScanParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)((p.dim + 15) / 16), (unsigned)p.batch);
+template <typename In, bool AGG = false>
+hipError_t launch_chan(const ScanParams& p, hipStream_t stream, int nz = 1) {
+  dim3 grid((unsigned)((p.dim + 15) / 16), (unsigned)p.batch, (unsigned)nz);
   constexpr int kVec = sizeof(In) == 4 ? kChanLoadSpread : kChanLoadAfter;
   if (p.seqlen % Elem<In>::kPer16B == 0)
-    hipLaunchKernelGGL((selective_scan_chan_kernel<In, kVec>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((selective_scan_chan_kernel<In, kVec, AGG>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((selective_scan_chan_kernel<In, kChanLoadElem>), grid, dim3(256), 0, stream,
-                       p);
+    hipLaunchKernelGGL((selective_scan_chan_kernel<In, kChanLoadElem, AGG>), grid, dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
-template <typename In, int S>
-hipError_t launch_chanw(const ScanParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)((p.dim + 4 * (64 / S) - 1) / (4 * (64 / S))), (unsigned)p.batch);
+template <typename In, int S, bool AGG = false>
+hipError_t launch_chanw(const ScanParams& p, hipStream_t stream, int nz = 1) {
+  dim3 grid((unsigned)((p.dim + 4 * (64 / S) - 1) / (4 * (64 / S))), (unsigned)p.batch,
+            (unsigned)nz);
   constexpr int kVec = sizeof(In) == 4 ? kChanLoadSpread : kChanLoadAfter;
   if (p.seqlen % Elem<In>::kPer16B == 0)
-    hipLaunchKernelGGL((selective_scan_chanw_kernel<In, S, kVec>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((selective_scan_chanw_kernel<In, S, kVec, AGG>), grid, dim3(256), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((selective_scan_chanw_kernel<In, S, kChanLoadElem>), grid, dim3(256), 0,
-                       stream, p);
+    hipLaunchKernelGGL((selective_scan_chanw_kernel<In, S, kChanLoadElem, AGG>), grid, dim3(256),
+                       0, stream, p);
   return hipGetLastError();
+}
+
+// Per-row B, C kernel by dstate: one state per lane, 16 / 32 / 64 lanes per row.
+template <typename In, bool AGG>
+hipError_t launch_rowbc_typed(const ScanParams& p, hipStream_t stream, int nz) {
+  if (p.dstate <= 16) return launch_chan<In, AGG>(p, stream, nz);
+  if (p.dstate <= 32) return launch_chanw<In, 32, AGG>(p, stream, nz);
+  return launch_chanw<In, 64, AGG>(p, stream, nz);
 }
 
 hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream_t stream) {
@@ -1539,11 +1588,48 @@ hipError_t launch_selective_scan_rowbc(const ScanParams& p, bool bf16, hipStream
   // (per channel at the 1.4B shape, bf16 / f32: 16 states 2.50 / 5.21 ->
   // 1.2 / 2.9 ms against four states per lane and 32-byte pieces; 4 states
   // 0.95 / 2.13 -> 0.59 / 0.80 ms; 1 state 0.48 / 1.27 -> 0.52 / 0.56 ms)
-  if (p.dstate <= 16)
-    return bf16 ? launch_chan<uint16_t>(p, stream) : launch_chan<float>(p, stream);
-  if (p.dstate <= 32)
-    return bf16 ? launch_chanw<uint16_t, 32>(p, stream) : launch_chanw<float, 32>(p, stream);
-  return bf16 ? launch_chanw<uint16_t, 64>(p, stream) : launch_chanw<float, 64>(p, stream);
+  return bf16 ? launch_rowbc_typed<uint16_t, false>(p, stream, 1)
+              : launch_rowbc_typed<float, false>(p, stream, 1);
+}
+
+ScanSegments plan_scan_segments_rowbc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                      int num_cus) {
+  // rows per wave of the per-row kernels; segments are whole 64-step chunks
+  // (a multiple of both chunk lengths, 64 bf16 and 32 float32 steps).
+  // Split only below one wave per CU: the aggregate pass reads B a second
+  // time, which these kernels feel (per channel, float32: batch 1, dim 256,
+  // 64 waves 177 -> 41 us split; batch 2, dim 1536, 768 waves 267 -> 426 us).
+  const int rpw = dstate <= 16 ? 4 : dstate <= 32 ? 2 : 1;
+  constexpr int kSegUnit = 64;
+  ScanSegments sg{1, 0, 4 * rpw, 0};
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t waves = batch * ((dim + rpw - 1) / rpw);
+  const int64_t target = 12 * cus;
+  const int64_t units = (seqlen + kSegUnit - 1) / kSegUnit;
+  if (waves > cus || units < 8) return sg;
+  const int64_t want = std::min<int64_t>({(target + waves - 1) / waves, units, 64});
+  if (want <= 1) return sg;
+  const int64_t seg_len = ((seqlen + want - 1) / want + kSegUnit - 1) / kSegUnit * kSegUnit;
+  const int64_t nseg = (seqlen + seg_len - 1) / seg_len;
+  if (nseg <= 1) return sg;
+  sg.nseg = (int)nseg;
+  sg.seg_len = (int)seg_len;
+  sg.bytes = (size_t)(nseg - 1) * (size_t)batch * (size_t)dim * (size_t)dstate * 2 * sizeof(float);
+  return sg;
+}
+
+hipError_t launch_selective_scan_rowbc_segmented(const ScanParams& p0, const ScanSegments& sg,
+                                                 bool bf16, hipStream_t stream) {
+  ScanParams p = p0;
+  p.seg_len = sg.seg_len;
+  hipError_t e = bf16 ? launch_rowbc_typed<uint16_t, true>(p, stream, sg.nseg - 1)
+                      : launch_rowbc_typed<float, true>(p, stream, sg.nseg - 1);
+  if (e != hipSuccess) return e;
+  e = launch_segment_carry(p.seg_agg, sg.nseg - 1, (int64_t)p.batch * p.dim * p.dstate, p.h0,
+                           false, stream);
+  if (e != hipSuccess) return e;
+  return bf16 ? launch_rowbc_typed<uint16_t, false>(p, stream, sg.nseg)
+              : launch_rowbc_typed<float, false>(p, stream, sg.nseg);
 }
 
 }  // namespace ssm

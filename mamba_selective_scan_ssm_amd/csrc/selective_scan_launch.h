@@ -73,6 +73,12 @@ ScanSegments plan_scan_segments(int64_t batch, int64_t dim, int64_t dstate, int6
 // p.seg_agg must point at sg.bytes of workspace.
 hipError_t launch_selective_scan_segmented(const ScanParams& p, const ScanSegments& sg, bool bf16,
                                            hipStream_t stream);
+// The same for the per-row B, C kernels (groups of channels smaller than a
+// workgroup): segments of whole 64-step chunks.
+ScanSegments plan_scan_segments_rowbc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                      int num_cus);
+hipError_t launch_selective_scan_rowbc_segmented(const ScanParams& p, const ScanSegments& sg,
+                                                 bool bf16, hipStream_t stream);
 
 // Scratch of ssm_selective_scan_fwd_noalloc: a file-scope device array in
 // selective_scan.hip, one copy per GPU, holding the time-split aggregates.

@@ -278,10 +278,35 @@ def test_grouped_B_C(lib, case):
     compare_full(lib, x, dtype, label=f"grouped {case}")
 
 
+PER_ROW_SPLIT = [  # (batch, dim, dstate, seqlen, ngroups), dtype: per-row B, C cut in time
+    ((1, 256, 16, 2048, 256), "f32"),  # the spec page's speed-up shape, per channel
+    ((1, 64, 8, 1000, 64), "bf16"),    # 16 lanes per row, 8 of them idle
+    ((1, 40, 48, 700, 40), "f32"),     # 64 lanes per row (one row per wave)
+    ((2, 30, 20, 900, 10), "bf16"),    # 32 lanes per row, groups of 3 rows
+    ((1, 16, 1, 1500, 16), "f32"),     # one state
+    ((1, 50, 16, 777, 50), "bf16"),    # rows not a multiple of 16 bytes, short last segment
+]
+
+
+@pytest.mark.parametrize("case", PER_ROW_SPLIT)
+def test_per_row_time_split(lib, case):
+    """Per-row B, C at small batches, cut in time across workgroups (the
+    aggregate pass, the combine scan, the rescan of each segment from its
+    carry-in); every y and last_state entry."""
+    (b, d, n, L, G), dtype = case
+    print(f"case per-row time split {case}", flush=True)
+    assert lib.ssm_selective_scan_fwd_workspace_size(b, d, n, L, ngroups=G) > 0, \
+        "this case is meant to be split in time"
+    x = grouped_inputs(300 + n, b, d, n, L, G, dtype)
+    compare_full(lib, x, dtype, label=f"per-row split {case}")
+
+
 @pytest.mark.parametrize("case", [
     ((2, 96, 16, 200, 3), "f32"),     # per-row B, C, one state per lane
     ((1, 40, 48, 150, 40), "bf16"),   # per channel, 64 lanes per row
     ((1, 30, 20, 77, 30), "f32"),     # per channel, 32 lanes per row, element reads
+    ((1, 128, 16, 1200, 128), "f32"), # per channel, split in time
+    ((1, 40, 33, 900, 40), "bf16"),   # per channel, 64 lanes per row, split in time
 ])
 def test_grouped_with_initial_state(lib, case):
     (b, d, n, L, G), dtype = case

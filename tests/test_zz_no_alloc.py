@@ -87,13 +87,48 @@ def test_noalloc_matches_workspace_entry(lib, pair):
         assert torch.equal(s0, s1), f"call {i}: last_state differs from the workspace entry point"
 
 
+def test_noalloc_matches_workspace_entry_per_row(lib):
+    """B, C per channel (the per-row kernels, cut in time): two no-allocation
+    calls in a row, the second smaller, against the workspace entry point."""
+    cases = [((1, 256, 16, 2048), "f32"), ((1, 40, 48, 700), "bf16")]
+    ins, refs = [], []
+    for i, ((b, d, n, L), dtype) in enumerate(cases):
+        t = inputs(900 + i, b, d, n, L, dtype)
+        rng = np.random.default_rng(901 + i)
+        for k in ("B", "C"):
+            v = rng.standard_normal((b, d, n, L)).astype(np.float32)
+            t[k] = synth.to_device(synth.round_bf16(v) if dtype == "bf16" else v, dtype, "cuda")
+        nbytes = lib.ssm_selective_scan_fwd_workspace_size(b, d, n, L, ngroups=d)
+        print(f"case noalloc per channel call {i}: {(b, d, n, L)} {dtype}, "
+              f"time-split workspace {nbytes} bytes", flush=True)
+        assert 0 < nbytes <= SCRATCH_BYTES
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        y0, s0 = outputs(t, 0.0)
+        lib.ssm_selective_scan_fwd_ws(*args_of(t), y0, s0, ws)
+        ins.append(t)
+        refs.append((y0, s0))
+    torch.cuda.synchronize()
+    got = []
+    for t in ins:
+        y1, s1 = outputs(t, float("nan"))
+        lib.ssm_selective_scan_fwd_noalloc(*args_of(t), y1, s1)
+        got.append((y1, s1))
+    torch.cuda.synchronize()
+    for i, ((y0, s0), (y1, s1)) in enumerate(zip(refs, got)):
+        assert torch.equal(y0, y1), f"call {i}: y differs from the workspace entry point"
+        assert torch.equal(s0, s1), f"call {i}: last_state differs from the workspace entry point"
+
+
 def test_scratch_holds_every_plan(lib):
-    """The real planner's workspace for a sweep of shapes fits the scratch."""
+    """The real planner's workspace for a sweep of shapes fits the scratch,
+    shared B, C and per row (one group per channel, groups of 3 channels)."""
     worst = 0
     for n in (1, 4, 8, 16, 33, 64):
         for b in (1, 2, 3, 16):
-            for d in (1, 64, 65, 256, 1000, 1536, 4096):
+            for d in (1, 64, 66, 256, 1002, 1536, 4098):
                 for L in (128, 1000, 4096, 1 << 20):
-                    worst = max(worst, lib.ssm_selective_scan_fwd_workspace_size(b, d, n, L))
+                    for g in (1, d, d // 3 if d % 3 == 0 else 1):
+                        worst = max(worst, lib.ssm_selective_scan_fwd_workspace_size(
+                            b, d, n, L, ngroups=g))
     print(f"  largest planned workspace {worst} bytes", flush=True)
     assert 0 < worst <= SCRATCH_BYTES
