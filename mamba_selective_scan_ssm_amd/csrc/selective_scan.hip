@@ -10,7 +10,7 @@
 //               section 3.2 (chunk long sequences instead of materialising
 //               [B, L, ED, N] tensors).
 //
-// Two kernels:
+// Kernels:
 //
 // selective_scan_fwd_kernel (whenever there are rows enough to fill the chip):
 //   * a channel d of one batch entry b is a row; its dstate axis is split
@@ -28,15 +28,24 @@
 //     group's partial readouts sum_n C h are reduce-scattered back to the
 //     owners of the steps with DPP adds.  No per-step value goes through LDS.
 //
-//   Two variants of it: with per-row B and C (groups of channels smaller
-//   than a workgroup, down to one channel: each lane loads its own states'
-//   B and C into registers), and with the sequence cut into segments across
-//   workgroups (given a workspace: a first launch stores every segment's
-//   aggregate (prod a, v), a second folds the earlier aggregates into each
-//   segment's carry-in with the combine operator and rescans it).
+//   With a workspace it also runs with the sequence cut into segments
+//   across workgroups: a first launch stores every segment's aggregate
+//   (prod a, v), a DPP scan over the segments turns the aggregates into
+//   carry-ins with the combine operator, and a second launch rescans each
+//   segment from its carry-in.
 //
-// selective_scan_split_kernel (too few rows to give every SIMD a wave and no
-// workspace for the segments):
+// selective_scan_chan_kernel / selective_scan_chanw_kernel (B and C read per
+// row: groups of channels smaller than a workgroup, down to one channel):
+//   one state per lane, a row's states over 16, 32 or 64 lanes, whole
+//   128-byte lines of each state's B and C per chunk; the same segments.
+//
+// selective_scan_slot_kernel (too few rows to give every SIMD a wave, no
+// workspace, up to 16 states): the row-parallel lane layout, with the waves
+// of a workgroup on the same rows taking consecutive time slots of every
+// chunk (slot aggregates and carries through LDS).
+//
+// selective_scan_split_kernel (too few rows to give every SIMD a wave, no
+// workspace, 17..64 states):
 //   * lane = row (64 rows per wave); G waves split the dstate axis (NG
 //     states each) and share the per-step work through LDS; their partial
 //     readouts are added in LDS;
@@ -46,8 +55,8 @@
 //     [EXPLAINED] eq. (10) with the running carry to produce every slot's
 //     carry-in; the slots then rescan with their carry-in.
 //
-// Both compute exp(delta*A) as exp2(delta*A2) with A2 = A*log2(e) pre-scaled
-// once per row; the product of a slot's decays is exp2(A2 * sum(delta)), one
+// All compute exp(delta*A) as exp2(delta*A2) with A2 = A*log2(e) pre-scaled
+// once per row (or delta kept in log2 units); the product of a slot's decays is exp2(A2 * sum(delta)), one
 // exp per state per slot.  Nothing of size [b, d, L, N] is ever written to
 // memory.
 #include <hip/hip_runtime.h>
@@ -1547,8 +1556,9 @@ int scan_tile_rows(const ScanTile& tile) {
   }
 }
 
-// Per-row B and C: chunks of 16 bf16 / 8 float32 steps for 4 states per
-// lane (the raw B and C of a chunk stay in registers), half that for 16.
+// Per-row B and C, one state per lane: 16 lanes per row up to 16 states
+// (selective_scan_chan_kernel), else S = 32 or 64 lanes per row
+// (selective_scan_chanw_kernel).  nz > 1: one z slice per time segment.
 template <typename In, bool AGG = false>
 hipError_t launch_chan(const ScanParams& p, hipStream_t stream, int nz = 1) {
   dim3 grid((unsigned)((p.dim + 15) / 16), (unsigned)p.batch, (unsigned)nz);
