@@ -309,13 +309,17 @@ ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle,
  *   dB, dC : [batch, ngroups, dstate, seqlen] float32, each group's
  *            gradient summed over its channels only
  *   workspace: ssm_selective_scan_bwd_grouped_workspace_size bytes.
- * ngroups >= 1 must divide dim (else SSM_ERR_INVALID_ARG), and with
- * ngroups > 1, dim / ngroups must be a multiple of the channels one
- * workgroup of the backward kernels handles (64 for dstate 9..64, 128 for
- * 5..8, 256 for 1..4), else SSM_ERR_UNSUPPORTED (per-channel B and C, for
- * instance, are not supported by the backward pass).  ngroups = 1 is
- * ssm_selective_scan_bwd.  Every other argument, layout, limit and error
- * is as for ssm_selective_scan_bwd.
+ * ngroups >= 1 must divide dim (else SSM_ERR_INVALID_ARG); any such value
+ * is supported.  When dim / ngroups is a multiple of the channels one
+ * workgroup of the shared-B/C backward kernels handles (64 for dstate
+ * 9..64, 128 for 5..8, 256 for 1..4), those kernels run and sum dB, dC
+ * over whole workgroups; otherwise (per-channel B and C, ngroups = dim,
+ * down to groups of a few channels) a kernel with one state per lane reads
+ * each row's own B and C, and for groups of more than one channel writes
+ * per-row dB, dC to the workspace (2 * batch * dim * dstate * seqlen floats
+ * of it) that a second kernel adds up per group, in channel order.  Both
+ * are deterministic.  ngroups = 1 is ssm_selective_scan_bwd.  Every other
+ * argument, layout, limit and error is as for ssm_selective_scan_bwd.
  */
 ssm_status ssm_selective_scan_bwd_grouped(
     ssm_handle handle, const void *u, const void *delta, const float *A,

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "ssmscan")
 LIB = os.path.join(PKG, "libssmscan.so")
 
-SOURCES = ["api.cpp", "selective_scan.hip", "selective_scan_bwd.hip", "ssd_chunk_scan.hip",
+SOURCES = ["api.cpp", "selective_scan.hip", "selective_scan_bwd.hip",
+           "selective_scan_bwd_rows.hip", "ssd_chunk_scan.hip",
            "state_update.hip", "ssd_state_update.hip"]
 ARCH = "gfx950"
 

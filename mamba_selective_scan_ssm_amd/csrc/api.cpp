@@ -378,18 +378,19 @@ ssm_status ssm_selective_scan_fwd_noalloc(ssm_handle handle, const void* u, cons
 
 namespace {
 
-// The grouped backward's condition on ngroups (the kernels sum dB, dC of a
-// group over whole workgroups).
-ssm_status check_bwd_groups(int64_t dim, int64_t dstate, int64_t ngroups) {
+// The grouped backward's condition on ngroups.
+ssm_status check_bwd_groups(int64_t dim, int64_t ngroups) {
   if (ngroups <= 0 || dim % ngroups != 0)
     return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
                 (long long)ngroups, (long long)dim);
-  const int rpw = ssm::selective_scan_bwd_rows_per_workgroup((int)dstate);
-  if (ngroups > 1 && (dim / ngroups) % rpw != 0)
-    return fail(SSM_ERR_UNSUPPORTED,
-                "backward: dim / ngroups = %lld must be a multiple of %d at dstate %lld",
-                (long long)(dim / ngroups), rpw, (long long)dstate);
   return SSM_OK;
+}
+
+// B, C read per row: a group's channels are not a whole number of the
+// shared-B/C backward workgroups (those sum dB, dC over whole workgroups).
+bool bwd_per_row(int64_t dim, int64_t dstate, int64_t ngroups) {
+  const int rpw = ssm::selective_scan_bwd_rows_per_workgroup((int)dstate);
+  return ngroups > 1 && (dim / ngroups) % rpw != 0;
 }
 
 }  // namespace
@@ -409,7 +410,7 @@ ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle, int6
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0)
     return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 64", (long long)dstate);
-  ssm_status gs = check_bwd_groups(dim, dstate, ngroups);
+  ssm_status gs = check_bwd_groups(dim, ngroups);
   if (gs != SSM_OK) return gs;
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
@@ -417,8 +418,11 @@ ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle, int6
   if (batch * dim > (int64_t(1) << 62) / seqlen / 64)
     return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
-  *bytes = ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen,
-                                          handle->num_cus, 4, (int)ngroups).total;
+  *bytes = bwd_per_row(dim, dstate, ngroups)
+               ? ssm::selective_scan_bwd_rows_workspace((int)batch, (int)dim, (int)dstate,
+                                                        (int)seqlen, (int)ngroups)
+               : ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen,
+                                                handle->num_cus, 4, (int)ngroups).total;
   return ok();
 }
 
@@ -457,7 +461,7 @@ ssm_status ssm_selective_scan_bwd_grouped(
     return fail(SSM_ERR_UNSUPPORTED, "batch*dim and seqlen must fit in int32");
   if (batch * dim > (int64_t(1) << 62) / seqlen / 64)
     return fail(SSM_ERR_UNSUPPORTED, "tensor too large");
-  ssm_status gs = check_bwd_groups(dim, dstate, ngroups);
+  ssm_status gs = check_bwd_groups(dim, ngroups);
   if (gs != SSM_OK) return gs;
   const struct { const char* name; const void* p; } required[] = {
       {"u", u}, {"delta", delta}, {"A", A}, {"B", B}, {"C", C}, {"dy", dy}, {"du", du},
@@ -485,11 +489,15 @@ ssm_status ssm_selective_scan_bwd_grouped(
   ssm_status st = check_spans(in, 11, out, 10);
   if (st != SSM_OK) return st;
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
+  const bool per_row = bwd_per_row(dim, dstate, ngroups);
   const ssm::BwdLayout lay = ssm::selective_scan_bwd_layout(
       (int)batch, (int)dim, (int)dstate, (int)seqlen, handle->num_cus, 4, (int)ngroups);
-  if (workspace_bytes < lay.total)
+  const size_t need = per_row ? ssm::selective_scan_bwd_rows_workspace(
+                                    (int)batch, (int)dim, (int)dstate, (int)seqlen, (int)ngroups)
+                              : lay.total;
+  if (workspace_bytes < need)
     return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
-                lay.total);
+                need);
 
   ssm::BwdParams p;
   ssm::ScanParams& f = p.fwd;
@@ -503,7 +511,8 @@ ssm_status ssm_selective_scan_bwd_grouped(
   p.dh0 = dinitial_state; p.workspace = workspace;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = ssm::launch_selective_scan_bwd(p, lay, in_dtype == SSM_BF16, stream);
+  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, in_dtype == SSM_BF16, stream)
+                         : ssm::launch_selective_scan_bwd(p, lay, in_dtype == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -161,6 +161,11 @@ BwdLayout selective_scan_bwd_layout(int batch, int dim, int dstate, int seqlen, 
 // dstate 9..64, 128 for 5..8, 256 for 1..4): with ngroups > 1, dim / ngroups
 // must be a multiple of it.
 int selective_scan_bwd_rows_per_workgroup(int dstate);
+// Backward with B, C read per row (groups of channels that are not a whole
+// number of the workgroups above, down to one channel): workspace bytes and
+// launch (BwdParams::workspace of at least that size).
+size_t selective_scan_bwd_rows_workspace(int batch, int dim, int dstate, int seqlen, int ngroups);
+hipError_t launch_selective_scan_bwd_rows(const BwdParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
                                      hipStream_t stream);
 

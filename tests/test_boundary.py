@@ -272,21 +272,20 @@ def bwd_grouped(ngroups, dim=256, dstate=16, handle=None, dB=P[13]):
 
 
 def test_grouped_backward_rules():
-    """Groups must divide dim, and (the kernels sum a group's dB, dC over
-    whole workgroups) hold a multiple of the backward's channels per
-    workgroup: 64 at dstate 9..64, 128 at 5..8, 256 at 1..4."""
+    """Groups must divide dim; any such group count is accepted: whole
+    workgroups of the shared-B/C kernels (64 channels at dstate 9..64, 128 at
+    5..8, 256 at 1..4), or the per-row kernels for smaller groups down to one
+    channel.  (Without a handle every valid call stops at the handle check.)"""
     for g, dim, n in ((1, 256, 16), (2, 256, 16), (4, 256, 16), (2, 256, 8), (1, 100, 4),
-                      (2, 128, 64)):
+                      (2, 128, 64), (8, 256, 16), (4, 256, 8), (2, 256, 4), (256, 256, 16),
+                      (3, 300, 48)):
         st, msg = bwd_grouped(g, dim, n)
         assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, (g, dim, n, msg)
     for g, dim, n in ((3, 256, 16), (0, 256, 16)):
         st, msg = bwd_grouped(g, dim, n)
         assert st == ssm.SSM_ERR_INVALID_ARG and "ngroups" in msg, (g, msg)
-    for g, dim, n in ((8, 256, 16), (4, 256, 8), (2, 256, 4), (256, 256, 16)):
-        st, msg = bwd_grouped(g, dim, n)
-        assert st == ssm.SSM_ERR_UNSUPPORTED and "multiple" in msg, (g, dim, n, msg)
     n = ctypes.c_size_t(1)
     lib = ssm.load_library()
     st = lib.ssm_selective_scan_bwd_grouped_workspace_size(None, 2, 256, 16, 8, 8,
                                                            ctypes.byref(n))
-    assert st == ssm.SSM_ERR_UNSUPPORTED and n.value == 0
+    assert st == ssm.SSM_ERR_INVALID_ARG and n.value == 0

@@ -210,6 +210,42 @@ def test_grouped_backward_matches_oracle(lib, case):
     compare(g, ref, dtype, True, True, h0)
 
 
+PER_ROW = [  # (b, d, n, L, dtype, groups, h0, dlast, gate, bias, softplus): per-row kernels
+    (2, 40, 16, 100, "f32", 40, True, True, True, True, True),    # per channel, 16 lanes per row
+    (1, 33, 4, 77, "bf16", 33, False, True, True, True, True),    # per channel, 4 states
+    (2, 30, 1, 65, "f32", 30, True, False, False, True, True),    # one state
+    (1, 20, 24, 130, "bf16", 20, True, True, True, False, True),  # 32 lanes per row
+    (2, 12, 64, 97, "f32", 12, True, True, True, True, True),     # 64 lanes per row
+    (1, 48, 33, 64, "f32", 48, False, False, True, False, False),  # softplus off (no bias)
+    (2, 96, 16, 200, "f32", 3, True, True, True, True, True),     # groups of 32 channels
+    (1, 30, 8, 150, "bf16", 6, True, True, True, True, True),     # groups of 5 channels
+    (3, 20, 48, 45, "f32", 4, True, True, False, False, True),    # groups of 5, 48 states
+    (1, 16, 16, 1, "f32", 16, True, True, True, True, True),      # one step
+    (1, 8, 16, 2049, "bf16", 8, True, True, True, True, True),    # 65 chunks, a ragged last one
+]
+
+
+@pytest.mark.parametrize("case", PER_ROW)
+def test_per_row_backward_matches_oracle(lib, case):
+    """B, C per channel, or per group of channels smaller than a backward
+    workgroup: the one-state-per-lane backward kernels; every gradient
+    against the oracle's grouped backward."""
+    b, d, n, L, dtype, groups, h0, dlast, gate, bias, softplus = case
+    print(f"case bwd per-row {case}", flush=True)
+    g, ref = run_case(lib, 400 + n, b, d, n, L, dtype, gate, bias, softplus, h0, dlast, groups)
+    assert tuple(g["dB"].shape) == (b, groups, n, L)
+    compare(g, ref, dtype, gate, bias, h0)
+
+
+def test_per_row_backward_repeatable(lib):
+    """The per-row backward sums in a fixed order: bitwise repeatable."""
+    g1, _ = run_case(lib, 9, 2, 30, 16, 80, "bf16", groups=6)
+    g2, _ = run_case(lib, 9, 2, 30, 16, 80, "bf16", groups=6)
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
+
+
 def test_grouped_backward_through_autograd(lib):
     """selective_scan_fn with grouped B, C: torch.autograd reaches the grouped
     backward, and its gradients equal the oracle's."""
