@@ -317,8 +317,10 @@ ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle,
  * down to groups of a few channels) a kernel with one state per lane reads
  * each row's own B and C, and for groups of more than one channel writes
  * per-row dB, dC to the workspace (2 * batch * dim * dstate * seqlen floats
- * of it) that a second kernel adds up per group, in channel order.  Both
- * are deterministic.  ngroups = 1 is ssm_selective_scan_bwd.  Every other
+ * of it) that a second kernel adds up per group, in channel order; at small
+ * batches it cuts the sequence in time as the shared-B/C kernels do (the
+ * workspace then also holds the segments' aggregates).  Both are
+ * deterministic.  ngroups = 1 is ssm_selective_scan_bwd.  Every other
  * argument, layout, limit and error is as for ssm_selective_scan_bwd.
  */
 ssm_status ssm_selective_scan_bwd_grouped(

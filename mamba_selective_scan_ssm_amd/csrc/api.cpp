@@ -420,7 +420,7 @@ ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle, int6
   if (!handle) return fail(SSM_ERR_INVALID_ARG, "handle is NULL");
   *bytes = bwd_per_row(dim, dstate, ngroups)
                ? ssm::selective_scan_bwd_rows_workspace((int)batch, (int)dim, (int)dstate,
-                                                        (int)seqlen, (int)ngroups)
+                                                        (int)seqlen, (int)ngroups, handle->num_cus)
                : ssm::selective_scan_bwd_layout((int)batch, (int)dim, (int)dstate, (int)seqlen,
                                                 handle->num_cus, 4, (int)ngroups).total;
   return ok();
@@ -493,7 +493,8 @@ ssm_status ssm_selective_scan_bwd_grouped(
   const ssm::BwdLayout lay = ssm::selective_scan_bwd_layout(
       (int)batch, (int)dim, (int)dstate, (int)seqlen, handle->num_cus, 4, (int)ngroups);
   const size_t need = per_row ? ssm::selective_scan_bwd_rows_workspace(
-                                    (int)batch, (int)dim, (int)dstate, (int)seqlen, (int)ngroups)
+                                    (int)batch, (int)dim, (int)dstate, (int)seqlen, (int)ngroups,
+                                    handle->num_cus)
                               : lay.total;
   if (workspace_bytes < need)
     return fail(SSM_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
@@ -511,7 +512,8 @@ ssm_status ssm_selective_scan_bwd_grouped(
   p.dh0 = dinitial_state; p.workspace = workspace;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, in_dtype == SSM_BF16, stream)
+  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, in_dtype == SSM_BF16,
+                                                                handle->num_cus, stream)
                          : ssm::launch_selective_scan_bwd(p, lay, in_dtype == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();

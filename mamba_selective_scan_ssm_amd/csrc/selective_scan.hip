@@ -1628,6 +1628,18 @@ ScanSegments plan_scan_segments_rowbc(int64_t batch, int64_t dim, int64_t dstate
   return sg;
 }
 
+hipError_t launch_selective_scan_rowbc_carries(const ScanParams& p, bool bf16, hipStream_t stream) {
+  // every segment but the last scanned from the identity by the per-row
+  // kernels (aggregates into p.seg_agg), then the combine scan in place
+  const int nz = (p.seqlen + p.seg_len - 1) / p.seg_len;
+  if (nz <= 1) return hipSuccess;
+  hipError_t e = bf16 ? launch_rowbc_typed<uint16_t, true>(p, stream, nz - 1)
+                      : launch_rowbc_typed<float, true>(p, stream, nz - 1);
+  if (e != hipSuccess) return e;
+  return launch_segment_carry(p.seg_agg, nz - 1, (int64_t)p.batch * p.dim * p.dstate, p.h0, false,
+                              stream);
+}
+
 hipError_t launch_selective_scan_rowbc_segmented(const ScanParams& p0, const ScanSegments& sg,
                                                  bool bf16, hipStream_t stream) {
   ScanParams p = p0;

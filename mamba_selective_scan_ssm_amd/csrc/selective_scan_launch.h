@@ -108,6 +108,9 @@ hipError_t launch_segment_carry(float* slots, int nslots, int64_t npairs, const 
 // segment_carry_kernel; slot s of p.seg_agg then holds the state entering
 // segment s + 1.
 hipError_t launch_selective_scan_carries(const ScanParams& p, bool bf16, hipStream_t stream);
+// The same with B, C read per row (the one-state-per-lane kernels; p.seg_len
+// a multiple of 64, dstate <= 64).
+hipError_t launch_selective_scan_rowbc_carries(const ScanParams& p, bool bf16, hipStream_t stream);
 
 // Backward pass (selective_scan_bwd.hip).
 struct BwdParams {
@@ -164,8 +167,10 @@ int selective_scan_bwd_rows_per_workgroup(int dstate);
 // Backward with B, C read per row (groups of channels that are not a whole
 // number of the workgroups above, down to one channel): workspace bytes and
 // launch (BwdParams::workspace of at least that size).
-size_t selective_scan_bwd_rows_workspace(int batch, int dim, int dstate, int seqlen, int ngroups);
-hipError_t launch_selective_scan_bwd_rows(const BwdParams& p, bool bf16, hipStream_t stream);
+size_t selective_scan_bwd_rows_workspace(int batch, int dim, int dstate, int seqlen, int ngroups,
+                                         int num_cus);
+hipError_t launch_selective_scan_bwd_rows(const BwdParams& p, bool bf16, int num_cus,
+                                          hipStream_t stream);
 hipError_t launch_selective_scan_bwd(const BwdParams& p, const BwdLayout& lay, bool bf16,
                                      hipStream_t stream);
 

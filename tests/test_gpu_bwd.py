@@ -221,7 +221,13 @@ PER_ROW = [  # (b, d, n, L, dtype, groups, h0, dlast, gate, bias, softplus): per
     (1, 30, 8, 150, "bf16", 6, True, True, True, True, True),     # groups of 5 channels
     (3, 20, 48, 45, "f32", 4, True, True, False, False, True),    # groups of 5, 48 states
     (1, 16, 16, 1, "f32", 16, True, True, True, True, True),      # one step
-    (1, 8, 16, 2049, "bf16", 8, True, True, True, True, True),    # 65 chunks, a ragged last one
+    (1, 8, 16, 2049, "bf16", 8, True, True, True, True, True),    # 33 segments, a ragged last one
+    # few rows: cut in time (forward and adjoint carries across segments)
+    (1, 256, 16, 2048, "f32", 256, True, True, True, True, True),  # the spec page's shape, per channel
+    (1, 40, 48, 700, "bf16", 40, True, True, True, True, True),    # 64 lanes per row, 11 segments
+    (2, 30, 20, 900, "bf16", 10, False, True, True, True, True),   # groups of 3 channels
+    (1, 16, 1, 1500, "f32", 16, True, False, False, False, True),  # one state
+    (1, 64, 8, 1000, "f32", 64, True, True, True, False, False),   # softplus off, split
 ]
 
 
