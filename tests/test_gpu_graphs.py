@@ -142,6 +142,50 @@ def test_backward_graph_replays(lib, case):
     check_replays(call, inp, (du, dd, dA, dB, dC, dD, dz, dbias, dh0), new_values)
 
 
+BWD_ROWS = [  # (batch, dim, dstate, seqlen, ngroups, dtype): B, C per row
+    ((1, 64, 16, 1024, 64), "f32"),   # per channel, split in time
+    ((2, 30, 20, 150, 10), "bf16"),   # groups of 3 channels (per-row dB, dC summed)
+]
+
+
+@pytest.mark.parametrize("case", BWD_ROWS)
+def test_per_row_backward_graph_replays(lib, case):
+    (b, d, n, L, G), dtype = case
+    print(f"case graph bwd per-row {case}", flush=True)
+
+    def values(seed):
+        v = mamba1_values(seed, b, d, n, L, dtype, h0=True)
+        rng = np.random.default_rng(seed + 7)
+        for k in ("B", "C"):
+            x = rng.standard_normal((b, G, n, L)).astype(np.float32)
+            v[k] = synth.to_device(synth.round_bf16(x) if dtype == "bf16" else x, dtype, "cuda")
+        return v
+
+    base = values(800)
+    keys = ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0", "dy", "dlast")
+    inp = {k: base[k] for k in keys}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    du, dd, dz = (torch.empty_like(inp["u"]) for _ in range(3))
+    dA = torch.empty((d, n), **f32)
+    dB, dC = torch.empty((b, G, n, L), **f32), torch.empty((b, G, n, L), **f32)
+    dD, dbias = torch.empty((d,), **f32), torch.empty((d,), **f32)
+    dh0 = torch.empty((b, d, n), **f32)
+    ws = torch.empty(lib.ssm_selective_scan_bwd_grouped_workspace_size(b, d, n, L, G),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        lib.ssm_selective_scan_bwd_grouped(
+            inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+            inp["delta_bias"], True, inp["h0"], inp["dy"], inp["dlast"], du, dd, dA, dB, dC, dD,
+            dz, dbias, dh0, ws)
+
+    def new_values(r):
+        v = values(801 + r)
+        return {k: v[k] for k in inp}
+
+    check_replays(call, inp, (du, dd, dA, dB, dC, dD, dz, dbias, dh0), new_values)
+
+
 SSD = [  # (batch, seqlen, heads, headdim, dstate, chunk)
     (1, 600, 4, 64, 128, 256),
     (2, 300, 2, 80, 96, 128),   # off-tile sizes: the zero-padded copies
