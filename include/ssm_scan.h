@@ -365,6 +365,24 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float *state,
                                       ssm_dtype in_dtype, hipStream_t stream);
 
 /*
+ * ssm_selective_state_update with B and C given per group of channels, as
+ * in ssm_selective_scan_fwd_grouped ([SPEC] reference kernel's per-channel
+ * B, C at ngroups = dim): channel d reads group g = d / (dim / ngroups),
+ *   B, C : [batch, ngroups, dstate] in_dtype.
+ * ngroups >= 1 must divide dim (else SSM_ERR_INVALID_ARG); ngroups = 1 is
+ * ssm_selective_state_update.  Calling it token after token equals
+ * ssm_selective_scan_fwd_grouped over the tokens with the state carried
+ * (up to float32 rounding).  Every other argument, layout, limit and error
+ * is as for ssm_selective_state_update.
+ */
+ssm_status ssm_selective_state_update_grouped(
+    ssm_handle handle, float *state, const void *u, const void *delta,
+    const float *A, const void *B, const void *C, const float *D, const void *z,
+    const float *delta_bias, int delta_softplus, void *y, int64_t batch,
+    int64_t dim, int64_t dstate, int64_t ngroups, ssm_dtype in_dtype,
+    hipStream_t stream);
+
+/*
  * One decode step of the Mamba-2 (SSD) recurrence: one new token per
  * (batch, head), the state updated in place ([CUTILE]: the recurrence with
  * a scalar A per head; [EXPLAINED] eq. (2): the skip term).  For every

@@ -29,7 +29,8 @@ EXPORTS = ("ssm_status_string", "ssm_last_error_message", "ssm_scan_create",
            "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_with_state",
            "ssm_selective_scan_fwd_grouped", "ssm_selective_scan_fwd_workspace_size",
            "ssm_selective_scan_fwd_ws", "ssm_selective_scan_fwd_noalloc",
-           "ssm_selective_state_update", "ssm_selective_scan_bwd_workspace_size",
+           "ssm_selective_state_update", "ssm_selective_state_update_grouped",
+           "ssm_selective_scan_bwd_workspace_size",
            "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_grouped_workspace_size",
            "ssm_selective_scan_bwd_grouped",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_fwd",
@@ -99,6 +100,10 @@ def load_library() -> ctypes.CDLL:
         lib.ssm_selective_state_update.argtypes = [
             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
             _i64, _i64, _i64, ctypes.c_int, _vp]
+        lib.ssm_selective_state_update_grouped.restype = ctypes.c_int
+        lib.ssm_selective_state_update_grouped.argtypes = [
+            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+            _i64, _i64, _i64, _i64, ctypes.c_int, _vp]
         lib.ssm_selective_scan_bwd_workspace_size.restype = ctypes.c_int
         lib.ssm_selective_scan_bwd_workspace_size.argtypes = [
             _vp, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -487,20 +492,29 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
 def ssm_selective_state_update(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, y,
                                handle=None) -> None:
     """One decode step, state [batch, dim, dstate] float32 updated in place;
-    u, delta, z, y: [batch, dim]; B, C: [batch, dstate]."""
+    u, delta, z, y: [batch, dim]; B, C: [batch, dstate], or [batch, ngroups,
+    dstate] (ssm_selective_state_update_grouped: channel d reads group
+    d // (dim // ngroups))."""
     import torch
-    sp = _Spec("ssm_selective_state_update")
+    fn = ("ssm_selective_state_update_grouped" if getattr(B, "dim", lambda: 0)() == 3
+          else "ssm_selective_state_update")
+    sp = _Spec(fn)
     ty = sp.in_dtype("u", u)
     sp.ndim("u", u, 2)
     sp.ndim("A", A, 2)
     batch, dim = (int(v) for v in u.shape)
     dstate = int(A.shape[1])
+    grouped = fn.endswith("_grouped")
+    ngroups = int(B.shape[1]) if grouped else 1
+    if ngroups < 1 or dim % ngroups:
+        raise ValueError(f"{fn}: B has {ngroups} groups, which must divide dim {dim}")
+    bc = (batch, ngroups, dstate) if grouped else (batch, dstate)
     f32 = torch.float32
     sp.tensor("A", A, f32, (dim, dstate))
     sp.tensor("state", state, f32, (batch, dim, dstate))
     sp.tensor("delta", delta, ty, (batch, dim))
-    sp.tensor("B", B, ty, (batch, dstate))
-    sp.tensor("C", C, ty, (batch, dstate))
+    sp.tensor("B", B, ty, bc)
+    sp.tensor("C", C, ty, bc)
     sp.tensor("D", D, f32, (dim,), optional=True)
     sp.tensor("z", z, ty, (batch, dim), optional=True)
     sp.tensor("delta_bias", delta_bias, f32, (dim,), optional=True)
@@ -514,11 +528,12 @@ def ssm_selective_state_update(state, u, delta, A, B, C, D, z, delta_bias, delta
     dev = u.device.index if u.device.index is not None else 0
     if handle is None:
         handle = get_handle(dev)
-    st = load_library().ssm_selective_state_update(
-        handle, _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), batch, dim, dstate,
-        _dtype_code(u), _stream_ptr(u.device))
-    _check("ssm_selective_state_update", st)
+    args = [handle, _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), batch, dim, dstate]
+    if grouped:
+        args.append(ngroups)
+    st = getattr(load_library(), fn)(*args, _dtype_code(u), _stream_ptr(u.device))
+    _check(fn, st)
 
 
 def ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen, handle=None,

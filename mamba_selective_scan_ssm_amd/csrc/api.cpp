@@ -525,11 +525,26 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const voi
                                       const float* delta_bias, int delta_softplus, void* y,
                                       int64_t batch, int64_t dim, int64_t dstate,
                                       ssm_dtype in_dtype, hipStream_t stream) {
+  return ssm_selective_state_update_grouped(handle, state, u, delta, A, B, C, D, z, delta_bias,
+                                            delta_softplus, y, batch, dim, dstate, 1, in_dtype,
+                                            stream);
+}
+
+ssm_status ssm_selective_state_update_grouped(ssm_handle handle, float* state, const void* u,
+                                              const void* delta, const float* A, const void* B,
+                                              const void* C, const float* D, const void* z,
+                                              const float* delta_bias, int delta_softplus,
+                                              void* y, int64_t batch, int64_t dim,
+                                              int64_t dstate, int64_t ngroups,
+                                              ssm_dtype in_dtype, hipStream_t stream) {
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
   if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
     return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (ngroups <= 0 || dim % ngroups != 0)
+    return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
+                (long long)ngroups, (long long)dim);
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
   if (dim > INT32_MAX || batch > INT32_MAX || batch * dim > (int64_t(1) << 40))
     return fail(SSM_ERR_UNSUPPORTED, "batch*dim too large");
@@ -542,7 +557,7 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const voi
   if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
   const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim;
-  const uint64_t nbc = (uint64_t)batch * dstate;
+  const uint64_t nbc = (uint64_t)batch * ngroups * dstate;
   const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
                      {"A", A, (uint64_t)dim * dstate * 4}, {"B", B, nbc * es},
                      {"C", C, nbc * es},           {"D", D, (uint64_t)dim * 4},
@@ -557,6 +572,7 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const voi
   p.delta_bias = delta_bias; p.y = y;
   p.batch = (int)batch; p.dim = (int)dim; p.dstate = (int)dstate;
   p.delta_softplus = delta_softplus ? 1 : 0;
+  p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
   hipError_t e = ssm::launch_state_update(p, in_dtype == SSM_BF16, stream);

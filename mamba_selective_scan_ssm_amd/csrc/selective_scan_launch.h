@@ -180,8 +180,8 @@ struct StepParams {
   const void* u;            // [batch, dim]
   const void* delta;        // [batch, dim]
   const float* A;           // [dim, dstate]
-  const void* B;            // [batch, dstate]
-  const void* C;            // [batch, dstate]
+  const void* B;            // [batch, ngroups, dstate]
+  const void* C;            // [batch, ngroups, dstate]
   const float* D;           // nullable
   const void* z;            // nullable
   const float* delta_bias;  // nullable
@@ -190,6 +190,7 @@ struct StepParams {
   int dim;
   int dstate;
   int delta_softplus;
+  int ngroups = 1;          // channel d reads group d / (dim / ngroups)
 };
 
 hipError_t launch_state_update(const StepParams& p, bool bf16, hipStream_t stream);

@@ -13,7 +13,8 @@
 // few flops per state entry, so the kernel is bound by the state traffic
 // (8 bytes per entry): each lane owns 4 consecutive states of a row (one
 // 16-byte load and store), the LPR lanes of a row are consecutive, and the
-// readout is summed over them with lane shuffles.
+// readout is summed over them with lane shuffles.  B and C may be given per
+// group of channels ([batch, ngroups, dstate]; ngroups = dim: per channel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,6 +59,8 @@ __global__ void __launch_bounds__(256) selective_state_update_kernel(StepParams 
   if (prm.delta_softplus) dt = softplus_f(dt);
   const float dtu = dt * ut;
 
+  // B, C of the row's group
+  const int64_t bc = ((int64_t)b * prm.ngroups + d / (prm.dim / prm.ngroups)) * N;
   float* st = prm.state + r * N;
   const int n0 = 4 * slot;
   float h[4], acc = 0.0f;
@@ -75,8 +78,8 @@ __global__ void __launch_bounds__(256) selective_state_update_kernel(StepParams 
     if (n < N) {
       // [EXPLAINED] eqs. (5)-(7): a = exp(delta*A), v = a v + delta B u
       const float a = fast_exp2(dt * prm.A[(int64_t)d * N + n] * kLog2e);
-      h[k] = __builtin_fmaf(a, h[k], dtu * load_in<In>(Bm, (int64_t)b * N + n));
-      acc = __builtin_fmaf(load_in<In>(Cm, (int64_t)b * N + n), h[k], acc);
+      h[k] = __builtin_fmaf(a, h[k], dtu * load_in<In>(Bm, bc + n));
+      acc = __builtin_fmaf(load_in<In>(Cm, bc + n), h[k], acc);
     }
   }
   if (ok) {

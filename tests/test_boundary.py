@@ -169,6 +169,24 @@ def test_state_update_checks():
     assert st == ssm.SSM_ERR_INVALID_ARG and "aligned" in msg
 
 
+def step_grouped(ngroups, dim=4):
+    lib = ssm.load_library()
+    st = lib.ssm_selective_state_update_grouped(None, P[9], P[0], P[1], P[2], P[3], P[4], None,
+                                                None, None, 1, P[5], 2, dim, 16, ngroups,
+                                                ssm.SSM_F32, None)
+    return st, ssm.ssm_last_error_message()
+
+
+def test_grouped_state_update_checks():
+    """ngroups must divide dim; a valid grouped call stops at the handle."""
+    for g in (1, 2, 4):
+        st, msg = step_grouped(g)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "handle" in msg, (g, msg)
+    for g in (0, 3, -1):
+        st, msg = step_grouped(g)
+        assert st == ssm.SSM_ERR_INVALID_ARG and "ngroups" in msg, (g, msg)
+
+
 def scan_grouped(ngroups, B=P[3], C=P[4], y=P[5], dim=4, seqlen=8):
     lib = ssm.load_library()
     st = lib.ssm_selective_scan_fwd_grouped(None, P[0], P[1], P[2], B, C, None, None, None, 1,

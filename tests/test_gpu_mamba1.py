@@ -448,6 +448,53 @@ def test_state_update_matches_one_step_scan(lib, shape, dtype):
     check("state", synth.to_host_f64(state).reshape(b * d, n), rs, dtype, f32_rel=True)
 
 
+@pytest.mark.parametrize("shape,dtype", [((2, 40, 16, 40), "bf16"), ((3, 30, 5, 10), "f32"),
+                                         ((2, 64, 48, 4), "f32"), ((1, 12, 1, 12), "bf16")])
+def test_grouped_state_update_matches_one_step_scan(lib, shape, dtype):
+    """B, C per group of channels (ngroups = dim: per channel): one decode
+    step against one step of the grouped scan from the same state."""
+    b, d, n, G = shape
+    print(f"case grouped decode step {shape} {dtype}", flush=True)
+    x = grouped_inputs(130 + n, b, d, n, 1, G, dtype)
+    h0 = np.random.default_rng(n + 2).standard_normal((b, d, n)).astype(np.float32)
+    dev = "cuda"
+    t = {k: (None if v is None else synth.to_device(v, dtype if k in ("u", "delta", "z", "B", "C")
+                                                     else "f32", dev))
+         for k, v in x.items()}
+    sq = {k: (t[k][..., 0].contiguous() if k in ("u", "delta", "z", "B", "C") else t[k])
+          for k in t}
+    assert tuple(sq["B"].shape) == (b, G, n)
+    state = torch.from_numpy(h0).to(dev)
+    y = torch.empty_like(sq["u"])
+    lib.ssm_selective_state_update(state, sq["u"], sq["delta"], sq["A"], sq["B"], sq["C"], sq["D"],
+                                   sq["z"], sq["delta_bias"], True, y)
+    torch.cuda.synchronize()
+    ry, rs = oracle.selective_scan(**x, h0=h0.astype(np.float64))
+    check("y", synth.to_host_f64(y).reshape(b * d, 1), ry, dtype, f32_rel=True)
+    check("state", synth.to_host_f64(state).reshape(b * d, n), rs, dtype, f32_rel=True)
+
+
+def test_grouped_decode_loop_matches_grouped_scan(lib):
+    """Thirty per-channel decode steps from a zero state give the grouped
+    scan's y and state."""
+    b, d, n, L = 2, 48, 16, 30
+    x = grouped_inputs(140, b, d, n, L, d, "f32")
+    dev = "cuda"
+    t = {k: (None if v is None else synth.to_device(v, "f32", dev)) for k, v in x.items()}
+    state = torch.zeros((b, d, n), dtype=torch.float32, device=dev)
+    ys = []
+    for s in range(L):
+        col = {k: t[k][..., s].contiguous() for k in ("u", "delta", "z", "B", "C")}
+        y = torch.empty_like(col["u"])
+        lib.ssm_selective_state_update(state, col["u"], col["delta"], t["A"], col["B"], col["C"],
+                                       t["D"], col["z"], t["delta_bias"], True, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    ry, rs = oracle.selective_scan(**x)
+    check("y", synth.to_host_f64(torch.stack(ys, dim=2)).reshape(b * d, L), ry, "f32", f32_rel=True)
+    check("state", synth.to_host_f64(state).reshape(b * d, n), rs, "f32", f32_rel=True)
+
+
 def test_decode_loop_matches_scan(lib):
     """Twenty decode steps from a zero state give the scan's y and state."""
     b, d, n, L = 2, 256, 16, 20
