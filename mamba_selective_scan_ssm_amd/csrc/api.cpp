@@ -15,6 +15,20 @@
 #include "ssd_launch.h"
 #include "ssm_scan.h"
 
+namespace {
+
+// The value of an ABI enum argument as an int.  A C caller may pass any int,
+// and in C++ a load of an enum object holding a value outside its
+// enumerators' range is undefined, so the bytes are copied instead.
+int dtype_code(const ssm_dtype& d) {
+  int c;
+  memcpy(&c, &d, sizeof c);
+  return c;
+}
+int dtype_code(int d) { return d; }
+
+}  // namespace
+
 struct ssm_scan_context {
   int device;
   int num_cus;
@@ -141,7 +155,11 @@ ssm::ScanTile pick_scan_tile(const ssm_scan_context* h, int64_t batch, int64_t d
 extern "C" {
 
 const char* ssm_status_string(ssm_status status) {
-  switch (status) {
+  // A C caller may pass any int; read it as one (a C++ load of an enum
+  // value outside its enumerators' range is undefined).
+  int code;
+  memcpy(&code, &status, sizeof code);
+  switch (code) {
     case SSM_OK: return "SSM_OK";
     case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG: invalid argument";
     case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: outside the supported limits";
@@ -194,7 +212,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
                                const float* initial_state, void* y, float* last_state,
                                int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                int64_t ngroups, void* workspace, size_t workspace_bytes,
-                               ssm_dtype in_dtype, hipStream_t stream, bool use_scratch = false) {
+                               int in_dtype, hipStream_t stream, bool use_scratch = false) {
   // ---- sizes -------------------------------------------------------------
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
@@ -203,8 +221,8 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   if (ngroups <= 0 || dim % ngroups != 0)
     return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
                 (long long)ngroups, (long long)dim);
-  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
@@ -218,7 +236,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
   if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
   if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
-  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate * seqlen;
   const uint64_t state_bytes = (uint64_t)batch * dim * dstate * 4;
@@ -269,7 +287,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  const bool bf16 = in_dtype == SSM_BF16;
+  const bool bf16 = dtype_code(in_dtype) == SSM_BF16;
   hipError_t e;
   if (segmented) {
     p.seg_agg = static_cast<float*>(workspace);
@@ -296,7 +314,7 @@ ssm_status ssm_selective_scan_fwd(ssm_handle handle, const void* u, const void* 
                                   hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              nullptr, y, last_state, batch, dim, dstate, seqlen, 1, nullptr, 0,
-                             in_dtype, stream);
+                             dtype_code(in_dtype), stream);
 }
 
 ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
@@ -309,7 +327,7 @@ ssm_status ssm_selective_scan_fwd_with_state(ssm_handle handle, const void* u,
                                              hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, 1, nullptr,
-                             0, in_dtype, stream);
+                             0, dtype_code(in_dtype), stream);
 }
 
 ssm_status ssm_selective_scan_fwd_grouped(ssm_handle handle, const void* u, const void* delta,
@@ -322,7 +340,7 @@ ssm_status ssm_selective_scan_fwd_grouped(ssm_handle handle, const void* u, cons
                                           ssm_dtype in_dtype, hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
-                             nullptr, 0, in_dtype, stream);
+                             nullptr, 0, dtype_code(in_dtype), stream);
 }
 
 ssm_status ssm_selective_scan_fwd_workspace_size(ssm_handle handle, int64_t batch, int64_t dim,
@@ -360,7 +378,7 @@ ssm_status ssm_selective_scan_fwd_ws(ssm_handle handle, const void* u, const voi
                                      ssm_dtype in_dtype, hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
-                             workspace, workspace_bytes, in_dtype, stream);
+                             workspace, workspace_bytes, dtype_code(in_dtype), stream);
 }
 
 ssm_status ssm_selective_scan_fwd_noalloc(ssm_handle handle, const void* u, const void* delta,
@@ -373,7 +391,7 @@ ssm_status ssm_selective_scan_fwd_noalloc(ssm_handle handle, const void* u, cons
                                           ssm_dtype in_dtype, hipStream_t stream) {
   return selective_scan_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
                              initial_state, y, last_state, batch, dim, dstate, seqlen, ngroups,
-                             nullptr, 0, in_dtype, stream, /*use_scratch=*/true);
+                             nullptr, 0, dtype_code(in_dtype), stream, /*use_scratch=*/true);
 }
 
 namespace {
@@ -426,6 +444,14 @@ ssm_status ssm_selective_scan_bwd_grouped_workspace_size(ssm_handle handle, int6
   return ok();
 }
 
+static ssm_status selective_scan_bwd_impl(
+    ssm_handle handle, const void* u, const void* delta, const float* A, const void* B,
+    const void* C, const float* D, const void* z, const float* delta_bias, int delta_softplus,
+    const float* initial_state, const void* dy, const float* dlast_state, void* du,
+    void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+    float* dinitial_state, void* workspace, size_t workspace_bytes, int64_t batch, int64_t dim,
+    int64_t dstate, int64_t seqlen, int64_t ngroups, int in_dtype, hipStream_t stream);
+
 ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* delta,
                                   const float* A, const void* B, const void* C, const float* D,
                                   const void* z, const float* delta_bias, int delta_softplus,
@@ -435,26 +461,26 @@ ssm_status ssm_selective_scan_bwd(ssm_handle handle, const void* u, const void* 
                                   float* dinitial_state, void* workspace, size_t workspace_bytes,
                                   int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                   ssm_dtype in_dtype, hipStream_t stream) {
-  return ssm_selective_scan_bwd_grouped(handle, u, delta, A, B, C, D, z, delta_bias,
+  return selective_scan_bwd_impl(handle, u, delta, A, B, C, D, z, delta_bias,
                                         delta_softplus, initial_state, dy, dlast_state, du,
                                         ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state,
                                         workspace, workspace_bytes, batch, dim, dstate, seqlen, 1,
-                                        in_dtype, stream);
+                                        dtype_code(in_dtype), stream);
 }
 
-ssm_status ssm_selective_scan_bwd_grouped(
+static ssm_status selective_scan_bwd_impl(
     ssm_handle handle, const void* u, const void* delta, const float* A, const void* B,
     const void* C, const float* D, const void* z, const float* delta_bias, int delta_softplus,
     const float* initial_state, const void* dy, const float* dlast_state, void* du,
     void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
     float* dinitial_state, void* workspace, size_t workspace_bytes, int64_t batch, int64_t dim,
-    int64_t dstate, int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream) {
+    int64_t dstate, int64_t seqlen, int64_t ngroups, int in_dtype, hipStream_t stream) {
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
   if (seqlen <= 0) return fail(SSM_ERR_INVALID_ARG, "seqlen must be >= 1 (got %lld)", (long long)seqlen);
-  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 64", (long long)dstate);
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
@@ -469,7 +495,7 @@ ssm_status ssm_selective_scan_bwd_grouped(
   for (const auto& r : required)
     if (!r.p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", r.name);
   if (z && !dz) return fail(SSM_ERR_INVALID_ARG, "dz is NULL while z is given");
-  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate * seqlen;
   const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
@@ -512,12 +538,33 @@ ssm_status ssm_selective_scan_bwd_grouped(
   p.dh0 = dinitial_state; p.workspace = workspace;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, in_dtype == SSM_BF16,
+  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, dtype_code(in_dtype) == SSM_BF16,
                                                                 handle->num_cus, stream)
-                         : ssm::launch_selective_scan_bwd(p, lay, in_dtype == SSM_BF16, stream);
+                         : ssm::launch_selective_scan_bwd(p, lay, dtype_code(in_dtype) == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+ssm_status ssm_selective_scan_bwd_grouped(
+    ssm_handle handle, const void* u, const void* delta, const float* A, const void* B,
+    const void* C, const float* D, const void* z, const float* delta_bias, int delta_softplus,
+    const float* initial_state, const void* dy, const float* dlast_state, void* du,
+    void* ddelta, float* dA, float* dB, float* dC, float* dD, void* dz, float* ddelta_bias,
+    float* dinitial_state, void* workspace, size_t workspace_bytes, int64_t batch, int64_t dim,
+    int64_t dstate, int64_t seqlen, int64_t ngroups, ssm_dtype in_dtype, hipStream_t stream) {
+  return selective_scan_bwd_impl(handle, u, delta, A, B, C, D, z, delta_bias, delta_softplus,
+                                 initial_state, dy, dlast_state, du, ddelta, dA, dB, dC, dD, dz,
+                                 ddelta_bias, dinitial_state, workspace, workspace_bytes, batch,
+                                 dim, dstate, seqlen, ngroups, dtype_code(in_dtype), stream);
+}
+
+static ssm_status selective_state_update_impl(ssm_handle handle, float* state, const void* u,
+                                              const void* delta, const float* A, const void* B,
+                                              const void* C, const float* D, const void* z,
+                                              const float* delta_bias, int delta_softplus,
+                                              void* y, int64_t batch, int64_t dim,
+                                              int64_t dstate, int64_t ngroups,
+                                              int in_dtype, hipStream_t stream);
 
 ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const void* u,
                                       const void* delta, const float* A, const void* B,
@@ -525,23 +572,23 @@ ssm_status ssm_selective_state_update(ssm_handle handle, float* state, const voi
                                       const float* delta_bias, int delta_softplus, void* y,
                                       int64_t batch, int64_t dim, int64_t dstate,
                                       ssm_dtype in_dtype, hipStream_t stream) {
-  return ssm_selective_state_update_grouped(handle, state, u, delta, A, B, C, D, z, delta_bias,
-                                            delta_softplus, y, batch, dim, dstate, 1, in_dtype,
+  return selective_state_update_impl(handle, state, u, delta, A, B, C, D, z, delta_bias,
+                                            delta_softplus, y, batch, dim, dstate, 1, dtype_code(in_dtype),
                                             stream);
 }
 
-ssm_status ssm_selective_state_update_grouped(ssm_handle handle, float* state, const void* u,
+static ssm_status selective_state_update_impl(ssm_handle handle, float* state, const void* u,
                                               const void* delta, const float* A, const void* B,
                                               const void* C, const float* D, const void* z,
                                               const float* delta_bias, int delta_softplus,
                                               void* y, int64_t batch, int64_t dim,
                                               int64_t dstate, int64_t ngroups,
-                                              ssm_dtype in_dtype, hipStream_t stream) {
+                                              int in_dtype, hipStream_t stream) {
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
-  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
   if (ngroups <= 0 || dim % ngroups != 0)
     return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
                 (long long)ngroups, (long long)dim);
@@ -555,7 +602,7 @@ ssm_status ssm_selective_state_update_grouped(ssm_handle handle, float* state, c
   if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
   if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
   if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
-  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate;
   const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
@@ -575,9 +622,21 @@ ssm_status ssm_selective_state_update_grouped(ssm_handle handle, float* state, c
   p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = ssm::launch_state_update(p, in_dtype == SSM_BF16, stream);
+  hipError_t e = ssm::launch_state_update(p, dtype_code(in_dtype) == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+ssm_status ssm_selective_state_update_grouped(ssm_handle handle, float* state, const void* u,
+                                              const void* delta, const float* A, const void* B,
+                                              const void* C, const float* D, const void* z,
+                                              const float* delta_bias, int delta_softplus,
+                                              void* y, int64_t batch, int64_t dim,
+                                              int64_t dstate, int64_t ngroups,
+                                              ssm_dtype in_dtype, hipStream_t stream) {
+  return selective_state_update_impl(handle, state, u, delta, A, B, C, D, z, delta_bias,
+                                     delta_softplus, y, batch, dim, dstate, ngroups,
+                                     dtype_code(in_dtype), stream);
 }
 
 ssm_status ssd_state_update(ssm_handle handle, float* state, const void* x, const void* dt,
@@ -589,8 +648,8 @@ ssm_status ssd_state_update(ssm_handle handle, float* state, const void* x, cons
     return fail(SSM_ERR_INVALID_ARG, "all sizes must be >= 1");
   if (nheads % ngroups != 0)
     return fail(SSM_ERR_INVALID_ARG, "nheads must be a multiple of ngroups");
-  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
+  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
   if (dstate > 256) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 256", (long long)dstate);
   if (batch > INT32_MAX || nheads > INT32_MAX || headdim > INT32_MAX ||
       batch * nheads * headdim > (int64_t(1) << 40))
@@ -599,7 +658,7 @@ ssm_status ssd_state_update(ssm_handle handle, float* state, const void* x, cons
       {"state", state}, {"x", x}, {"dt", dt}, {"A", A}, {"B", B}, {"C", C}, {"y", y}};
   for (const auto& r : required)
     if (!r.p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", r.name);
-  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
+  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
   const uint64_t nx = (uint64_t)batch * nheads * headdim;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate;
   const Span in[] = {{"x", x, nx * es},
@@ -621,7 +680,7 @@ ssm_status ssd_state_update(ssm_handle handle, float* state, const void* x, cons
   p.dstate = (int)dstate; p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = ssm::launch_ssd_state_update(p, in_dtype == SSM_BF16, stream);
+  hipError_t e = ssm::launch_ssd_state_update(p, dtype_code(in_dtype) == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -649,14 +708,14 @@ ssm_status ssd_impl(ssm_handle handle, const void* x, const void* dt, const floa
                     int dt_softplus, const float* initial_state, void* y, float* final_state,
                     void* workspace, size_t workspace_bytes, int64_t batch, int64_t seqlen,
                     int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                    int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream) {
+                    int64_t chunk_size, int in_dtype, hipStream_t stream) {
   ssm::SsdShape s;
   ssm_status st = ssm::ssd_validate_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                           chunk_size, &s, &g_last_error);
   if (st != SSM_OK) return st;
-  if (in_dtype != SSM_BF16 && in_dtype != SSM_F32)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", (int)in_dtype);
-  if (in_dtype != SSM_BF16)
+  if (dtype_code(in_dtype) != SSM_BF16 && dtype_code(in_dtype) != SSM_F32)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
+  if (dtype_code(in_dtype) != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "ssd_chunk_scan_fwd supports bf16 inputs only");
   if (!x) return fail(SSM_ERR_INVALID_ARG, "x is NULL");
   if (!dt) return fail(SSM_ERR_INVALID_ARG, "dt is NULL");
@@ -713,7 +772,7 @@ ssm_status ssd_chunk_scan_fwd(ssm_handle handle, const void* x, const void* dt, 
                               int64_t chunk_size, ssm_dtype in_dtype, hipStream_t stream) {
   return ssd_impl(handle, x, dt, A, B, C, D, dt_bias, dt_softplus, nullptr, y, final_state,
                   workspace, workspace_bytes, batch, seqlen, nheads, headdim, dstate, ngroups,
-                  chunk_size, in_dtype, stream);
+                  chunk_size, dtype_code(in_dtype), stream);
 }
 
 ssm_status ssd_chunk_scan_fwd_with_state(ssm_handle handle, const void* x, const void* dt,
@@ -726,7 +785,7 @@ ssm_status ssd_chunk_scan_fwd_with_state(ssm_handle handle, const void* x, const
                                          ssm_dtype in_dtype, hipStream_t stream) {
   return ssd_impl(handle, x, dt, A, B, C, D, dt_bias, dt_softplus, initial_state, y,
                   final_state, workspace, workspace_bytes, batch, seqlen, nheads, headdim, dstate,
-                  ngroups, chunk_size, in_dtype, stream);
+                  ngroups, chunk_size, dtype_code(in_dtype), stream);
 }
 
 }  // extern "C"
