@@ -1,9 +1,14 @@
 """Build libssmscan.so (the C-ABI library) in-tree with hipcc for gfx950.
 
     python -m mamba_selective_scan_ssm_amd.build
+    python -m mamba_selective_scan_ssm_amd.build --poison-lds
 
 Every HIP translation unit is compiled with packed-FP32 instructions
-disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).
+disabled (-Xclang -target-feature -Xclang -packed-fp32-ops).  The second
+form builds a debug library, _build/poison/libssmscan.so, whose kernels fill
+their workgroup's LDS with NaN bit patterns at entry (SSM_POISON_LDS): run
+the GPU parity tests against it (copied over the in-tree library) to catch a
+read of LDS that nothing wrote first.
 """
 from __future__ import annotations
 
@@ -19,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "ssmscan")
 LIB = os.path.join(PKG, "libssmscan.so")
+POISON_BUILD = os.path.join(ROOT, "_build", "poison")
 
 SOURCES = ["api.cpp", "selective_scan.hip", "selective_scan_bwd.hip",
            "selective_scan_bwd_rows.hip", "ssd_chunk_scan.hip",
@@ -40,10 +46,11 @@ def common_flags():
             "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + common_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + common_flags() + [f"-D{d}" for d in defines] + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -51,22 +58,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source (always) and link libssmscan.so next to this file."""
-    os.makedirs(BUILD, exist_ok=True)
+def build_library(verbose: bool = False, poison_lds: bool = False) -> str:
+    """Compile every source (always) and link libssmscan.so next to this file
+    (poison_lds: the LDS-poisoning debug library under _build/poison)."""
+    build_dir = POISON_BUILD if poison_lds else BUILD
+    lib = os.path.join(POISON_BUILD, "libssmscan.so") if poison_lds else LIB
+    defines = ("SSM_POISON_LDS",) if poison_lds else ()
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("linking libssmscan.so failed")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(LIB)
-    return LIB
+        print(lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build_library(verbose=True)
+    build_library(verbose=True, poison_lds="--poison-lds" in sys.argv[1:])

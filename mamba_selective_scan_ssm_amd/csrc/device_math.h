@@ -5,6 +5,24 @@
 
 namespace ssm {
 
+// Debug builds with SSM_POISON_LDS defined fill the workgroup's whole static
+// LDS with NaN bit patterns at kernel entry, so that a read of LDS that no
+// thread of the workgroup wrote first (a missing store or barrier) shows up
+// as NaN in the parity tests instead of reading whatever an earlier
+// workgroup left there.  Release builds: nothing.
+#ifdef SSM_POISON_LDS
+__device__ __forceinline__ void poison_lds() {
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  const uint32_t words = __builtin_amdgcn_groupstaticsize() / 4;
+  const uint32_t nthr = blockDim.x * blockDim.y * blockDim.z;
+  for (uint32_t i = threadIdx.x; i < words; i += nthr) ((lds_u32*)0)[i] = 0xffffffffu;
+  __syncthreads();
+}
+#define SSM_POISON_LDS_AT_ENTRY() ::ssm::poison_lds()
+#else
+#define SSM_POISON_LDS_AT_ENTRY() ((void)0)
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -89,6 +89,7 @@ using namespace scan;
 //                segment and write its y (and, for the last one, last_state).
 template <typename In, int NG, int LPC, int T, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_fwd_kernel(ScanParams prm) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
   constexpr int RPW = 64 / LPC;      // rows per wave
   constexpr int RPB = 4 * RPW;       // rows per workgroup
@@ -389,6 +390,7 @@ constexpr int kChanLoadElem = 0, kChanLoadAfter = 1, kChanLoadSpread = 2;
 // carry-in the combine scan left for it.
 template <typename In, int LOAD, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr bool VEC = LOAD != kChanLoadElem;
   constexpr int EPU = Elem<In>::kPer16B;
   constexpr int T = 128 / (int)sizeof(In);  // steps per chunk: one 128-byte line per state
@@ -573,6 +575,7 @@ __global__ void __launch_bounds__(256) selective_scan_chan_kernel(ScanParams prm
 // after the chunk the owner of each step adds its S partials.
 template <typename In, int S, int LOAD, bool AGG = false>
 __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams prm) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr bool VEC = LOAD != kChanLoadElem;
   constexpr int EPU = Elem<In>::kPer16B;
   constexpr int T = 128 / (int)sizeof(In);  // steps per chunk: one 128-byte line per state
@@ -781,6 +784,7 @@ __global__ void __launch_bounds__(256) selective_scan_chanw_kernel(ScanParams pr
 // costs about three issue slots per state update on top of the scan).
 template <typename In, int NG, int LPC, int T, int W>
 __global__ void __launch_bounds__(64 * W) selective_scan_slot_kernel(ScanParams prm) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int NS = NG * LPC;       // states covered per row (>= dstate)
   constexpr int RPB = 64 / LPC;      // rows per workgroup (shared by its waves)
   constexpr int TS = T / LPC;        // steps of the slot whose per-step work one lane owns
@@ -1087,6 +1091,7 @@ template <bool REV, int RPP>
 __global__ void __launch_bounds__(256) segment_carry_kernel(float2* __restrict__ slots, int nslots,
                                                           int64_t npairs,
                                                           const float* __restrict__ init) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int SL = 16 * RPP;         // lanes (slots) per pair
   constexpr int PPS = 4 / RPP;         // pairs per wave scan
   constexpr int ILP = 4;               // interleaved scans per wave
@@ -1144,6 +1149,7 @@ __global__ void __launch_bounds__(256) segment_carry_kernel(float2* __restrict__
 template <typename In, int NG, int G, int W, int T>
 __global__ void __launch_bounds__(64 * G * W)
 selective_scan_split_kernel(ScanParams prm) {
+  SSM_POISON_LDS_AT_ENTRY();
   static_assert(W > 1, "the row-parallel kernel covers W = 1");
   constexpr int NT = NG * G;       // states covered by one workgroup (>= dstate)
   constexpr int TC = W * T;        // steps per chunk

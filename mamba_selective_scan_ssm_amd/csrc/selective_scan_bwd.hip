@@ -106,6 +106,7 @@ __device__ __forceinline__ float* junk_slot(const float* real, float* junk, int 
 // instead (dz and dD are formed from the totals by the finishing kernel).
 template <typename In, int LPC, int T>
 __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayout lay) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int NG = kBwdNG;
   constexpr int NS = NG * LPC;       // states covered per row
   constexpr int RPW = 64 / LPC;      // rows per wave
@@ -391,6 +392,7 @@ __global__ void __launch_bounds__(256) bwd_fwd_sweep_kernel(BwdParams P, BwdLayo
 // acc_ddt, acc_du instead.
 template <typename In, int LPC>
 __global__ void __launch_bounds__(256) bwd_rev_sweep_kernel(BwdParams P, BwdLayout lay) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int NG = kBwdNG, T = kBwdT;
   constexpr int NS = NG * LPC;
   constexpr int RPW = 64 / LPC;
@@ -730,6 +732,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_params_kernel(BwdParams P, Bwd
 // lam_in entering it from the right ([EXPLAINED] eq. (10), run backwards).
 template <typename In, int LPC>
 __global__ void __launch_bounds__(256) bwd_lambda_agg_kernel(BwdParams P, BwdLayout lay) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int NG = kBwdNG, T = kBwdT;
   constexpr int NS = NG * LPC, RPW = 64 / LPC, RPB = 4 * RPW, TS = T / LPC;
   constexpr int EPU = Elem<In>::kPer16B;
@@ -998,6 +1001,7 @@ hipError_t copy_cols(const void* src, int64_t src_stride, int64_t src_off, void*
 // and the row's sums of dyh u (for dD) and ddelta (for ddelta_bias).
 template <typename In>
 __global__ void __launch_bounds__(256) bwd_finish_blocks_kernel(BwdParams P, BwdLayout lay) {
+  SSM_POISON_LDS_AT_ENTRY();
   const ScanParams& F = P.fwd;
   const int64_t row = blockIdx.x;
   const int d = (int)(row % F.dim);

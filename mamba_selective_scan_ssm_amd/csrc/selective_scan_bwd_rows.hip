@@ -103,6 +103,7 @@ RowsBwdLayout rows_bwd_layout(int batch, int dim, int dstate, int seqlen, int ng
 
 template <typename In, int S>
 __global__ void __launch_bounds__(64) bwd_rows_kernel(BwdParams P, RowsBwdLayout lay) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int T = kRowsBwdT;
   constexpr int RPW = 64 / S;                 // rows per wave (= workgroup)
   constexpr int NOWN = (T + S - 1) / S;       // steps of a chunk a lane may own
@@ -339,6 +340,7 @@ __global__ void __launch_bounds__(64) bwd_rows_kernel(BwdParams P, RowsBwdLayout
 // lam_in entering it from the right ([EXPLAINED] eq. (10), run backwards).
 template <typename In, int S>
 __global__ void __launch_bounds__(64) bwd_rows_lam_agg_kernel(BwdParams P, RowsBwdLayout lay) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int T = kRowsBwdT;
   constexpr int RPW = 64 / S;
   constexpr int NOWN = (T + S - 1) / S;

@@ -261,6 +261,7 @@ __device__ void group_log_decay(const SsdArgs& a, int c, int nh, const GroupRaw<
 // several heads' loads are in flight while the small per-head product runs.
 template <int P, int NB, int QT>
 __global__ void __launch_bounds__(1024) ssd_chunk_state_kernel(SsdArgs a) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int NTHR = 1024, NW = 16;
   // LDS row strides (bf16), in bytes 32 and 16 modulo 128 past the row
   // (B: NB + 16 elements; x: P + 8): the four rows that a 16-lane group of
@@ -542,6 +543,7 @@ constexpr int out_kb(int N) { return W == 8 ? (N < 128 ? N : 128) : (N < 64 ? N 
 
 template <int P, int N, int W>
 __global__ void __launch_bounds__(64 * W, 8 / W) ssd_chunk_out_kernel(SsdArgs a) {
+  SSM_POISON_LDS_AT_ENTRY();
   constexpr int KN = N / 32;         // contraction steps over the state axis
   constexpr int NPN = kQMax / 32 - 1; // off-diagonal s-tile pairs per wave (at Q = 256)
   constexpr int PT = P / 16;
