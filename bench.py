@@ -219,15 +219,32 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(x, cfg, oracle, min_seconds=1.0):
+def parity_vs_oracle(got, ref):
+    """Errors of the GPU outputs against the oracle's, as the parity tests
+    measure them: max |err|, the norm-wise relative error, and the largest
+    |err| / (|ref| + rms(ref)) (the bf16 bound is 2e-2 of that)."""
+    import numpy as np
+    out = {}
+    for name, g, r in zip(("y", "last_state"), got, ref):
+        err = np.abs(g - r)
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        out[name] = {"max_abs_err": float(err.max()),
+                     "rel_l2": float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)),
+                     "max_err_over_abs_ref_plus_rms": float((err / (np.abs(r) + rms)).max())}
+    return out
+
+
+def cpu_baseline(x, cfg, oracle, min_seconds=1.0, gpu_out=None):
     """Time the oracle (as it stands) on the whole workload on the host,
     repeating it until at least `min_seconds` of wall time (about 16 s of CPU
-    work on 16 threads)."""
+    work on 16 threads).  With gpu_out (y [rows, L], last_state [rows, N] of
+    the timed GPU run, float64), also the GPU's errors against the oracle's
+    outputs of the same run."""
     threads = oracle.default_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.selective_scan(**x, delta_softplus=cfg.softplus, want_y=True, want_state=True,
-                              nthreads=threads)
+        ref = oracle.selective_scan(**x, delta_softplus=cfg.softplus, want_y=True,
+                                    want_state=True, nthreads=threads)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -240,8 +257,10 @@ def cpu_baseline(x, cfg, oracle, min_seconds=1.0):
     t1 = time.perf_counter()
     oracle.selective_scan(**x, delta_softplus=cfg.softplus, rows=rows, nthreads=1)
     one = time.perf_counter() - t1
+    parity = parity_vs_oracle(gpu_out, ref) if gpu_out is not None else None
     return {"value": reps * mamba1_bytes(b, d, n, L, es) / dt / 1e9, "unit": "GB/s",
             "cores": threads, "kind": "oracle", "seconds": round(dt, 3), "repetitions": reps,
+            "gpu_parity": parity,
             "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "one_thread_state_updates_per_s": round(len(rows) * L * n / one, 1),
             "sample": f"the whole {cfg.name} workload ({b * d} rows x {L} steps x {n} states, "
@@ -309,6 +328,10 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+    # the timed run's outputs, for the comparison with the oracle (host copy,
+    # outside the timed region)
+    gpu_out = None if args.no_cpu_baseline else (
+        synth.to_host_f64(y).reshape(b * d, L), synth.to_host_f64(ls).reshape(b * d, n))
 
     nbytes = mamba1_bytes(b, d, n, L, es)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -357,7 +380,7 @@ def main():
         out["spec_point"] = bench_spec_point(torch, ssm, synth)
     if not args.no_cpu_baseline:
         import oracle
-        out["cpu_baseline"] = cpu_baseline(x, cfg, oracle)
+        out["cpu_baseline"] = cpu_baseline(x, cfg, oracle, gpu_out=gpu_out)
         out["speedup_vs_oracle"] = round(value / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
