@@ -25,7 +25,6 @@ int dtype_code(const ssm_dtype& d) {
   memcpy(&c, &d, sizeof c);
   return c;
 }
-int dtype_code(int d) { return d; }
 
 }  // namespace
 
@@ -221,8 +220,8 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   if (ngroups <= 0 || dim % ngroups != 0)
     return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
                 (long long)ngroups, (long long)dim);
-  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "dstate %lld > 64", (long long)dstate);
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
@@ -236,7 +235,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
   if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
   if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
-  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate * seqlen;
   const uint64_t state_bytes = (uint64_t)batch * dim * dstate * 4;
@@ -287,7 +286,7 @@ ssm_status selective_scan_impl(ssm_handle handle, const void* u, const void* del
   p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  const bool bf16 = dtype_code(in_dtype) == SSM_BF16;
+  const bool bf16 = in_dtype == SSM_BF16;
   hipError_t e;
   if (segmented) {
     p.seg_agg = static_cast<float*>(workspace);
@@ -479,8 +478,8 @@ static ssm_status selective_scan_bwd_impl(
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
   if (seqlen <= 0) return fail(SSM_ERR_INVALID_ARG, "seqlen must be >= 1 (got %lld)", (long long)seqlen);
-  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (dstate > 64) return fail(SSM_ERR_UNSUPPORTED, "backward: dstate %lld > 64", (long long)dstate);
   if (batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "batch %lld > 65535", (long long)batch);
   if (seqlen > INT32_MAX || dim > INT32_MAX || batch * dim > INT32_MAX)
@@ -495,7 +494,7 @@ static ssm_status selective_scan_bwd_impl(
   for (const auto& r : required)
     if (!r.p) return fail(SSM_ERR_INVALID_ARG, "%s is NULL", r.name);
   if (z && !dz) return fail(SSM_ERR_INVALID_ARG, "dz is NULL while z is given");
-  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim * seqlen;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate * seqlen;
   const uint64_t nst = (uint64_t)batch * dim * dstate * 4;
@@ -538,9 +537,9 @@ static ssm_status selective_scan_bwd_impl(
   p.dh0 = dinitial_state; p.workspace = workspace;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, dtype_code(in_dtype) == SSM_BF16,
+  hipError_t e = per_row ? ssm::launch_selective_scan_bwd_rows(p, in_dtype == SSM_BF16,
                                                                 handle->num_cus, stream)
-                         : ssm::launch_selective_scan_bwd(p, lay, dtype_code(in_dtype) == SSM_BF16, stream);
+                         : ssm::launch_selective_scan_bwd(p, lay, in_dtype == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -587,8 +586,8 @@ static ssm_status selective_state_update_impl(ssm_handle handle, float* state, c
   if (batch <= 0) return fail(SSM_ERR_INVALID_ARG, "batch must be >= 1 (got %lld)", (long long)batch);
   if (dim <= 0) return fail(SSM_ERR_INVALID_ARG, "dim must be >= 1 (got %lld)", (long long)dim);
   if (dstate <= 0) return fail(SSM_ERR_INVALID_ARG, "dstate must be >= 1 (got %lld)", (long long)dstate);
-  if (dtype_code(in_dtype) != SSM_F32 && dtype_code(in_dtype) != SSM_BF16)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
+  if (in_dtype != SSM_F32 && in_dtype != SSM_BF16)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
   if (ngroups <= 0 || dim % ngroups != 0)
     return fail(SSM_ERR_INVALID_ARG, "ngroups %lld must be >= 1 and divide dim %lld",
                 (long long)ngroups, (long long)dim);
@@ -602,7 +601,7 @@ static ssm_status selective_state_update_impl(ssm_handle handle, float* state, c
   if (!B) return fail(SSM_ERR_INVALID_ARG, "B is NULL");
   if (!C) return fail(SSM_ERR_INVALID_ARG, "C is NULL");
   if (!y) return fail(SSM_ERR_INVALID_ARG, "y is NULL");
-  const uint64_t es = dtype_code(in_dtype) == SSM_BF16 ? 2 : 4;
+  const uint64_t es = in_dtype == SSM_BF16 ? 2 : 4;
   const uint64_t nrow = (uint64_t)batch * dim;
   const uint64_t nbc = (uint64_t)batch * ngroups * dstate;
   const Span in[] = {{"u", u, nrow * es},          {"delta", delta, nrow * es},
@@ -622,7 +621,7 @@ static ssm_status selective_state_update_impl(ssm_handle handle, float* state, c
   p.ngroups = (int)ngroups;
   DeviceGuard guard(handle->device);
   if (guard.failed()) return fail(SSM_ERR_HIP, "cannot select device %d", handle->device);
-  hipError_t e = ssm::launch_state_update(p, dtype_code(in_dtype) == SSM_BF16, stream);
+  hipError_t e = ssm::launch_state_update(p, in_dtype == SSM_BF16, stream);
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -713,9 +712,9 @@ ssm_status ssd_impl(ssm_handle handle, const void* x, const void* dt, const floa
   ssm_status st = ssm::ssd_validate_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                           chunk_size, &s, &g_last_error);
   if (st != SSM_OK) return st;
-  if (dtype_code(in_dtype) != SSM_BF16 && dtype_code(in_dtype) != SSM_F32)
-    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", dtype_code(in_dtype));
-  if (dtype_code(in_dtype) != SSM_BF16)
+  if (in_dtype != SSM_BF16 && in_dtype != SSM_F32)
+    return fail(SSM_ERR_INVALID_ARG, "unknown in_dtype %d", in_dtype);
+  if (in_dtype != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "ssd_chunk_scan_fwd supports bf16 inputs only");
   if (!x) return fail(SSM_ERR_INVALID_ARG, "x is NULL");
   if (!dt) return fail(SSM_ERR_INVALID_ARG, "dt is NULL");
